@@ -1,0 +1,200 @@
+#!/usr/bin/env python3
+"""Benchmark of the fp16 TN GEMM on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload lds_4096] [--algo auto]
+
+One step = one D = A B^T GEMM (the whole path: one kernel launch) over the
+synthetic 4096^3 workload (A (M,K), B (N,K) fp16 K-contiguous, uniform
+[-1,1), C absent, fp32 output), inputs resident in HBM before timing starts.
+Prints one JSON line: TFLOP/s over the timed steps (2MNK per step), the
+per-launch kernel time from HIP events on the launch stream, the roofline
+entry of the GEMM kernel (MFMA bound, dense fp16 peak of the chip), and the
+float64 CPU oracle timed on a bounded row sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_FP16_DENSE_TFLOPS = 2516.6   # 256 CU x 4 SIMD x 1024 FLOP/clk x 2.4 GHz
+METRIC = "TFLOP/s for fp16 TN GEMM at 4096³ (fp32 acc) and % of dense FP16 MFMA peak"
+KERNEL_SOURCES = ["mma_fragment_layouts_tn_amd/csrc/gemm_kernels.hip",
+                  "mma_fragment_layouts_tn_amd/csrc/gemm_tile.hpp",
+                  "mma_fragment_layouts_tn_amd/csrc/gemm_launch.hpp"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str, algo: str):
+    """HBM bytes per launch measured with rocprofv3 counters (committed under
+    profiles/), or None when absent or taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}_{algo}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, x, target_s: float):
+    """The float64 oracle, as it stands, on rows [0, r) of the workload."""
+    from oracle import gemm as G
+    cores = G.max_threads()
+    rows = 8
+    t0 = time.perf_counter()
+    G.gemm_f64(w.M, w.N, w.K, x.A, w.lda_, w.a_order == "m", x.B, w.ldb_, x.C, rows=(0, rows))
+    t_cal = time.perf_counter() - t0
+    rows = max(8, min(w.M, int(rows * target_s / max(t_cal, 1e-3))))
+    t0 = time.perf_counter()
+    G.gemm_f64(w.M, w.N, w.K, x.A, w.lda_, w.a_order == "m", x.B, w.ldb_, x.C, rows=(0, rows))
+    t = time.perf_counter() - t0
+    flops = 2.0 * rows * w.N * w.K
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"rows 0..{rows - 1} of the {w.M}x{w.N}x{w.K} GEMM "
+                      f"({flops / 1e9:.1f} GFLOP in {t:.2f} s, float64 triple loop incl. "
+                      f"fp16 decode)"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="lds_4096")
+    ap.add_argument("--algo", default="auto", choices=["auto", "direct", "lds128", "lds256"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB per step "
+                         "(calibration of the HBM byte counters)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE={world}); this GEMM build has no multi-GPU path.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import mma_fragment_layouts_tn_amd as mfl
+    import workloads as W
+
+    w = W.WORKLOADS[args.workload]
+    x = W.make_inputs(w)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    A = torch.from_numpy(x.A).to(dev)
+    B = torch.from_numpy(x.B).to(dev)
+    C = torch.from_numpy(x.C).to(dev) if x.C is not None else None
+    D = torch.empty((w.M, w.ldd_), dtype=torch.float16 if w.d == "f16" else torch.float32,
+                    device=dev)
+    ck = {None: mfl.NONE, "f16": mfl.F16, "f32": mfl.F32}[w.c]
+    dk = mfl.F16 if w.d == "f16" else mfl.F32
+    a_order = mfl.A_KMAJOR if w.a_order == "k" else mfl.A_MMAJOR
+    dt = mfl.dtypes(ck, dk, a_order, mfl.ALGOS[args.algo])
+    rc, algo = mfl.validate(w.M, w.N, w.K, A.data_ptr(), w.lda_, B.data_ptr(), w.ldb_,
+                            None if C is None else C.data_ptr(), w.ldc_, D.data_ptr(), w.ldd_, dt)
+    if rc != 0:
+        print(f"invalid arguments: {mfl.strerror(rc)}", file=sys.stderr)
+        return 1
+    algo_name = mfl.ALGO_NAMES[algo]
+    info = mfl.kernel_info(algo_name, ck, dk, a_order)
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+    cptr = None if C is None else C.data_ptr()
+    copy_src = copy_dst = None
+    if args.copy_mib:
+        copy_src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
+        copy_dst = torch.empty_like(copy_src)
+
+    def step():
+        r = mfl.gemm_tn_raw(w.M, w.N, w.K, A.data_ptr(), w.lda_, B.data_ptr(), w.ldb_, cptr,
+                            w.ldc_, D.data_ptr(), w.ldd_, dt, sptr)
+        if r != 0:
+            raise RuntimeError(mfl.strerror(r))
+        if copy_dst is not None:
+            copy_dst.copy_(copy_src)
+
+    print(f"[bench] {w.name} algo={algo_name} tile={info['bm']}x{info['bn']}x{info['bk']} "
+          f"warmup={args.warmup} steps={args.steps}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])   # ms
+    ms_per_step = wall * 1e3 / args.steps
+    flops = float(w.flops)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    kern_ms = float(per.mean())
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+    print(f"[bench] kernel ms: mean {kern_ms:.4f} median {np.median(per):.4f} "
+          f"min {per.min():.4f} p90 {np.percentile(per, 90):.4f}; wall/step {ms_per_step:.4f}",
+          file=sys.stderr, flush=True)
+
+    traffic = load_traffic(w.name, algo_name)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K,
+                   "a": "f16 K-contiguous" if w.a_order == "k" else f"f16 M-contiguous lda={w.lda_}",
+                   "b": "f16 K-contiguous", "c": w.c, "d": w.d, "accumulate": "f32",
+                   "algo": algo_name, "block_tile": f"{info['bm']}x{info['bn']}x{info['bk']}",
+                   "threads": info["threads"], "lds_bytes": info["lds_bytes"]},
+        "pct_of_peak": round(100.0 * value / PEAK_FP16_DENSE_TFLOPS, 2),
+        "kernel_ms": {"mean": round(kern_ms, 5), "median": round(float(np.median(per)), 5),
+                      "min": round(float(per.min()), 5),
+                      "p90": round(float(np.percentile(per, 90)), 5)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_FP16_DENSE_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_FP16_DENSE_TFLOPS, 4),
+                     "traffic": traffic},
+        "cpu_baseline": None,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    if args.copy_mib:
+        out["config"]["copy_mib_per_step"] = args.copy_mib
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a row sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

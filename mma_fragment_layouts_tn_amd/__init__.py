@@ -1,0 +1,269 @@
+"""Python binding of the MI355X fp16 TN GEMM library (libmfl_gemm.so).
+
+Argument marshalling only: every step of the GEMM runs in the HIP kernels
+behind the C ABI declared in include/mfl_gemm.h, include/mfl_layout.h and
+include/mfl_probe.h.  PyTorch provides device memory and the current stream.
+There is no fallback: if the library is missing, importing this package
+raises.
+
+D(m,n) = C(m,n) + sum_k A(m,k) * B(n,k); A (M,K), B (N,K) fp16, both
+K-contiguous (or A M-contiguous), C absent/fp16/fp32, D fp16/fp32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+# torch first: its HIP runtime (soname libamdhip64.so.7) must be the one the
+# library binds to, so device pointers and streams are shared.
+import torch  # noqa: E402
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmfl_gemm.so")
+
+NONE, F16, F32 = 0, 1, 2
+A_KMAJOR, A_MMAJOR = 0, 1
+ALGOS = {"auto": 0, "direct": 1, "lds128": 2, "lds256": 3}
+ALGO_NAMES = {v: k for k, v in ALGOS.items()}
+MFMA_OPS = {"f32_32x32x16_f16": 0, "f32_16x16x32_f16": 1, "f32_32x32x8_f16": 2,
+            "f32_16x16x16_f16": 3}
+
+ERRORS = {
+    0: "MFL_OK", -1: "MFL_E_NEGATIVE_DIM", -2: "MFL_E_LEADING_DIM", -3: "MFL_E_NULL_POINTER",
+    -4: "MFL_E_UNSUPPORTED", -5: "MFL_E_LAUNCH", -6: "MFL_E_ALGO_CASE",
+    -7: "MFL_E_MISALIGNED", -8: "MFL_E_ALIAS", -9: "MFL_E_TOO_LARGE",
+}
+
+
+class GemmDtypes(ctypes.Structure):
+    _fields_ = [("a", ctypes.c_int32), ("b", ctypes.c_int32), ("c", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("a_order", ctypes.c_int32), ("algo", ctypes.c_int32)]
+
+
+class MflError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{ERRORS.get(code, code)}: {msg}")
+        self.code = code
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python mma_fragment_layouts_tn_amd/_build.py` "
+            "(hipcc, gfx950).  There is no CPU fallback.")
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, i32, vp, cp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_char_p
+    P = ctypes.POINTER
+    lib.gemm_tn.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp, i64, GemmDtypes, vp]
+    lib.gemm_tn.restype = ctypes.c_int
+    lib.gemm_tn_validate.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp, i64,
+                                     GemmDtypes, P(i32)]
+    lib.gemm_tn_validate.restype = ctypes.c_int
+    lib.gemm_strerror.argtypes = [ctypes.c_int]
+    lib.gemm_strerror.restype = cp
+    lib.mfl_kernel_info.argtypes = [i32, GemmDtypes] + [P(i32)] * 6
+    lib.mfl_kernel_info.restype = ctypes.c_int
+    for name in ("mfl_layout_size", "mfl_layout_cosize"):
+        getattr(lib, name).argtypes = [cp, P(i64)]
+        getattr(lib, name).restype = ctypes.c_int
+    lib.mfl_layout_eval.argtypes = [cp, i64, P(i64)]
+    lib.mfl_layout_eval.restype = ctypes.c_int
+    lib.mfl_layout_table.argtypes = [cp, vp, i64]
+    lib.mfl_layout_table.restype = ctypes.c_int
+    for name in ("mfl_layout_coalesce", "mfl_layout_right_inverse"):
+        getattr(lib, name).argtypes = [cp, ctypes.c_char_p, i64]
+        getattr(lib, name).restype = ctypes.c_int
+    lib.mfl_layout_compose.argtypes = [cp, cp, ctypes.c_char_p, i64]
+    lib.mfl_layout_compose.restype = ctypes.c_int
+    lib.mfl_layout_mfma_tv.argtypes = [i32, i32, ctypes.c_char_p, i64]
+    lib.mfl_layout_mfma_tv.restype = ctypes.c_int
+    lib.mfl_fragment_coords.argtypes = [i32, i32, vp, i64, P(i32), P(i32)]
+    lib.mfl_fragment_coords.restype = ctypes.c_int
+    lib.mfl_probe_mfma.argtypes = [i32, vp, vp, vp, vp, vp]
+    lib.mfl_probe_mfma.restype = ctypes.c_int
+    return lib
+
+
+_lib = _load()
+lib = _lib
+
+
+def strerror(code: int) -> str:
+    return _lib.gemm_strerror(code).decode()
+
+
+def _check(code: int):
+    if code != 0:
+        raise MflError(code, strerror(code))
+
+
+def dtypes(c: int = NONE, d: int = F32, a_order: int = A_KMAJOR, algo: int = 0) -> GemmDtypes:
+    return GemmDtypes(F16, F16, c, d, a_order, algo)
+
+
+# ----------------------------------------------------------------- GEMM
+def gemm_tn_raw(M: int, N: int, K: int, A: int, lda: int, B: int, ldb: int, C: Optional[int],
+                ldc: int, D: int, ldd: int, dt: GemmDtypes, stream: int) -> int:
+    """Direct call of the C ABI with integer pointers; returns the code."""
+    return _lib.gemm_tn(M, N, K, A, lda, B, ldb, C, ldc, D, ldd, dt, stream)
+
+
+def validate(M, N, K, A, lda, B, ldb, C, ldc, D, ldd, dt: GemmDtypes) -> Tuple[int, int]:
+    """(code, algo AUTO would pick) without touching the GPU."""
+    algo = ctypes.c_int32(-1)
+    rc = _lib.gemm_tn_validate(M, N, K, A, lda, B, ldb, C, ldc, D, ldd, dt, ctypes.byref(algo))
+    return rc, algo.value
+
+
+def _kind(t: Optional[torch.Tensor]) -> int:
+    if t is None:
+        return NONE
+    if t.dtype == torch.float16:
+        return F16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def a_view_args(A: torch.Tensor):
+    """(a_order, lda) of a 2-D (M,K) fp16 tensor view."""
+    if A.dim() != 2:
+        raise ValueError("A must be 2-D (M,K)")
+    M, K = A.shape
+    if A.stride(1) == 1 and (M <= 1 or A.stride(0) >= max(K, 1)):
+        return A_KMAJOR, max(A.stride(0), max(K, 1))
+    if A.stride(0) == 1 and (K <= 1 or A.stride(1) >= max(M, 1)):
+        return A_MMAJOR, max(A.stride(1), max(M, 1))
+    raise ValueError("A must be K-contiguous or M-contiguous")
+
+
+def gemm_tn(A: torch.Tensor, B: torch.Tensor, C: Optional[torch.Tensor] = None,
+            out_dtype: torch.dtype = torch.float32, algo: str = "auto",
+            D: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """D = C + A @ B.T on the GPU.  A (M,K) fp16 K- or M-contiguous view,
+    B (N,K) fp16 K-contiguous, C (M,N) fp16/fp32 row-contiguous or None.
+    D is allocated (M,N) when not given."""
+    if A.dtype != torch.float16 or B.dtype != torch.float16:
+        raise TypeError("A and B must be float16")
+    if not (A.is_cuda and B.is_cuda):
+        raise ValueError("A and B must be device tensors (no CPU path)")
+    M, K = A.shape
+    N, K2 = B.shape
+    if K2 != K:
+        raise ValueError("A and B disagree on K")
+    a_order, lda = a_view_args(A)
+    if B.stride(1) != 1 and K > 1:
+        raise ValueError("B must be K-contiguous")
+    ldb = max(B.stride(0), max(K, 1)) if N > 1 else max(K, 1)
+    if C is not None:
+        if tuple(C.shape) != (M, N) or (C.stride(1) != 1 and N > 1):
+            raise ValueError("C must be (M,N) with contiguous rows")
+        ldc = max(C.stride(0), max(N, 1)) if M > 1 else max(N, 1)
+    else:
+        ldc = 0
+    if D is None:
+        D = torch.empty((M, N), dtype=out_dtype, device=A.device)
+    if tuple(D.shape) != (M, N) or (D.stride(1) != 1 and N > 1):
+        raise ValueError("D must be (M,N) with contiguous rows")
+    ldd = max(D.stride(0), max(N, 1)) if M > 1 else max(N, 1)
+    dt = dtypes(_kind(C), _kind(D), a_order, ALGOS[algo])
+    if stream is None:
+        stream = torch.cuda.current_stream(A.device).cuda_stream
+    rc = gemm_tn_raw(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb,
+                     None if C is None else C.data_ptr(), ldc, D.data_ptr(), ldd, dt, stream)
+    _check(rc)
+    return D
+
+
+def kernel_info(algo: str, c: int = NONE, d: int = F32, a_order: int = A_KMAJOR) -> dict:
+    vals = [ctypes.c_int32(-1) for _ in range(6)]
+    rc = _lib.mfl_kernel_info(ALGOS[algo], dtypes(c, d, a_order, ALGOS[algo]),
+                              *[ctypes.byref(v) for v in vals])
+    _check(rc)
+    keys = ("bm", "bn", "bk", "threads", "lds_bytes", "scratch_bytes")
+    return dict(zip(keys, (v.value for v in vals)))
+
+
+# --------------------------------------------------------------- layouts
+class LayoutError(ValueError):
+    pass
+
+
+def _lay_check(rc: int, what: str):
+    if rc != 0:
+        raise LayoutError(f"{what}: code {rc}")
+
+
+def layout_size(text: str) -> int:
+    out = ctypes.c_int64()
+    _lay_check(_lib.mfl_layout_size(text.encode(), ctypes.byref(out)), text)
+    return out.value
+
+
+def layout_cosize(text: str) -> int:
+    out = ctypes.c_int64()
+    _lay_check(_lib.mfl_layout_cosize(text.encode(), ctypes.byref(out)), text)
+    return out.value
+
+
+def layout_eval(text: str, idx: int) -> int:
+    out = ctypes.c_int64()
+    _lay_check(_lib.mfl_layout_eval(text.encode(), idx, ctypes.byref(out)), text)
+    return out.value
+
+
+def layout_table(text: str) -> np.ndarray:
+    n = layout_size(text)
+    out = np.empty(n, dtype=np.int64)
+    _lay_check(_lib.mfl_layout_table(text.encode(), out.ctypes.data, n), text)
+    return out
+
+
+def _text_op(fn, *args) -> str:
+    buf = ctypes.create_string_buffer(1024)
+    _lay_check(fn(*[a.encode() if isinstance(a, str) else a for a in args], buf, 1024),
+               str(args))
+    return buf.value.decode()
+
+
+def layout_coalesce(text: str) -> str:
+    return _text_op(_lib.mfl_layout_coalesce, text)
+
+
+def layout_compose(a: str, b: str) -> str:
+    return _text_op(_lib.mfl_layout_compose, a, b)
+
+
+def layout_right_inverse(text: str) -> str:
+    return _text_op(_lib.mfl_layout_right_inverse, text)
+
+
+def mfma_tv(op: str, operand: str) -> str:
+    return _text_op(_lib.mfl_layout_mfma_tv, MFMA_OPS[op], {"A": 0, "B": 1, "C": 2}[operand])
+
+
+def fragment_coords(algo: str, operand: str) -> np.ndarray:
+    """(threads, slots, 2) int32 array of the kernel's per-lane coordinates."""
+    opnd = {"A": 0, "B": 1, "C": 2}[operand]
+    t, s = ctypes.c_int32(), ctypes.c_int32()
+    _lay_check(_lib.mfl_fragment_coords(ALGOS[algo], opnd, None, 0, ctypes.byref(t),
+                                        ctypes.byref(s)), algo)
+    out = np.empty((t.value, s.value, 2), dtype=np.int32)
+    _lay_check(_lib.mfl_fragment_coords(ALGOS[algo], opnd, out.ctypes.data, out.size,
+                                        ctypes.byref(t), ctypes.byref(s)), algo)
+    return out
+
+
+# ----------------------------------------------------------------- probes
+def probe_mfma(op: str, a_slots: torch.Tensor, b_slots: torch.Tensor,
+               c_slots: torch.Tensor) -> torch.Tensor:
+    """Run one matrix instruction; slot tensors are device tensors (64, VA)
+    fp16 / (64, VC) fp32.  Returns the (64, VC) fp32 outputs."""
+    d = torch.empty_like(c_slots)
+    stream = torch.cuda.current_stream(c_slots.device).cuda_stream
+    rc = _lib.mfl_probe_mfma(MFMA_OPS[op], a_slots.data_ptr(), b_slots.data_ptr(),
+                             c_slots.data_ptr(), d.data_ptr(), stream)
+    _check(rc)
+    return d

@@ -1,0 +1,420 @@
+// C ABI: argument checks, kernel choice and launch for gemm_tn (mfl_gemm.h),
+// and the text interface of the layout module (mfl_layout.h).
+#include <hip/hip_runtime.h>
+#include <limits.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/mfl_gemm.h"
+#include "../../include/mfl_layout.h"
+#include "gemm_launch.hpp"
+#include "gemm_tile.hpp"
+#include "layout.hpp"
+#include "mfma_atoms.hpp"
+
+namespace {
+
+using mfl::GemmParams;
+
+bool dtype_ok_cd(int32_t c, int32_t d) {
+  return (c == MFL_NONE || c == MFL_F16 || c == MFL_F32) && (d == MFL_F16 || d == MFL_F32);
+}
+
+int64_t elem_size(int32_t t) { return t == MFL_F32 ? 4 : 2; }
+
+// Largest byte offset an operand's fetch can form, relative to its base:
+// rows x ld storage with `cols` valid elements in the last row.
+bool span_fits(int64_t rows, int64_t ld, int64_t cols) {
+  if (rows <= 0 || cols <= 0) return true;
+  const int64_t last = (rows - 1) * ld + cols;   // elements
+  return last * 2 < ((int64_t)1 << 31) - 64;
+}
+
+int pick_algo(int64_t M, int64_t N, int64_t K, bool a_mmajor) {
+  (void)K;
+  const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
+  if (t256 >= 192) return mfl::kAlgoLds256;
+  (void)a_mmajor;
+  return mfl::kAlgoLds128;
+}
+
+int check(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+          int64_t ldb, const void* C, int64_t ldc, const void* D, int64_t ldd,
+          gemm_dtypes_t dt, int32_t* algo_out) {
+  if (M < 0 || N < 0 || K < 0) return MFL_E_NEGATIVE_DIM;
+  if (dt.a != MFL_F16 || dt.b != MFL_F16 || !dtype_ok_cd(dt.c, dt.d)) return MFL_E_UNSUPPORTED;
+  if (dt.a_order != MFL_A_KMAJOR && dt.a_order != MFL_A_MMAJOR) return MFL_E_UNSUPPORTED;
+  if (dt.algo < 0 || dt.algo >= MFL_ALGO_COUNT) return MFL_E_UNSUPPORTED;
+  const bool mm = dt.a_order == MFL_A_MMAJOR;
+  const int64_t one = 1;
+  if (lda < (mm ? (M > one ? M : one) : (K > one ? K : one))) return MFL_E_LEADING_DIM;
+  if (ldb < (K > one ? K : one)) return MFL_E_LEADING_DIM;
+  if (dt.c != MFL_NONE && ldc < (N > one ? N : one)) return MFL_E_LEADING_DIM;
+  if (ldd < (N > one ? N : one)) return MFL_E_LEADING_DIM;
+  if ((dt.c == MFL_NONE) != (C == nullptr)) return MFL_E_NULL_POINTER;
+  if (M > 0 && N > 0) {
+    if (!D) return MFL_E_NULL_POINTER;
+    if (K > 0 && (!A || !B)) return MFL_E_NULL_POINTER;
+  }
+  if (((uintptr_t)A & 1) || ((uintptr_t)B & 1)) return MFL_E_MISALIGNED;
+  if (C && ((uintptr_t)C % (uintptr_t)elem_size(dt.c))) return MFL_E_MISALIGNED;
+  if (D && ((uintptr_t)D % (uintptr_t)elem_size(dt.d))) return MFL_E_MISALIGNED;
+  if (C && C == D && (ldc != ldd || dt.c != dt.d)) return MFL_E_ALIAS;
+  if (M > INT_MAX / 2 || N > INT_MAX / 2 || K > INT_MAX / 2 || lda > INT_MAX ||
+      ldb > INT_MAX || ldc > INT_MAX || ldd > INT_MAX)
+    return MFL_E_TOO_LARGE;
+  if (mm ? !span_fits(K, lda, M) : !span_fits(M, lda, K)) return MFL_E_TOO_LARGE;
+  if (!span_fits(N, ldb, K)) return MFL_E_TOO_LARGE;
+  int algo = dt.algo;
+  if (algo == MFL_ALGO_AUTO) algo = pick_algo(M, N, K, mm);
+  if (algo == MFL_ALGO_DIRECT && mm) return MFL_E_ALGO_CASE;
+  const mfl::KernelInfo ki = mfl::kernel_info(algo);
+  if (ki.algo < 0) return MFL_E_UNSUPPORTED;
+  const int64_t tiles = ((M + ki.bm - 1) / ki.bm) * ((N + ki.bn - 1) / ki.bn);
+  if (tiles > INT_MAX) return MFL_E_TOO_LARGE;
+  if (algo_out) *algo_out = algo;
+  return MFL_OK;
+}
+
+// ------------------------------------------------------- layout text form
+struct Parser {
+  const char* s;
+  int pos = 0;
+  bool ok = true;
+  void ws() {
+    while (s[pos] == ' ') ++pos;
+  }
+  bool number(int64_t& v) {
+    ws();
+    if (s[pos] == '_') ++pos;
+    bool neg = false;
+    if (s[pos] == '-') {
+      neg = true;
+      ++pos;
+    }
+    if (s[pos] < '0' || s[pos] > '9') return false;
+    int64_t x = 0;
+    while (s[pos] >= '0' && s[pos] <= '9') {
+      x = x * 10 + (s[pos] - '0');
+      if (x > ((int64_t)1 << 40)) return false;
+      ++pos;
+    }
+    v = neg ? -x : x;
+    return true;
+  }
+  // flatten everything below the top level into one list of leaves
+  bool leaves(int64_t* out, int& n, int cap) {
+    ws();
+    if (s[pos] == '(') {
+      ++pos;
+      for (;;) {
+        if (!leaves(out, n, cap)) return false;
+        ws();
+        if (s[pos] == ',') {
+          ++pos;
+          continue;
+        }
+        if (s[pos] == ')') {
+          ++pos;
+          return true;
+        }
+        return false;
+      }
+    }
+    int64_t v;
+    if (!number(v)) return false;
+    if (n >= cap) return false;
+    out[n++] = v;
+    return true;
+  }
+  // top level: list of modes, each a flat leaf list; mode_len[] sizes
+  bool top(int64_t* out, int& n, int* mode_len, int& nm) {
+    ws();
+    n = 0;
+    nm = 0;
+    if (s[pos] != '(') {
+      int before = n;
+      if (!leaves(out, n, mfl::kMaxLeaves)) return false;
+      mode_len[nm++] = n - before;
+      return true;
+    }
+    ++pos;
+    for (;;) {
+      if (nm >= mfl::kMaxModes) return false;
+      int before = n;
+      if (!leaves(out, n, mfl::kMaxLeaves)) return false;
+      mode_len[nm++] = n - before;
+      ws();
+      if (s[pos] == ',') {
+        ++pos;
+        continue;
+      }
+      if (s[pos] == ')') {
+        ++pos;
+        return true;
+      }
+      return false;
+    }
+  }
+};
+
+int parse_layout(const char* text, mfl::Layout& L) {
+  if (!text) return mfl::kLayoutBadText;
+  const char* colon = strchr(text, ':');
+  if (!colon) return mfl::kLayoutBadText;
+  std::string shape_txt(text, colon - text), stride_txt(colon + 1);
+  int64_t sh[mfl::kMaxLeaves], st[mfl::kMaxLeaves];
+  int nsh = 0, nst = 0, ml_sh[mfl::kMaxModes], ml_st[mfl::kMaxModes], nm_sh = 0, nm_st = 0;
+  Parser p1{shape_txt.c_str()}, p2{stride_txt.c_str()};
+  if (!p1.top(sh, nsh, ml_sh, nm_sh) || !p2.top(st, nst, ml_st, nm_st))
+    return mfl::kLayoutBadText;
+  p1.ws();
+  p2.ws();
+  if (p1.s[p1.pos] != 0 || p2.s[p2.pos] != 0) return mfl::kLayoutBadText;
+  if (nsh != nst || nm_sh != nm_st) return mfl::kLayoutBadText;
+  for (int m = 0; m < nm_sh; ++m)
+    if (ml_sh[m] != ml_st[m]) return mfl::kLayoutBadText;
+  L = mfl::Layout{};
+  int k = 0;
+  for (int m = 0; m < nm_sh; ++m) {
+    L.open_mode();
+    for (int i = 0; i < ml_sh[m]; ++i, ++k) {
+      if (sh[k] <= 0) return mfl::kLayoutBadText;
+      L.push_leaf(sh[k], st[k]);
+    }
+  }
+  return L.status;
+}
+
+std::string print_mode(const mfl::Layout& L, int m, bool strides) {
+  const int b = L.mode_begin(m), e = L.mode_end[m];
+  const int64_t* v = strides ? L.stride : L.shape;
+  if (e - b == 1) return std::to_string(v[b]);
+  std::string s = "(";
+  for (int i = b; i < e; ++i) {
+    if (i > b) s += ",";
+    s += std::to_string(v[i]);
+  }
+  return s + ")";
+}
+
+std::string print_layout(const mfl::Layout& L) {
+  auto part = [&](bool strides) {
+    if (L.nmodes == 1) return print_mode(L, 0, strides);
+    std::string s = "(";
+    for (int m = 0; m < L.nmodes; ++m) {
+      if (m) s += ",";
+      s += print_mode(L, m, strides);
+    }
+    return s + ")";
+  };
+  return part(false) + ":" + part(true);
+}
+
+int emit(const mfl::Layout& L, char* out, int64_t cap) {
+  if (L.status != mfl::kLayoutOk) return L.status;
+  const std::string s = print_layout(L);
+  if (!out || (int64_t)s.size() + 1 > cap) return mfl::kLayoutBadIndex;
+  memcpy(out, s.c_str(), s.size() + 1);
+  return 0;
+}
+
+template <class Cfg>
+int frag_coords(int operand, int32_t* out, int64_t cap, int32_t* threads, int32_t* slots) {
+  int ns = 0;
+  if (operand == 0) ns = Cfg::KSUB * Cfg::RM * 8;
+  else if (operand == 1) ns = Cfg::KSUB * Cfg::RN * 8;
+  else if (operand == 2) ns = Cfg::RM * Cfg::RN * 16;
+  else return mfl::kLayoutBadIndex;
+  if (threads) *threads = Cfg::kThreads;
+  if (slots) *slots = ns;
+  if (!out) return 0;
+  if ((int64_t)2 * Cfg::kThreads * ns > cap) return mfl::kLayoutBadIndex;
+  for (int t = 0; t < Cfg::kThreads; ++t) {
+    const int w = t / 64, lane = t % 64;
+    int s = 0;
+    auto put = [&](int a, int b) {
+      out[2 * ((int64_t)t * ns + s) + 0] = a;
+      out[2 * ((int64_t)t * ns + s) + 1] = b;
+      ++s;
+    };
+    if (operand == 2) {
+      for (int i = 0; i < Cfg::RM; ++i)
+        for (int j = 0; j < Cfg::RN; ++j)
+          for (int v = 0; v < 16; ++v) {
+            const mfl::RowK c = mfl::frag_c_coord<Cfg>(w, lane, i, j, v);
+            put(c.row, c.k);
+          }
+    } else {
+      const int R = operand == 0 ? Cfg::RM : Cfg::RN;
+      for (int kk = 0; kk < Cfg::KSUB; ++kk)
+        for (int i = 0; i < R; ++i)
+          for (int v = 0; v < 8; ++v) {
+            const mfl::RowK c = operand == 0 ? mfl::frag_a_coord<Cfg>(w, lane, i, kk)
+                                             : mfl::frag_b_coord<Cfg>(w, lane, i, kk);
+            put(c.row, c.k + v);
+          }
+    }
+  }
+  return 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_tn_validate(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                     const void* B, int64_t ldb, const void* C, int64_t ldc, const void* D,
+                     int64_t ldd, gemm_dtypes_t dtypes, int32_t* algo_out) {
+  return check(M, N, K, A, lda, B, ldb, C, ldc, D, ldd, dtypes, algo_out);
+}
+
+int gemm_tn(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+            int64_t ldb, const void* C, int64_t ldc, void* D, int64_t ldd,
+            gemm_dtypes_t dtypes, void* stream) {
+  int32_t algo = 0;
+  const int rc = check(M, N, K, A, lda, B, ldb, C, ldc, D, ldd, dtypes, &algo);
+  if (rc != MFL_OK) return rc;
+  if (M == 0 || N == 0) return MFL_OK;
+  const mfl::KernelInfo ki = mfl::kernel_info(algo);
+  GemmParams p{};
+  p.M = (int)M;
+  p.N = (int)N;
+  p.K = (int)K;
+  p.lda = (int)lda;
+  p.ldb = (int)ldb;
+  p.ldc = (int)(dtypes.c == MFL_NONE ? 0 : ldc);
+  p.ldd = (int)ldd;
+  p.tiles_m = (int)((M + ki.bm - 1) / ki.bm);
+  p.tiles_n = (int)((N + ki.bn - 1) / ki.bn);
+  p.group_m = algo == mfl::kAlgoLds256 ? 4 : 8;
+  p.A = A;
+  p.B = B;
+  p.C = C;
+  p.D = D;
+  const int lr = mfl::launch_gemm(algo, dtypes.a_order == MFL_A_MMAJOR, dtypes.c, dtypes.d, p,
+                                  (hipStream_t)stream);
+  return lr == 0 ? MFL_OK : (lr == -1 ? MFL_E_UNSUPPORTED : MFL_E_LAUNCH);
+}
+
+const char* gemm_strerror(int code) {
+  switch (code) {
+    case MFL_OK: return "ok";
+    case MFL_E_NEGATIVE_DIM: return "negative dimension";
+    case MFL_E_LEADING_DIM: return "leading dimension too small";
+    case MFL_E_NULL_POINTER: return "null pointer (or C pointer inconsistent with its dtype)";
+    case MFL_E_UNSUPPORTED: return "unsupported dtype, A order or algorithm";
+    case MFL_E_LAUNCH: return "HIP kernel launch failed";
+    case MFL_E_ALGO_CASE: return "the forced algorithm cannot run this case";
+    case MFL_E_MISALIGNED: return "pointer not aligned to its element size";
+    case MFL_E_ALIAS: return "D aliases C with a different leading dimension or dtype";
+    case MFL_E_TOO_LARGE: return "size beyond the supported index range";
+    default: return "unknown error code";
+  }
+}
+
+int mfl_kernel_info(int32_t algo, gemm_dtypes_t dt, int32_t* bm, int32_t* bn, int32_t* bk,
+                    int32_t* threads, int32_t* lds_bytes, int32_t* vgprs_spilled) {
+  const mfl::KernelInfo ki = mfl::kernel_info(algo);
+  if (ki.algo < 0 || !dtype_ok_cd(dt.c, dt.d)) return MFL_E_UNSUPPORTED;
+  if (bm) *bm = ki.bm;
+  if (bn) *bn = ki.bn;
+  if (bk) *bk = ki.bk;
+  if (threads) *threads = ki.threads;
+  const void* fn = mfl::kernel_symbol(algo, dt.a_order == MFL_A_MMAJOR, dt.c, dt.d);
+  if (!fn) return MFL_E_ALGO_CASE;
+  if (lds_bytes || vgprs_spilled) {
+    hipFuncAttributes attr{};
+    if (hipFuncGetAttributes(&attr, fn) != hipSuccess) return MFL_E_LAUNCH;
+    if (lds_bytes) *lds_bytes = (int32_t)attr.sharedSizeBytes;
+    if (vgprs_spilled) *vgprs_spilled = (int32_t)attr.localSizeBytes;
+  }
+  return MFL_OK;
+}
+
+// ------------------------------------------------------------ layout C ABI
+int mfl_layout_size(const char* layout, int64_t* out) {
+  mfl::Layout L;
+  const int rc = parse_layout(layout, L);
+  if (rc) return rc;
+  if (out) *out = mfl::size(L);
+  return 0;
+}
+
+int mfl_layout_cosize(const char* layout, int64_t* out) {
+  mfl::Layout L;
+  const int rc = parse_layout(layout, L);
+  if (rc) return rc;
+  for (int i = 0; i < L.nleaves; ++i)
+    if (L.stride[i] < 0) return mfl::kLayoutNegativeStride;
+  if (out) *out = mfl::cosize(L);
+  return 0;
+}
+
+int mfl_layout_eval(const char* layout, int64_t idx, int64_t* out) {
+  mfl::Layout L;
+  const int rc = parse_layout(layout, L);
+  if (rc) return rc;
+  if (idx < 0 || idx >= mfl::size(L)) return mfl::kLayoutBadIndex;
+  if (out) *out = mfl::eval(L, idx);
+  return 0;
+}
+
+int mfl_layout_table(const char* layout, int64_t* out, int64_t cap) {
+  mfl::Layout L;
+  const int rc = parse_layout(layout, L);
+  if (rc) return rc;
+  const int64_t n = mfl::size(L);
+  if (!out || n > cap) return mfl::kLayoutBadIndex;
+  for (int64_t i = 0; i < n; ++i) out[i] = mfl::eval(L, i);
+  return 0;
+}
+
+int mfl_layout_coalesce(const char* layout, char* out, int64_t cap) {
+  mfl::Layout L;
+  const int rc = parse_layout(layout, L);
+  if (rc) return rc;
+  return emit(mfl::coalesce(L), out, cap);
+}
+
+int mfl_layout_compose(const char* a, const char* b, char* out, int64_t cap) {
+  mfl::Layout A, B;
+  int rc = parse_layout(a, A);
+  if (rc) return rc;
+  rc = parse_layout(b, B);
+  if (rc) return rc;
+  const mfl::Layout AB = mfl::compose(A, B);
+  if (AB.status != mfl::kLayoutOk) return AB.status;
+  // reject inputs whose leaves interact (the result would not be A o B)
+  if (mfl::size(B) > ((int64_t)1 << 22) || !mfl::compose_is_exact(A, B, AB))
+    return mfl::kLayoutNotComposable;
+  return emit(AB, out, cap);
+}
+
+int mfl_layout_right_inverse(const char* layout, char* out, int64_t cap) {
+  mfl::Layout L;
+  const int rc = parse_layout(layout, L);
+  if (rc) return rc;
+  return emit(mfl::right_inverse(L), out, cap);
+}
+
+int mfl_layout_mfma_tv(int32_t op, int32_t operand, char* out, int64_t cap) {
+  if (op < 0 || op >= mfl::kMfmaOpCount || operand < 0 || operand > 2)
+    return mfl::kLayoutBadIndex;
+  return emit(mfl::mfma_tv(op, operand), out, cap);
+}
+
+int mfl_fragment_coords(int32_t algo, int32_t operand, int32_t* out, int64_t cap,
+                        int32_t* threads, int32_t* slots) {
+  switch (algo) {
+    case mfl::kAlgoDirect: return frag_coords<mfl::CfgDirect>(operand, out, cap, threads, slots);
+    case mfl::kAlgoLds128: return frag_coords<mfl::CfgLds128>(operand, out, cap, threads, slots);
+    case mfl::kAlgoLds256: return frag_coords<mfl::CfgLds256>(operand, out, cap, threads, slots);
+    default: return mfl::kLayoutBadIndex;
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,43 @@
+// Kernel registry shared by the C ABI (host) and the kernel file.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gemm_tile.hpp"
+
+namespace mfl {
+
+// Kernel arguments (passed by value).  Offsets inside A and B are 32-bit
+// byte offsets, so each operand's span must stay below 2^31 bytes (checked
+// by the C ABI before launch).
+struct GemmParams {
+  int M, N, K;
+  int lda, ldb, ldc, ldd;
+  int tiles_m, tiles_n, group_m;
+  const void* A;
+  const void* B;
+  const void* C;
+  void* D;
+};
+
+enum Algo : int { kAlgoAuto = 0, kAlgoDirect = 1, kAlgoLds128 = 2, kAlgoLds256 = 3, kAlgoCount = 4 };
+
+// direct-from-global: 128x128 block (the simple-GEMM page's CTA tile), 2x2 waves
+using CfgDirect = TileCfg<128, 128, 32, 2, 2>;
+// LDS-staged 128x128x32 block tile, 2x2 waves of 64x64
+using CfgLds128 = TileCfg<128, 128, 32, 2, 2>;
+// LDS-staged 256x256x64 block tile, 2x2 waves of 128x128
+using CfgLds256 = TileCfg<256, 256, 64, 2, 2>;
+
+struct KernelInfo {
+  int algo, bm, bn, bk, threads;
+};
+
+KernelInfo kernel_info(int algo);
+const void* kernel_symbol(int algo, bool a_mmajor, int c_kind, int d_kind);
+// 0 ok, -1 no such kernel, -2 launch error
+int launch_gemm(int algo, bool a_mmajor, int c_kind, int d_kind, const GemmParams& p,
+                hipStream_t stream);
+
+}  // namespace mfl

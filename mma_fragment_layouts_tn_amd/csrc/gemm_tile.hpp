@@ -1,0 +1,144 @@
+// Tile configurations and per-lane index maps shared by the kernels and the
+// host-side fragment-coordinate export (the same functions run in both).
+//
+// Structure (pages' prior art, redone for wave64 + MFMA):
+//  * a workgroup owns a BM x BN block of D and walks K in BK steps, the CTA
+//    tiling of "CuTe Layout 到 Tensor Core" §4 (local_tile with cta_tiler
+//    (128,128,32)) and of the simple-GEMM page ("cute(7) simple_gemm" §3.1);
+//  * the workgroup's waves are arranged WAVES_M x WAVES_N, wave id
+//    w = wm + WAVES_M*wn (M fastest, the compact arrangement of the TiledMMA
+//    page, section "第二个参数怎样把一个 warp 扩展成四个");
+//  * each wave repeats the MFMA atom RM x RN times over its WTM x WTN tile
+//    and KSUB times along BK (the repeat modes of the TiledMMA page, section
+//    "输入扩大以后，后两个 mode 怎样工作", and the register reuse of the
+//    simple-GEMM page §2.4);
+//  * operand (row, k) of lane/value comes from the atom's TV layout
+//    (mfma_atoms.hpp), composed with the LDS tile layout below, the role the
+//    route page ("ldmatrix 怎样对上 MMA 的寄存器") gives F o right_inverse(R)
+//    o S.  On gfx950 one 16-byte LDS read fills a whole operand, so the copy
+//    needs no regrouping (retile is the identity).
+//
+// LDS tile layout: rows of BK halves, K contiguous, split into 16-byte chunks
+// (8 halves); chunk c of row r is stored at chunk c ^ swz(r).  The XOR keeps
+// the 16-byte reads of consecutive rows on distinct banks.  The pages name
+// swizzling as an option without giving a function ("CuTe Layout 到 Tensor
+// Core" §5); this one is our own.
+#pragma once
+
+#include "layout.hpp"
+#include "mfma_atoms.hpp"
+
+namespace mfl {
+
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_>
+struct TileCfg {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_;
+  static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+  static constexpr int kWaves = WAVES_M * WAVES_N;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
+  static constexpr int kAtomM = 32, kAtomN = 32, kAtomK = 16;   // 32x32x16 f16
+  static constexpr int RM = WTM / kAtomM, RN = WTN / kAtomN;
+  static constexpr int KSUB = BK / kAtomK;
+  static constexpr int CH = BK / 8;               // 16-byte chunks per LDS row
+  static constexpr int kLdsA = BM * BK;           // halves per stage
+  static constexpr int kLdsB = BN * BK;
+
+  static_assert(BM % (WAVES_M * kAtomM) == 0 && BN % (WAVES_N * kAtomN) == 0,
+                "wave tile must be a multiple of the atom");
+  static_assert(BK % kAtomK == 0, "BK must be a multiple of the atom K");
+  static_assert((BM * CH) % kThreads == 0 && (BN * CH) % kThreads == 0,
+                "operand tile chunks must divide evenly over the threads");
+  static_assert(CH == 4 || CH == 8, "swizzle defined for 4 or 8 chunks per row");
+};
+
+// XOR swizzle of the 16-byte chunk index within an LDS row
+template <int CH>
+MFL_HD constexpr int swz(int row) {
+  return CH == 8 ? (row & 7) : ((row >> 1) & 3);
+}
+
+// element offset (in halves) of (row, k) in one LDS operand tile
+template <int BK>
+MFL_HD constexpr int lds_offset(int row, int k) {
+  constexpr int CH = BK / 8;
+  return row * BK + (((k >> 3) ^ swz<CH>(row)) << 3) + (k & 7);
+}
+
+// Atom TV layouts of the instruction the kernels issue.
+MFL_HD constexpr Layout atom_ab_tv() { return mfma_tv(kMfma32x32x16, 0); }
+MFL_HD constexpr Layout atom_c_tv() { return mfma_tv(kMfma32x32x16, 2); }
+
+struct RowK {
+  int row, k;
+};
+
+// Operand value 0 of `lane`: (row within atom, k within atom); values 1..7
+// follow at k+1..k+7 (the value mode of the layout has stride ROWS, i.e. unit
+// step in k).
+MFL_HD constexpr RowK atom_ab_coord(int lane) {
+  const Layout tv = atom_ab_tv();
+  const int64_t q = eval2(tv, lane, 0);
+  return RowK{int(q % 32), int(q / 32)};
+}
+
+// Accumulator value v of `lane`: (m, n) within the 32x32 atom block.
+MFL_HD constexpr RowK atom_c_coord(int lane, int v) {
+  const Layout tv = atom_c_tv();
+  const int64_t q = eval2(tv, lane, v);
+  return RowK{int(q % 32), int(q / 32)};
+}
+
+// The value mode must step k by one, so 8 values are one 16-byte run.
+static_assert(eval2(atom_ab_tv(), 0, 1) - eval2(atom_ab_tv(), 0, 0) == 32,
+              "operand values must be K-contiguous");
+static_assert(size(atom_ab_tv()) == 32 * 16 && size(atom_c_tv()) == 32 * 32,
+              "atom layouts must cover the atom");
+
+// Operand fragment of wave `w`, repeat i (along M or N), K sub-step kk:
+// (row, k) of value 0 within the workgroup tile.
+template <class Cfg>
+MFL_HD constexpr RowK frag_a_coord(int w, int lane, int i, int kk) {
+  const RowK a = atom_ab_coord(lane);
+  const int wm = w % Cfg::WAVES_M;
+  return RowK{wm * Cfg::WTM + i * Cfg::kAtomM + a.row, kk * Cfg::kAtomK + a.k};
+}
+
+template <class Cfg>
+MFL_HD constexpr RowK frag_b_coord(int w, int lane, int j, int kk) {
+  const RowK b = atom_ab_coord(lane);
+  const int wn = w / Cfg::WAVES_M;
+  return RowK{wn * Cfg::WTN + j * Cfg::kAtomN + b.row, kk * Cfg::kAtomK + b.k};
+}
+
+template <class Cfg>
+MFL_HD constexpr RowK frag_c_coord(int w, int lane, int i, int j, int v) {
+  const RowK c = atom_c_coord(lane, v);
+  const int wm = w % Cfg::WAVES_M, wn = w / Cfg::WAVES_M;
+  return RowK{wm * Cfg::WTM + i * Cfg::kAtomM + c.row,
+              wn * Cfg::WTN + j * Cfg::kAtomN + c.k};
+}
+
+// Workgroup -> output tile.  Workgroups are handed to the 8 XCDs round-robin
+// (XCD = id % 8); regrouping ids so each XCD gets a contiguous run, then
+// walking that run in GROUP_M-tall column bands, keeps the A rows and B
+// columns one XCD touches together in its L2.
+struct TileIndex {
+  int tm, tn;
+};
+
+MFL_HD constexpr TileIndex tile_of_block(int bid, int nb, int tiles_m, int tiles_n,
+                                         int group_m) {
+  constexpr int kXcds = 8;
+  const int q = nb / kXcds, r = nb % kXcds;
+  const int xcd = bid % kXcds, idx = bid / kXcds;
+  const int lin = xcd * q + (xcd < r ? xcd : r) + idx;
+  const int band = group_m * tiles_n;
+  const int g = lin / band;
+  const int first_m = g * group_m;
+  const int gm = (tiles_m - first_m) < group_m ? (tiles_m - first_m) : group_m;
+  const int in = lin - g * band;
+  return TileIndex{first_m + in % gm, in / gm};
+}
+
+}  // namespace mfl

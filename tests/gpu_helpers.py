@@ -1,0 +1,139 @@
+"""Shared helpers for the GPU tests: guarded device buffers, one GEMM call
+through the C ABI, and the oracle comparison."""
+import sys
+
+import numpy as np
+import torch
+
+import mma_fragment_layouts_tn_amd as mfl
+import workloads as W
+from oracle import compare
+from oracle import gemm as G
+
+GUARD = 64
+CANARY16 = 0x7E5A          # an fp16 NaN pattern
+CANARY32 = 0x7FC0DEAD      # an fp32 NaN pattern
+
+
+def say(*args):
+    print(*args, flush=True)
+    sys.stdout.flush()
+
+
+class Guarded:
+    """Device copy of a host buffer followed by GUARD canary elements."""
+
+    def __init__(self, host: np.ndarray, dev="cuda"):
+        flat = np.ascontiguousarray(host).reshape(-1)
+        self.n = flat.size
+        if flat.dtype.itemsize == 2:
+            bits = flat.view(np.int16)
+            t = torch.full((self.n + GUARD,), CANARY16 - (1 << 16) if CANARY16 >= 1 << 15 else CANARY16,
+                           dtype=torch.int16)
+        else:
+            bits = flat.view(np.int32)
+            t = torch.full((self.n + GUARD,), CANARY32 - (1 << 32), dtype=torch.int32)
+        t[: self.n] = torch.from_numpy(bits.copy())
+        self.host_bits = t.clone()
+        self.t = t.to(dev)
+
+    @property
+    def ptr(self):
+        return self.t.data_ptr()
+
+    def guard_intact(self):
+        return torch.equal(self.t[self.n:].cpu(), self.host_bits[self.n:])
+
+    def unchanged(self):
+        return torch.equal(self.t.cpu(), self.host_bits)
+
+
+def out_buffer(M, ldd, d, dev="cuda"):
+    n = M * ldd
+    if d == "f16":
+        t = torch.full((n + GUARD,), CANARY16 - (1 << 16), dtype=torch.int16, device=dev)
+    else:
+        t = torch.full((n + GUARD,), CANARY32 - (1 << 32), dtype=torch.int32, device=dev)
+    return t
+
+
+def run_gemm(w: W.Workload, x: W.Inputs, algo: str, in_place: bool = False):
+    """Upload, call gemm_tn through the C ABI, download.  Returns
+    (D as float64 (M,N) array, raw output bits, checks dict)."""
+    say(f"[gpu] {w.name} algo={algo} M={w.M} N={w.N} K={w.K} a={w.a_order} "
+        f"c={w.c} d={w.d} int={x.integer}")
+    A = Guarded(x.A)
+    B = Guarded(x.B)
+    C = Guarded(x.C) if x.C is not None else None
+    ldd = w.ldd_
+    if in_place:
+        assert C is not None and w.c == w.d and w.ldc_ == ldd
+        Dt = C.t
+    else:
+        Dt = out_buffer(w.M, ldd, w.d)
+    ckind = {None: mfl.NONE, "f16": mfl.F16, "f32": mfl.F32}[w.c]
+    dkind = {"f16": mfl.F16, "f32": mfl.F32}[w.d]
+    a_order = mfl.A_KMAJOR if w.a_order == "k" else mfl.A_MMAJOR
+    dt = mfl.dtypes(ckind, dkind, a_order, mfl.ALGOS[algo])
+    stream = torch.cuda.current_stream().cuda_stream
+    rc = mfl.gemm_tn_raw(w.M, w.N, w.K, A.ptr, w.lda_, B.ptr, w.ldb_,
+                         None if C is None else C.ptr, w.ldc_ if C is not None else 0,
+                         Dt.data_ptr(), ldd, dt, stream)
+    assert rc == 0, (rc, mfl.strerror(rc))
+    torch.cuda.synchronize()
+    raw = Dt.cpu().numpy()
+    n = w.M * ldd
+    if w.d == "f16":
+        D = raw[:n].view(np.float16).reshape(w.M, ldd)[:, : w.N].astype(np.float64)
+        guard_ok = (raw[n:] == np.int16(CANARY16 - (1 << 16))).all()
+        pad_ok = (raw[:n].reshape(w.M, ldd)[:, w.N:] == np.int16(CANARY16 - (1 << 16))).all()
+    else:
+        D = raw[:n].view(np.float32).reshape(w.M, ldd)[:, : w.N].astype(np.float64)
+        guard_ok = (raw[n:] == np.int32(CANARY32 - (1 << 32))).all()
+        pad_ok = (raw[:n].reshape(w.M, ldd)[:, w.N:] == np.int32(CANARY32 - (1 << 32))).all()
+    checks = {"A_unchanged": A.unchanged(), "B_unchanged": B.unchanged(),
+              "C_unchanged": (C is None or in_place or C.unchanged()),
+              "D_guard": bool(guard_ok), "D_padding": bool(pad_ok)}
+    if in_place:
+        checks["C_guard"] = C.guard_intact()
+        checks["D_guard"] = checks["C_guard"]
+    return D, checks
+
+
+def oracle_full(w: W.Workload, x: W.Inputs):
+    return G.gemm_f64(w.M, w.N, w.K, x.A, w.lda_, w.a_order == "m", x.B, w.ldb_, x.C)
+
+
+def oracle_sampled(w: W.Workload, x: W.Inputs, ms, ns):
+    return G.gemm_f64_sampled(w.M, w.N, w.K, x.A, w.lda_, w.a_order == "m", x.B, w.ldb_,
+                              x.C, ms, ns)
+
+
+def verdict(D, ref, w: W.Workload, integer: bool):
+    return compare.check(D, ref, w.d, w.K, integer)
+
+
+def freivalds_exact(D, w: W.Workload, x: W.Inputs, trials=2, seed=0):
+    """Full-matrix check for integer-valued inputs with exact fp32 output:
+    D x == C x + A (B^T x) in int64 for random x (any wrong element of D
+    changes D x)."""
+    rng = np.random.default_rng(seed)
+    M, N, K = w.M, w.N, w.K
+    Di = D.astype(np.int64)
+    if not np.array_equal(Di.astype(np.float64), D):
+        return False
+    if w.a_order == "k":
+        Ai = x.A[:, :K].astype(np.int64)
+    else:
+        Ai = x.A[:, :M].astype(np.int64).T
+    Bi = x.B[:, :K].astype(np.int64)
+    Ci = x.C[:, :N].astype(np.int64) if x.C is not None else None
+    for _ in range(trials):
+        v = rng.integers(1, 1 << 20, size=N, dtype=np.int64)
+        lhs = Di @ v
+        rhs = Ai @ (Bi.T @ v)
+        if Ci is not None:
+            rhs = rhs + Ci @ v
+        if not np.array_equal(lhs, rhs):
+            return False
+    return True

@@ -1,0 +1,95 @@
+"""The C ABI without a GPU: every declared symbol is exported, and the
+argument checks return the documented codes (gemm_tn_validate runs the same
+checks gemm_tn runs before launching)."""
+import glob
+import os
+import re
+import subprocess
+
+import pytest
+
+import mma_fragment_layouts_tn_amd as mfl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+P = 0x10000          # a fake, aligned device address (never dereferenced)
+
+
+def _declared():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^\s*(?:int|const char\*|void)\s+(\w+)\s*\(", text, flags=re.M):
+            names.add(m.group(1))
+    return names
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert {"gemm_tn", "gemm_tn_validate", "gemm_strerror", "mfl_layout_compose",
+            "mfl_probe_mfma"} <= names
+    out = subprocess.run(["nm", "-D", "--defined-only", mfl.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    missing = names - exported
+    assert not missing, missing
+    for n in names:
+        assert hasattr(mfl.lib, n)
+
+
+def _v(M=64, N=64, K=64, A=P, lda=None, B=P, ldb=None, C=None, ldc=0, D=P, ldd=None, **kw):
+    dt = mfl.dtypes(**kw)
+    lda = lda if lda is not None else (K if dt.a_order == mfl.A_KMAJOR else M)
+    ldb = ldb if ldb is not None else K
+    ldd = ldd if ldd is not None else N
+    return mfl.validate(M, N, K, A, lda, B, ldb, C, ldc, D, ldd, dt)
+
+
+def test_valid_cases():
+    assert _v()[0] == 0
+    assert _v(c=mfl.F32, C=P + 0x100000, ldc=64)[0] == 0
+    assert _v(a_order=mfl.A_MMAJOR, lda=72)[0] == 0
+    assert _v(M=8191, N=6143, K=4097, c=mfl.F16, d=mfl.F16, C=P, ldc=6143)[0] == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(M=-1), -1), (dict(K=-5), -1),
+    (dict(lda=63), -2), (dict(ldb=10), -2), (dict(ldd=63), -2),
+    (dict(c=mfl.F16, C=P, ldc=63), -2),
+    (dict(a_order=mfl.A_MMAJOR, lda=63), -2),
+    (dict(A=0), -3), (dict(B=0), -3), (dict(D=0), -3),
+    (dict(c=mfl.F32, ldc=64), -3), (dict(C=P + 4096, ldc=64), -3),
+    (dict(d=mfl.NONE), -4), (dict(c=7, C=P, ldc=64), -4), (dict(a_order=2), -4),
+    (dict(algo=9), -4),
+    (dict(a_order=mfl.A_MMAJOR, algo=1), -6),
+    (dict(A=P + 1), -7), (dict(d=mfl.F32, D=P + 2), -7),
+    (dict(c=mfl.F16, C=P, ldc=64, d=mfl.F32, D=P), -8),
+    (dict(c=mfl.F32, C=P, ldc=128, d=mfl.F32, D=P, ldd=64), -8),
+    (dict(M=1 << 20, K=1 << 11, lda=1 << 11), -9),
+])
+def test_error_codes(kw, code):
+    assert _v(**kw)[0] == code
+    assert mfl.strerror(code) not in ("", "unknown error code")
+
+
+def test_in_place_accumulate_allowed():
+    assert _v(c=mfl.F32, C=P, ldc=64, d=mfl.F32, D=P)[0] == 0
+
+
+def test_degenerate_sizes_are_ok():
+    assert _v(M=0)[0] == 0
+    assert _v(N=0, D=0, ldd=1)[0] == 0
+    assert _v(K=0, A=0, B=0, lda=1, ldb=1)[0] == 0
+
+
+def test_auto_choice():
+    assert _v(M=4096, N=4096, K=4096)[1] == mfl.ALGOS["lds256"]
+    assert _v(M=256, N=256, K=256)[1] == mfl.ALGOS["lds128"]
+    assert _v(M=32, N=16, K=16, algo=1)[1] == mfl.ALGOS["direct"]
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    a = torch.zeros(4, 4, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        mfl.gemm_tn(a, a)

@@ -1,0 +1,140 @@
+"""GEMM parity on the GPU: the HIP path (through the C ABI) against the
+float64 oracle.
+
+* small and ragged shapes: every element, integer inputs bit-exact and float
+  inputs within tolerance, for every kernel and dtype combination;
+* the five named workloads at full size, in the launch configuration the
+  benchmark times: sampled outputs (corners, tile seams, random positions)
+  computed one by one by the oracle, plus, for integer inputs with fp32
+  output, a Freivalds check of the whole matrix in exact integer arithmetic;
+* guard canaries after every buffer and untouched padding."""
+import math
+
+import numpy as np
+import pytest
+
+import mma_fragment_layouts_tn_amd as mfl
+import workloads as W
+from gpu_helpers import (freivalds_exact, oracle_full, oracle_sampled, run_gemm, say,
+                         verdict)
+
+pytestmark = pytest.mark.gpu
+
+ALGOS = ["direct", "lds128", "lds256"]
+
+
+def _assert_checks(checks):
+    assert all(checks.values()), checks
+
+
+# ------------------------------------------------------------ small shapes
+SMALL = [(1, 1, 1), (5, 7, 3), (32, 16, 16), (33, 17, 9), (64, 64, 64), (127, 129, 31),
+         (130, 260, 65), (257, 255, 97), (300, 70, 200), (129, 383, 8), (16, 300, 47)]
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("shape", SMALL)
+def test_small_integer_bit_exact(algo, shape):
+    M, N, K = shape
+    for c, d in ((None, "f32"), ("f16", "f16"), ("f32", "f32"), (None, "f16"), ("f32", "f16")):
+        w = W.custom(M, N, K, c=c, d=d, dist="int", seed=M * 7 + N * 3 + K, lda=K + 3,
+                     ldb=K + 1)
+        x = W.make_inputs(w)
+        D, checks = run_gemm(w, x, algo)
+        _assert_checks(checks)
+        v = verdict(D, oracle_full(w, x), w, True)
+        assert v.ok, (w.name, c, d, str(v))
+
+
+@pytest.mark.parametrize("algo", ["lds128", "lds256"])
+@pytest.mark.parametrize("shape", [(40, 24, 33), (130, 260, 65), (257, 129, 100), (8, 9, 10)])
+def test_mmajor_a_bit_exact(algo, shape):
+    M, N, K = shape
+    for c, d in ((None, "f32"), ("f32", "f32"), ("f16", "f16")):
+        w = W.custom(M, N, K, a_order="m", lda=M + 8, c=c, d=d, dist="int", seed=M + N + K)
+        x = W.make_inputs(w)
+        D, checks = run_gemm(w, x, algo)
+        _assert_checks(checks)
+        v = verdict(D, oracle_full(w, x), w, True)
+        assert v.ok, (w.name, c, d, str(v))
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+def test_float_inputs_within_tolerance(algo):
+    for (M, N, K, c, d) in ((513, 384, 300, None, "f32"), (300, 517, 1000, "f16", "f16"),
+                            (256, 256, 256, "f32", "f32")):
+        w = W.custom(M, N, K, c=c, d=d, dist="unif", seed=M + K)
+        x = W.make_inputs(w)
+        D, checks = run_gemm(w, x, algo)
+        _assert_checks(checks)
+        v = verdict(D, oracle_full(w, x), w, False)
+        assert v.ok, (w.name, str(v))
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+def test_k_zero_gives_c(algo):
+    w = W.custom(70, 50, 0, c="f32", d="f32", dist="int", seed=3, lda=1, ldb=1)
+    x = W.make_inputs(w)
+    D, checks = run_gemm(w, x, algo)
+    _assert_checks(checks)
+    assert np.array_equal(D, x.C.astype(np.float64))
+
+
+def test_in_place_accumulate():
+    w = W.custom(200, 136, 72, c="f32", d="f32", dist="int", seed=9)
+    x = W.make_inputs(w)
+    ref = oracle_full(w, x)
+    D, checks = run_gemm(w, x, "lds128", in_place=True)
+    _assert_checks(checks)
+    assert verdict(D, ref, w, True).ok
+
+
+def test_kernel_properties():
+    info = mfl.kernel_info("direct")
+    assert info["lds_bytes"] == 0          # the direct kernel uses no LDS
+    assert mfl.kernel_info("lds128")["lds_bytes"] == 2 * (128 + 128) * 32 * 2
+    assert mfl.kernel_info("lds256")["lds_bytes"] == 2 * (256 + 256) * 64 * 2
+    say("[gpu] kernel info", {a: mfl.kernel_info(a) for a in ALGOS})
+
+
+# --------------------------------------------------------- named workloads
+NAMED = [
+    ("tiny_32x16x16", ["direct", "lds128", "lds256"], False),
+    ("direct_256", ["direct"], True),
+    ("lds_4096", ["lds128", "lds256"], True),
+    ("accum_mmajor_8192x8192x2048", ["auto"], True),
+    ("ragged_8191x6143x4097", ["auto", "lds128"], True),
+]
+
+
+def _named_cases():
+    for name, algos, twin in NAMED:
+        for algo in algos:
+            yield pytest.param(name, algo, False, id=f"{name}-{algo}")
+            if twin:
+                yield pytest.param(name, algo, True, id=f"{name}-{algo}-int")
+
+
+@pytest.mark.parametrize("name,algo,integer", list(_named_cases()))
+def test_named_workload(name, algo, integer):
+    w = W.WORKLOADS[name]
+    if integer:
+        w = w.twin()
+    x = W.make_inputs(w)
+    D, checks = run_gemm(w, x, algo)
+    _assert_checks(checks)
+    assert np.isfinite(D).all()
+    small = w.M * w.N * w.K <= 1 << 26
+    if small:
+        ref = oracle_full(w, x)
+        v = verdict(D, ref, w, x.integer)
+        assert v.ok, str(v)
+        return
+    ms, ns = W.sample_indices(w.M, w.N, 20000, seed=w.seed,
+                              tile=256 if algo in ("auto", "lds256") else 128)
+    ref = oracle_sampled(w, x, ms, ns)
+    v = verdict(D[ms, ns], ref, w, x.integer)
+    say(f"[gpu] {w.name} sampled {len(ms)}: {v}")
+    assert v.ok, str(v)
+    if x.integer and w.d == "f32":
+        assert freivalds_exact(D, w, x), "full-matrix integer check failed"

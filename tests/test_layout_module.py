@@ -1,0 +1,211 @@
+"""The HIP-side layout module (C++ behind include/mfl_layout.h) against the
+independent oracle evaluator, on full domains.  No GPU needed."""
+import itertools
+import random
+
+import numpy as np
+import pytest
+
+import mma_fragment_layouts_tn_amd as mfl
+from oracle import layout as L
+from helpers import keyed
+
+PAGE_LAYOUTS = [
+    L.SM80_C_TV, L.SM80_A_TV, L.SM80_B_TV,
+    "(2,2,1):(1,2,4)", "(32,2,2,1):(1,32,64,0)", "(32,2,2,1):(1,64,32,0)",
+    "(32,1,1,2):(1,0,0,32)", "((16,8),(2,2)):((16,1),(256,8))",
+    "((2,2),1,1):((1,128),0,0)", "((2,2),2,2):((1,256),1024,16)",
+    "((2,2,2),2,2):((1,2,4),8,16)", "((2,2),2,2):((1,2),4,8)", "(8,4):(4,1)",
+    "(8,(2,4,2)):(4,(32,1,64))", "(8,(2,4,4)):(4,(32,1,64))",
+    "((2,2,2),1,1):((1,2,4),0,0)", "((2,4),1,1):((1,2),0,0)", "(2,4):(1,2)",
+    "((4,1),1,1):((1,0),0,0)", "(4,4,2):(1,8,4)",
+    "(32,8):(8,1)", "(32,(2,4)):(2,(1,64))", "(16,16):(16,1)",
+    "(128,16,4):(64,1,16)", "((2,2,2),4,1,4):((1,512,8),2048,0,16)",
+    "((2,2),(2,4),1,4):((1,8),(1024,2048),0,16)", "((2,2),4,8):((1,2048),8192,16)",
+    "_8:_1", "(_2,_4):(_1,_2)",
+]
+
+
+@pytest.mark.parametrize("text", PAGE_LAYOUTS)
+def test_eval_size_cosize_match_oracle(text):
+    lay = L.parse(text)
+    assert mfl.layout_size(text) == L.size(lay[0])
+    assert list(mfl.layout_table(text)) == L.table(lay)
+    assert mfl.layout_cosize(text) == L.cosize(lay)
+    assert mfl.layout_eval(text, L.size(lay[0]) - 1) == L.table(lay)[-1]
+
+
+@pytest.mark.parametrize("text", PAGE_LAYOUTS)
+def test_coalesce_is_same_function(text):
+    c = mfl.layout_coalesce(text)
+    assert L.table(L.parse(c)) == L.table(L.parse(text))
+
+
+def test_partition_c_composition_from_pages():
+    # atom block of a row-major 32x16 C composed with the C TV layout gives
+    # lane 0 offsets 0, 1, 128, 129 (TiledMMA page, partition_C section)
+    out = mfl.layout_compose("(16,8):(16,1)", L.SM80_C_TV)
+    tab = L.table(L.parse(out))
+    assert [tab[32 * v] for v in range(4)] == [0, 1, 128, 129]
+    assert tab == L.compose_table(L.parse("(16,8):(16,1)"), L.parse(L.SM80_C_TV))
+
+
+def test_route_through_module():
+    # route page: right_inverse(S) o D at (0,5) -> flat 48 == source (16,1);
+    # F o right_inverse(R) o D at (0,5) -> q = 144 == A(0,9)
+    S, D = "(32,8):(8,1)", "(32,(2,4)):(2,(1,64))"
+    s_inv = mfl.layout_right_inverse(S)
+    route = mfl.layout_compose(s_inv, D)
+    flat = L.evaluate(L.parse(route), (0, 5))
+    assert flat == 48 and L.decode(flat, (32, 8)) == (16, 1)
+    r_inv = mfl.layout_right_inverse(D)
+    f_r = mfl.layout_compose(L.SM80_A_TV, r_inv)
+    f_r_d = mfl.layout_compose(f_r, D)
+    assert L.evaluate(L.parse(f_r_d), (0, 5)) == 144
+    # and the same map equals the MMA layout F everywhere (R = D)
+    assert L.table(L.parse(f_r_d)) == L.table(L.parse(L.SM80_A_TV))
+
+
+def test_right_inverse_of_page_tv_layouts():
+    for text in (L.SM80_A_TV, L.SM80_B_TV, L.SM80_C_TV, "(32,(2,4)):(2,(1,64))"):
+        r = mfl.layout_right_inverse(text)
+        assert list(L.table(L.parse(r))) == L.right_inverse_table(L.table(L.parse(text)))
+    r = mfl.layout_right_inverse(L.SM80_B_TV)
+    assert L.table(L.parse(r)) == L.table(L.parse("(8,(2,4,2)):(4,(32,1,64))"))
+
+
+def _rand_compact(rng, nleaf):
+    shapes = [rng.choice([1, 2, 3, 4, 8]) for _ in range(nleaf)]
+    order = list(range(nleaf))
+    rng.shuffle(order)
+    strides = [0] * nleaf
+    acc = 1
+    for i in order:
+        strides[i] = acc
+        acc *= shapes[i]
+    return shapes, strides
+
+
+def _fmt(shapes, strides):
+    if len(shapes) == 1:
+        return f"{shapes[0]}:{strides[0]}"
+    return "(" + ",".join(map(str, shapes)) + "):(" + ",".join(map(str, strides)) + ")"
+
+
+def test_right_inverse_random_permutation_layouts():
+    rng = random.Random(5)
+    for _ in range(300):
+        shapes, strides = _rand_compact(rng, rng.randint(1, 5))
+        if rng.random() < 0.3:          # a broadcast mode
+            shapes.append(rng.choice([2, 3]))
+            strides.append(0)
+        text = _fmt(shapes, strides)
+        r = mfl.layout_right_inverse(text)
+        want = L.right_inverse_table(L.table(L.parse(text)))
+        assert L.table(L.parse(r)) == want, (text, r)
+
+
+def test_compose_random_against_tables():
+    rng = random.Random(7)
+    checked = 0
+    for _ in range(600):
+        a_sh, a_st = _rand_compact(rng, rng.randint(1, 4))
+        if rng.random() < 0.3:
+            a_st = [d * rng.choice([1, 2, 3]) for d in a_st]   # gaps
+        A = _fmt(a_sh, a_st)
+        # B: arbitrary small shapes and strides; the module must either
+        # return exactly A o B or refuse
+        n = rng.randint(1, 3)
+        b_sh = [rng.choice([1, 2, 4]) for _ in range(n)]
+        b_st = [rng.choice([0, 1, 2, 4, 8, 16]) for _ in range(n)]
+        B = _fmt(b_sh, b_st)
+        try:
+            out = mfl.layout_compose(A, B)
+        except mfl.LayoutError:
+            continue
+        want = L.compose_table(L.parse(A), L.parse(B))
+        assert L.table(L.parse(out)) == want, (A, B, out)
+        checked += 1
+    assert checked > 250
+
+
+def test_compose_rejects_non_divisible():
+    with pytest.raises(mfl.LayoutError):
+        mfl.layout_compose("(3,4):(1,5)", "2:2")
+
+
+def test_bad_text_rejected():
+    for bad in ("(2,2):(1)", "((2,2):(1,2)", "2,2:1,2", "(2,a):(1,2)", ""):
+        with pytest.raises(mfl.LayoutError):
+            mfl.layout_size(bad)
+
+
+# --------------------------------------------------- gfx950 atom TV layouts
+@pytest.mark.parametrize("op", sorted(L.MFMA_OPS))
+def test_mfma_tv_layouts_equal_oracle_closed_forms(op):
+    M, N, K, nv, nacc = L.MFMA_OPS[op]
+    for operand in ("A", "B"):
+        lay = L.parse(mfl.mfma_tv(op, operand))
+        for lane, v in itertools.product(range(64), range(nv)):
+            q = L.evaluate(lay, (lane, v))
+            assert (q % M, q // M) == L.mfma_ab_coord(op, lane, v)
+    lay = L.parse(mfl.mfma_tv(op, "C"))
+    for lane, v in itertools.product(range(64), range(nacc)):
+        q = L.evaluate(lay, (lane, v))
+        assert (q % M, q // M) == L.mfma_c_coord(op, lane, v)
+
+
+# --------------------------------------------- kernel fragment addressing
+KERNEL_TILES = {"direct": (128, 128, 32, 2, 2), "lds128": (128, 128, 32, 2, 2),
+                "lds256": (256, 256, 64, 2, 2)}
+
+
+@pytest.mark.parametrize("algo", sorted(KERNEL_TILES))
+def test_fragment_coords_follow_the_atom_layout(algo):
+    BM, BN, BK, WM, WN = KERNEL_TILES[algo]
+    op = "f32_32x32x16_f16"
+    fa = mfl.fragment_coords(algo, "A")
+    fb = mfl.fragment_coords(algo, "B")
+    fc = mfl.fragment_coords(algo, "C")
+    T = 64 * WM * WN
+    assert fa.shape[0] == fb.shape[0] == fc.shape[0] == T
+    RM, RN = BM // WM // 32, BN // WN // 32
+    for t in range(T):
+        w, lane = divmod(t, 64)
+        wm, wn = w % WM, w // WM
+        s = 0
+        for kk in range(BK // 16):
+            for i in range(RM):
+                for v in range(8):
+                    r, k = L.mfma_ab_coord(op, lane, v)
+                    assert tuple(fa[t, s]) == (wm * (BM // WM) + 32 * i + r, 16 * kk + k)
+                    s += 1
+        s = 0
+        for kk in range(BK // 16):
+            for j in range(RN):
+                for v in range(8):
+                    r, k = L.mfma_ab_coord(op, lane, v)
+                    assert tuple(fb[t, s]) == (wn * (BN // WN) + 32 * j + r, 16 * kk + k)
+                    s += 1
+        s = 0
+        for i in range(RM):
+            for j in range(RN):
+                for v in range(16):
+                    m, n = L.mfma_c_coord(op, lane, v)
+                    assert tuple(fc[t, s]) == (wm * (BM // WM) + 32 * i + m,
+                                               wn * (BN // WN) + 32 * j + n)
+                    s += 1
+
+
+@pytest.mark.parametrize("algo", sorted(KERNEL_TILES))
+def test_fragment_multiplicities(algo):
+    """A held WAVES_N times, B WAVES_M times, C once (the pages' 2/2/1)."""
+    BM, BN, BK, WM, WN = KERNEL_TILES[algo]
+    for operand, rows, mult in (("A", BM, WN), ("B", BN, WM)):
+        f = mfl.fragment_coords(algo, operand).reshape(-1, 2)
+        idx = f[:, 0] * BK + f[:, 1]
+        counts = np.bincount(idx, minlength=rows * BK)
+        assert counts.shape[0] == rows * BK and (counts == mult).all()
+    f = mfl.fragment_coords(algo, "C").reshape(-1, 2)
+    counts = np.bincount(f[:, 0] * BN + f[:, 1], minlength=BM * BN)
+    assert (counts == 1).all()
