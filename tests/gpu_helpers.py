@@ -11,8 +11,8 @@ from oracle import compare
 from oracle import gemm as G
 
 GUARD = 64
-CANARY16 = 0x7E5A          # an fp16 NaN pattern
-CANARY32 = 0x7FC0DEAD      # an fp32 NaN pattern
+CANARY16 = int(np.array([0x7E5A], np.uint16).view(np.int16)[0])        # an fp16 NaN
+CANARY32 = int(np.array([0x7FC0DEAD], np.uint32).view(np.int32)[0])    # an fp32 NaN
 
 
 def say(*args):
@@ -28,11 +28,10 @@ class Guarded:
         self.n = flat.size
         if flat.dtype.itemsize == 2:
             bits = flat.view(np.int16)
-            t = torch.full((self.n + GUARD,), CANARY16 - (1 << 16) if CANARY16 >= 1 << 15 else CANARY16,
-                           dtype=torch.int16)
+            t = torch.full((self.n + GUARD,), CANARY16, dtype=torch.int16)
         else:
             bits = flat.view(np.int32)
-            t = torch.full((self.n + GUARD,), CANARY32 - (1 << 32), dtype=torch.int32)
+            t = torch.full((self.n + GUARD,), CANARY32, dtype=torch.int32)
         t[: self.n] = torch.from_numpy(bits.copy())
         self.host_bits = t.clone()
         self.t = t.to(dev)
@@ -51,9 +50,9 @@ class Guarded:
 def out_buffer(M, ldd, d, dev="cuda"):
     n = M * ldd
     if d == "f16":
-        t = torch.full((n + GUARD,), CANARY16 - (1 << 16), dtype=torch.int16, device=dev)
+        t = torch.full((n + GUARD,), CANARY16, dtype=torch.int16, device=dev)
     else:
-        t = torch.full((n + GUARD,), CANARY32 - (1 << 32), dtype=torch.int32, device=dev)
+        t = torch.full((n + GUARD,), CANARY32, dtype=torch.int32, device=dev)
     return t
 
 
@@ -85,12 +84,12 @@ def run_gemm(w: W.Workload, x: W.Inputs, algo: str, in_place: bool = False):
     n = w.M * ldd
     if w.d == "f16":
         D = raw[:n].view(np.float16).reshape(w.M, ldd)[:, : w.N].astype(np.float64)
-        guard_ok = (raw[n:] == np.int16(CANARY16 - (1 << 16))).all()
-        pad_ok = (raw[:n].reshape(w.M, ldd)[:, w.N:] == np.int16(CANARY16 - (1 << 16))).all()
+        guard_ok = (raw[n:] == np.int16(CANARY16)).all()
+        pad_ok = (raw[:n].reshape(w.M, ldd)[:, w.N:] == np.int16(CANARY16)).all()
     else:
         D = raw[:n].view(np.float32).reshape(w.M, ldd)[:, : w.N].astype(np.float64)
-        guard_ok = (raw[n:] == np.int32(CANARY32 - (1 << 32))).all()
-        pad_ok = (raw[:n].reshape(w.M, ldd)[:, w.N:] == np.int32(CANARY32 - (1 << 32))).all()
+        guard_ok = (raw[n:] == np.int32(CANARY32)).all()
+        pad_ok = (raw[:n].reshape(w.M, ldd)[:, w.N:] == np.int32(CANARY32)).all()
     checks = {"A_unchanged": A.unchanged(), "B_unchanged": B.unchanged(),
               "C_unchanged": (C is None or in_place or C.unchanged()),
               "D_guard": bool(guard_ok), "D_padding": bool(pad_ok)}
