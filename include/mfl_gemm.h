@@ -54,13 +54,19 @@ typedef enum { MFL_A_KMAJOR = 0, MFL_A_MMAJOR = 1 } mfl_a_order;
  * from global memory into registers (no LDS; the simple-GEMM page's
  * "不用 Shared Memory" kernel).  LDS_128 stages 128x128x32 block tiles
  * through LDS (the block tile of "CuTe Layout 到 Tensor Core" §4).  LDS_256
- * stages 256x256x64 block tiles (a larger tile for large shapes). */
+ * stages 256x256x64 block tiles through registers into LDS.  LDS_256_DMA
+ * (4 waves of 128x128) and LDS_256_DMA_W8 (8 waves of 128x64) load the
+ * 256x256x64 tiles straight from global memory into LDS; they need A
+ * K-contiguous and A, B, lda*2 and ldb*2 multiples of 16 bytes
+ * (MFL_E_ALGO_CASE otherwise). */
 typedef enum {
   MFL_ALGO_AUTO = 0,
   MFL_ALGO_DIRECT = 1,
   MFL_ALGO_LDS_128 = 2,
   MFL_ALGO_LDS_256 = 3,
-  MFL_ALGO_COUNT = 4
+  MFL_ALGO_LDS_256_DMA = 4,
+  MFL_ALGO_LDS_256_DMA_W8 = 5,
+  MFL_ALGO_COUNT = 6
 } mfl_algo;
 
 typedef struct {

@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(_PKG, "libmfl_gemm.so")
 
 NONE, F16, F32 = 0, 1, 2
 A_KMAJOR, A_MMAJOR = 0, 1
-ALGOS = {"auto": 0, "direct": 1, "lds128": 2, "lds256": 3}
+ALGOS = {"auto": 0, "direct": 1, "lds128": 2, "lds256": 3, "dma256": 4, "dma256w8": 5}
 ALGO_NAMES = {v: k for k, v in ALGOS.items()}
 MFMA_OPS = {"f32_32x32x16_f16": 0, "f32_16x16x32_f16": 1, "f32_32x32x8_f16": 2,
             "f32_16x16x16_f16": 3}

@@ -33,11 +33,18 @@ bool span_fits(int64_t rows, int64_t ld, int64_t cols) {
   return last * 2 < ((int64_t)1 << 31) - 64;
 }
 
-int pick_algo(int64_t M, int64_t N, int64_t K, bool a_mmajor) {
+// direct-to-LDS loads move whole 16-byte chunks: rows and bases must be
+// 16-byte aligned and K contiguous
+bool dma_ok(bool a_mmajor, const void* A, int64_t lda, const void* B, int64_t ldb) {
+  return !a_mmajor && ((uintptr_t)A % 16 == 0) && ((uintptr_t)B % 16 == 0) && (lda % 8 == 0) &&
+         (ldb % 8 == 0);
+}
+
+int pick_algo(int64_t M, int64_t N, int64_t K, bool a_mmajor, const void* A, int64_t lda,
+              const void* B, int64_t ldb) {
   (void)K;
   const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
-  if (t256 >= 192) return mfl::kAlgoLds256;
-  (void)a_mmajor;
+  if (t256 >= 192) return dma_ok(a_mmajor, A, lda, B, ldb) ? mfl::kAlgoDma256W8 : mfl::kAlgoLds256;
   return mfl::kAlgoLds128;
 }
 
@@ -69,8 +76,11 @@ int check(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const voi
   if (mm ? !span_fits(K, lda, M) : !span_fits(M, lda, K)) return MFL_E_TOO_LARGE;
   if (!span_fits(N, ldb, K)) return MFL_E_TOO_LARGE;
   int algo = dt.algo;
-  if (algo == MFL_ALGO_AUTO) algo = pick_algo(M, N, K, mm);
+  if (algo == MFL_ALGO_AUTO) algo = pick_algo(M, N, K, mm, A, lda, B, ldb);
   if (algo == MFL_ALGO_DIRECT && mm) return MFL_E_ALGO_CASE;
+  if ((algo == MFL_ALGO_LDS_256_DMA || algo == MFL_ALGO_LDS_256_DMA_W8) &&
+      !dma_ok(mm, A, lda, B, ldb))
+    return MFL_E_ALGO_CASE;
   const mfl::KernelInfo ki = mfl::kernel_info(algo);
   if (ki.algo < 0) return MFL_E_UNSUPPORTED;
   const int64_t tiles = ((M + ki.bm - 1) / ki.bm) * ((N + ki.bn - 1) / ki.bn);
@@ -290,7 +300,7 @@ int gemm_tn(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const v
   p.ldd = (int)ldd;
   p.tiles_m = (int)((M + ki.bm - 1) / ki.bm);
   p.tiles_n = (int)((N + ki.bn - 1) / ki.bn);
-  p.group_m = algo == mfl::kAlgoLds256 ? 4 : 8;
+  p.group_m = ki.bm >= 256 ? 4 : 8;
   p.A = A;
   p.B = B;
   p.C = C;
@@ -413,6 +423,8 @@ int mfl_fragment_coords(int32_t algo, int32_t operand, int32_t* out, int64_t cap
     case mfl::kAlgoDirect: return frag_coords<mfl::CfgDirect>(operand, out, cap, threads, slots);
     case mfl::kAlgoLds128: return frag_coords<mfl::CfgLds128>(operand, out, cap, threads, slots);
     case mfl::kAlgoLds256: return frag_coords<mfl::CfgLds256>(operand, out, cap, threads, slots);
+    case mfl::kAlgoDma256: return frag_coords<mfl::CfgDma256>(operand, out, cap, threads, slots);
+    case mfl::kAlgoDma256W8: return frag_coords<mfl::CfgDma256W8>(operand, out, cap, threads, slots);
     default: return mfl::kLayoutBadIndex;
   }
 }

@@ -247,6 +247,198 @@ __global__ void __launch_bounds__(Cfg::kThreads, 1) gemm_lds(const GemmParams p)
 }
 
 // ---------------------------------------------------------------------------
+// LDS-staged kernel, direct-to-LDS fetch (K-contiguous, 16-byte aligned rows)
+// ---------------------------------------------------------------------------
+// Same tile structure as gemm_lds, different pipeline:
+//  * operand tiles go global -> LDS with global_load_lds_dwordx4: lane l of
+//    a wave writes LDS bytes [16 l, 16 l + 16) of a 1 KB run (8 rows of
+//    BK=64 halves), so the XOR swizzle is applied by choosing which 16-byte
+//    chunk of its row each lane fetches;
+//  * the fetch of tile kt+2 is issued right after the barrier of step kt and
+//    has a whole step to land; each step has one barrier, placed after the
+//    third K sub-step so the fragment reads for the next stage and the
+//    barrier wait overlap the MFMAs still queued;
+//  * fragments are double-buffered across K sub-steps;
+//  * a K remainder (K % BK) is staged once through registers with zero fill.
+using lds_ptr_t = __attribute__((address_space(3))) void*;
+
+template <class Cfg>
+struct DmaPlan {
+  // per wave: A and B runs of 8 rows each
+  static constexpr int kRunsA = Cfg::BM / 8 / Cfg::kWaves;
+  static constexpr int kRunsB = Cfg::BN / 8 / Cfg::kWaves;
+  static_assert(Cfg::BK == 64, "one 1 KB run = 8 rows of 64 halves");
+  static_assert(Cfg::BM % (8 * Cfg::kWaves) == 0 && Cfg::BN % (8 * Cfg::kWaves) == 0, "runs");
+};
+
+template <class Cfg, int CK, int DK>
+__global__ void __launch_bounds__(Cfg::kThreads, 1) gemm_dma(const GemmParams p) {
+  constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK;
+  constexpr int RA = DmaPlan<Cfg>::kRunsA, RB = DmaPlan<Cfg>::kRunsB;
+  constexpr int RM = Cfg::RM, RN = Cfg::RN, KSUB = Cfg::KSUB;
+  static_assert(KSUB == 4, "the schedule below is written for 4 K sub-steps");
+  // stage s: A at smem + s*kStage, B at smem + s*kStage + BM*BK (halves)
+  constexpr int kStage = (BM + BN) * BK;
+  __shared__ __attribute__((aligned(1024))) _Float16 smem[2 * kStage];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const TileIndex ti = tile_of_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m);
+  const int m0 = ti.tm * BM, n0 = ti.tn * BN;
+
+  // lane's 16-byte chunk within its 8-row run: row r = 8*run + lane/8 holds
+  // physical chunk lane%8, i.e. logical chunk (lane%8) ^ swz(r)
+  const int rsub = lane >> 3;
+  unsigned a_off[RA], b_off[RB];
+#pragma unroll
+  for (int i = 0; i < RA; ++i) {
+    const int row = 8 * (w * RA + i) + rsub;
+    const int kchunk = ((lane & 7) ^ swz<Cfg::CH>(row)) * 8;
+    a_off[i] = (unsigned)((int64_t)min(m0 + row, p.M - 1) * p.lda * 2) + kchunk * 2;
+  }
+#pragma unroll
+  for (int i = 0; i < RB; ++i) {
+    const int row = 8 * (w * RB + i) + rsub;
+    const int kchunk = ((lane & 7) ^ swz<Cfg::CH>(row)) * 8;
+    b_off[i] = (unsigned)((int64_t)min(n0 + row, p.N - 1) * p.ldb * 2) + kchunk * 2;
+  }
+
+  auto dma = [&](int kt, int stage) {
+    const char* a = (const char*)p.A + (int64_t)kt * BK * 2;
+    const char* b = (const char*)p.B + (int64_t)kt * BK * 2;
+    _Float16* sa = smem + stage * kStage;
+    _Float16* sb = sa + BM * BK;
+#pragma unroll
+    for (int i = 0; i < RA; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(a + (uint64_t)a_off[i]),
+                                       (lds_ptr_t)(sa + (w * RA + i) * 8 * BK), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(b + (uint64_t)b_off[i]),
+                                       (lds_ptr_t)(sb + (w * RB + i) * 8 * BK), 16, 0, 0);
+  };
+
+  // fragment read offsets within a stage (halves), per K sub-step
+  int fa_off[KSUB][RM], fb_off[KSUB][RN];
+#pragma unroll
+  for (int kk = 0; kk < KSUB; ++kk) {
+#pragma unroll
+    for (int i = 0; i < RM; ++i) {
+      const RowK a = frag_a_coord<Cfg>(w, lane, i, kk);
+      fa_off[kk][i] = lds_offset<BK>(a.row, a.k);
+    }
+#pragma unroll
+    for (int j = 0; j < RN; ++j) {
+      const RowK b = frag_b_coord<Cfg>(w, lane, j, kk);
+      fb_off[kk][j] = BM * BK + lds_offset<BK>(b.row, b.k);
+    }
+  }
+
+  half8 fa[2][RM], fb[2][RN];
+  auto frags = [&](int buf, int kk, int stage) {
+    const _Float16* st = smem + stage * kStage;
+#pragma unroll
+    for (int i = 0; i < RM; ++i) fa[buf][i] = *(const half8*)&st[fa_off[kk][i]];
+#pragma unroll
+    for (int j = 0; j < RN; ++j) fb[buf][j] = *(const half8*)&st[fb_off[kk][j]];
+  };
+
+  floatx16 acc[RM][RN];
+#pragma unroll
+  for (int i = 0; i < RM; ++i)
+#pragma unroll
+    for (int j = 0; j < RN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  auto mma = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < RM; ++i)
+#pragma unroll
+      for (int j = 0; j < RN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
+  };
+  // interleave: the group's fragment reads spread between its MFMAs
+  constexpr int kReads = RM + RN, kMfma = RM * RN;
+  auto interleave = [&]() {
+#pragma unroll
+    for (int g = 0; g < kReads; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, kMfma / kReads > 0 ? kMfma / kReads : 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kMfma, 0);
+  };
+
+  const int nfull = p.K / BK;
+  if (nfull > 0) {
+    dma(0, 0);
+    if (nfull > 1) dma(1, 1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    frags(0, 0, 0);
+  }
+  for (int kt = 0; kt < nfull; ++kt) {
+    const int cur = kt & 1;
+    frags(1, 1, cur);
+    mma(0);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+    frags(0, 2, cur);
+    mma(1);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+    frags(1, 3, cur);
+    mma(0);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0);        // own reads of this stage and DMA of tile kt+1 done
+    __builtin_amdgcn_s_barrier();         // ... in every wave: this stage is free, next is full
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + 2 < nfull) dma(kt + 2, cur);
+    if (kt + 1 < nfull) frags(0, 0, cur ^ 1);
+    mma(1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // K remainder: one step staged through registers with zero fill
+  if (p.K % BK != 0) {
+    const int k0 = nfull * BK;
+    _Float16* sA0 = smem;
+    _Float16* sB0 = smem + BM * BK;
+    __syncthreads();
+    constexpr int T = Cfg::kThreads, CH = Cfg::CH;
+#pragma unroll
+    for (int i = 0; i < BM * CH / T; ++i) {
+      const int q = tid + i * T, row = q / CH, c = q % CH;
+      const int gm = min(m0 + row, p.M - 1);
+      const _Float16* src = (const _Float16*)p.A + (int64_t)gm * p.lda + k0 + c * 8;
+      const int valid = p.K - (k0 + c * 8);
+      *(uint4*)&sA0[lds_offset<BK>(row, c * 8)] =
+          valid >= 8 ? load16((const char*)src, 0)
+                     : valid <= 0 ? make_uint4(0, 0, 0, 0) : load8_tail(src, valid);
+    }
+#pragma unroll
+    for (int i = 0; i < BN * CH / T; ++i) {
+      const int q = tid + i * T, row = q / CH, c = q % CH;
+      const int gn = min(n0 + row, p.N - 1);
+      const _Float16* src = (const _Float16*)p.B + (int64_t)gn * p.ldb + k0 + c * 8;
+      const int valid = p.K - (k0 + c * 8);
+      *(uint4*)&sB0[lds_offset<BK>(row, c * 8)] =
+          valid >= 8 ? load16((const char*)src, 0)
+                     : valid <= 0 ? make_uint4(0, 0, 0, 0) : load8_tail(src, valid);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < KSUB; ++kk) {
+      frags(0, kk, 0);
+      mma(0);
+    }
+  }
+  epilogue<Cfg, CK, DK>(p, w, lane, m0, n0, acc);
+}
+
+// ---------------------------------------------------------------------------
 // Direct kernel: fragments from global memory, no LDS
 // ---------------------------------------------------------------------------
 template <class Cfg, int CK, int DK>
@@ -326,6 +518,12 @@ constexpr KernelFn direct_table[3][2] = {
     {gemm_direct<Cfg, 2, 1>, gemm_direct<Cfg, 2, 2>}};
 
 template <class Cfg>
+constexpr KernelFn dma_table[3][2] = {
+    {gemm_dma<Cfg, 0, 1>, gemm_dma<Cfg, 0, 2>},
+    {gemm_dma<Cfg, 1, 1>, gemm_dma<Cfg, 1, 2>},
+    {gemm_dma<Cfg, 2, 1>, gemm_dma<Cfg, 2, 2>}};
+
+template <class Cfg>
 KernelInfo info_of(int algo) {
   return KernelInfo{algo, Cfg::BM, Cfg::BN, Cfg::BK, Cfg::kThreads};
 }
@@ -337,6 +535,8 @@ KernelInfo kernel_info(int algo) {
     case kAlgoDirect: return info_of<CfgDirect>(algo);
     case kAlgoLds128: return info_of<CfgLds128>(algo);
     case kAlgoLds256: return info_of<CfgLds256>(algo);
+    case kAlgoDma256: return info_of<CfgDma256>(algo);
+    case kAlgoDma256W8: return info_of<CfgDma256W8>(algo);
     default: return KernelInfo{-1, 0, 0, 0, 0};
   }
 }
@@ -348,6 +548,10 @@ const void* kernel_symbol(int algo, bool a_mmajor, int c_kind, int d_kind) {
       return a_mmajor ? nullptr : (const void*)direct_table<CfgDirect>[c_kind][d_kind - 1];
     case kAlgoLds128: return (const void*)lds_table<CfgLds128>[a_mmajor][c_kind][d_kind - 1];
     case kAlgoLds256: return (const void*)lds_table<CfgLds256>[a_mmajor][c_kind][d_kind - 1];
+    case kAlgoDma256:
+      return a_mmajor ? nullptr : (const void*)dma_table<CfgDma256>[c_kind][d_kind - 1];
+    case kAlgoDma256W8:
+      return a_mmajor ? nullptr : (const void*)dma_table<CfgDma256W8>[c_kind][d_kind - 1];
     default: return nullptr;
   }
 }

@@ -21,7 +21,18 @@ struct GemmParams {
   void* D;
 };
 
-enum Algo : int { kAlgoAuto = 0, kAlgoDirect = 1, kAlgoLds128 = 2, kAlgoLds256 = 3, kAlgoCount = 4 };
+// values match mfl_algo in include/mfl_gemm.h
+enum Algo : int {
+  kAlgoAuto = 0,
+  kAlgoDirect = 1,
+  kAlgoLds128 = 2,
+  kAlgoLds256 = 3,
+  kAlgoDma256 = 4,     // direct-to-LDS fetch, 4 waves of 128x128
+  kAlgoDma256W8 = 5,   // direct-to-LDS fetch, 8 waves of 128x64
+  kAlgoCount = 6
+};
+using CfgDma256 = TileCfg<256, 256, 64, 2, 2>;
+using CfgDma256W8 = TileCfg<256, 256, 64, 2, 4>;
 
 // direct-from-global: 128x128 block (the simple-GEMM page's CTA tile), 2x2 waves
 using CfgDirect = TileCfg<128, 128, 32, 2, 2>;

@@ -20,7 +20,7 @@
 //
 // LDS tile layout: rows of BK halves, K contiguous, split into 16-byte chunks
 // (8 halves); chunk c of row r is stored at chunk c ^ swz(r).  The XOR keeps
-// the 16-byte reads of consecutive rows on distinct banks.  The pages name
+// the 16-byte reads of 16 consecutive rows on distinct banks.  The pages name
 // swizzling as an option without giving a function ("CuTe Layout 到 Tensor
 // Core" §5); this one is our own.
 #pragma once
@@ -52,10 +52,15 @@ struct TileCfg {
   static_assert(CH == 4 || CH == 8, "swizzle defined for 4 or 8 chunks per row");
 };
 
-// XOR swizzle of the 16-byte chunk index within an LDS row
+// XOR swizzle of the 16-byte chunk index within an LDS row.  A 16-byte LDS
+// read is served 16 lanes at a time across 64 four-byte banks (256 bytes), so
+// the 16 rows that 16 consecutive lanes read (same logical chunk) must land
+// on 16 different 16-byte bank groups: (row*CH + chunk') mod 16 distinct.
+// For CH = 8 that is parity(row) and (row>>1)&7; for CH = 4, row&3 and
+// (row>>2)&3.
 template <int CH>
 MFL_HD constexpr int swz(int row) {
-  return CH == 8 ? (row & 7) : ((row >> 1) & 3);
+  return CH == 8 ? ((row >> 1) & 7) : ((row >> 2) & 3);
 }
 
 // element offset (in halves) of (row, k) in one LDS operand tile

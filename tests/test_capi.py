@@ -62,6 +62,8 @@ def test_valid_cases():
     (dict(d=mfl.NONE), -4), (dict(c=7, C=P, ldc=64), -4), (dict(a_order=2), -4),
     (dict(algo=9), -4),
     (dict(a_order=mfl.A_MMAJOR, algo=1), -6),
+    (dict(a_order=mfl.A_MMAJOR, lda=64, algo=4), -6), (dict(lda=68, algo=5), -6),
+    (dict(B=P + 2, algo=4), -6),
     (dict(A=P + 1), -7), (dict(d=mfl.F32, D=P + 2), -7),
     (dict(c=mfl.F16, C=P, ldc=64, d=mfl.F32, D=P), -8),
     (dict(c=mfl.F32, C=P, ldc=128, d=mfl.F32, D=P, ldd=64), -8),
@@ -83,7 +85,8 @@ def test_degenerate_sizes_are_ok():
 
 
 def test_auto_choice():
-    assert _v(M=4096, N=4096, K=4096)[1] == mfl.ALGOS["lds256"]
+    assert _v(M=4096, N=4096, K=4096)[1] == mfl.ALGOS["dma256w8"]
+    assert _v(M=4096, N=4096, K=4097, lda=4097, ldb=4097)[1] == mfl.ALGOS["lds256"]
     assert _v(M=256, N=256, K=256)[1] == mfl.ALGOS["lds128"]
     assert _v(M=32, N=16, K=16, algo=1)[1] == mfl.ALGOS["direct"]
 

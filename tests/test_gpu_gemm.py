@@ -20,7 +20,8 @@ from gpu_helpers import (freivalds_exact, oracle_full, oracle_sampled, run_gemm,
 
 pytestmark = pytest.mark.gpu
 
-ALGOS = ["direct", "lds128", "lds256"]
+ALGOS = ["direct", "lds128", "lds256", "dma256", "dma256w8"]
+DMA = {"dma256", "dma256w8"}
 
 
 def _assert_checks(checks):
@@ -36,9 +37,11 @@ SMALL = [(1, 1, 1), (5, 7, 3), (32, 16, 16), (33, 17, 9), (64, 64, 64), (127, 12
 @pytest.mark.parametrize("shape", SMALL)
 def test_small_integer_bit_exact(algo, shape):
     M, N, K = shape
+    # odd leading dimensions for the register-staged kernels, 16-byte rows for DMA
+    pad = (lambda k: (k + 7) // 8 * 8 + 8) if algo in DMA else (lambda k: k + 3)
     for c, d in ((None, "f32"), ("f16", "f16"), ("f32", "f32"), (None, "f16"), ("f32", "f16")):
-        w = W.custom(M, N, K, c=c, d=d, dist="int", seed=M * 7 + N * 3 + K, lda=K + 3,
-                     ldb=K + 1)
+        w = W.custom(M, N, K, c=c, d=d, dist="int", seed=M * 7 + N * 3 + K, lda=pad(K),
+                     ldb=pad(K) + (0 if algo in DMA else -2))
         x = W.make_inputs(w)
         D, checks = run_gemm(w, x, algo)
         _assert_checks(checks)
@@ -63,7 +66,8 @@ def test_mmajor_a_bit_exact(algo, shape):
 def test_float_inputs_within_tolerance(algo):
     for (M, N, K, c, d) in ((513, 384, 300, None, "f32"), (300, 517, 1000, "f16", "f16"),
                             (256, 256, 256, "f32", "f32")):
-        w = W.custom(M, N, K, c=c, d=d, dist="unif", seed=M + K)
+        ld = (K + 7) // 8 * 8 if algo in DMA else None
+        w = W.custom(M, N, K, c=c, d=d, dist="unif", seed=M + K, lda=ld, ldb=ld)
         x = W.make_inputs(w)
         D, checks = run_gemm(w, x, algo)
         _assert_checks(checks)
@@ -73,7 +77,7 @@ def test_float_inputs_within_tolerance(algo):
 
 @pytest.mark.parametrize("algo", ALGOS)
 def test_k_zero_gives_c(algo):
-    w = W.custom(70, 50, 0, c="f32", d="f32", dist="int", seed=3, lda=1, ldb=1)
+    w = W.custom(70, 50, 0, c="f32", d="f32", dist="int", seed=3, lda=8, ldb=8)
     x = W.make_inputs(w)
     D, checks = run_gemm(w, x, algo)
     _assert_checks(checks)
@@ -94,6 +98,8 @@ def test_kernel_properties():
     assert info["lds_bytes"] == 0          # the direct kernel uses no LDS
     assert mfl.kernel_info("lds128")["lds_bytes"] == 2 * (128 + 128) * 32 * 2
     assert mfl.kernel_info("lds256")["lds_bytes"] == 2 * (256 + 256) * 64 * 2
+    assert mfl.kernel_info("dma256")["lds_bytes"] == 2 * (256 + 256) * 64 * 2
+    assert mfl.kernel_info("dma256w8")["threads"] == 512
     say("[gpu] kernel info", {a: mfl.kernel_info(a) for a in ALGOS})
 
 
@@ -101,7 +107,7 @@ def test_kernel_properties():
 NAMED = [
     ("tiny_32x16x16", ["direct", "lds128", "lds256"], False),
     ("direct_256", ["direct"], True),
-    ("lds_4096", ["lds128", "lds256"], True),
+    ("lds_4096", ["lds128", "lds256", "dma256", "dma256w8"], True),
     ("accum_mmajor_8192x8192x2048", ["auto"], True),
     ("ragged_8191x6143x4097", ["auto", "lds128"], True),
 ]
