@@ -26,7 +26,7 @@ if ROOT not in sys.path:
 
 PEAK_FP16_DENSE_TFLOPS = 2516.6   # 256 CU x 4 SIMD x 1024 FLOP/clk x 2.4 GHz
 METRIC = "TFLOP/s for fp16 TN GEMM at 4096³ (fp32 acc) and % of dense FP16 MFMA peak"
-KERNEL_SOURCES = ["mma_fragment_layouts_tn_amd/csrc/gemm_kernels.hip",
+KERNEL_SOURCES = ["mma_fragment_layouts_tn_amd/csrc/gemm_kernels.hpp",
                   "mma_fragment_layouts_tn_amd/csrc/gemm_tile.hpp",
                   "mma_fragment_layouts_tn_amd/csrc/gemm_launch.hpp"]
 
@@ -77,7 +77,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="lds_4096")
-    ap.add_argument("--algo", default="auto", choices=["auto", "direct", "lds128", "lds256", "dma256", "dma256w8"])
+    ap.add_argument("--algo", default="auto",
+                    help="auto, direct, lds128, lds256, lds256w4; '+reg' forces register fetch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -108,9 +109,10 @@ def main() -> int:
     ck = {None: mfl.NONE, "f16": mfl.F16, "f32": mfl.F32}[w.c]
     dk = mfl.F16 if w.d == "f16" else mfl.F32
     a_order = mfl.A_KMAJOR if w.a_order == "k" else mfl.A_MMAJOR
-    dt = mfl.dtypes(ck, dk, a_order, mfl.ALGOS[args.algo])
-    rc, algo = mfl.validate(w.M, w.N, w.K, A.data_ptr(), w.lda_, B.data_ptr(), w.ldb_,
-                            None if C is None else C.data_ptr(), w.ldc_, D.data_ptr(), w.ldd_, dt)
+    dt = mfl.dtypes(ck, dk, a_order, mfl.algo_code(args.algo))
+    rc, algo, fetch_a, fetch_b = mfl.plan(w.M, w.N, w.K, A.data_ptr(), w.lda_, B.data_ptr(),
+                                          w.ldb_, None if C is None else C.data_ptr(), w.ldc_,
+                                          D.data_ptr(), w.ldd_, dt)
     if rc != 0:
         print(f"invalid arguments: {mfl.strerror(rc)}", file=sys.stderr)
         return 1
@@ -132,7 +134,8 @@ def main() -> int:
         if copy_dst is not None:
             copy_dst.copy_(copy_src)
 
-    print(f"[bench] {w.name} algo={algo_name} tile={info['bm']}x{info['bn']}x{info['bk']} "
+    print(f"[bench] {w.name} algo={algo_name} fetch A:{mfl.FETCH_NAMES[fetch_a]} "
+          f"B:{mfl.FETCH_NAMES[fetch_b]} tile={info['bm']}x{info['bn']}x{info['bk']} "
           f"warmup={args.warmup} steps={args.steps}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
@@ -169,7 +172,7 @@ def main() -> int:
           f"wall/step {ms_per_step:.4f} ms; single-launch median {np.median(per):.4f} "
           f"min {per.min():.4f} p90 {np.percentile(per, 90):.4f}", file=sys.stderr, flush=True)
 
-    traffic = load_traffic(w.name, algo_name)
+    traffic = load_traffic(w.name, algo_name + "_" + mfl.FETCH_NAMES[fetch_a] + mfl.FETCH_NAMES[fetch_b])
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -187,6 +190,7 @@ def main() -> int:
                    "a": "f16 K-contiguous" if w.a_order == "k" else f"f16 M-contiguous lda={w.lda_}",
                    "b": "f16 K-contiguous", "c": w.c, "d": w.d, "accumulate": "f32",
                    "algo": algo_name, "block_tile": f"{info['bm']}x{info['bn']}x{info['bk']}",
+                   "fetch": f"A:{mfl.FETCH_NAMES[fetch_a]} B:{mfl.FETCH_NAMES[fetch_b]}",
                    "threads": info["threads"], "lds_bytes": info["lds_bytes"]},
         "pct_of_peak": round(100.0 * value / PEAK_FP16_DENSE_TFLOPS, 2),
         "kernel_ms": {"avg_back_to_back": round(kern_ms, 5),

@@ -50,23 +50,26 @@ extern "C" {
 typedef enum { MFL_NONE = 0, MFL_F16 = 1, MFL_F32 = 2 } mfl_dtype;
 typedef enum { MFL_A_KMAJOR = 0, MFL_A_MMAJOR = 1 } mfl_a_order;
 
-/* Kernel choice.  AUTO picks per shape.  DIRECT reads fragments straight
- * from global memory into registers (no LDS; the simple-GEMM page's
- * "不用 Shared Memory" kernel).  LDS_128 stages 128x128x32 block tiles
- * through LDS (the block tile of "CuTe Layout 到 Tensor Core" §4).  LDS_256
- * stages 256x256x64 block tiles through registers into LDS.  LDS_256_DMA
- * (4 waves of 128x128) and LDS_256_DMA_W8 (8 waves of 128x64) load the
- * 256x256x64 tiles straight from global memory into LDS; they need A
- * K-contiguous and A, B, lda*2 and ldb*2 multiples of 16 bytes
- * (MFL_E_ALGO_CASE otherwise). */
+/* Kernel choice (low 8 bits of gemm_dtypes_t.algo).  AUTO picks per shape.
+ * DIRECT reads fragments straight from global memory into registers (no
+ * LDS; the simple-GEMM page's "不用 Shared Memory" kernel).  LDS_128 stages
+ * 128x128x32 block tiles through LDS (the block tile of "CuTe Layout 到
+ * Tensor Core" §4) with 4 waves of 64x64.  LDS_256 stages 256x256x64 block
+ * tiles with 8 waves of 128x64; LDS_256_W4 the same tile with 4 waves of
+ * 128x128.  The LDS kernels fetch each K-contiguous operand straight into
+ * LDS (global_load_lds_dwordx4) when its base and leading dimension are
+ * 16-byte aligned, else through registers with 16-byte loads at any 2-byte
+ * alignment; an M-contiguous A goes through registers and is transposed
+ * there.  MFL_ALGO_REG_FETCH or-ed into algo forces register fetch. */
 typedef enum {
   MFL_ALGO_AUTO = 0,
   MFL_ALGO_DIRECT = 1,
   MFL_ALGO_LDS_128 = 2,
   MFL_ALGO_LDS_256 = 3,
-  MFL_ALGO_LDS_256_DMA = 4,
-  MFL_ALGO_LDS_256_DMA_W8 = 5,
-  MFL_ALGO_COUNT = 6
+  MFL_ALGO_LDS_256_W4 = 4,
+  MFL_ALGO_COUNT = 5,
+  MFL_ALGO_MASK = 0xff,
+  MFL_ALGO_REG_FETCH = 0x100
 } mfl_algo;
 
 typedef struct {
@@ -85,7 +88,7 @@ enum {
                                 ldc < N with C present; ldd < N */
   MFL_E_NULL_POINTER = -3,   /* A, B or D NULL when M*N*K > 0 (D when M*N > 0);
                                 C NULL with c != NONE or non-NULL with NONE */
-  MFL_E_UNSUPPORTED = -4,    /* dtype, a_order or algo value not supported */
+  MFL_E_UNSUPPORTED = -4,    /* dtype, a_order or algo value (or flag) not supported */
   MFL_E_LAUNCH = -5,         /* the HIP launch reported an error */
   MFL_E_ALGO_CASE = -6,      /* the forced algo cannot run this case */
   MFL_E_MISALIGNED = -7,     /* a pointer not aligned to its element size */
@@ -111,6 +114,17 @@ int gemm_tn_validate(int64_t M, int64_t N, int64_t K,
                      const void* C, int64_t ldc,
                      const void* D, int64_t ldd,
                      gemm_dtypes_t dtypes, int32_t* algo_out);
+
+/* The same checks; on success also reports the kernel the call would run:
+ * *algo (mfl_algo without flags) and the fetch policy of A and B
+ * (0 direct-to-LDS, 1 through registers, 2 through registers with transpose).
+ * Any out pointer may be NULL. */
+int gemm_tn_plan(int64_t M, int64_t N, int64_t K,
+                 const void* A, int64_t lda,
+                 const void* B, int64_t ldb,
+                 const void* C, int64_t ldc,
+                 const void* D, int64_t ldd,
+                 gemm_dtypes_t dtypes, int32_t* algo, int32_t* fetch_a, int32_t* fetch_b);
 
 /* Static text for an MFL_* code (never NULL). */
 const char* gemm_strerror(int code);

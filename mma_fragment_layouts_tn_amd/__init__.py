@@ -25,8 +25,21 @@ LIB_PATH = os.path.join(_PKG, "libmfl_gemm.so")
 
 NONE, F16, F32 = 0, 1, 2
 A_KMAJOR, A_MMAJOR = 0, 1
-ALGOS = {"auto": 0, "direct": 1, "lds128": 2, "lds256": 3, "dma256": 4, "dma256w8": 5}
+ALGOS = {"auto": 0, "direct": 1, "lds128": 2, "lds256": 3, "lds256w4": 4}
+REG_FETCH = 0x100          # or-ed into the algo: fetch through registers
+FETCH_NAMES = {0: "dma", 1: "reg", 2: "regT"}
 ALGO_NAMES = {v: k for k, v in ALGOS.items()}
+
+
+def algo_code(name: str) -> int:
+    """'lds256' -> 3; 'lds256+reg' -> 3 | REG_FETCH."""
+    base, _, flag = name.partition("+")
+    code = ALGOS[base]
+    if flag == "reg":
+        code |= REG_FETCH
+    elif flag:
+        raise ValueError(name)
+    return code
 MFMA_OPS = {"f32_32x32x16_f16": 0, "f32_16x16x32_f16": 1, "f32_32x32x8_f16": 2,
             "f32_16x16x16_f16": 3}
 
@@ -61,6 +74,9 @@ def _load() -> ctypes.CDLL:
     lib.gemm_tn_validate.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp, i64,
                                      GemmDtypes, P(i32)]
     lib.gemm_tn_validate.restype = ctypes.c_int
+    lib.gemm_tn_plan.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp, i64,
+                                 GemmDtypes, P(i32), P(i32), P(i32)]
+    lib.gemm_tn_plan.restype = ctypes.c_int
     lib.gemm_strerror.argtypes = [ctypes.c_int]
     lib.gemm_strerror.restype = cp
     lib.mfl_kernel_info.argtypes = [i32, GemmDtypes] + [P(i32)] * 6
@@ -117,6 +133,14 @@ def validate(M, N, K, A, lda, B, ldb, C, ldc, D, ldd, dt: GemmDtypes) -> Tuple[i
     return rc, algo.value
 
 
+def plan(M, N, K, A, lda, B, ldb, C, ldc, D, ldd, dt: GemmDtypes):
+    """(code, algo, fetch_a, fetch_b) the call would use, without the GPU."""
+    a, fa, fb = ctypes.c_int32(-1), ctypes.c_int32(-1), ctypes.c_int32(-1)
+    rc = _lib.gemm_tn_plan(M, N, K, A, lda, B, ldb, C, ldc, D, ldd, dt, ctypes.byref(a),
+                           ctypes.byref(fa), ctypes.byref(fb))
+    return rc, a.value, fa.value, fb.value
+
+
 def _kind(t: Optional[torch.Tensor]) -> int:
     if t is None:
         return NONE
@@ -168,7 +192,7 @@ def gemm_tn(A: torch.Tensor, B: torch.Tensor, C: Optional[torch.Tensor] = None,
     if tuple(D.shape) != (M, N) or (D.stride(1) != 1 and N > 1):
         raise ValueError("D must be (M,N) with contiguous rows")
     ldd = max(D.stride(0), max(N, 1)) if M > 1 else max(N, 1)
-    dt = dtypes(_kind(C), _kind(D), a_order, ALGOS[algo])
+    dt = dtypes(_kind(C), _kind(D), a_order, algo_code(algo))
     if stream is None:
         stream = torch.cuda.current_stream(A.device).cuda_stream
     rc = gemm_tn_raw(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb,
@@ -179,7 +203,7 @@ def gemm_tn(A: torch.Tensor, B: torch.Tensor, C: Optional[torch.Tensor] = None,
 
 def kernel_info(algo: str, c: int = NONE, d: int = F32, a_order: int = A_KMAJOR) -> dict:
     vals = [ctypes.c_int32(-1) for _ in range(6)]
-    rc = _lib.mfl_kernel_info(ALGOS[algo], dtypes(c, d, a_order, ALGOS[algo]),
+    rc = _lib.mfl_kernel_info(algo_code(algo), dtypes(c, d, a_order, algo_code(algo)),
                               *[ctypes.byref(v) for v in vals])
     _check(rc)
     keys = ("bm", "bn", "bk", "threads", "lds_bytes", "scratch_bytes")
@@ -248,10 +272,10 @@ def fragment_coords(algo: str, operand: str) -> np.ndarray:
     """(threads, slots, 2) int32 array of the kernel's per-lane coordinates."""
     opnd = {"A": 0, "B": 1, "C": 2}[operand]
     t, s = ctypes.c_int32(), ctypes.c_int32()
-    _lay_check(_lib.mfl_fragment_coords(ALGOS[algo], opnd, None, 0, ctypes.byref(t),
+    _lay_check(_lib.mfl_fragment_coords(algo_code(algo), opnd, None, 0, ctypes.byref(t),
                                         ctypes.byref(s)), algo)
     out = np.empty((t.value, s.value, 2), dtype=np.int32)
-    _lay_check(_lib.mfl_fragment_coords(ALGOS[algo], opnd, out.ctypes.data, out.size,
+    _lay_check(_lib.mfl_fragment_coords(algo_code(algo), opnd, out.ctypes.data, out.size,
                                         ctypes.byref(t), ctypes.byref(s)), algo)
     return out
 

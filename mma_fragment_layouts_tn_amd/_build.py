@@ -18,7 +18,8 @@ OUT = os.path.join(PKG, "libmfl_gemm.so")
 OBJDIR = os.path.join(os.path.dirname(PKG), "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["gemm_kernels.hip", "probe_kernels.hip", "capi.cpp"]
+SOURCES = ["gemm_inst_256.hip", "gemm_inst_256w4.hip", "gemm_inst_128.hip",
+           "gemm_dispatch.hip", "probe_kernels.hip", "capi.cpp"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-mcode-object-version=5",

@@ -33,28 +33,30 @@ bool span_fits(int64_t rows, int64_t ld, int64_t cols) {
   return last * 2 < ((int64_t)1 << 31) - 64;
 }
 
-// direct-to-LDS loads move whole 16-byte chunks: rows and bases must be
-// 16-byte aligned and K contiguous
-bool dma_ok(bool a_mmajor, const void* A, int64_t lda, const void* B, int64_t ldb) {
-  return !a_mmajor && ((uintptr_t)A % 16 == 0) && ((uintptr_t)B % 16 == 0) && (lda % 8 == 0) &&
-         (ldb % 8 == 0);
-}
+// direct-to-LDS loads move whole 16-byte chunks: the base and every row
+// start must be 16-byte aligned
+bool dma_ok(const void* X, int64_t ld) { return ((uintptr_t)X % 16 == 0) && (ld % 8 == 0); }
 
-int pick_algo(int64_t M, int64_t N, int64_t K, bool a_mmajor, const void* A, int64_t lda,
-              const void* B, int64_t ldb) {
+int pick_algo(int64_t M, int64_t N, int64_t K) {
   (void)K;
   const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
-  if (t256 >= 192) return dma_ok(a_mmajor, A, lda, B, ldb) ? mfl::kAlgoDma256W8 : mfl::kAlgoLds256;
-  return mfl::kAlgoLds128;
+  return t256 >= 192 ? mfl::kAlgoLds256 : mfl::kAlgoLds128;
 }
+
+struct Plan {
+  int algo, fetch_a, fetch_b;
+};
 
 int check(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
           int64_t ldb, const void* C, int64_t ldc, const void* D, int64_t ldd,
-          gemm_dtypes_t dt, int32_t* algo_out) {
+          gemm_dtypes_t dt, Plan* plan) {
   if (M < 0 || N < 0 || K < 0) return MFL_E_NEGATIVE_DIM;
   if (dt.a != MFL_F16 || dt.b != MFL_F16 || !dtype_ok_cd(dt.c, dt.d)) return MFL_E_UNSUPPORTED;
   if (dt.a_order != MFL_A_KMAJOR && dt.a_order != MFL_A_MMAJOR) return MFL_E_UNSUPPORTED;
-  if (dt.algo < 0 || dt.algo >= MFL_ALGO_COUNT) return MFL_E_UNSUPPORTED;
+  if (dt.algo & ~(MFL_ALGO_MASK | MFL_ALGO_REG_FETCH)) return MFL_E_UNSUPPORTED;
+  int algo = dt.algo & MFL_ALGO_MASK;
+  const bool force_reg = (dt.algo & MFL_ALGO_REG_FETCH) != 0;
+  if (algo >= MFL_ALGO_COUNT) return MFL_E_UNSUPPORTED;
   const bool mm = dt.a_order == MFL_A_MMAJOR;
   const int64_t one = 1;
   if (lda < (mm ? (M > one ? M : one) : (K > one ? K : one))) return MFL_E_LEADING_DIM;
@@ -75,17 +77,18 @@ int check(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const voi
     return MFL_E_TOO_LARGE;
   if (mm ? !span_fits(K, lda, M) : !span_fits(M, lda, K)) return MFL_E_TOO_LARGE;
   if (!span_fits(N, ldb, K)) return MFL_E_TOO_LARGE;
-  int algo = dt.algo;
-  if (algo == MFL_ALGO_AUTO) algo = pick_algo(M, N, K, mm, A, lda, B, ldb);
+  if (algo == MFL_ALGO_AUTO) algo = pick_algo(M, N, K);
   if (algo == MFL_ALGO_DIRECT && mm) return MFL_E_ALGO_CASE;
-  if ((algo == MFL_ALGO_LDS_256_DMA || algo == MFL_ALGO_LDS_256_DMA_W8) &&
-      !dma_ok(mm, A, lda, B, ldb))
-    return MFL_E_ALGO_CASE;
   const mfl::KernelInfo ki = mfl::kernel_info(algo);
   if (ki.algo < 0) return MFL_E_UNSUPPORTED;
   const int64_t tiles = ((M + ki.bm - 1) / ki.bm) * ((N + ki.bn - 1) / ki.bn);
   if (tiles > INT_MAX) return MFL_E_TOO_LARGE;
-  if (algo_out) *algo_out = algo;
+  if (plan) {
+    plan->algo = algo;
+    plan->fetch_a = mm ? mfl::kFetchRegT
+                       : (!force_reg && dma_ok(A, lda) ? mfl::kFetchDma : mfl::kFetchReg);
+    plan->fetch_b = !force_reg && dma_ok(B, ldb) ? mfl::kFetchDma : mfl::kFetchReg;
+  }
   return MFL_OK;
 }
 
@@ -279,17 +282,33 @@ extern "C" {
 int gemm_tn_validate(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                      const void* B, int64_t ldb, const void* C, int64_t ldc, const void* D,
                      int64_t ldd, gemm_dtypes_t dtypes, int32_t* algo_out) {
-  return check(M, N, K, A, lda, B, ldb, C, ldc, D, ldd, dtypes, algo_out);
+  Plan plan{};
+  const int rc = check(M, N, K, A, lda, B, ldb, C, ldc, D, ldd, dtypes, &plan);
+  if (rc == MFL_OK && algo_out) *algo_out = plan.algo;
+  return rc;
+}
+
+int gemm_tn_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                 int64_t ldb, const void* C, int64_t ldc, const void* D, int64_t ldd,
+                 gemm_dtypes_t dtypes, int32_t* algo, int32_t* fetch_a, int32_t* fetch_b) {
+  Plan plan{};
+  const int rc = check(M, N, K, A, lda, B, ldb, C, ldc, D, ldd, dtypes, &plan);
+  if (rc == MFL_OK) {
+    if (algo) *algo = plan.algo;
+    if (fetch_a) *fetch_a = plan.fetch_a;
+    if (fetch_b) *fetch_b = plan.fetch_b;
+  }
+  return rc;
 }
 
 int gemm_tn(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
             int64_t ldb, const void* C, int64_t ldc, void* D, int64_t ldd,
             gemm_dtypes_t dtypes, void* stream) {
-  int32_t algo = 0;
-  const int rc = check(M, N, K, A, lda, B, ldb, C, ldc, D, ldd, dtypes, &algo);
+  Plan plan{};
+  const int rc = check(M, N, K, A, lda, B, ldb, C, ldc, D, ldd, dtypes, &plan);
   if (rc != MFL_OK) return rc;
   if (M == 0 || N == 0) return MFL_OK;
-  const mfl::KernelInfo ki = mfl::kernel_info(algo);
+  const mfl::KernelInfo ki = mfl::kernel_info(plan.algo);
   GemmParams p{};
   p.M = (int)M;
   p.N = (int)N;
@@ -305,7 +324,7 @@ int gemm_tn(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const v
   p.B = B;
   p.C = C;
   p.D = D;
-  const int lr = mfl::launch_gemm(algo, dtypes.a_order == MFL_A_MMAJOR, dtypes.c, dtypes.d, p,
+  const int lr = mfl::launch_gemm(plan.algo, plan.fetch_a, plan.fetch_b, dtypes.c, dtypes.d, p,
                                   (hipStream_t)stream);
   return lr == 0 ? MFL_OK : (lr == -1 ? MFL_E_UNSUPPORTED : MFL_E_LAUNCH);
 }
@@ -328,13 +347,15 @@ const char* gemm_strerror(int code) {
 
 int mfl_kernel_info(int32_t algo, gemm_dtypes_t dt, int32_t* bm, int32_t* bn, int32_t* bk,
                     int32_t* threads, int32_t* lds_bytes, int32_t* vgprs_spilled) {
+  algo &= MFL_ALGO_MASK;
   const mfl::KernelInfo ki = mfl::kernel_info(algo);
   if (ki.algo < 0 || !dtype_ok_cd(dt.c, dt.d)) return MFL_E_UNSUPPORTED;
   if (bm) *bm = ki.bm;
   if (bn) *bn = ki.bn;
   if (bk) *bk = ki.bk;
   if (threads) *threads = ki.threads;
-  const void* fn = mfl::kernel_symbol(algo, dt.a_order == MFL_A_MMAJOR, dt.c, dt.d);
+  const int fa = dt.a_order == MFL_A_MMAJOR ? mfl::kFetchRegT : mfl::kFetchDma;
+  const void* fn = mfl::kernel_symbol(algo, fa, mfl::kFetchDma, dt.c, dt.d);
   if (!fn) return MFL_E_ALGO_CASE;
   if (lds_bytes || vgprs_spilled) {
     hipFuncAttributes attr{};
@@ -423,8 +444,7 @@ int mfl_fragment_coords(int32_t algo, int32_t operand, int32_t* out, int64_t cap
     case mfl::kAlgoDirect: return frag_coords<mfl::CfgDirect>(operand, out, cap, threads, slots);
     case mfl::kAlgoLds128: return frag_coords<mfl::CfgLds128>(operand, out, cap, threads, slots);
     case mfl::kAlgoLds256: return frag_coords<mfl::CfgLds256>(operand, out, cap, threads, slots);
-    case mfl::kAlgoDma256: return frag_coords<mfl::CfgDma256>(operand, out, cap, threads, slots);
-    case mfl::kAlgoDma256W8: return frag_coords<mfl::CfgDma256W8>(operand, out, cap, threads, slots);
+    case mfl::kAlgoLds256W4: return frag_coords<mfl::CfgLds256W4>(operand, out, cap, threads, slots);
     default: return mfl::kLayoutBadIndex;
   }
 }

@@ -1,0 +1,51 @@
+// Kernel registry: tile shapes, symbol lookup and launch.
+#include <hip/hip_runtime.h>
+
+#include "gemm_launch.hpp"
+
+namespace mfl {
+
+const void* tiled_symbol_128(int fa, int fb, int ck, int dk);
+const void* tiled_symbol_256(int fa, int fb, int ck, int dk);
+const void* tiled_symbol_256w4(int fa, int fb, int ck, int dk);
+const void* direct_symbol(int ck, int dk);
+
+namespace {
+template <class Cfg>
+KernelInfo info_of(int algo) {
+  return KernelInfo{algo, Cfg::BM, Cfg::BN, Cfg::BK, Cfg::kThreads};
+}
+}  // namespace
+
+KernelInfo kernel_info(int algo) {
+  switch (algo) {
+    case kAlgoDirect: return info_of<CfgDirect>(algo);
+    case kAlgoLds128: return info_of<CfgLds128>(algo);
+    case kAlgoLds256: return info_of<CfgLds256>(algo);
+    case kAlgoLds256W4: return info_of<CfgLds256W4>(algo);
+    default: return KernelInfo{-1, 0, 0, 0, 0};
+  }
+}
+
+const void* kernel_symbol(int algo, int fetch_a, int fetch_b, int c_kind, int d_kind) {
+  switch (algo) {
+    case kAlgoDirect: return fetch_a == kFetchRegT ? nullptr : direct_symbol(c_kind, d_kind);
+    case kAlgoLds128: return tiled_symbol_128(fetch_a, fetch_b, c_kind, d_kind);
+    case kAlgoLds256: return tiled_symbol_256(fetch_a, fetch_b, c_kind, d_kind);
+    case kAlgoLds256W4: return tiled_symbol_256w4(fetch_a, fetch_b, c_kind, d_kind);
+    default: return nullptr;
+  }
+}
+
+int launch_gemm(int algo, int fetch_a, int fetch_b, int c_kind, int d_kind, const GemmParams& p,
+                hipStream_t stream) {
+  const void* fn = kernel_symbol(algo, fetch_a, fetch_b, c_kind, d_kind);
+  const KernelInfo ki = kernel_info(algo);
+  if (!fn || ki.algo < 0) return -1;
+  const int64_t nb = (int64_t)p.tiles_m * p.tiles_n;
+  void* args[] = {(void*)&p};
+  const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)nb), dim3(ki.threads), args, 0, stream);
+  return e == hipSuccess ? 0 : -2;
+}
+
+}  // namespace mfl

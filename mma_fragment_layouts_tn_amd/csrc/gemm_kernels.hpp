@@ -1,0 +1,480 @@
+// gfx950 kernels for D = C + A * B^T with fp16 A (M,K), B (N,K).
+//
+// Two kernel families (tile structure in gemm_tile.hpp):
+//  * gemm_tiled: the block tile is staged through LDS in two stages.  This is
+//    the shared-memory GEMM the simple-GEMM page names as the faster
+//    successor of its global-only kernel ("cute(7) simple_gemm" §10), with the
+//    block tile and shared-memory layout choices of "CuTe Layout 到 Tensor
+//    Core" §4-5.  Each operand is fetched by one of three policies:
+//      DMA   global_load_lds_dwordx4 straight into LDS (K-contiguous rows,
+//            16-byte aligned);
+//      REG   16-byte loads into registers (any 2-byte alignment), written to
+//            LDS one step later;
+//      REGT  M-contiguous A: 4 k-rows x 8 m loaded into registers, transposed
+//            in registers to 8 runs of 4 k, written with 8-byte LDS stores.
+//    Per K-step: fragment reads for sub-step kk+1 overlap the MFMAs of kk;
+//    register-staged tiles are written to the idle stage before the step's
+//    single barrier; right after the barrier the fetch of tile kt+2 is
+//    issued (it has a whole step to land) and the first fragments of the next
+//    stage are read while the last sub-step's MFMAs are still queued.
+//  * gemm_direct: the global-only kernel of the simple-GEMM page (§1, §3.4):
+//    every lane reads its operand fragments straight from global memory into
+//    registers, no LDS at all.
+// Both accumulate in fp32 with v_mfma_f32_32x32x16_f16 and finish with the
+// epilogue D = acc + C, rounded once to fp16 (nearest even) when D is fp16.
+//
+// Edges (partial tiles, which the TiledMMA page leaves to the caller,
+// section "打印布局，核对一次"): operand rows past M or N are clamped to the
+// last row (they only feed outputs that are never stored); a K remainder is
+// staged once with zero fill in BOTH operands (0 * Inf would be NaN); stores
+// are predicated.
+#include <hip/hip_runtime.h>
+
+#pragma once
+
+#include "gemm_launch.hpp"
+#include "gemm_tile.hpp"
+
+namespace mfl {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+using lds_ptr_t = __attribute__((address_space(3))) void*;
+
+// 16-byte global load at any 2-byte alignment (gfx9 runs in unaligned access
+// mode, so this is one global_load_dwordx4 either way).
+__device__ __forceinline__ uint4 load16(const char* base, int64_t byte_off) {
+  uint4 v;
+  __builtin_memcpy(&v, base + byte_off, 16);
+  return v;
+}
+
+// 8 consecutive elements of which the first `valid` are read, the rest zero.
+__device__ __forceinline__ uint4 load8_tail(const _Float16* p, int valid) {
+  union {
+    uint4 u;
+    _Float16 h[8];
+  } r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r.h[e] = e < valid ? p[e] : (_Float16)0.0f;
+  return r.u;
+}
+
+__device__ __forceinline__ half8 as_half8(uint4 u) {
+  half8 h;
+  __builtin_memcpy(&h, &u, 16);
+  return h;
+}
+
+template <int CK>
+__device__ __forceinline__ float c_value(const GemmParams& p, int m, int n) {
+  if constexpr (CK == 1) return (float)((const _Float16*)p.C)[(int64_t)m * p.ldc + n];
+  if constexpr (CK == 2) return ((const float*)p.C)[(int64_t)m * p.ldc + n];
+  return 0.0f;
+}
+
+template <int DK>
+__device__ __forceinline__ void d_store(const GemmParams& p, int m, int n, float x) {
+  if constexpr (DK == 1)
+    ((_Float16*)p.D)[(int64_t)m * p.ldd + n] = (_Float16)x;   // v_cvt_f16_f32, RNE
+  else
+    ((float*)p.D)[(int64_t)m * p.ldd + n] = x;
+}
+
+// Epilogue shared by both kernels: acc[i][j] value v -> (m, n) from the
+// accumulator TV layout.
+template <class Cfg, int CK, int DK>
+__device__ __forceinline__ void epilogue(const GemmParams& p, int w, int lane, int m0,
+                                         int n0, const floatx16 (&acc)[Cfg::RM][Cfg::RN]) {
+#pragma unroll
+  for (int i = 0; i < Cfg::RM; ++i)
+#pragma unroll
+    for (int j = 0; j < Cfg::RN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const RowK c = frag_c_coord<Cfg>(w, lane, i, j, v);
+        const int m = m0 + c.row, n = n0 + c.k;
+        if (m < p.M && n < p.N) d_store<DK>(p, m, n, acc[i][j][v] + c_value<CK>(p, m, n));
+      }
+}
+
+// ---------------------------------------------------------------------------
+// Operand fetchers: one operand tile (ROWS x BK halves) per stage
+// ---------------------------------------------------------------------------
+// Common interface:
+//   init(row0, rows_valid, ld, tid, w, lane)   per-thread offsets, once
+//   issue(base, kt, stage_ptr)                 start fetching K-tile kt
+//   stash(stage_ptr)                           registers -> LDS (REG policies)
+
+// DMA: global_load_lds_dwordx4 writes the 64 lanes' 16-byte chunks to 1 KB of
+// LDS after M0, lane l at byte 16 l.  A 1 KB run holds RUN = 512/BK rows; lane
+// l takes row RUN*run + l/CH, physical chunk l%CH, so it fetches logical chunk
+// (l%CH) ^ swz(row) of that row.
+template <class Cfg, int ROWS>
+struct FetchDma {
+  static constexpr int BK = Cfg::BK, CH = Cfg::CH, RUN = 512 / BK;
+  static constexpr int kRuns = ROWS / RUN / Cfg::kWaves;
+  static_assert(ROWS % (RUN * Cfg::kWaves) == 0, "runs must divide over the waves");
+  unsigned off[kRuns];
+  int run0;
+  __device__ void init(int row0, int rows_valid, int ld, int tid, int w, int lane) {
+    (void)tid;
+    run0 = w * kRuns;
+    const int rsub = lane / CH;
+#pragma unroll
+    for (int i = 0; i < kRuns; ++i) {
+      const int row = RUN * (run0 + i) + rsub;
+      const int kc = ((lane % CH) ^ swz<CH>(row)) * 8;
+      off[i] = (unsigned)((int64_t)min(row0 + row, row0 + rows_valid - 1) * ld * 2) + kc * 2;
+    }
+  }
+  __device__ void issue(const void* base, int kt, _Float16* stage) {
+    const char* b = (const char*)base + (int64_t)kt * BK * 2;
+#pragma unroll
+    for (int i = 0; i < kRuns; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(b + (uint64_t)off[i]),
+                                       (lds_ptr_t)(stage + (run0 + i) * RUN * BK), 16, 0, 0);
+  }
+  __device__ void stash(_Float16*) {}
+};
+
+// REG: K-contiguous rows, 16-byte chunks q = tid + i*T (row q/CH, chunk q%CH)
+template <class Cfg, int ROWS>
+struct FetchReg {
+  static constexpr int BK = Cfg::BK, CH = Cfg::CH, T = Cfg::kThreads;
+  static constexpr int kChunks = ROWS * CH / T;
+  static_assert((ROWS * CH) % T == 0, "chunks must divide over the threads");
+  int off[kChunks], lds[kChunks];
+  uint4 r[kChunks];
+  __device__ void init(int row0, int rows_valid, int ld, int tid, int w, int lane) {
+    (void)w;
+    (void)lane;
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+      const int q = tid + i * T, row = q / CH, c = q % CH;
+      off[i] = (int)((int64_t)min(row0 + row, row0 + rows_valid - 1) * ld * 2) + c * 16;
+      lds[i] = lds_offset<BK>(row, c * 8);
+    }
+  }
+  __device__ void issue(const void* base, int kt, _Float16*) {
+    const char* b = (const char*)base + (int64_t)kt * BK * 2;
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) r[i] = load16(b, off[i]);
+  }
+  __device__ void stash(_Float16* stage) {
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) *(uint4*)&stage[lds[i]] = r[i];
+  }
+};
+
+// REGT: M-contiguous A.  Chunk = KR k-rows x 8 m (KR 16-byte loads, one
+// per k-row); transposed in registers into 8 runs of KR k, one per m, and
+// written with KR*2-byte LDS stores into the K-contiguous tile.  KR = 4 when
+// the chunks divide over the threads, else 2.
+template <class Cfg, int ROWS>
+struct FetchRegT {
+  static constexpr int BK = Cfg::BK, T = Cfg::kThreads;
+  static constexpr int KR = ((BK / 4) * (ROWS / 8)) % T == 0 ? 4 : 2;
+  static constexpr int kChunks = (BK / KR) * (ROWS / 8) / T;
+  static_assert(((BK / KR) * (ROWS / 8)) % T == 0 && kChunks > 0,
+                "chunks must divide over the threads");
+  int off[kChunks], mvalid[kChunks], lds_k[kChunks], lds_m[kChunks];
+  int ld;
+  uint4 r[kChunks][KR];
+  __device__ void init(int row0, int rows_valid, int ld_, int tid, int w, int lane) {
+    (void)w;
+    (void)lane;
+    ld = ld_;
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+      const int q = tid + i * T, kg = q / (ROWS / 8), mc = q % (ROWS / 8);
+      off[i] = (int)((int64_t)kg * KR * ld * 2) + (row0 + mc * 8) * 2;
+      mvalid[i] = rows_valid - mc * 8;
+      lds_k[i] = kg * KR;
+      lds_m[i] = mc * 8;
+    }
+  }
+  __device__ void issue(const void* base, int kt, _Float16*) {
+    const char* b = (const char*)base + (int64_t)kt * BK * ld * 2;
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i)
+#pragma unroll
+      for (int rr = 0; rr < KR; ++rr) {
+        const int64_t o = off[i] + (int64_t)rr * ld * 2;
+        r[i][rr] = mvalid[i] >= 8 ? load16(b, o)
+                   : mvalid[i] <= 0 ? make_uint4(0, 0, 0, 0)
+                                    : load8_tail((const _Float16*)(b + o), mvalid[i]);
+      }
+  }
+  // halves e of two 8-half vectors x, y packed as (x[e], y[e])
+  __device__ static unsigned pack(const uint4& x, const uint4& y, int e) {
+    const unsigned* a = (const unsigned*)&x;
+    const unsigned* b = (const unsigned*)&y;
+    const int d = e >> 1;
+    return (e & 1) ? ((a[d] >> 16) | (b[d] & 0xffff0000u)) : ((a[d] & 0xffffu) | (b[d] << 16));
+  }
+  __device__ void stash(_Float16* stage) {
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        _Float16* dst = &stage[lds_offset<BK>(lds_m[i] + e, lds_k[i])];
+        if constexpr (KR == 4)
+          *(uint2*)dst = make_uint2(pack(r[i][0], r[i][1], e), pack(r[i][2], r[i][3], e));
+        else
+          *(unsigned*)dst = pack(r[i][0], r[i][1], e);
+      }
+    }
+  }
+};
+
+template <class Cfg, int ROWS, int POLICY>
+struct FetchSel;
+template <class Cfg, int ROWS>
+struct FetchSel<Cfg, ROWS, kFetchDma> {
+  using type = FetchDma<Cfg, ROWS>;
+};
+template <class Cfg, int ROWS>
+struct FetchSel<Cfg, ROWS, kFetchReg> {
+  using type = FetchReg<Cfg, ROWS>;
+};
+template <class Cfg, int ROWS>
+struct FetchSel<Cfg, ROWS, kFetchRegT> {
+  using type = FetchRegT<Cfg, ROWS>;
+};
+
+// ---------------------------------------------------------------------------
+// LDS-staged pipelined kernel
+// ---------------------------------------------------------------------------
+template <class Cfg, int FA, int FB, int CK, int DK>
+__global__ void __launch_bounds__(Cfg::kThreads, 1) gemm_tiled(const GemmParams p) {
+  constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK;
+  constexpr int RM = Cfg::RM, RN = Cfg::RN, KSUB = Cfg::KSUB;
+  static_assert(KSUB % 2 == 0, "fragment buffers alternate per K sub-step");
+  static_assert(FB != kFetchRegT, "B is always K-contiguous");
+  // stage s: A at smem + s*kStage, B at smem + s*kStage + BM*BK (halves)
+  constexpr int kStage = (BM + BN) * BK;
+  __shared__ __attribute__((aligned(1024))) _Float16 smem[2 * kStage];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const TileIndex ti = tile_of_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m);
+  const int m0 = ti.tm * BM, n0 = ti.tn * BN;
+
+  typename FetchSel<Cfg, BM, FA>::type fa_;
+  typename FetchSel<Cfg, BN, FB>::type fb_;
+  fa_.init(m0, p.M - m0, p.lda, tid, w, lane);
+  fb_.init(n0, p.N - n0, p.ldb, tid, w, lane);
+  auto stage_a = [&](int s) { return smem + s * kStage; };
+  auto stage_b = [&](int s) { return smem + s * kStage + BM * BK; };
+  auto issue = [&](int kt, int s) {
+    fa_.issue(p.A, kt, stage_a(s));
+    fb_.issue(p.B, kt, stage_b(s));
+  };
+  auto stash = [&](int s) {
+    fa_.stash(stage_a(s));
+    fb_.stash(stage_b(s));
+  };
+  constexpr bool kAnyReg = FA != kFetchDma || FB != kFetchDma;
+
+  // fragment read offsets within a stage (halves), per K sub-step
+  int fa_off[KSUB][RM], fb_off[KSUB][RN];
+#pragma unroll
+  for (int kk = 0; kk < KSUB; ++kk) {
+#pragma unroll
+    for (int i = 0; i < RM; ++i) {
+      const RowK a = frag_a_coord<Cfg>(w, lane, i, kk);
+      fa_off[kk][i] = lds_offset<BK>(a.row, a.k);
+    }
+#pragma unroll
+    for (int j = 0; j < RN; ++j) {
+      const RowK b = frag_b_coord<Cfg>(w, lane, j, kk);
+      fb_off[kk][j] = BM * BK + lds_offset<BK>(b.row, b.k);
+    }
+  }
+
+  half8 fa[2][RM], fb[2][RN];
+  auto frags = [&](int buf, int kk, int s) {
+    const _Float16* st = smem + s * kStage;
+#pragma unroll
+    for (int i = 0; i < RM; ++i) fa[buf][i] = *(const half8*)&st[fa_off[kk][i]];
+#pragma unroll
+    for (int j = 0; j < RN; ++j) fb[buf][j] = *(const half8*)&st[fb_off[kk][j]];
+  };
+
+  floatx16 acc[RM][RN];
+#pragma unroll
+  for (int i = 0; i < RM; ++i)
+#pragma unroll
+    for (int j = 0; j < RN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  auto mma = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < RM; ++i)
+#pragma unroll
+      for (int j = 0; j < RN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
+  };
+  // spread a group's fragment reads between its MFMAs
+  constexpr int kReads = RM + RN, kMfma = RM * RN;
+  auto interleave = [&]() {
+#pragma unroll
+    for (int g = 0; g < kReads; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, kMfma / kReads > 0 ? kMfma / kReads : 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kMfma, 0);
+  };
+
+  const int nfull = p.K / BK;
+  if (nfull > 0) {
+    issue(0, 0);
+    if constexpr (kAnyReg) stash(0);
+    if (nfull > 1) issue(1, 1);       // REG operands: held in registers until step 0
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    frags(0, 0, 0);
+  }
+  for (int kt = 0; kt < nfull; ++kt) {
+    const int cur = kt & 1;
+#pragma unroll
+    for (int kk = 0; kk + 1 < KSUB; ++kk) {
+      frags((kk + 1) & 1, kk + 1, cur);
+      mma(kk & 1);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // register-staged tile kt+1 goes to the idle stage before the barrier
+    if constexpr (kAnyReg) {
+      if (kt + 1 < nfull) stash(cur ^ 1);
+    }
+    __builtin_amdgcn_s_waitcnt(0);        // own reads, stores and fetch of tile kt+1 done
+    __builtin_amdgcn_s_barrier();         // ... in every wave: stage cur is free
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + 2 < nfull) issue(kt + 2, cur);
+    if (kt + 1 < nfull) frags(0, 0, cur ^ 1);
+    mma((KSUB - 1) & 1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // K remainder: one step staged element by element with zero fill
+  if (p.K % BK != 0) {
+    const int k0 = nfull * BK;
+    __syncthreads();
+    _Float16* sa = stage_a(0);
+    _Float16* sb = stage_b(0);
+    const _Float16* A = (const _Float16*)p.A;
+    const _Float16* B = (const _Float16*)p.B;
+    for (int e = tid; e < BM * BK; e += Cfg::kThreads) {
+      const int row = e / BK, k = e % BK, gk = k0 + k;
+      const int gm = min(m0 + row, p.M - 1);
+      _Float16 v = (_Float16)0.0f;
+      if (gk < p.K)
+        v = FA == kFetchRegT ? A[(int64_t)gk * p.lda + gm] : A[(int64_t)gm * p.lda + gk];
+      sa[lds_offset<BK>(row, k)] = v;
+    }
+    for (int e = tid; e < BN * BK; e += Cfg::kThreads) {
+      const int row = e / BK, k = e % BK, gk = k0 + k;
+      const int gn = min(n0 + row, p.N - 1);
+      sb[lds_offset<BK>(row, k)] = gk < p.K ? B[(int64_t)gn * p.ldb + gk] : (_Float16)0.0f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < KSUB; ++kk) {
+      frags(0, kk, 0);
+      mma(0);
+    }
+  }
+  epilogue<Cfg, CK, DK>(p, w, lane, m0, n0, acc);
+}
+
+// ---------------------------------------------------------------------------
+// Direct kernel: fragments from global memory, no LDS
+// ---------------------------------------------------------------------------
+template <class Cfg, int CK, int DK>
+__global__ void __launch_bounds__(Cfg::kThreads, 1) gemm_direct(const GemmParams p) {
+  constexpr int BK = Cfg::BK;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const TileIndex ti = tile_of_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m);
+  const int m0 = ti.tm * Cfg::BM, n0 = ti.tn * Cfg::BN;
+  const _Float16* A = (const _Float16*)p.A;
+  const _Float16* B = (const _Float16*)p.B;
+
+  floatx16 acc[Cfg::RM][Cfg::RN];
+#pragma unroll
+  for (int i = 0; i < Cfg::RM; ++i)
+#pragma unroll
+    for (int j = 0; j < Cfg::RN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  const int nk = (p.K + BK - 1) / BK;
+  for (int kt = 0; kt < nk; ++kt) {
+#pragma unroll
+    for (int kk = 0; kk < Cfg::KSUB; ++kk) {
+      half8 af[Cfg::RM], bf[Cfg::RN];
+#pragma unroll
+      for (int i = 0; i < Cfg::RM; ++i) {
+        const RowK a = frag_a_coord<Cfg>(w, lane, i, kk);
+        const int m = min(m0 + a.row, p.M - 1);
+        const int k = kt * BK + a.k;
+        const _Float16* src = A + (int64_t)m * p.lda + k;
+        const int valid = p.K - k;
+        af[i] = as_half8(valid >= 8 ? load16((const char*)src, 0)
+                         : valid <= 0 ? make_uint4(0, 0, 0, 0)
+                                      : load8_tail(src, valid));
+      }
+#pragma unroll
+      for (int j = 0; j < Cfg::RN; ++j) {
+        const RowK b = frag_b_coord<Cfg>(w, lane, j, kk);
+        const int n = min(n0 + b.row, p.N - 1);
+        const int k = kt * BK + b.k;
+        const _Float16* src = B + (int64_t)n * p.ldb + k;
+        const int valid = p.K - k;
+        bf[j] = as_half8(valid >= 8 ? load16((const char*)src, 0)
+                         : valid <= 0 ? make_uint4(0, 0, 0, 0)
+                                      : load8_tail(src, valid));
+      }
+#pragma unroll
+      for (int i = 0; i < Cfg::RM; ++i)
+#pragma unroll
+        for (int j = 0; j < Cfg::RN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+  }
+  epilogue<Cfg, CK, DK>(p, w, lane, m0, n0, acc);
+}
+
+// ---------------------------------------------------------------------------
+// instantiation tables (one translation unit per tile configuration)
+// ---------------------------------------------------------------------------
+using KernelFn = void (*)(const GemmParams);
+
+// [c_kind][d_kind-1]
+template <class Cfg, int FA, int FB>
+constexpr KernelFn tiled_table[3][2] = {
+    {gemm_tiled<Cfg, FA, FB, 0, 1>, gemm_tiled<Cfg, FA, FB, 0, 2>},
+    {gemm_tiled<Cfg, FA, FB, 1, 1>, gemm_tiled<Cfg, FA, FB, 1, 2>},
+    {gemm_tiled<Cfg, FA, FB, 2, 1>, gemm_tiled<Cfg, FA, FB, 2, 2>}};
+
+// fetch policy pairs used: (A, B) = (DMA, DMA), (REG, REG), (REG, DMA),
+// (DMA, REG), (REGT, DMA), (REGT, REG)
+template <class Cfg>
+const void* tiled_symbol(int fa, int fb, int ck, int dk) {
+  if (ck < 0 || ck > 2 || dk < 1 || dk > 2) return nullptr;
+  if (fa == kFetchDma && fb == kFetchDma) return (const void*)tiled_table<Cfg, kFetchDma, kFetchDma>[ck][dk - 1];
+  if (fa == kFetchReg && fb == kFetchReg) return (const void*)tiled_table<Cfg, kFetchReg, kFetchReg>[ck][dk - 1];
+  if (fa == kFetchReg && fb == kFetchDma) return (const void*)tiled_table<Cfg, kFetchReg, kFetchDma>[ck][dk - 1];
+  if (fa == kFetchDma && fb == kFetchReg) return (const void*)tiled_table<Cfg, kFetchDma, kFetchReg>[ck][dk - 1];
+  if (fa == kFetchRegT && fb == kFetchDma) return (const void*)tiled_table<Cfg, kFetchRegT, kFetchDma>[ck][dk - 1];
+  if (fa == kFetchRegT && fb == kFetchReg) return (const void*)tiled_table<Cfg, kFetchRegT, kFetchReg>[ck][dk - 1];
+  return nullptr;
+}
+
+}  // namespace
+}  // namespace mfl

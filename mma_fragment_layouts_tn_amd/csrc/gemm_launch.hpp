@@ -26,29 +26,35 @@ enum Algo : int {
   kAlgoAuto = 0,
   kAlgoDirect = 1,
   kAlgoLds128 = 2,
-  kAlgoLds256 = 3,
-  kAlgoDma256 = 4,     // direct-to-LDS fetch, 4 waves of 128x128
-  kAlgoDma256W8 = 5,   // direct-to-LDS fetch, 8 waves of 128x64
-  kAlgoCount = 6
+  kAlgoLds256 = 3,      // 8 waves of 128x64
+  kAlgoLds256W4 = 4,    // 4 waves of 128x128
+  kAlgoCount = 5
 };
-using CfgDma256 = TileCfg<256, 256, 64, 2, 2>;
-using CfgDma256W8 = TileCfg<256, 256, 64, 2, 4>;
+
+// how an operand tile travels from global memory to LDS
+enum Fetch : int {
+  kFetchDma = 0,    // global_load_lds_dwordx4 (K-contiguous, 16-byte aligned rows)
+  kFetchReg = 1,    // 16-byte loads into registers, any 2-byte alignment
+  kFetchRegT = 2,   // M-contiguous A, transposed in registers
+};
 
 // direct-from-global: 128x128 block (the simple-GEMM page's CTA tile), 2x2 waves
 using CfgDirect = TileCfg<128, 128, 32, 2, 2>;
-// LDS-staged 128x128x32 block tile, 2x2 waves of 64x64
+// 128x128x32 block tile, 2x2 waves of 64x64
 using CfgLds128 = TileCfg<128, 128, 32, 2, 2>;
-// LDS-staged 256x256x64 block tile, 2x2 waves of 128x128
-using CfgLds256 = TileCfg<256, 256, 64, 2, 2>;
+// 256x256x64 block tile, 2x4 waves of 128x64 (two waves per SIMD)
+using CfgLds256 = TileCfg<256, 256, 64, 2, 4>;
+// 256x256x64 block tile, 2x2 waves of 128x128 (one wave per SIMD)
+using CfgLds256W4 = TileCfg<256, 256, 64, 2, 2>;
 
 struct KernelInfo {
   int algo, bm, bn, bk, threads;
 };
 
 KernelInfo kernel_info(int algo);
-const void* kernel_symbol(int algo, bool a_mmajor, int c_kind, int d_kind);
+const void* kernel_symbol(int algo, int fetch_a, int fetch_b, int c_kind, int d_kind);
 // 0 ok, -1 no such kernel, -2 launch error
-int launch_gemm(int algo, bool a_mmajor, int c_kind, int d_kind, const GemmParams& p,
+int launch_gemm(int algo, int fetch_a, int fetch_b, int c_kind, int d_kind, const GemmParams& p,
                 hipStream_t stream);
 
 }  // namespace mfl

@@ -73,7 +73,7 @@ def run_gemm(w: W.Workload, x: W.Inputs, algo: str, in_place: bool = False):
     ckind = {None: mfl.NONE, "f16": mfl.F16, "f32": mfl.F32}[w.c]
     dkind = {"f16": mfl.F16, "f32": mfl.F32}[w.d]
     a_order = mfl.A_KMAJOR if w.a_order == "k" else mfl.A_MMAJOR
-    dt = mfl.dtypes(ckind, dkind, a_order, mfl.ALGOS[algo])
+    dt = mfl.dtypes(ckind, dkind, a_order, mfl.algo_code(algo))
     stream = torch.cuda.current_stream().cuda_stream
     rc = mfl.gemm_tn_raw(w.M, w.N, w.K, A.ptr, w.lda_, B.ptr, w.ldb_,
                          None if C is None else C.ptr, w.ldc_ if C is not None else 0,

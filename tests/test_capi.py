@@ -62,8 +62,7 @@ def test_valid_cases():
     (dict(d=mfl.NONE), -4), (dict(c=7, C=P, ldc=64), -4), (dict(a_order=2), -4),
     (dict(algo=9), -4),
     (dict(a_order=mfl.A_MMAJOR, algo=1), -6),
-    (dict(a_order=mfl.A_MMAJOR, lda=64, algo=4), -6), (dict(lda=68, algo=5), -6),
-    (dict(B=P + 2, algo=4), -6),
+    (dict(algo=0x200), -4), (dict(algo=7), -4),
     (dict(A=P + 1), -7), (dict(d=mfl.F32, D=P + 2), -7),
     (dict(c=mfl.F16, C=P, ldc=64, d=mfl.F32, D=P), -8),
     (dict(c=mfl.F32, C=P, ldc=128, d=mfl.F32, D=P, ldd=64), -8),
@@ -84,9 +83,26 @@ def test_degenerate_sizes_are_ok():
     assert _v(K=0, A=0, B=0, lda=1, ldb=1)[0] == 0
 
 
+def _plan(M=64, N=64, K=64, A=P, lda=None, B=P, ldb=None, **kw):
+    dt = mfl.dtypes(**kw)
+    lda = lda if lda is not None else (K if dt.a_order == mfl.A_KMAJOR else M)
+    ldb = ldb if ldb is not None else K
+    return mfl.plan(M, N, K, A, lda, B, ldb, None, 0, P, N, dt)
+
+
+def test_fetch_policy_choice():
+    DMA, REG, REGT = 0, 1, 2
+    assert _plan(M=4096, N=4096, K=4096)[1:] == (mfl.ALGOS["lds256"], DMA, DMA)
+    assert _plan(M=4096, N=4096, K=4097, lda=4097, ldb=4097)[1:] == (mfl.ALGOS["lds256"], REG, REG)
+    assert _plan(lda=72, ldb=68)[2:] == (DMA, REG)
+    assert _plan(A=P + 2, lda=64)[2:] == (REG, DMA)
+    assert _plan(a_order=mfl.A_MMAJOR, lda=72)[2:] == (REGT, DMA)
+    assert _plan(algo=mfl.ALGOS["lds256"] | mfl.REG_FETCH)[1:] == (mfl.ALGOS["lds256"], REG, REG)
+    assert _plan(algo=mfl.algo_code("lds128+reg"))[2:] == (REG, REG)
+
+
 def test_auto_choice():
-    assert _v(M=4096, N=4096, K=4096)[1] == mfl.ALGOS["dma256w8"]
-    assert _v(M=4096, N=4096, K=4097, lda=4097, ldb=4097)[1] == mfl.ALGOS["lds256"]
+    assert _v(M=4096, N=4096, K=4096)[1] == mfl.ALGOS["lds256"]
     assert _v(M=256, N=256, K=256)[1] == mfl.ALGOS["lds128"]
     assert _v(M=32, N=16, K=16, algo=1)[1] == mfl.ALGOS["direct"]
 

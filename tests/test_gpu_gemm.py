@@ -20,8 +20,8 @@ from gpu_helpers import (freivalds_exact, oracle_full, oracle_sampled, run_gemm,
 
 pytestmark = pytest.mark.gpu
 
-ALGOS = ["direct", "lds128", "lds256", "dma256", "dma256w8"]
-DMA = {"dma256", "dma256w8"}
+ALGOS = ["direct", "lds128", "lds256", "lds256w4"]
+LDS_ALGOS = ["lds128", "lds256", "lds256w4"]
 
 
 def _assert_checks(checks):
@@ -37,11 +37,13 @@ SMALL = [(1, 1, 1), (5, 7, 3), (32, 16, 16), (33, 17, 9), (64, 64, 64), (127, 12
 @pytest.mark.parametrize("shape", SMALL)
 def test_small_integer_bit_exact(algo, shape):
     M, N, K = shape
-    # odd leading dimensions for the register-staged kernels, 16-byte rows for DMA
-    pad = (lambda k: (k + 7) // 8 * 8 + 8) if algo in DMA else (lambda k: k + 3)
-    for c, d in ((None, "f32"), ("f16", "f16"), ("f32", "f32"), (None, "f16"), ("f32", "f16")):
-        w = W.custom(M, N, K, c=c, d=d, dist="int", seed=M * 7 + N * 3 + K, lda=pad(K),
-                     ldb=pad(K) + (0 if algo in DMA else -2))
+    # odd leading dimensions: register fetch; 16-byte rows: direct-to-LDS fetch
+    ld16 = (K + 7) // 8 * 8 + 8
+    cases = (((None, "f32"), K + 3, K + 1), (("f16", "f16"), ld16, ld16),
+             (("f32", "f32"), ld16, K + 1), ((None, "f16"), K + 3, ld16),
+             (("f32", "f16"), ld16, ld16))
+    for (c, d), lda, ldb in cases:
+        w = W.custom(M, N, K, c=c, d=d, dist="int", seed=M * 7 + N * 3 + K, lda=lda, ldb=ldb)
         x = W.make_inputs(w)
         D, checks = run_gemm(w, x, algo)
         _assert_checks(checks)
@@ -49,12 +51,14 @@ def test_small_integer_bit_exact(algo, shape):
         assert v.ok, (w.name, c, d, str(v))
 
 
-@pytest.mark.parametrize("algo", ["lds128", "lds256"])
-@pytest.mark.parametrize("shape", [(40, 24, 33), (130, 260, 65), (257, 129, 100), (8, 9, 10)])
+@pytest.mark.parametrize("algo", LDS_ALGOS)
+@pytest.mark.parametrize("shape", [(40, 24, 33), (130, 260, 65), (257, 129, 100), (8, 9, 10),
+                                   (300, 264, 200)])
 def test_mmajor_a_bit_exact(algo, shape):
     M, N, K = shape
-    for c, d in ((None, "f32"), ("f32", "f32"), ("f16", "f16")):
-        w = W.custom(M, N, K, a_order="m", lda=M + 8, c=c, d=d, dist="int", seed=M + N + K)
+    for c, d, ldb in ((None, "f32", K), ("f32", "f32", (K + 7) // 8 * 8), ("f16", "f16", K + 1)):
+        w = W.custom(M, N, K, a_order="m", lda=M + 8, ldb=ldb, c=c, d=d, dist="int",
+                     seed=M + N + K)
         x = W.make_inputs(w)
         D, checks = run_gemm(w, x, algo)
         _assert_checks(checks)
@@ -62,11 +66,11 @@ def test_mmajor_a_bit_exact(algo, shape):
         assert v.ok, (w.name, c, d, str(v))
 
 
-@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("algo", ALGOS + ["lds256+reg", "lds128+reg"])
 def test_float_inputs_within_tolerance(algo):
     for (M, N, K, c, d) in ((513, 384, 300, None, "f32"), (300, 517, 1000, "f16", "f16"),
                             (256, 256, 256, "f32", "f32")):
-        ld = (K + 7) // 8 * 8 if algo in DMA else None
+        ld = (K + 7) // 8 * 8
         w = W.custom(M, N, K, c=c, d=d, dist="unif", seed=M + K, lda=ld, ldb=ld)
         x = W.make_inputs(w)
         D, checks = run_gemm(w, x, algo)
@@ -98,8 +102,8 @@ def test_kernel_properties():
     assert info["lds_bytes"] == 0          # the direct kernel uses no LDS
     assert mfl.kernel_info("lds128")["lds_bytes"] == 2 * (128 + 128) * 32 * 2
     assert mfl.kernel_info("lds256")["lds_bytes"] == 2 * (256 + 256) * 64 * 2
-    assert mfl.kernel_info("dma256")["lds_bytes"] == 2 * (256 + 256) * 64 * 2
-    assert mfl.kernel_info("dma256w8")["threads"] == 512
+    assert mfl.kernel_info("lds256w4")["lds_bytes"] == 2 * (256 + 256) * 64 * 2
+    assert mfl.kernel_info("lds256")["threads"] == 512
     say("[gpu] kernel info", {a: mfl.kernel_info(a) for a in ALGOS})
 
 
@@ -107,9 +111,9 @@ def test_kernel_properties():
 NAMED = [
     ("tiny_32x16x16", ["direct", "lds128", "lds256"], False),
     ("direct_256", ["direct"], True),
-    ("lds_4096", ["lds128", "lds256", "dma256", "dma256w8"], True),
-    ("accum_mmajor_8192x8192x2048", ["auto"], True),
-    ("ragged_8191x6143x4097", ["auto", "lds128"], True),
+    ("lds_4096", ["lds128", "lds256", "lds256w4", "lds256+reg"], True),
+    ("accum_mmajor_8192x8192x2048", ["auto", "lds128"], True),
+    ("ragged_8191x6143x4097", ["auto", "lds128", "lds256w4"], True),
 ]
 
 
@@ -137,7 +141,7 @@ def test_named_workload(name, algo, integer):
         assert v.ok, str(v)
         return
     ms, ns = W.sample_indices(w.M, w.N, 20000, seed=w.seed,
-                              tile=256 if algo in ("auto", "lds256") else 128)
+                              tile=128 if algo.startswith(("lds128", "direct")) else 256)
     ref = oracle_sampled(w, x, ms, ns)
     v = verdict(D[ms, ns], ref, w, x.integer)
     say(f"[gpu] {w.name} sampled {len(ms)}: {v}")

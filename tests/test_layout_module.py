@@ -157,8 +157,7 @@ def test_mfma_tv_layouts_equal_oracle_closed_forms(op):
 
 # --------------------------------------------- kernel fragment addressing
 KERNEL_TILES = {"direct": (128, 128, 32, 2, 2), "lds128": (128, 128, 32, 2, 2),
-                "lds256": (256, 256, 64, 2, 2), "dma256": (256, 256, 64, 2, 2),
-                "dma256w8": (256, 256, 64, 2, 4)}
+                "lds256": (256, 256, 64, 2, 4), "lds256w4": (256, 256, 64, 2, 2)}
 
 
 @pytest.mark.parametrize("algo", sorted(KERNEL_TILES))
