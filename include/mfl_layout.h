@@ -64,6 +64,19 @@ int mfl_layout_mfma_tv(int32_t op, int32_t operand, char* out, int64_t cap);
 int mfl_fragment_coords(int32_t algo, int32_t operand, int32_t* out, int64_t cap,
                         int32_t* threads, int32_t* slots);
 
+/* LDS operand-tile layout of a kernel: out[row*BK + k] = element offset
+ * (halves) of (row, k) inside one operand stage, for row < rows (BM for
+ * operand 0, BN for 1) and k < BK (the XOR-swizzled K-contiguous tile).
+ * *rows and *bk receive the tile shape; fails with -13 if rows*BK > cap.
+ * Pure host code. */
+int mfl_lds_tile_offsets(int32_t algo, int32_t operand, int32_t* out, int64_t cap,
+                         int32_t* rows, int32_t* bk);
+
+/* Workgroup -> output tile order the kernels use for a grid of
+ * tiles_m x tiles_n tiles (XCD-aware grouping, band height group_m):
+ * tm[b], tn[b] for every workgroup id b < tiles_m*tiles_n.  Pure host code. */
+int mfl_tile_order(int32_t tiles_m, int32_t tiles_n, int32_t group_m, int32_t* tm, int32_t* tn);
+
 #ifdef __cplusplus
 }
 #endif

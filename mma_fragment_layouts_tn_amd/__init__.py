@@ -97,6 +97,10 @@ def _load() -> ctypes.CDLL:
     lib.mfl_layout_mfma_tv.restype = ctypes.c_int
     lib.mfl_fragment_coords.argtypes = [i32, i32, vp, i64, P(i32), P(i32)]
     lib.mfl_fragment_coords.restype = ctypes.c_int
+    lib.mfl_lds_tile_offsets.argtypes = [i32, i32, vp, i64, P(i32), P(i32)]
+    lib.mfl_lds_tile_offsets.restype = ctypes.c_int
+    lib.mfl_tile_order.argtypes = [i32, i32, i32, vp, vp]
+    lib.mfl_tile_order.restype = ctypes.c_int
     lib.mfl_probe_mfma.argtypes = [i32, vp, vp, vp, vp, vp]
     lib.mfl_probe_mfma.restype = ctypes.c_int
     return lib
@@ -278,6 +282,27 @@ def fragment_coords(algo: str, operand: str) -> np.ndarray:
     _lay_check(_lib.mfl_fragment_coords(algo_code(algo), opnd, out.ctypes.data, out.size,
                                         ctypes.byref(t), ctypes.byref(s)), algo)
     return out
+
+
+def lds_tile_offsets(algo: str, operand: str) -> np.ndarray:
+    """(rows, BK) int32 array: LDS element offset of (row, k) in one stage."""
+    opnd = {"A": 0, "B": 1}[operand]
+    r, k = ctypes.c_int32(), ctypes.c_int32()
+    _lay_check(_lib.mfl_lds_tile_offsets(algo_code(algo), opnd, None, 0, ctypes.byref(r),
+                                         ctypes.byref(k)), algo)
+    out = np.empty((r.value, k.value), dtype=np.int32)
+    _lay_check(_lib.mfl_lds_tile_offsets(algo_code(algo), opnd, out.ctypes.data, out.size,
+                                         ctypes.byref(r), ctypes.byref(k)), algo)
+    return out
+
+
+def tile_order(tiles_m: int, tiles_n: int, group_m: int):
+    """(tm, tn) int32 arrays indexed by workgroup id."""
+    tm = np.empty(tiles_m * tiles_n, dtype=np.int32)
+    tn = np.empty_like(tm)
+    _lay_check(_lib.mfl_tile_order(tiles_m, tiles_n, group_m, tm.ctypes.data, tn.ctypes.data),
+               "tile_order")
+    return tm, tn
 
 
 # ----------------------------------------------------------------- probes

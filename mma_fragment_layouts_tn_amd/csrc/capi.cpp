@@ -236,6 +236,19 @@ int emit(const mfl::Layout& L, char* out, int64_t cap) {
 }
 
 template <class Cfg>
+int lds_offsets(int operand, int32_t* out, int64_t cap, int32_t* rows, int32_t* bk) {
+  const int R = operand == 0 ? Cfg::BM : Cfg::BN;
+  if (operand < 0 || operand > 1) return mfl::kLayoutBadIndex;
+  if (rows) *rows = R;
+  if (bk) *bk = Cfg::BK;
+  if (!out) return 0;
+  if ((int64_t)R * Cfg::BK > cap) return mfl::kLayoutBadIndex;
+  for (int r = 0; r < R; ++r)
+    for (int k = 0; k < Cfg::BK; ++k) out[r * Cfg::BK + k] = mfl::lds_offset<Cfg::BK>(r, k);
+  return 0;
+}
+
+template <class Cfg>
 int frag_coords(int operand, int32_t* out, int64_t cap, int32_t* threads, int32_t* slots) {
   int ns = 0;
   if (operand == 0) ns = Cfg::KSUB * Cfg::RM * 8;
@@ -438,9 +451,30 @@ int mfl_layout_mfma_tv(int32_t op, int32_t operand, char* out, int64_t cap) {
   return emit(mfl::mfma_tv(op, operand), out, cap);
 }
 
+int mfl_lds_tile_offsets(int32_t algo, int32_t operand, int32_t* out, int64_t cap,
+                         int32_t* rows, int32_t* bk) {
+  switch (algo & MFL_ALGO_MASK) {
+    case mfl::kAlgoLds128: return lds_offsets<mfl::CfgLds128>(operand, out, cap, rows, bk);
+    case mfl::kAlgoLds256: return lds_offsets<mfl::CfgLds256>(operand, out, cap, rows, bk);
+    case mfl::kAlgoLds256W4: return lds_offsets<mfl::CfgLds256W4>(operand, out, cap, rows, bk);
+    default: return mfl::kLayoutBadIndex;
+  }
+}
+
+int mfl_tile_order(int32_t tiles_m, int32_t tiles_n, int32_t group_m, int32_t* tm, int32_t* tn) {
+  if (tiles_m <= 0 || tiles_n <= 0 || group_m <= 0 || !tm || !tn) return mfl::kLayoutBadIndex;
+  const int nb = tiles_m * tiles_n;
+  for (int b = 0; b < nb; ++b) {
+    const mfl::TileIndex t = mfl::tile_of_block(b, nb, tiles_m, tiles_n, group_m);
+    tm[b] = t.tm;
+    tn[b] = t.tn;
+  }
+  return 0;
+}
+
 int mfl_fragment_coords(int32_t algo, int32_t operand, int32_t* out, int64_t cap,
                         int32_t* threads, int32_t* slots) {
-  switch (algo) {
+  switch (algo & MFL_ALGO_MASK) {
     case mfl::kAlgoDirect: return frag_coords<mfl::CfgDirect>(operand, out, cap, threads, slots);
     case mfl::kAlgoLds128: return frag_coords<mfl::CfgLds128>(operand, out, cap, threads, slots);
     case mfl::kAlgoLds256: return frag_coords<mfl::CfgLds256>(operand, out, cap, threads, slots);

@@ -209,3 +209,38 @@ def test_fragment_multiplicities(algo):
     f = mfl.fragment_coords(algo, "C").reshape(-1, 2)
     counts = np.bincount(f[:, 0] * BN + f[:, 1], minlength=BM * BN)
     assert (counts == 1).all()
+
+
+# ------------------------------------------------ LDS tile layout, tile order
+@pytest.mark.parametrize("algo", ["lds128", "lds256", "lds256w4"])
+@pytest.mark.parametrize("operand", ["A", "B"])
+def test_lds_tile_layout_bijective_and_conflict_free(algo, operand):
+    """The swizzled tile is a permutation of rows*BK halves that keeps each
+    8-half chunk contiguous, and the 16 rows read by 16 consecutive lanes at a
+    fixed K chunk land in 16 different 16-byte bank groups (64 banks of 4 B)."""
+    off = mfl.lds_tile_offsets(algo, operand)
+    rows, bk = off.shape
+    assert sorted(off.reshape(-1).tolist()) == list(range(rows * bk))
+    assert (off[:, 1:8] - off[:, 0:1] == np.arange(1, 8)).all()
+    for k0 in range(0, bk, 8):
+        for r0 in range(0, rows, 16):
+            groups = {(int(off[r, k0]) * 2 // 16) % 16 for r in range(r0, r0 + 16)}
+            assert len(groups) == 16, (algo, operand, k0, r0)
+
+
+@pytest.mark.parametrize("tiles", [(1, 1), (16, 16), (32, 24), (64, 48), (3, 7), (33, 5)])
+@pytest.mark.parametrize("group_m", [4, 8])
+def test_tile_order_is_a_bijection(tiles, group_m):
+    tm, tn = mfl.tile_order(tiles[0], tiles[1], group_m)
+    pairs = set(zip(tm.tolist(), tn.tolist()))
+    assert len(pairs) == tiles[0] * tiles[1]
+    assert tm.min() >= 0 and tm.max() < tiles[0] and tn.min() >= 0 and tn.max() < tiles[1]
+
+
+def test_tile_order_keeps_xcd_blocks_compact():
+    """With 256 tiles of 16x16 and 8 XCDs (workgroup id % 8), each XCD's 32
+    tiles span 4 A-row blocks and 8 B-column blocks (the minimum, 12)."""
+    tm, tn = mfl.tile_order(16, 16, 4)
+    for x in range(8):
+        ids = np.arange(x, 256, 8)
+        assert len(set(tm[ids].tolist())) + len(set(tn[ids].tolist())) == 12
