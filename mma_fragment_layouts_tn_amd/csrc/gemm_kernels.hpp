@@ -13,10 +13,10 @@
 //      REGT  M-contiguous A: 4 k-rows x 8 m loaded into registers, transposed
 //            in registers to 8 runs of 4 k, written with 8-byte LDS stores.
 //    Per K-step: fragment reads for sub-step kk+1 overlap the MFMAs of kk;
-//    register-staged tiles are written to the idle stage before the step's
-//    single barrier; right after the barrier the fetch of tile kt+2 is
-//    issued (it has a whole step to land) and the first fragments of the next
-//    stage are read while the last sub-step's MFMAs are still queued.
+//    register-staged tiles are written to the idle stage during the last
+//    sub-step before the step's single barrier; after the barrier the fetch
+//    of tile kt+2 (it has a whole step to land) and the first fragment reads
+//    of the next stage are interleaved with the last sub-step's MFMAs.
 //  * gemm_direct: the global-only kernel of the simple-GEMM page (§1, §3.4):
 //    every lane reads its operand fragments straight from global memory into
 //    registers, no LDS at all.
@@ -116,6 +116,7 @@ struct FetchDma {
   static constexpr int BK = Cfg::BK, CH = Cfg::CH, RUN = 512 / BK;
   static constexpr int kRuns = ROWS / RUN / Cfg::kWaves;
   static_assert(ROWS % (RUN * Cfg::kWaves) == 0, "runs must divide over the waves");
+  static constexpr int kVmem = kRuns, kDsWrites = 0;   // instructions per issue / stash
   unsigned off[kRuns];
   int run0;
   __device__ void init(int row0, int rows_valid, int ld, int tid, int w, int lane) {
@@ -129,14 +130,12 @@ struct FetchDma {
       off[i] = (unsigned)((int64_t)min(row0 + row, row0 + rows_valid - 1) * ld * 2) + kc * 2;
     }
   }
-  __device__ void issue(const void* base, int kt, _Float16* stage) {
+  __device__ void issue_one(int i, const void* base, int kt, _Float16* stage) {
     const char* b = (const char*)base + (int64_t)kt * BK * 2;
-#pragma unroll
-    for (int i = 0; i < kRuns; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(b + (uint64_t)off[i]),
-                                       (lds_ptr_t)(stage + (run0 + i) * RUN * BK), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(b + (uint64_t)off[i]),
+                                     (lds_ptr_t)(stage + (run0 + i) * RUN * BK), 16, 0, 0);
   }
-  __device__ void stash(_Float16*) {}
+  __device__ void stash_one(int, _Float16*) {}
 };
 
 // REG: K-contiguous rows, 16-byte chunks q = tid + i*T (row q/CH, chunk q%CH)
@@ -145,6 +144,7 @@ struct FetchReg {
   static constexpr int BK = Cfg::BK, CH = Cfg::CH, T = Cfg::kThreads;
   static constexpr int kChunks = ROWS * CH / T;
   static_assert((ROWS * CH) % T == 0, "chunks must divide over the threads");
+  static constexpr int kVmem = kChunks, kDsWrites = kChunks;
   int off[kChunks], lds[kChunks];
   uint4 r[kChunks];
   __device__ void init(int row0, int rows_valid, int ld, int tid, int w, int lane) {
@@ -157,15 +157,10 @@ struct FetchReg {
       lds[i] = lds_offset<BK>(row, c * 8);
     }
   }
-  __device__ void issue(const void* base, int kt, _Float16*) {
-    const char* b = (const char*)base + (int64_t)kt * BK * 2;
-#pragma unroll
-    for (int i = 0; i < kChunks; ++i) r[i] = load16(b, off[i]);
+  __device__ void issue_one(int i, const void* base, int kt, _Float16*) {
+    r[i] = load16((const char*)base + (int64_t)kt * BK * 2, off[i]);
   }
-  __device__ void stash(_Float16* stage) {
-#pragma unroll
-    for (int i = 0; i < kChunks; ++i) *(uint4*)&stage[lds[i]] = r[i];
-  }
+  __device__ void stash_one(int i, _Float16* stage) { *(uint4*)&stage[lds[i]] = r[i]; }
 };
 
 // REGT: M-contiguous A.  Chunk = KR k-rows x 8 m (KR 16-byte loads, one
@@ -179,6 +174,7 @@ struct FetchRegT {
   static constexpr int kChunks = (BK / KR) * (ROWS / 8) / T;
   static_assert(((BK / KR) * (ROWS / 8)) % T == 0 && kChunks > 0,
                 "chunks must divide over the threads");
+  static constexpr int kVmem = kChunks * KR, kDsWrites = kChunks * 8;
   int off[kChunks], mvalid[kChunks], lds_k[kChunks], lds_m[kChunks];
   int ld;
   uint4 r[kChunks][KR];
@@ -195,17 +191,14 @@ struct FetchRegT {
       lds_m[i] = mc * 8;
     }
   }
-  __device__ void issue(const void* base, int kt, _Float16*) {
+  // instruction v loads k-row v % KR of chunk v / KR
+  __device__ void issue_one(int v, const void* base, int kt, _Float16*) {
+    const int i = v / KR, rr = v % KR;
     const char* b = (const char*)base + (int64_t)kt * BK * ld * 2;
-#pragma unroll
-    for (int i = 0; i < kChunks; ++i)
-#pragma unroll
-      for (int rr = 0; rr < KR; ++rr) {
-        const int64_t o = off[i] + (int64_t)rr * ld * 2;
-        r[i][rr] = mvalid[i] >= 8 ? load16(b, o)
-                   : mvalid[i] <= 0 ? make_uint4(0, 0, 0, 0)
-                                    : load8_tail((const _Float16*)(b + o), mvalid[i]);
-      }
+    const int64_t o = off[i] + (int64_t)rr * ld * 2;
+    r[i][rr] = mvalid[i] >= 8 ? load16(b, o)
+               : mvalid[i] <= 0 ? make_uint4(0, 0, 0, 0)
+                                : load8_tail((const _Float16*)(b + o), mvalid[i]);
   }
   // halves e of two 8-half vectors x, y packed as (x[e], y[e])
   __device__ static unsigned pack(const uint4& x, const uint4& y, int e) {
@@ -214,18 +207,14 @@ struct FetchRegT {
     const int d = e >> 1;
     return (e & 1) ? ((a[d] >> 16) | (b[d] & 0xffff0000u)) : ((a[d] & 0xffffu) | (b[d] << 16));
   }
-  __device__ void stash(_Float16* stage) {
-#pragma unroll
-    for (int i = 0; i < kChunks; ++i) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        _Float16* dst = &stage[lds_offset<BK>(lds_m[i] + e, lds_k[i])];
-        if constexpr (KR == 4)
-          *(uint2*)dst = make_uint2(pack(r[i][0], r[i][1], e), pack(r[i][2], r[i][3], e));
-        else
-          *(unsigned*)dst = pack(r[i][0], r[i][1], e);
-      }
-    }
+  // store d writes the KR k of m = lds_m + d % 8 of chunk d / 8
+  __device__ void stash_one(int d, _Float16* stage) {
+    const int i = d / 8, e = d % 8;
+    _Float16* dst = &stage[lds_offset<BK>(lds_m[i] + e, lds_k[i])];
+    if constexpr (KR == 4)
+      *(uint2*)dst = make_uint2(pack(r[i][0], r[i][1], e), pack(r[i][2], r[i][3], e));
+    else
+      *(unsigned*)dst = pack(r[i][0], r[i][1], e);
   }
 };
 
@@ -242,6 +231,11 @@ struct FetchSel<Cfg, ROWS, kFetchReg> {
 template <class Cfg, int ROWS>
 struct FetchSel<Cfg, ROWS, kFetchRegT> {
   using type = FetchRegT<Cfg, ROWS>;
+};
+
+template <bool B>
+struct BoolC {
+  static constexpr bool value = B;
 };
 
 // ---------------------------------------------------------------------------
@@ -262,19 +256,36 @@ __global__ void __launch_bounds__(Cfg::kThreads, 1) gemm_tiled(const GemmParams 
   const TileIndex ti = tile_of_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m);
   const int m0 = ti.tm * BM, n0 = ti.tn * BN;
 
-  typename FetchSel<Cfg, BM, FA>::type fa_;
-  typename FetchSel<Cfg, BN, FB>::type fb_;
+  using FetchA = typename FetchSel<Cfg, BM, FA>::type;
+  using FetchB = typename FetchSel<Cfg, BN, FB>::type;
+  FetchA fa_;
+  FetchB fb_;
   fa_.init(m0, p.M - m0, p.lda, tid, w, lane);
   fb_.init(n0, p.N - n0, p.ldb, tid, w, lane);
   auto stage_a = [&](int s) { return smem + s * kStage; };
   auto stage_b = [&](int s) { return smem + s * kStage + BM * BK; };
+  // fetch instruction v / LDS store d of both operands (A first)
+  constexpr int kVmem = FetchA::kVmem + FetchB::kVmem;
+  constexpr int kDsW = FetchA::kDsWrites + FetchB::kDsWrites;
+  auto issue_one = [&](int v, int kt, int s) {
+    if (v < FetchA::kVmem)
+      fa_.issue_one(v, p.A, kt, stage_a(s));
+    else
+      fb_.issue_one(v - FetchA::kVmem, p.B, kt, stage_b(s));
+  };
+  auto stash_one = [&](int d, int s) {
+    if (d < FetchA::kDsWrites)
+      fa_.stash_one(d, stage_a(s));
+    else
+      fb_.stash_one(d - FetchA::kDsWrites, stage_b(s));
+  };
   auto issue = [&](int kt, int s) {
-    fa_.issue(p.A, kt, stage_a(s));
-    fb_.issue(p.B, kt, stage_b(s));
+#pragma unroll
+    for (int v = 0; v < kVmem; ++v) issue_one(v, kt, s);
   };
   auto stash = [&](int s) {
-    fa_.stash(stage_a(s));
-    fb_.stash(stage_b(s));
+#pragma unroll
+    for (int d = 0; d < kDsW; ++d) stash_one(d, s);
   };
   constexpr bool kAnyReg = FA != kFetchDma || FB != kFetchDma;
 
@@ -295,12 +306,21 @@ __global__ void __launch_bounds__(Cfg::kThreads, 1) gemm_tiled(const GemmParams 
   }
 
   half8 fa[2][RM], fb[2][RN];
-  auto frags = [&](int buf, int kk, int s) {
+  // fragment read r in the order the MFMAs consume them (i-major, so A0,
+  // then B0..B(RN-1), then A1..A(RM-1))
+  constexpr int kReads = RM + RN, kMfma = RM * RN;
+  auto read_one = [&](int r, int buf, int kk, int s) {
     const _Float16* st = smem + s * kStage;
+    if (r == 0)
+      fa[buf][0] = *(const half8*)&st[fa_off[kk][0]];
+    else if (r <= RN)
+      fb[buf][r - 1] = *(const half8*)&st[fb_off[kk][r - 1]];
+    else
+      fa[buf][r - RN] = *(const half8*)&st[fa_off[kk][r - RN]];
+  };
+  auto frags = [&](int buf, int kk, int s) {
 #pragma unroll
-    for (int i = 0; i < RM; ++i) fa[buf][i] = *(const half8*)&st[fa_off[kk][i]];
-#pragma unroll
-    for (int j = 0; j < RN; ++j) fb[buf][j] = *(const half8*)&st[fb_off[kk][j]];
+    for (int r = 0; r < kReads; ++r) read_one(r, buf, kk, s);
   };
 
   floatx16 acc[RM][RN];
@@ -318,16 +338,43 @@ __global__ void __launch_bounds__(Cfg::kThreads, 1) gemm_tiled(const GemmParams 
       for (int j = 0; j < RN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
   };
-  // spread a group's fragment reads between its MFMAs
-  constexpr int kReads = RM + RN, kMfma = RM * RN;
-  auto interleave = [&]() {
+
+  // One group: the RM x RN MFMAs on fragment buffer `buf`.  A wave can issue
+  // other instructions while its previous MFMA occupies the matrix core, so
+  // each MFMA is followed by its share of the group's memory instructions:
+  // fragment reads (buffer rbuf, sub-step rkk of stage rs) in the first half
+  // of the group, since they feed the next one; fetch instructions (tile fkt
+  // into stage fs) and LDS stores of register-staged data (stage ss) over the
+  // whole group.  The fences keep the compiler from regrouping them.
+  auto group = [&](int buf, auto reads, int rbuf, int rkk, int rs, auto fetch, int fkt, int fs,
+                   auto stores, int ss) {
+    constexpr bool kR = decltype(reads)::value, kF = decltype(fetch)::value;
+    constexpr bool kS = decltype(stores)::value;
+    constexpr int rslots = kMfma / 2 > 0 ? kMfma / 2 : 1;
 #pragma unroll
-    for (int g = 0; g < kReads; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x008, kMfma / kReads > 0 ? kMfma / kReads : 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    for (int g = 0; g < kMfma; ++g) {
+      const int i = g / RN, j = g % RN;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
+      if constexpr (kR) {
+        if (g < rslots) {
+#pragma unroll
+          for (int r = g * kReads / rslots; r < (g + 1) * kReads / rslots; ++r)
+            read_one(r, rbuf, rkk, rs);
+        }
+      }
+      if constexpr (kF) {
+#pragma unroll
+        for (int v = g * kVmem / kMfma; v < (g + 1) * kVmem / kMfma; ++v) issue_one(v, fkt, fs);
+      }
+      if constexpr (kS) {
+#pragma unroll
+        for (int d = g * kDsW / kMfma; d < (g + 1) * kDsW / kMfma; ++d) stash_one(d, ss);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, kMfma, 0);
   };
+  using Yes = BoolC<true>;
+  using No = BoolC<false>;
 
   const int nfull = p.K / BK;
   if (nfull > 0) {
@@ -339,27 +386,32 @@ __global__ void __launch_bounds__(Cfg::kThreads, 1) gemm_tiled(const GemmParams 
     __builtin_amdgcn_sched_barrier(0);
     frags(0, 0, 0);
   }
-  for (int kt = 0; kt < nfull; ++kt) {
+  // One K-step on tile kt (stage kt&1).  FETCH: tile kt+2 exists and is
+  // fetched; NEXT: tile kt+1 exists.  The last two steps are peeled off the
+  // loop so its body is one straight block.
+  auto step = [&](const int kt, auto fetch, auto next) {
+    constexpr bool kFetch = decltype(fetch)::value, kNext = decltype(next)::value;
     const int cur = kt & 1;
 #pragma unroll
-    for (int kk = 0; kk + 1 < KSUB; ++kk) {
-      frags((kk + 1) & 1, kk + 1, cur);
-      mma(kk & 1);
-      interleave();
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // register-staged tile kt+1 goes to the idle stage before the barrier
-    if constexpr (kAnyReg) {
-      if (kt + 1 < nfull) stash(cur ^ 1);
-    }
+    for (int kk = 0; kk + 2 < KSUB; ++kk)
+      group(kk & 1, Yes(), (kk + 1) & 1, kk + 1, cur, No(), 0, 0, No(), 0);
+    // last sub-step before the barrier: register-staged tile kt+1 goes to
+    // the idle stage
+    group(KSUB & 1, Yes(), (KSUB - 1) & 1, KSUB - 1, cur, No(), 0, 0,
+          BoolC<kAnyReg && kNext>(), cur ^ 1);
     __builtin_amdgcn_s_waitcnt(0);        // own reads, stores and fetch of tile kt+1 done
     __builtin_amdgcn_s_barrier();         // ... in every wave: stage cur is free
     __builtin_amdgcn_sched_barrier(0);
-    if (kt + 2 < nfull) issue(kt + 2, cur);
-    if (kt + 1 < nfull) frags(0, 0, cur ^ 1);
-    mma((KSUB - 1) & 1);
-    __builtin_amdgcn_sched_barrier(0);
-  }
+    // The last sub-step's fragments are already in registers: its MFMAs
+    // cover the fetch of tile kt+2 into stage cur and the first fragment
+    // reads of stage cur^1.
+    group((KSUB - 1) & 1, next, 0, 0, cur ^ 1, fetch, kt + 2, cur, No(), 0);
+    (void)kFetch;
+  };
+  int kt = 0;
+  for (; kt + 2 < nfull; ++kt) step(kt, Yes(), Yes());
+  if (kt + 1 < nfull) step(kt++, No(), Yes());
+  if (kt < nfull) step(kt, No(), No());
 
   // K remainder: one step staged element by element with zero fill
   if (p.K % BK != 0) {
