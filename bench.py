@@ -8,8 +8,9 @@ synthetic 4096^3 workload (A (M,K), B (N,K) fp16 K-contiguous, uniform
 [-1,1), C absent, fp32 output), inputs resident in HBM before timing starts.
 Prints one JSON line: TFLOP/s over the timed steps (2MNK per step), the
 per-launch kernel time from HIP events on the launch stream, the roofline
-entry of the GEMM kernel (MFMA bound, dense fp16 peak of the chip), and the
-float64 CPU oracle timed on a bounded row sample of the same workload.
+entry of the GEMM kernel (MFMA bound, dense fp16 peak of the chip), the
+shader clock the chip holds under sustained load with the peak scaled to it,
+and the float64 CPU oracle timed on a bounded row sample of the same workload.
 """
 from __future__ import annotations
 
@@ -52,6 +53,36 @@ def load_traffic(workload: str, algo: str):
     return rec.get("bytes_per_launch")
 
 
+def sustained_clock(step, sync, seconds: float):
+    """Shader clock (MHz) read with rocm-smi, in a child process, while the
+    step runs back to back for `seconds`; None when rocm-smi is unavailable."""
+    import re
+    import subprocess
+    import threading
+    found = {}
+
+    def sample():
+        time.sleep(seconds / 2)
+        try:
+            out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True,
+                                 timeout=20).stdout
+        except (OSError, subprocess.SubprocessError):
+            return
+        m = re.search(r"sclk clock level: \d+: \((\d+)Mhz\)", out)
+        if m:
+            found["sclk"] = int(m.group(1))
+
+    th = threading.Thread(target=sample)
+    t0 = time.perf_counter()
+    th.start()
+    while time.perf_counter() - t0 < seconds or th.is_alive():
+        for _ in range(50):
+            step()
+        sync()
+    th.join()
+    return found.get("sclk")
+
+
 def cpu_baseline(w, x, target_s: float):
     """The float64 oracle, as it stands, on rows [0, r) of the workload."""
     from oracle import gemm as G
@@ -80,6 +111,9 @@ def main() -> int:
     ap.add_argument("--algo", default="auto",
                     help="auto, direct, lds128, lds256, lds256w4; '+reg' forces register fetch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--clock-seconds", type=float, default=2.0,
+                    help="after the timed region, run the step this long and read the shader "
+                         "clock under load (0 = skip)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB per step "
@@ -172,6 +206,11 @@ def main() -> int:
           f"wall/step {ms_per_step:.4f} ms; single-launch median {np.median(per):.4f} "
           f"min {per.min():.4f} p90 {np.percentile(per, 90):.4f}", file=sys.stderr, flush=True)
 
+    sclk = None
+    if args.clock_seconds > 0:
+        sclk = sustained_clock(step, torch.cuda.synchronize, args.clock_seconds)
+        print(f"[bench] shader clock under sustained load: {sclk} MHz", file=sys.stderr, flush=True)
+
     traffic = load_traffic(w.name, algo_name + "_" + mfl.FETCH_NAMES[fetch_a] + mfl.FETCH_NAMES[fetch_b])
     out = {
         "metric": METRIC,
@@ -204,6 +243,12 @@ def main() -> int:
         "cpu_baseline": None,
         "kernel_source_hash": kernel_source_hash(),
     }
+    if sclk:
+        # the dense peak scales with the shader clock (2400 MHz nominal)
+        adj = PEAK_FP16_DENSE_TFLOPS * sclk / 2400.0
+        out["clock"] = {"sclk_mhz_sustained": sclk, "peak_at_sclk": round(adj, 1),
+                        "pct_of_peak_at_sclk": round(100.0 * value / adj, 2),
+                        "how": f"rocm-smi during {args.clock_seconds:g} s of back-to-back steps"}
     if args.copy_mib:
         out["config"]["copy_mib_per_step"] = args.copy_mib
     if not args.no_cpu_baseline:
