@@ -50,7 +50,9 @@ extern "C" {
 typedef enum { MFL_NONE = 0, MFL_F16 = 1, MFL_F32 = 2 } mfl_dtype;
 typedef enum { MFL_A_KMAJOR = 0, MFL_A_MMAJOR = 1 } mfl_a_order;
 
-/* Kernel choice (low 8 bits of gemm_dtypes_t.algo).  AUTO picks per shape.
+/* Kernel choice (low 8 bits of gemm_dtypes_t.algo).  AUTO picks per shape:
+ * LDS_256 (LDS_256_W4 when both operands go straight into LDS and C is
+ * absent) once the grid has at least 192 tiles of 256x256, else LDS_128.
  * DIRECT reads fragments straight from global memory into registers (no
  * LDS; the simple-GEMM page's "不用 Shared Memory" kernel).  LDS_128 stages
  * 128x128x32 block tiles through LDS (the block tile of "CuTe Layout 到
@@ -59,8 +61,11 @@ typedef enum { MFL_A_KMAJOR = 0, MFL_A_MMAJOR = 1 } mfl_a_order;
  * 128x128.  The LDS kernels fetch each K-contiguous operand straight into
  * LDS (global_load_lds_dwordx4) when its base and leading dimension are
  * 16-byte aligned, else through registers with 16-byte loads at any 2-byte
- * alignment; an M-contiguous A goes through registers and is transposed
- * there.  MFL_ALGO_REG_FETCH or-ed into algo forces register fetch. */
+ * alignment.  An M-contiguous A goes straight into an M-contiguous LDS tile
+ * when its base and lda are 16-byte aligned and M % 8 == 0, and its operand
+ * fragments are read with the transposing LDS read; otherwise it is
+ * transposed in registers.  MFL_ALGO_REG_FETCH or-ed into algo forces
+ * register fetch. */
 typedef enum {
   MFL_ALGO_AUTO = 0,
   MFL_ALGO_DIRECT = 1,
@@ -117,7 +122,8 @@ int gemm_tn_validate(int64_t M, int64_t N, int64_t K,
 
 /* The same checks; on success also reports the kernel the call would run:
  * *algo (mfl_algo without flags) and the fetch policy of A and B
- * (0 direct-to-LDS, 1 through registers, 2 through registers with transpose).
+ * (0 direct-to-LDS, 1 through registers, 2 M-contiguous A through registers
+ * with transpose, 3 M-contiguous A direct-to-LDS with transposing reads).
  * Any out pointer may be NULL. */
 int gemm_tn_plan(int64_t M, int64_t N, int64_t K,
                  const void* A, int64_t lda,

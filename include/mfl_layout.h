@@ -58,19 +58,23 @@ int mfl_layout_mfma_tv(int32_t op, int32_t operand, char* out, int64_t cap);
  * the kernel runs: for every thread t of one workgroup and every fragment
  * slot s of one K-step, the (row, k) (operand 0 A, 1 B) or (m, n)
  * (operand 2, accumulators) within the workgroup tile, written as pairs into
- * out[2*(t*slots + s) + {0,1}].  *threads and *slots receive the counts; the
+ * out[2*(t*slots + s) + {0,1}].  Operand 3: for an M-contiguous A, the
+ * (m, k) each lane addresses with the first of the two transposing LDS reads
+ * (ds_read_b64_tr_b16; 4 consecutive m, the second read 4 k further) per K
+ * sub-step and repeat, slot = kk*RM + i.  *threads and *slots receive the counts; the
  * call fails with -13 when 2*threads*slots > cap.  algo is an mfl_algo value
  * other than AUTO.  Pure host code. */
 int mfl_fragment_coords(int32_t algo, int32_t operand, int32_t* out, int64_t cap,
                         int32_t* threads, int32_t* slots);
 
-/* LDS operand-tile layout of a kernel: out[row*BK + k] = element offset
- * (halves) of (row, k) inside one operand stage, for row < rows (BM for
- * operand 0, BN for 1) and k < BK (the XOR-swizzled K-contiguous tile).
- * *rows and *bk receive the tile shape; fails with -13 if rows*BK > cap.
- * Pure host code. */
+/* LDS operand-tile layout of a kernel: out[o*inner + i] = element offset
+ * (halves) inside one operand stage.  Operand 0 (A) and 1 (B): (o, i) =
+ * (row, k), row < BM or BN, k < BK, the XOR-swizzled K-contiguous tile.
+ * Operand 2: (o, i) = (k, m) of the M-contiguous A tile, k < BK, m < BM.
+ * *outer and *inner receive the tile shape; fails with -13 if
+ * outer*inner > cap.  Pure host code. */
 int mfl_lds_tile_offsets(int32_t algo, int32_t operand, int32_t* out, int64_t cap,
-                         int32_t* rows, int32_t* bk);
+                         int32_t* outer, int32_t* inner);
 
 /* Workgroup -> output tile order the kernels use for a grid of
  * tiles_m x tiles_n tiles (XCD-aware grouping, band height group_m):

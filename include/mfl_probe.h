@@ -26,6 +26,17 @@ extern "C" {
 int mfl_probe_mfma(int32_t op, const uint16_t* a_slots, const uint16_t* b_slots,
                    const float* c_slots, float* d_out, void* stream);
 
+/* One wave fills a 4096-half LDS array from lds_in (device, 4096 fp16 bit
+ * patterns) and issues one transposing LDS read (ds_read_b64_tr_b16) where
+ * lane l addresses halves [lane_offsets[l], +4) (lane_offsets: host array of
+ * 64 values, each a multiple of 4 in [0, 4092]); lane l writes the 4 halves it
+ * receives to out[4l .. 4l+4) (device, 256 elements).  This pins the lane
+ * regrouping the kernels rely on for an M-contiguous A operand (the role the
+ * route page "ldmatrix 怎样对上 MMA 的寄存器" gives ldmatrix).  Returns 0,
+ * -4 for a NULL pointer or an offset outside the rules, -5 on a launch error. */
+int mfl_probe_lds_tr16(const int32_t* lane_offsets, const uint16_t* lds_in, uint16_t* out,
+                       void* stream);
+
 #ifdef __cplusplus
 }
 #endif

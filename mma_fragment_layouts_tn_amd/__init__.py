@@ -27,7 +27,7 @@ NONE, F16, F32 = 0, 1, 2
 A_KMAJOR, A_MMAJOR = 0, 1
 ALGOS = {"auto": 0, "direct": 1, "lds128": 2, "lds256": 3, "lds256w4": 4}
 REG_FETCH = 0x100          # or-ed into the algo: fetch through registers
-FETCH_NAMES = {0: "dma", 1: "reg", 2: "regT"}
+FETCH_NAMES = {0: "dma", 1: "reg", 2: "regT", 3: "dmaT"}
 ALGO_NAMES = {v: k for k, v in ALGOS.items()}
 
 
@@ -103,6 +103,8 @@ def _load() -> ctypes.CDLL:
     lib.mfl_tile_order.restype = ctypes.c_int
     lib.mfl_probe_mfma.argtypes = [i32, vp, vp, vp, vp, vp]
     lib.mfl_probe_mfma.restype = ctypes.c_int
+    lib.mfl_probe_lds_tr16.argtypes = [vp, vp, vp, vp]
+    lib.mfl_probe_lds_tr16.restype = ctypes.c_int
     return lib
 
 
@@ -274,7 +276,7 @@ def mfma_tv(op: str, operand: str) -> str:
 
 def fragment_coords(algo: str, operand: str) -> np.ndarray:
     """(threads, slots, 2) int32 array of the kernel's per-lane coordinates."""
-    opnd = {"A": 0, "B": 1, "C": 2}[operand]
+    opnd = {"A": 0, "B": 1, "C": 2, "A_tr": 3}[operand]
     t, s = ctypes.c_int32(), ctypes.c_int32()
     _lay_check(_lib.mfl_fragment_coords(algo_code(algo), opnd, None, 0, ctypes.byref(t),
                                         ctypes.byref(s)), algo)
@@ -285,8 +287,9 @@ def fragment_coords(algo: str, operand: str) -> np.ndarray:
 
 
 def lds_tile_offsets(algo: str, operand: str) -> np.ndarray:
-    """(rows, BK) int32 array: LDS element offset of (row, k) in one stage."""
-    opnd = {"A": 0, "B": 1}[operand]
+    """LDS element offsets of one operand stage: "A"/"B" (rows, BK) indexed
+    [row, k]; "A_mmajor" (BK, BM) indexed [k, m]."""
+    opnd = {"A": 0, "B": 1, "A_mmajor": 2}[operand]
     r, k = ctypes.c_int32(), ctypes.c_int32()
     _lay_check(_lib.mfl_lds_tile_offsets(algo_code(algo), opnd, None, 0, ctypes.byref(r),
                                          ctypes.byref(k)), algo)
@@ -316,3 +319,15 @@ def probe_mfma(op: str, a_slots: torch.Tensor, b_slots: torch.Tensor,
                              c_slots.data_ptr(), d.data_ptr(), stream)
     _check(rc)
     return d
+
+
+def probe_lds_tr16(lane_offsets, lds_in: torch.Tensor) -> torch.Tensor:
+    """One transposing LDS read: lds_in is a device int16 tensor of 4096
+    values, lane_offsets 64 ints (multiples of 4 in [0, 4092]).  Returns the
+    (64, 4) int16 values each lane receives."""
+    offs = (ctypes.c_int32 * 64)(*[int(v) for v in lane_offsets])
+    out = torch.empty((64, 4), dtype=torch.int16, device=lds_in.device)
+    stream = torch.cuda.current_stream(lds_in.device).cuda_stream
+    rc = _lib.mfl_probe_lds_tr16(offs, lds_in.data_ptr(), out.data_ptr(), stream)
+    _check(rc)
+    return out

@@ -77,7 +77,8 @@ int check(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const voi
     return MFL_E_TOO_LARGE;
   if (mm ? !span_fits(K, lda, M) : !span_fits(M, lda, K)) return MFL_E_TOO_LARGE;
   if (!span_fits(N, ldb, K)) return MFL_E_TOO_LARGE;
-  if (algo == MFL_ALGO_AUTO) algo = pick_algo(M, N, K);
+  const bool auto_algo = algo == MFL_ALGO_AUTO;
+  if (auto_algo) algo = pick_algo(M, N, K);
   if (algo == MFL_ALGO_DIRECT && mm) return MFL_E_ALGO_CASE;
   const mfl::KernelInfo ki = mfl::kernel_info(algo);
   if (ki.algo < 0) return MFL_E_UNSUPPORTED;
@@ -85,9 +86,21 @@ int check(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const voi
   if (tiles > INT_MAX) return MFL_E_TOO_LARGE;
   if (plan) {
     plan->algo = algo;
-    plan->fetch_a = mm ? mfl::kFetchRegT
-                       : (!force_reg && dma_ok(A, lda) ? mfl::kFetchDma : mfl::kFetchReg);
+    // M-contiguous A: straight into LDS when rows are 16-byte aligned and M
+    // splits into whole 16-byte chunks, else transposed through registers
+    if (mm)
+      plan->fetch_a = !force_reg && dma_ok(A, lda) && M % 8 == 0 ? mfl::kFetchDmaT
+                                                                 : mfl::kFetchRegT;
+    else
+      plan->fetch_a = !force_reg && dma_ok(A, lda) ? mfl::kFetchDma : mfl::kFetchReg;
     plan->fetch_b = !force_reg && dma_ok(B, ldb) ? mfl::kFetchDma : mfl::kFetchReg;
+    // One wave per SIMD (128x128 per wave) reads a third less from LDS and
+    // wins when both operands go straight into LDS and the epilogue only
+    // stores; register fetch or a C read need the second wave per SIMD to
+    // hide their latency.
+    if (auto_algo && algo == mfl::kAlgoLds256 && plan->fetch_a == mfl::kFetchDma &&
+        plan->fetch_b == mfl::kFetchDma && dt.c == MFL_NONE)
+      plan->algo = mfl::kAlgoLds256W4;
   }
   return MFL_OK;
 }
@@ -236,15 +249,19 @@ int emit(const mfl::Layout& L, char* out, int64_t cap) {
 }
 
 template <class Cfg>
-int lds_offsets(int operand, int32_t* out, int64_t cap, int32_t* rows, int32_t* bk) {
-  const int R = operand == 0 ? Cfg::BM : Cfg::BN;
-  if (operand < 0 || operand > 1) return mfl::kLayoutBadIndex;
-  if (rows) *rows = R;
-  if (bk) *bk = Cfg::BK;
+int lds_offsets(int operand, int32_t* out, int64_t cap, int32_t* outer, int32_t* inner) {
+  if (operand < 0 || operand > 2) return mfl::kLayoutBadIndex;
+  // operands 0/1: (row, k) K-contiguous; 2: (k, m) of an M-contiguous A
+  const int O = operand == 0 ? Cfg::BM : operand == 1 ? Cfg::BN : Cfg::BK;
+  const int I = operand == 2 ? Cfg::BM : Cfg::BK;
+  if (outer) *outer = O;
+  if (inner) *inner = I;
   if (!out) return 0;
-  if ((int64_t)R * Cfg::BK > cap) return mfl::kLayoutBadIndex;
-  for (int r = 0; r < R; ++r)
-    for (int k = 0; k < Cfg::BK; ++k) out[r * Cfg::BK + k] = mfl::lds_offset<Cfg::BK>(r, k);
+  if ((int64_t)O * I > cap) return mfl::kLayoutBadIndex;
+  for (int o = 0; o < O; ++o)
+    for (int i = 0; i < I; ++i)
+      out[o * I + i] = operand == 2 ? mfl::lds_offset_mn<Cfg::BM>(i, o)
+                                    : mfl::lds_offset<Cfg::BK>(o, i);
   return 0;
 }
 
@@ -254,6 +271,7 @@ int frag_coords(int operand, int32_t* out, int64_t cap, int32_t* threads, int32_
   if (operand == 0) ns = Cfg::KSUB * Cfg::RM * 8;
   else if (operand == 1) ns = Cfg::KSUB * Cfg::RN * 8;
   else if (operand == 2) ns = Cfg::RM * Cfg::RN * 16;
+  else if (operand == 3) ns = Cfg::KSUB * Cfg::RM;
   else return mfl::kLayoutBadIndex;
   if (threads) *threads = Cfg::kThreads;
   if (slots) *slots = ns;
@@ -267,7 +285,13 @@ int frag_coords(int operand, int32_t* out, int64_t cap, int32_t* threads, int32_
       out[2 * ((int64_t)t * ns + s) + 1] = b;
       ++s;
     };
-    if (operand == 2) {
+    if (operand == 3) {
+      for (int kk = 0; kk < Cfg::KSUB; ++kk)
+        for (int i = 0; i < Cfg::RM; ++i) {
+          const mfl::RowK c = mfl::frag_a_tr_coord<Cfg>(w, lane, i, kk);
+          put(c.row, c.k);
+        }
+    } else if (operand == 2) {
       for (int i = 0; i < Cfg::RM; ++i)
         for (int j = 0; j < Cfg::RN; ++j)
           for (int v = 0; v < 16; ++v) {
@@ -333,6 +357,7 @@ int gemm_tn(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const v
   p.tiles_m = (int)((M + ki.bm - 1) / ki.bm);
   p.tiles_n = (int)((N + ki.bn - 1) / ki.bn);
   p.group_m = ki.bm >= 256 ? 4 : 8;
+  p.d_vec = ((uintptr_t)D % (uintptr_t)(4 * elem_size(dtypes.d)) == 0) && (ldd % 4 == 0);
   p.A = A;
   p.B = B;
   p.C = C;
@@ -367,7 +392,7 @@ int mfl_kernel_info(int32_t algo, gemm_dtypes_t dt, int32_t* bm, int32_t* bn, in
   if (bn) *bn = ki.bn;
   if (bk) *bk = ki.bk;
   if (threads) *threads = ki.threads;
-  const int fa = dt.a_order == MFL_A_MMAJOR ? mfl::kFetchRegT : mfl::kFetchDma;
+  const int fa = dt.a_order == MFL_A_MMAJOR ? mfl::kFetchDmaT : mfl::kFetchDma;
   const void* fn = mfl::kernel_symbol(algo, fa, mfl::kFetchDma, dt.c, dt.d);
   if (!fn) return MFL_E_ALGO_CASE;
   if (lds_bytes || vgprs_spilled) {
@@ -452,11 +477,12 @@ int mfl_layout_mfma_tv(int32_t op, int32_t operand, char* out, int64_t cap) {
 }
 
 int mfl_lds_tile_offsets(int32_t algo, int32_t operand, int32_t* out, int64_t cap,
-                         int32_t* rows, int32_t* bk) {
+                         int32_t* outer, int32_t* inner) {
   switch (algo & MFL_ALGO_MASK) {
-    case mfl::kAlgoLds128: return lds_offsets<mfl::CfgLds128>(operand, out, cap, rows, bk);
-    case mfl::kAlgoLds256: return lds_offsets<mfl::CfgLds256>(operand, out, cap, rows, bk);
-    case mfl::kAlgoLds256W4: return lds_offsets<mfl::CfgLds256W4>(operand, out, cap, rows, bk);
+    case mfl::kAlgoLds128: return lds_offsets<mfl::CfgLds128>(operand, out, cap, outer, inner);
+    case mfl::kAlgoLds256: return lds_offsets<mfl::CfgLds256>(operand, out, cap, outer, inner);
+    case mfl::kAlgoLds256W4:
+      return lds_offsets<mfl::CfgLds256W4>(operand, out, cap, outer, inner);
     default: return mfl::kLayoutBadIndex;
   }
 }

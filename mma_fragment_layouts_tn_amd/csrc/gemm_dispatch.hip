@@ -29,7 +29,8 @@ KernelInfo kernel_info(int algo) {
 
 const void* kernel_symbol(int algo, int fetch_a, int fetch_b, int c_kind, int d_kind) {
   switch (algo) {
-    case kAlgoDirect: return fetch_a == kFetchRegT ? nullptr : direct_symbol(c_kind, d_kind);
+    case kAlgoDirect:
+      return fetch_a == kFetchRegT || fetch_a == kFetchDmaT ? nullptr : direct_symbol(c_kind, d_kind);
     case kAlgoLds128: return tiled_symbol_128(fetch_a, fetch_b, c_kind, d_kind);
     case kAlgoLds256: return tiled_symbol_256(fetch_a, fetch_b, c_kind, d_kind);
     case kAlgoLds256W4: return tiled_symbol_256w4(fetch_a, fetch_b, c_kind, d_kind);

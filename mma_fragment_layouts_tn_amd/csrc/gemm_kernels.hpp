@@ -11,7 +11,9 @@
 //      REG   16-byte loads into registers (any 2-byte alignment), written to
 //            LDS one step later;
 //      REGT  M-contiguous A: 4 k-rows x 8 m loaded into registers, transposed
-//            in registers to 8 runs of 4 k, written with 8-byte LDS stores.
+//            in registers to 8 runs of 4 k, written with 8-byte LDS stores;
+//      DMAT  M-contiguous A straight into an M-contiguous LDS tile, operand
+//            fragments read with the transposing LDS read (ds_read_b64_tr_b16).
 //    Per K-step: fragment reads for sub-step kk+1 overlap the MFMAs of kk;
 //    register-staged tiles are written to the idle stage during the last
 //    sub-step before the step's single barrier; after the barrier the fetch
@@ -82,11 +84,13 @@ __device__ __forceinline__ void d_store(const GemmParams& p, int m, int n, float
     ((float*)p.D)[(int64_t)m * p.ldd + n] = x;
 }
 
-// Epilogue shared by both kernels: acc[i][j] value v -> (m, n) from the
-// accumulator TV layout.
+// Register epilogue: acc[i][j] value v -> (m, n) from the accumulator TV
+// layout, one element per store (for a fixed value the 64 lanes cover two
+// 128-byte row runs).  Interior tiles skip the per-element bounds checks.
 template <class Cfg, int CK, int DK>
 __device__ __forceinline__ void epilogue(const GemmParams& p, int w, int lane, int m0,
                                          int n0, const floatx16 (&acc)[Cfg::RM][Cfg::RN]) {
+  const bool interior = m0 + Cfg::BM <= p.M && n0 + Cfg::BN <= p.N;
 #pragma unroll
   for (int i = 0; i < Cfg::RM; ++i)
 #pragma unroll
@@ -95,8 +99,137 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, int w, int lane, i
       for (int v = 0; v < 16; ++v) {
         const RowK c = frag_c_coord<Cfg>(w, lane, i, j, v);
         const int m = m0 + c.row, n = n0 + c.k;
-        if (m < p.M && n < p.N) d_store<DK>(p, m, n, acc[i][j][v] + c_value<CK>(p, m, n));
+        if (interior || (m < p.M && n < p.N))
+          d_store<DK>(p, m, n, acc[i][j][v] + c_value<CK>(p, m, n));
       }
+}
+
+// LDS-staged epilogue of the LDS kernels when C is read.  Accumulators leave
+// the MFMA layout through LDS so that every global access is a row-contiguous
+// run of 4 elements per lane: D = acc + C with one C load, four adds and one
+// D store per run.  (Without C the register epilogue is faster: its stores
+// need no staging.)  Interior tiles batch their C loads (no per-element
+// branches); edge tiles check each run and fall back to elements at the
+// right edge.  The runs of a D row are 16-byte (fp32) or 8-byte (fp16)
+// stores when d_vec says D allows it, single elements otherwise.
+__device__ __forceinline__ float4 load_c4_f32(const GemmParams& p, int m, int n) {
+  float4 c;
+  __builtin_memcpy(&c, (const float*)p.C + (int64_t)m * p.ldc + n, 16);
+  return c;
+}
+__device__ __forceinline__ float4 load_c4_f16(const GemmParams& p, int m, int n) {
+  typedef _Float16 half4v __attribute__((ext_vector_type(4)));
+  half4v h;
+  __builtin_memcpy(&h, (const _Float16*)p.C + (int64_t)m * p.ldc + n, 8);
+  return make_float4((float)h[0], (float)h[1], (float)h[2], (float)h[3]);
+}
+
+template <int CK>
+__device__ __forceinline__ float4 load_c4(const GemmParams& p, int m, int n) {
+  if constexpr (CK == 2) return load_c4_f32(p, m, n);
+  if constexpr (CK == 1) return load_c4_f16(p, m, n);
+  return make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+template <int DK>
+__device__ __forceinline__ void store_d4(const GemmParams& p, int m, int n, float4 x) {
+  if (p.d_vec) {
+    if constexpr (DK == 1) {
+      typedef _Float16 half4v __attribute__((ext_vector_type(4)));
+      const half4v h = {(_Float16)x.x, (_Float16)x.y, (_Float16)x.z, (_Float16)x.w};
+      *(half4v*)((_Float16*)p.D + (int64_t)m * p.ldd + n) = h;
+    } else {
+      *(float4*)((float*)p.D + (int64_t)m * p.ldd + n) = x;
+    }
+  } else {
+    d_store<DK>(p, m, n, x.x);
+    d_store<DK>(p, m, n + 1, x.y);
+    d_store<DK>(p, m, n + 2, x.z);
+    d_store<DK>(p, m, n + 3, x.w);
+  }
+}
+
+template <class Cfg, int CK, int DK>
+__device__ __forceinline__ void epilogue_lds(const GemmParams& p, float* sm, int w, int lane,
+                                             int m0, int n0,
+                                             const floatx16 (&acc)[Cfg::RM][Cfg::RN]) {
+  constexpr int RM = Cfg::RM, RN = Cfg::RN, WTN = Cfg::WTN, IG = Cfg::kEpiRows;
+  constexpr int ROWS = IG * 32, V4 = WTN / 4, NV = ROWS * V4 / 64, QB = 8;
+  static_assert((ROWS * V4) % 64 == 0 && NV % QB == 0, "runs must divide over the lanes");
+  float* reg = sm + w * ROWS * WTN;
+  const int wm = w % Cfg::WAVES_M, wn = w / Cfg::WAVES_M;
+  const int mw = m0 + wm * Cfg::WTM, nw = n0 + wn * WTN;
+  const bool interior = m0 + Cfg::BM <= p.M && n0 + Cfg::BN <= p.N;
+  __syncthreads();   // every wave is done with the operand stages
+#pragma unroll
+  for (int i0 = 0; i0 < RM; i0 += IG) {
+    // accumulators -> this wave's staging tile (rows i0*32 .. +ROWS)
+#pragma unroll
+    for (int ii = 0; ii < IG; ++ii)
+#pragma unroll
+      for (int j = 0; j < RN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const RowK c = atom_c_coord(lane, v);
+          reg[epi_offset<WTN>(ii * 32 + c.row, j * 32 + c.k)] = acc[i0 + ii][j][v];
+        }
+    // A wave's LDS operations complete in order, so the reads below see the
+    // stores above, and the next pass's stores follow these reads.
+#pragma unroll
+    for (int q0 = 0; q0 < NV; q0 += QB) {
+      float4 x[QB], c[QB];
+#pragma unroll
+      for (int q = 0; q < QB; ++q) {
+        const int t = lane + 64 * (q0 + q), r = t / V4, c4 = t % V4;
+        x[q] = *(const float4*)&reg[epi_offset<WTN>(r, 4 * c4)];
+      }
+      if (interior) {
+        if constexpr (CK != 0) {
+#pragma unroll
+          for (int q = 0; q < QB; ++q) {
+            const int t = lane + 64 * (q0 + q);
+            c[q] = load_c4<CK>(p, mw + i0 * 32 + t / V4, nw + 4 * (t % V4));
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < QB; ++q) {
+          const int t = lane + 64 * (q0 + q);
+          float4 y = x[q];
+          if constexpr (CK != 0) {
+            y.x += c[q].x;
+            y.y += c[q].y;
+            y.z += c[q].z;
+            y.w += c[q].w;
+          }
+          store_d4<DK>(p, mw + i0 * 32 + t / V4, nw + 4 * (t % V4), y);
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < QB; ++q) {
+          const int t = lane + 64 * (q0 + q);
+          const int m = mw + i0 * 32 + t / V4, n = nw + 4 * (t % V4);
+          if (m < p.M) {
+            if (n + 3 < p.N) {
+              float4 y = x[q];
+              if constexpr (CK != 0) {
+                const float4 cc = load_c4<CK>(p, m, n);
+                y.x += cc.x;
+                y.y += cc.y;
+                y.z += cc.z;
+                y.w += cc.w;
+              }
+              store_d4<DK>(p, m, n, y);
+            } else {
+              const float xv[4] = {x[q].x, x[q].y, x[q].z, x[q].w};
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (n + e < p.N) d_store<DK>(p, m, n + e, xv[e] + c_value<CK>(p, m, n + e));
+            }
+          }
+        }
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -218,6 +351,40 @@ struct FetchRegT {
   }
 };
 
+// DMAT: M-contiguous A straight into an M-contiguous LDS tile (BK rows of
+// ROWS halves, lds_offset_mn).  A 1 KB run holds RUN = 512/ROWS k-rows; lane
+// l takes k-row RUN*run + l/CPR, physical chunk l%CPR, so it fetches logical
+// chunk (l%CPR) ^ 4(krow&3), i.e. m = row0 + 8 * that.  Needs M % 8 == 0
+// (chunks are all-valid or all-past-M; the latter are clamped to the last
+// valid chunk and only feed outputs that are never stored).
+template <class Cfg, int ROWS>
+struct FetchDmaT {
+  static constexpr int BK = Cfg::BK, CPR = ROWS / 8, RUN = 64 / CPR;
+  static constexpr int kRuns = BK / RUN / Cfg::kWaves;
+  static_assert(BK % (RUN * Cfg::kWaves) == 0 && kRuns > 0, "runs must divide over the waves");
+  static constexpr int kVmem = kRuns, kDsWrites = 0;
+  unsigned off[kRuns];
+  int run0, ld;
+  __device__ void init(int row0, int rows_valid, int ld_, int tid, int w, int lane) {
+    (void)tid;
+    ld = ld_;
+    run0 = w * kRuns;
+#pragma unroll
+    for (int i = 0; i < kRuns; ++i) {
+      const int krow = RUN * (run0 + i) + lane / CPR;
+      const int c = (lane % CPR) ^ ((krow & 3) << 2);
+      const int m = min(8 * c, rows_valid - 8);
+      off[i] = (unsigned)(((int64_t)krow * ld + row0 + m) * 2);
+    }
+  }
+  __device__ void issue_one(int i, const void* base, int kt, _Float16* stage) {
+    const char* b = (const char*)base + (int64_t)kt * BK * ld * 2;
+    __builtin_amdgcn_global_load_lds((const void*)(b + (uint64_t)off[i]),
+                                     (lds_ptr_t)(stage + (run0 + i) * RUN * ROWS), 16, 0, 0);
+  }
+  __device__ void stash_one(int, _Float16*) {}
+};
+
 template <class Cfg, int ROWS, int POLICY>
 struct FetchSel;
 template <class Cfg, int ROWS>
@@ -232,6 +399,22 @@ template <class Cfg, int ROWS>
 struct FetchSel<Cfg, ROWS, kFetchRegT> {
   using type = FetchRegT<Cfg, ROWS>;
 };
+template <class Cfg, int ROWS>
+struct FetchSel<Cfg, ROWS, kFetchDmaT> {
+  using type = FetchDmaT<Cfg, ROWS>;
+};
+
+// Two transposed LDS reads (k0 and k0 + 4 of an M-contiguous tile) -> one
+// 8-half operand fragment.
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef short short8v __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ half8 read_tr_pair(const _Float16* p0, const _Float16* p1) {
+  using lds_s4 = __attribute__((address_space(3))) short4v*;
+  const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(p0));
+  const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(p1));
+  const short8v v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(half8, v);
+}
 
 template <bool B>
 struct BoolC {
@@ -246,7 +429,8 @@ __global__ void __launch_bounds__(Cfg::kThreads, 1) gemm_tiled(const GemmParams 
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK;
   constexpr int RM = Cfg::RM, RN = Cfg::RN, KSUB = Cfg::KSUB;
   static_assert(KSUB % 2 == 0, "fragment buffers alternate per K sub-step");
-  static_assert(FB != kFetchRegT, "B is always K-contiguous");
+  static_assert(FB != kFetchRegT && FB != kFetchDmaT, "B is always K-contiguous");
+  constexpr bool kAT = FA == kFetchDmaT;   // A tile M-contiguous in LDS
   // stage s: A at smem + s*kStage, B at smem + s*kStage + BM*BK (halves)
   constexpr int kStage = (BM + BN) * BK;
   __shared__ __attribute__((aligned(1024))) _Float16 smem[2 * kStage];
@@ -295,8 +479,14 @@ __global__ void __launch_bounds__(Cfg::kThreads, 1) gemm_tiled(const GemmParams 
   for (int kk = 0; kk < KSUB; ++kk) {
 #pragma unroll
     for (int i = 0; i < RM; ++i) {
-      const RowK a = frag_a_coord<Cfg>(w, lane, i, kk);
-      fa_off[kk][i] = lds_offset<BK>(a.row, a.k);
+      if constexpr (kAT) {
+        // first of the two transposed reads; the second is 4 k-rows on
+        const RowK t = frag_a_tr_coord<Cfg>(w, lane, i, kk);
+        fa_off[kk][i] = lds_offset_mn<BM>(t.row, t.k);
+      } else {
+        const RowK a = frag_a_coord<Cfg>(w, lane, i, kk);
+        fa_off[kk][i] = lds_offset<BK>(a.row, a.k);
+      }
     }
 #pragma unroll
     for (int j = 0; j < RN; ++j) {
@@ -309,14 +499,20 @@ __global__ void __launch_bounds__(Cfg::kThreads, 1) gemm_tiled(const GemmParams 
   // fragment read r in the order the MFMAs consume them (i-major, so A0,
   // then B0..B(RN-1), then A1..A(RM-1))
   constexpr int kReads = RM + RN, kMfma = RM * RN;
+  auto read_a = [&](int i, int buf, int kk, const _Float16* st) {
+    if constexpr (kAT)
+      fa[buf][i] = read_tr_pair(&st[fa_off[kk][i]], &st[fa_off[kk][i] + 4 * BM]);
+    else
+      fa[buf][i] = *(const half8*)&st[fa_off[kk][i]];
+  };
   auto read_one = [&](int r, int buf, int kk, int s) {
     const _Float16* st = smem + s * kStage;
     if (r == 0)
-      fa[buf][0] = *(const half8*)&st[fa_off[kk][0]];
+      read_a(0, buf, kk, st);
     else if (r <= RN)
       fb[buf][r - 1] = *(const half8*)&st[fb_off[kk][r - 1]];
     else
-      fa[buf][r - RN] = *(const half8*)&st[fa_off[kk][r - RN]];
+      read_a(r - RN, buf, kk, st);
   };
   auto frags = [&](int buf, int kk, int s) {
 #pragma unroll
@@ -426,8 +622,11 @@ __global__ void __launch_bounds__(Cfg::kThreads, 1) gemm_tiled(const GemmParams 
       const int gm = min(m0 + row, p.M - 1);
       _Float16 v = (_Float16)0.0f;
       if (gk < p.K)
-        v = FA == kFetchRegT ? A[(int64_t)gk * p.lda + gm] : A[(int64_t)gm * p.lda + gk];
-      sa[lds_offset<BK>(row, k)] = v;
+        v = (FA == kFetchRegT || kAT) ? A[(int64_t)gk * p.lda + gm] : A[(int64_t)gm * p.lda + gk];
+      if constexpr (kAT)
+        sa[lds_offset_mn<BM>(row, k)] = v;
+      else
+        sa[lds_offset<BK>(row, k)] = v;
     }
     for (int e = tid; e < BN * BK; e += Cfg::kThreads) {
       const int row = e / BK, k = e % BK, gk = k0 + k;
@@ -441,7 +640,10 @@ __global__ void __launch_bounds__(Cfg::kThreads, 1) gemm_tiled(const GemmParams 
       mma(0);
     }
   }
-  epilogue<Cfg, CK, DK>(p, w, lane, m0, n0, acc);
+  if constexpr (CK != 0)
+    epilogue_lds<Cfg, CK, DK>(p, (float*)smem, w, lane, m0, n0, acc);
+  else
+    epilogue<Cfg, CK, DK>(p, w, lane, m0, n0, acc);
 }
 
 // ---------------------------------------------------------------------------
@@ -515,7 +717,7 @@ constexpr KernelFn tiled_table[3][2] = {
     {gemm_tiled<Cfg, FA, FB, 2, 1>, gemm_tiled<Cfg, FA, FB, 2, 2>}};
 
 // fetch policy pairs used: (A, B) = (DMA, DMA), (REG, REG), (REG, DMA),
-// (DMA, REG), (REGT, DMA), (REGT, REG)
+// (DMA, REG), (REGT, DMA), (REGT, REG), (DMAT, DMA), (DMAT, REG)
 template <class Cfg>
 const void* tiled_symbol(int fa, int fb, int ck, int dk) {
   if (ck < 0 || ck > 2 || dk < 1 || dk > 2) return nullptr;
@@ -525,6 +727,8 @@ const void* tiled_symbol(int fa, int fb, int ck, int dk) {
   if (fa == kFetchDma && fb == kFetchReg) return (const void*)tiled_table<Cfg, kFetchDma, kFetchReg>[ck][dk - 1];
   if (fa == kFetchRegT && fb == kFetchDma) return (const void*)tiled_table<Cfg, kFetchRegT, kFetchDma>[ck][dk - 1];
   if (fa == kFetchRegT && fb == kFetchReg) return (const void*)tiled_table<Cfg, kFetchRegT, kFetchReg>[ck][dk - 1];
+  if (fa == kFetchDmaT && fb == kFetchDma) return (const void*)tiled_table<Cfg, kFetchDmaT, kFetchDma>[ck][dk - 1];
+  if (fa == kFetchDmaT && fb == kFetchReg) return (const void*)tiled_table<Cfg, kFetchDmaT, kFetchReg>[ck][dk - 1];
   return nullptr;
 }
 

@@ -15,6 +15,7 @@ struct GemmParams {
   int M, N, K;
   int lda, ldb, ldc, ldd;
   int tiles_m, tiles_n, group_m;
+  int d_vec;   // 1: D rows take aligned 4-element vector stores (base and ldd)
   const void* A;
   const void* B;
   const void* C;
@@ -36,6 +37,8 @@ enum Fetch : int {
   kFetchDma = 0,    // global_load_lds_dwordx4 (K-contiguous, 16-byte aligned rows)
   kFetchReg = 1,    // 16-byte loads into registers, any 2-byte alignment
   kFetchRegT = 2,   // M-contiguous A, transposed in registers
+  kFetchDmaT = 3,   // M-contiguous A, global_load_lds into an M-contiguous tile,
+                    // fragments read with the transposing LDS read
 };
 
 // direct-from-global: 128x128 block (the simple-GEMM page's CTA tile), 2x2 waves

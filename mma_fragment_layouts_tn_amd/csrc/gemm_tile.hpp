@@ -43,6 +43,10 @@ struct TileCfg {
   static constexpr int CH = BK / 8;               // 16-byte chunks per LDS row
   static constexpr int kLdsA = BM * BK;           // halves per stage
   static constexpr int kLdsB = BN * BK;
+  // epilogue: accumulator rows of 32 staged through LDS per pass (fp32,
+  // every wave at once), the most that fit in the two operand stages
+  static constexpr int kEpiRows = (RM % 2 == 0 && kWaves * 64 * WTN * 4 <= 4 * (BM + BN) * BK)
+                                      ? 2 : 1;
 
   static_assert(BM % (WAVES_M * kAtomM) == 0 && BN % (WAVES_N * kAtomN) == 0,
                 "wave tile must be a multiple of the atom");
@@ -50,7 +54,19 @@ struct TileCfg {
   static_assert((BM * CH) % kThreads == 0 && (BN * CH) % kThreads == 0,
                 "operand tile chunks must divide evenly over the threads");
   static_assert(CH == 4 || CH == 8, "swizzle defined for 4 or 8 chunks per row");
+  static_assert(kWaves * kEpiRows * 32 * WTN * 4 <= 4 * (BM + BN) * BK,
+                "epilogue staging must fit in the operand stages");
 };
+
+// Epilogue staging tile of one wave: rows of WTN fp32, 16-byte groups
+// XOR-swizzled by bit 2 of the row.  An accumulator store (32 lanes on row r,
+// 32 on row r+4, 32 consecutive n each) and a 16-byte read (16 lanes along
+// one row) both touch each 4-byte bank once.
+template <int WTN>
+MFL_HD constexpr int epi_offset(int r, int n) {
+  static_assert(WTN % 64 == 0, "needs 16 groups of 4 per row");
+  return r * WTN + (((n >> 2) ^ (((r >> 2) & 1) << 3)) << 2) + (n & 3);
+}
 
 // XOR swizzle of the 16-byte chunk index within an LDS row.  A 16-byte LDS
 // read is served 16 lanes at a time across 64 four-byte banks (256 bytes), so
@@ -63,6 +79,10 @@ MFL_HD constexpr int swz(int row) {
   return CH == 8 ? ((row >> 1) & 7) : ((row >> 2) & 3);
 }
 
+struct RowK {
+  int row, k;
+};
+
 // element offset (in halves) of (row, k) in one LDS operand tile
 template <int BK>
 MFL_HD constexpr int lds_offset(int row, int k) {
@@ -70,13 +90,31 @@ MFL_HD constexpr int lds_offset(int row, int k) {
   return row * BK + (((k >> 3) ^ swz<CH>(row)) << 3) + (k & 7);
 }
 
+// M-contiguous A tile (BK rows of BM halves, one per k): 16-byte chunk c of
+// row k is stored at chunk c ^ 4(k & 3).  The transposed LDS read below takes
+// four k-rows x 32 m per 32-lane pass; with this XOR those 16 chunks fall in
+// 16 different 16-byte bank groups.
+template <int BM>
+MFL_HD constexpr int lds_offset_mn(int m, int k) {
+  static_assert(BM % 128 == 0, "needs at least 16 chunks per row");
+  return k * BM + (((m >> 3) ^ ((k & 3) << 2)) << 3) + (m & 7);
+}
+
+// Transposed LDS read (ds_read_b64_tr_b16), as measured on gfx950: within
+// each block of 16 lanes, output lane i receives element e from source lane
+// 4e + i/4, element i%4 (each source lane supplies 4 consecutive halves at
+// its own address).  So if source lane s of the block addresses k-row
+// k0 + s/4 at m = m0 + 4(s%4), output lane i gets A(m0 + i, k0 + e) for
+// e = 0..3: an (m, k) tile stored M-contiguous arrives K-contiguous per
+// lane, the regrouping the route page gives ldmatrix ("ldmatrix 怎样对上
+// MMA 的寄存器").  Two such reads (k0 and k0 + 4) fill one 32x32x16 operand.
+// Source coordinates of lane `lane`'s first read for the atom operand
+// (row = l%32, k = 8(l/32) + v): m within the atom, k within the atom.
+MFL_HD constexpr RowK atom_a_tr_source(int lane);
+
 // Atom TV layouts of the instruction the kernels issue.
 MFL_HD constexpr Layout atom_ab_tv() { return mfma_tv(kMfma32x32x16, 0); }
 MFL_HD constexpr Layout atom_c_tv() { return mfma_tv(kMfma32x32x16, 2); }
-
-struct RowK {
-  int row, k;
-};
 
 // Operand value 0 of `lane`: (row within atom, k within atom); values 1..7
 // follow at k+1..k+7 (the value mode of the layout has stride ROWS, i.e. unit
@@ -94,6 +132,27 @@ MFL_HD constexpr RowK atom_c_coord(int lane, int v) {
   return RowK{int(q % 32), int(q / 32)};
 }
 
+MFL_HD constexpr RowK atom_a_tr_source(int lane) {
+  const int s = lane & 15, blk = lane >> 4;           // lane within / index of its 16-lane block
+  const int m0 = 16 * (blk & 1), k0 = 8 * (blk >> 1);  // block's destination rows and k
+  return RowK{m0 + 4 * (s & 3), k0 + (s >> 2)};
+}
+
+// The transposed reads deliver exactly the atom's operand layout: output
+// lane l, value v = 4h + e comes from source lane 16(l/16) + 4e + (l%16)/4 of
+// read h, element (l%16)%4.
+MFL_HD constexpr bool tr_reads_match_atom() {
+  for (int l = 0; l < 64; ++l)
+    for (int v = 0; v < 8; ++v) {
+      const int h = v / 4, e = v % 4, i = l % 16;
+      const RowK src = atom_a_tr_source(16 * (l / 16) + 4 * e + i / 4);
+      const RowK want = atom_ab_coord(l);
+      if (src.row + i % 4 != want.row || src.k + 4 * h != want.k + v) return false;
+    }
+  return true;
+}
+static_assert(tr_reads_match_atom(), "transposed reads must produce the MFMA operand layout");
+
 // The value mode must step k by one, so 8 values are one 16-byte run.
 static_assert(eval2(atom_ab_tv(), 0, 1) - eval2(atom_ab_tv(), 0, 0) == 32,
               "operand values must be K-contiguous");
@@ -107,6 +166,16 @@ MFL_HD constexpr RowK frag_a_coord(int w, int lane, int i, int kk) {
   const RowK a = atom_ab_coord(lane);
   const int wm = w % Cfg::WAVES_M;
   return RowK{wm * Cfg::WTM + i * Cfg::kAtomM + a.row, kk * Cfg::kAtomK + a.k};
+}
+
+// Source (m, k) within the workgroup tile of the first transposed read that
+// fills A fragment i, K sub-step kk, when A sits M-contiguous in LDS; the
+// second read is 4 k-rows further.
+template <class Cfg>
+MFL_HD constexpr RowK frag_a_tr_coord(int w, int lane, int i, int kk) {
+  const RowK t = atom_a_tr_source(lane);
+  const int wm = w % Cfg::WAVES_M;
+  return RowK{wm * Cfg::WTM + i * Cfg::kAtomM + t.row, kk * Cfg::kAtomK + t.k};
 }
 
 template <class Cfg>

@@ -58,7 +58,37 @@ __global__ void __launch_bounds__(64) probe_mfma(const uint16_t* a, const uint16
   (void)VC;
 }
 
+struct LaneOffsets {
+  int32_t h[64];
+};
+
+typedef short short4v __attribute__((ext_vector_type(4)));
+
+__global__ void __launch_bounds__(64) probe_tr16(const LaneOffsets offs, const uint16_t* in,
+                                                 uint16_t* out) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[4096];
+  const int l = threadIdx.x;
+  for (int i = l; i < 4096; i += 64) lds[i] = in[i];
+  __syncthreads();
+  using lds_s4 = __attribute__((address_space(3))) short4v*;
+  const short4v r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(lds + offs.h[l]));
+  for (int e = 0; e < 4; ++e) out[l * 4 + e] = (uint16_t)r[e];
+}
+
 }  // namespace
+
+extern "C" int mfl_probe_lds_tr16(const int32_t* lane_offsets, const uint16_t* lds_in,
+                                  uint16_t* out, void* stream) {
+  if (!lane_offsets || !lds_in || !out) return -4;
+  LaneOffsets offs;
+  for (int l = 0; l < 64; ++l) {
+    const int32_t h = lane_offsets[l];
+    if (h < 0 || h > 4092 || h % 4 != 0) return -4;
+    offs.h[l] = h;
+  }
+  hipLaunchKernelGGL(probe_tr16, dim3(1), dim3(64), 0, (hipStream_t)stream, offs, lds_in, out);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
 
 extern "C" int mfl_probe_mfma(int32_t op, const uint16_t* a_slots, const uint16_t* b_slots,
                               const float* c_slots, float* d_out, void* stream) {

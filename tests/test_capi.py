@@ -91,18 +91,26 @@ def _plan(M=64, N=64, K=64, A=P, lda=None, B=P, ldb=None, **kw):
 
 
 def test_fetch_policy_choice():
-    DMA, REG, REGT = 0, 1, 2
-    assert _plan(M=4096, N=4096, K=4096)[1:] == (mfl.ALGOS["lds256"], DMA, DMA)
+    DMA, REG, REGT, DMAT = 0, 1, 2, 3
+    assert _plan(M=4096, N=4096, K=4096)[1:] == (mfl.ALGOS["lds256w4"], DMA, DMA)
     assert _plan(M=4096, N=4096, K=4097, lda=4097, ldb=4097)[1:] == (mfl.ALGOS["lds256"], REG, REG)
     assert _plan(lda=72, ldb=68)[2:] == (DMA, REG)
     assert _plan(A=P + 2, lda=64)[2:] == (REG, DMA)
-    assert _plan(a_order=mfl.A_MMAJOR, lda=72)[2:] == (REGT, DMA)
+    assert _plan(a_order=mfl.A_MMAJOR, lda=72)[2:] == (DMAT, DMA)
+    assert _plan(a_order=mfl.A_MMAJOR, lda=68)[2:] == (REGT, DMA)           # rows not 16-byte
+    assert _plan(M=60, a_order=mfl.A_MMAJOR, lda=72)[2:] == (REGT, DMA)     # M % 8 != 0
+    assert _plan(a_order=mfl.A_MMAJOR, lda=72, A=P + 8)[2:] == (REGT, DMA)
+    assert _plan(a_order=mfl.A_MMAJOR, lda=72, algo=mfl.algo_code("lds256+reg"))[2:] == (REGT, REG)
+    assert _plan(M=8192, N=8192, K=2048, a_order=mfl.A_MMAJOR, lda=8200)[1:] == (
+        mfl.ALGOS["lds256"], DMAT, DMA)
     assert _plan(algo=mfl.ALGOS["lds256"] | mfl.REG_FETCH)[1:] == (mfl.ALGOS["lds256"], REG, REG)
     assert _plan(algo=mfl.algo_code("lds128+reg"))[2:] == (REG, REG)
 
 
 def test_auto_choice():
-    assert _v(M=4096, N=4096, K=4096)[1] == mfl.ALGOS["lds256"]
+    assert _v(M=4096, N=4096, K=4096)[1] == mfl.ALGOS["lds256w4"]
+    assert _v(M=4096, N=4096, K=4096, c=mfl.F32, C=P, ldc=4096)[1] == mfl.ALGOS["lds256"]
+    assert _v(M=4096, N=4096, K=4096, lda=4100)[1] == mfl.ALGOS["lds256"]
     assert _v(M=256, N=256, K=256)[1] == mfl.ALGOS["lds128"]
     assert _v(M=32, N=16, K=16, algo=1)[1] == mfl.ALGOS["direct"]
 

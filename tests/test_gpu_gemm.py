@@ -51,9 +51,15 @@ def test_small_integer_bit_exact(algo, shape):
         assert v.ok, (w.name, c, d, str(v))
 
 
-@pytest.mark.parametrize("algo", LDS_ALGOS)
-@pytest.mark.parametrize("shape", [(40, 24, 33), (130, 260, 65), (257, 129, 100), (8, 9, 10),
-                                   (300, 264, 200)])
+# lda = M + 8: with M % 8 == 0 the rows are 16-byte aligned and A goes
+# straight into LDS (transposing fragment reads); otherwise, or with the
+# register flag, it is transposed in registers
+MMAJOR_SHAPES = [(40, 24, 33), (130, 260, 65), (257, 129, 100), (8, 9, 10), (300, 264, 200),
+                 (264, 130, 100), (512, 300, 129), (136, 520, 64)]
+
+
+@pytest.mark.parametrize("algo", LDS_ALGOS + ["lds256+reg"])
+@pytest.mark.parametrize("shape", MMAJOR_SHAPES)
 def test_mmajor_a_bit_exact(algo, shape):
     M, N, K = shape
     for c, d, ldb in ((None, "f32", K), ("f32", "f32", (K + 7) // 8 * 8), ("f16", "f16", K + 1)):
@@ -64,6 +70,18 @@ def test_mmajor_a_bit_exact(algo, shape):
         _assert_checks(checks)
         v = verdict(D, oracle_full(w, x), w, True)
         assert v.ok, (w.name, c, d, str(v))
+
+
+@pytest.mark.parametrize("algo", LDS_ALGOS)
+def test_mmajor_a_float_within_tolerance(algo):
+    M, N, K = 520, 264, 700
+    w = W.custom(M, N, K, a_order="m", lda=M + 8, ldb=K + 8, c="f32", d="f32", dist="unif",
+                 seed=11)
+    x = W.make_inputs(w)
+    D, checks = run_gemm(w, x, algo)
+    _assert_checks(checks)
+    v = verdict(D, oracle_full(w, x), w, False)
+    assert v.ok, (w.name, str(v))
 
 
 @pytest.mark.parametrize("algo", ALGOS + ["lds256+reg", "lds128+reg"])
@@ -112,7 +130,7 @@ NAMED = [
     ("tiny_32x16x16", ["direct", "lds128", "lds256"], False),
     ("direct_256", ["direct"], True),
     ("lds_4096", ["lds128", "lds256", "lds256w4", "lds256+reg"], True),
-    ("accum_mmajor_8192x8192x2048", ["auto", "lds128"], True),
+    ("accum_mmajor_8192x8192x2048", ["auto", "lds128", "lds256+reg"], True),
     ("ragged_8191x6143x4097", ["auto", "lds128", "lds256w4"], True),
 ]
 

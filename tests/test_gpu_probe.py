@@ -49,3 +49,43 @@ def test_mfma_operand_maps(op):
         if d[l, v] != want[m, n]:
             bad.append((l, v, m, n, float(d[l, v]), want[m, n]))
     assert not bad, bad[:8]
+
+
+def _tr16_rule(offsets, values):
+    """The regrouping the kernels assume for ds_read_b64_tr_b16: in each
+    block of 16 lanes, lane i receives element e from lane 4e + i//4 of the
+    block, element i % 4 (each lane reads 4 halves at its own offset)."""
+    out = np.empty((64, 4), np.int16)
+    for l in range(64):
+        b, i = divmod(l, 16)
+        for e in range(4):
+            out[l, e] = values[offsets[16 * b + 4 * e + i // 4] + i % 4]
+    return out
+
+
+@pytest.mark.parametrize("pattern", ["contiguous", "rows", "random", "kernel"])
+def test_lds_transposing_read(pattern):
+    rng = np.random.default_rng(7)
+    values = rng.permutation(4096).astype(np.int16)      # distinct: each output names its source
+    if pattern == "contiguous":
+        offs = [4 * l for l in range(64)]
+    elif pattern == "rows":
+        offs = [32 * l for l in range(64)]
+    elif pattern == "random":
+        offs = [int(v) * 4 for v in rng.choice(1024, 64, replace=False)]
+    else:
+        # the kernel's own first read of A fragment (wave 0, repeat 0, K
+        # sub-step 0) in the 256-wide M-contiguous tile
+        lay = mfl.lds_tile_offsets("lds256", "A_mmajor")          # [k, m]
+        src = mfl.fragment_coords("lds256", "A_tr")[:64, 0]         # (m, k) per lane
+        offs = [int(lay[k, m]) for m, k in src]
+    say(f"[gpu] probe tr16 {pattern}")
+    got = mfl.probe_lds_tr16(offs, torch.from_numpy(values).cuda()).cpu().numpy()
+    assert np.array_equal(got, _tr16_rule(offs, values))
+    if pattern == "kernel":
+        # and the values are the MFMA operand: lane l gets (m, k) = (l%32, 8(l/32) + e)
+        lay = mfl.lds_tile_offsets("lds256", "A_mmajor")
+        for l in range(64):
+            for e in range(4):
+                m, k = l % 32, 8 * (l // 32) + e
+                assert got[l, e] == values[lay[k, m]], (l, e)

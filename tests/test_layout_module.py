@@ -244,3 +244,46 @@ def test_tile_order_keeps_xcd_blocks_compact():
     for x in range(8):
         ids = np.arange(x, 256, 8)
         assert len(set(tm[ids].tolist())) + len(set(tn[ids].tolist())) == 12
+
+
+# ----------------------------------------- M-contiguous A: transposing reads
+@pytest.mark.parametrize("algo", ["lds128", "lds256", "lds256w4"])
+def test_mmajor_tile_and_transposed_reads_conflict_free(algo):
+    """The M-contiguous A tile is a permutation keeping 8-half chunks whole,
+    and every transposing read (64 lanes x 8 bytes, served 32 lanes per pass)
+    touches each of the 64 four-byte banks exactly once per pass."""
+    lay = mfl.lds_tile_offsets(algo, "A_mmajor")                   # [k, m]
+    bk, bm = lay.shape
+    assert sorted(lay.reshape(-1).tolist()) == list(range(bk * bm))
+    chunks = lay.reshape(bk, bm // 8, 8)
+    assert (chunks - chunks[:, :, :1] == np.arange(8)).all()
+    src = mfl.fragment_coords(algo, "A_tr")                         # (threads, KSUB*RM, 2)
+    for t0 in range(0, src.shape[0], 64):
+        for slot in range(src.shape[1]):
+            for h in (0, 1):
+                for half in (0, 32):
+                    banks = []
+                    for l in range(half, half + 32):
+                        m, k = src[t0 + l, slot]
+                        byte = 2 * int(lay[k + 4 * h, m])
+                        assert byte % 8 == 0
+                        banks += [(byte // 4) % 64, (byte // 4 + 1) % 64]
+                    assert sorted(banks) == list(range(64)), (algo, t0, slot, h, half)
+
+
+@pytest.mark.parametrize("algo", ["lds128", "lds256", "lds256w4"])
+def test_transposed_reads_give_the_operand_fragments(algo):
+    """Applying the transposing read's lane regrouping (pinned on the GPU by
+    test_gpu_probe) to the kernel's source coordinates yields exactly the A
+    fragment coordinates of the K-contiguous path, value by value."""
+    src = mfl.fragment_coords(algo, "A_tr")                         # (T, KSUB*RM, 2)
+    frag = mfl.fragment_coords(algo, "A")                           # (T, KSUB*RM*8, 2)
+    T, slots, _ = src.shape
+    for t in range(T):
+        w, l = divmod(t, 64)
+        b, i = divmod(l, 16)
+        for slot in range(slots):
+            for v in range(8):
+                h, e = divmod(v, 4)
+                m, k = src[64 * w + 16 * b + 4 * e + i // 4, slot]
+                assert (m + i % 4, k + 4 * h) == tuple(frag[t, slot * 8 + v]), (algo, t, slot, v)
