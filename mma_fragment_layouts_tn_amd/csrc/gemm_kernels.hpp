@@ -86,11 +86,46 @@ __device__ __forceinline__ void d_store(const GemmParams& p, int m, int n, float
 
 // Register epilogue: acc[i][j] value v -> (m, n) from the accumulator TV
 // layout, one element per store (for a fixed value the 64 lanes cover two
-// 128-byte row runs).  Interior tiles skip the per-element bounds checks.
+// 128-byte row runs).  Interior tiles without C store through a buffer
+// descriptor based at the wave's tile origin: the lane part of the layout is
+// one per-lane offset, the row part of (repeat, value) a uniform scalar
+// offset and the column part the instruction's immediate, so each element is
+// one store instruction with no address arithmetic on the vector side.  Edge
+// tiles (and C reads, which only the direct kernel does here) check and
+// address each element.
 template <class Cfg, int CK, int DK>
 __device__ __forceinline__ void epilogue(const GemmParams& p, int w, int lane, int m0,
                                          int n0, const floatx16 (&acc)[Cfg::RM][Cfg::RN]) {
-  const bool interior = m0 + Cfg::BM <= p.M && n0 + Cfg::BN <= p.N;
+  constexpr int ES = DK == 1 ? 2 : 4;
+  if (CK == 0 && m0 + Cfg::BM <= p.M && n0 + Cfg::BN <= p.N &&
+      (int64_t)Cfg::BM * p.ldd * ES < ((int64_t)1 << 31)) {
+    const RowK cl = atom_c_coord(lane, 0);
+    const RowK w0 = frag_c_coord<Cfg>(w, 0, 0, 0, 0);
+    char* tile = (char*)p.D + ((int64_t)(m0 + w0.row) * p.ldd + (n0 + w0.k)) * ES;
+    // raw buffer (stride 0), records up to 2^31 bytes, 32-bit data format
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(tile, (short)0, 0x7fffffff, 0x00020000);
+    const int voff = (cl.row * p.ldd + cl.k) * ES;
+#pragma unroll
+    for (int i = 0; i < Cfg::RM; ++i)
+#pragma unroll
+      for (int j = 0; j < Cfg::RN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const RowK cv = atom_c_coord(0, v);
+          const int soff = (i * Cfg::kAtomM + cv.row) * p.ldd * ES;
+          const int dn = (j * Cfg::kAtomN + cv.k) * ES;
+          // (the element is copied to a scalar first: a bit cast applied to
+          // a vector element directly read element 0 with this compiler)
+          const float x = acc[i][j][v];
+          if constexpr (DK == 1)
+            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (_Float16)x),
+                                                  rsrc, voff + dn, soff, 0);
+          else
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), rsrc, voff + dn, soff, 0);
+        }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < Cfg::RM; ++i)
 #pragma unroll
@@ -99,8 +134,7 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, int w, int lane, i
       for (int v = 0; v < 16; ++v) {
         const RowK c = frag_c_coord<Cfg>(w, lane, i, j, v);
         const int m = m0 + c.row, n = n0 + c.k;
-        if (interior || (m < p.M && n < p.N))
-          d_store<DK>(p, m, n, acc[i][j][v] + c_value<CK>(p, m, n));
+        if (m < p.M && n < p.N) d_store<DK>(p, m, n, acc[i][j][v] + c_value<CK>(p, m, n));
       }
 }
 

@@ -153,6 +153,19 @@ MFL_HD constexpr bool tr_reads_match_atom() {
 }
 static_assert(tr_reads_match_atom(), "transposed reads must produce the MFMA operand layout");
 
+// The accumulator layout splits into a lane part and a value part:
+// coord(l, v) = coord(l, 0) + coord(0, v).  The epilogue keeps the lane part
+// in a per-lane offset and folds the value part into a uniform base address.
+MFL_HD constexpr bool c_layout_separable() {
+  for (int l = 0; l < 64; ++l)
+    for (int v = 0; v < 16; ++v) {
+      const RowK a = atom_c_coord(l, v), b = atom_c_coord(l, 0), c = atom_c_coord(0, v);
+      if (a.row != b.row + c.row || a.k != b.k + c.k) return false;
+    }
+  return true;
+}
+static_assert(c_layout_separable(), "accumulator (m, n) must split into lane + value parts");
+
 // The value mode must step k by one, so 8 values are one 16-byte run.
 static_assert(eval2(atom_ab_tv(), 0, 1) - eval2(atom_ab_tv(), 0, 0) == 32,
               "operand values must be K-contiguous");
