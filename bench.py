@@ -105,8 +105,11 @@ def cpu_baseline(w, x, target_s: float):
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=50)
+    # From idle the chip needs ~1000 back-to-back launches (~0.1 s at 4096^3)
+    # before the clock settles under the power limit; the defaults warm up
+    # well past that and time steady state.
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--workload", default="lds_4096")
     ap.add_argument("--algo", default="auto",
                     help="auto, direct, lds128, lds256, lds256w4; '+reg' forces register fetch")

@@ -463,6 +463,8 @@ __global__ void __launch_bounds__(Cfg::kThreads, 1) gemm_tiled(const GemmParams 
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK;
   constexpr int RM = Cfg::RM, RN = Cfg::RN, KSUB = Cfg::KSUB;
   static_assert(KSUB % 2 == 0, "fragment buffers alternate per K sub-step");
+  constexpr int kDist = Cfg::kFragDist;
+  constexpr int NBUF = kDist == 1 ? 2 : KSUB;     // fragment register buffers
   static_assert(FB != kFetchRegT && FB != kFetchDmaT, "B is always K-contiguous");
   constexpr bool kAT = FA == kFetchDmaT;   // A tile M-contiguous in LDS
   // stage s: A at smem + s*kStage, B at smem + s*kStage + BM*BK (halves)
@@ -529,7 +531,8 @@ __global__ void __launch_bounds__(Cfg::kThreads, 1) gemm_tiled(const GemmParams 
     }
   }
 
-  half8 fa[2][RM], fb[2][RN];
+  half8 fa[NBUF][RM], fb[NBUF][RN];
+  auto bufof = [](int kk) { return kDist == 1 ? (kk & 1) : kk; };   // buffer of sub-step kk
   // fragment read r in the order the MFMAs consume them (i-major, so A0,
   // then B0..B(RN-1), then A1..A(RM-1))
   constexpr int kReads = RM + RN, kMfma = RM * RN;
@@ -577,7 +580,7 @@ __global__ void __launch_bounds__(Cfg::kThreads, 1) gemm_tiled(const GemmParams 
   // into stage fs) and LDS stores of register-staged data (stage ss) over the
   // whole group.  The fences keep the compiler from regrouping them.
   auto group = [&](int buf, auto reads, int rbuf, int rkk, int rs, auto fetch, int fkt, int fs,
-                   auto stores, int ss) {
+                   auto stores, int ss, int v0, int v1) {
     constexpr bool kR = decltype(reads)::value, kF = decltype(fetch)::value;
     constexpr bool kS = decltype(stores)::value;
     constexpr int rslots = kMfma / 2 > 0 ? kMfma / 2 : 1;
@@ -593,8 +596,10 @@ __global__ void __launch_bounds__(Cfg::kThreads, 1) gemm_tiled(const GemmParams 
         }
       }
       if constexpr (kF) {
+        // fetch instructions [v0, v1) spread over the group
 #pragma unroll
-        for (int v = g * kVmem / kMfma; v < (g + 1) * kVmem / kMfma; ++v) issue_one(v, fkt, fs);
+        for (int v = v0 + g * (v1 - v0) / kMfma; v < v0 + (g + 1) * (v1 - v0) / kMfma; ++v)
+          issue_one(v, fkt, fs);
       }
       if constexpr (kS) {
 #pragma unroll
@@ -614,29 +619,36 @@ __global__ void __launch_bounds__(Cfg::kThreads, 1) gemm_tiled(const GemmParams 
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    frags(0, 0, 0);
+    frags(bufof(0), 0, 0);
+    if constexpr (kDist == 2) frags(bufof(1), 1, 0);
   }
   // One K-step on tile kt (stage kt&1).  FETCH: tile kt+2 exists and is
   // fetched; NEXT: tile kt+1 exists.  The last two steps are peeled off the
   // loop so its body is one straight block.
+  //
+  // Fragment distance 1: sub-steps 0..KSUB-2 read sub-step kk+1 of stage cur;
+  // the barrier; sub-step KSUB-1 fetches tile kt+2 and reads sub-step 0 of
+  // the next stage.  Distance 2: sub-steps 0..KSUB-3 read sub-step kk+2; the
+  // barrier; sub-steps KSUB-2 and KSUB-1 share the fetch and read sub-steps 0
+  // and 1 of the next stage.  Either way register-staged tile kt+1 goes to
+  // the idle stage in the last group before the barrier, and the groups after
+  // the barrier run on fragments already in registers.
   auto step = [&](const int kt, auto fetch, auto next) {
-    constexpr bool kFetch = decltype(fetch)::value, kNext = decltype(next)::value;
+    constexpr bool kNext = decltype(next)::value;
     const int cur = kt & 1;
+    constexpr int kPre = KSUB - kDist;   // groups before the barrier
 #pragma unroll
-    for (int kk = 0; kk + 2 < KSUB; ++kk)
-      group(kk & 1, Yes(), (kk + 1) & 1, kk + 1, cur, No(), 0, 0, No(), 0);
-    // last sub-step before the barrier: register-staged tile kt+1 goes to
-    // the idle stage
-    group(KSUB & 1, Yes(), (KSUB - 1) & 1, KSUB - 1, cur, No(), 0, 0,
-          BoolC<kAnyReg && kNext>(), cur ^ 1);
+    for (int kk = 0; kk + 1 < kPre; ++kk)
+      group(bufof(kk), Yes(), bufof(kk + kDist), kk + kDist, cur, No(), 0, 0, No(), 0, 0, 0);
+    group(bufof(kPre - 1), Yes(), bufof(KSUB - 1), KSUB - 1, cur, No(), 0, 0,
+          BoolC<kAnyReg && kNext>(), cur ^ 1, 0, 0);
     __builtin_amdgcn_s_waitcnt(0);        // own reads, stores and fetch of tile kt+1 done
     __builtin_amdgcn_s_barrier();         // ... in every wave: stage cur is free
     __builtin_amdgcn_sched_barrier(0);
-    // The last sub-step's fragments are already in registers: its MFMAs
-    // cover the fetch of tile kt+2 into stage cur and the first fragment
-    // reads of stage cur^1.
-    group((KSUB - 1) & 1, next, 0, 0, cur ^ 1, fetch, kt + 2, cur, No(), 0);
-    (void)kFetch;
+#pragma unroll
+    for (int d = 0; d < kDist; ++d)
+      group(bufof(kPre + d), next, bufof(d), d, cur ^ 1, fetch, kt + 2, cur, No(), 0,
+            d * kVmem / kDist, (d + 1) * kVmem / kDist);
   };
   int kt = 0;
   for (; kt + 2 < nfull; ++kt) step(kt, Yes(), Yes());

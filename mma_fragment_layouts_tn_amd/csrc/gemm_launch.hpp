@@ -47,8 +47,9 @@ using CfgDirect = TileCfg<128, 128, 32, 2, 2>;
 using CfgLds128 = TileCfg<128, 128, 32, 2, 2>;
 // 256x256x64 block tile, 2x4 waves of 128x64 (two waves per SIMD)
 using CfgLds256 = TileCfg<256, 256, 64, 2, 4>;
-// 256x256x64 block tile, 2x2 waves of 128x128 (one wave per SIMD)
-using CfgLds256W4 = TileCfg<256, 256, 64, 2, 2>;
+// 256x256x64 block tile, 2x2 waves of 128x128 (one wave per SIMD); with a
+// single wave per SIMD the fragments are read two K sub-steps ahead
+using CfgLds256W4 = TileCfg<256, 256, 64, 2, 2, 2>;
 
 struct KernelInfo {
   int algo, bm, bn, bk, threads;

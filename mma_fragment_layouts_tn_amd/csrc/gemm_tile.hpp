@@ -30,9 +30,13 @@
 
 namespace mfl {
 
-template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_>
+// DIST: how many K sub-steps ahead the operand fragments are read from LDS
+// (1: two register buffers; 2: one buffer per sub-step, the step's barrier
+// one sub-step earlier).
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int DIST_ = 1>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_;
+  static constexpr int kFragDist = DIST_;
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
   static constexpr int kWaves = WAVES_M * WAVES_N;
   static constexpr int kThreads = 64 * kWaves;
@@ -54,6 +58,7 @@ struct TileCfg {
   static_assert((BM * CH) % kThreads == 0 && (BN * CH) % kThreads == 0,
                 "operand tile chunks must divide evenly over the threads");
   static_assert(CH == 4 || CH == 8, "swizzle defined for 4 or 8 chunks per row");
+  static_assert(DIST_ == 1 || (DIST_ == 2 && KSUB >= 4), "fragment distance 1, or 2 with 4+ sub-steps");
   static_assert(kWaves * kEpiRows * 32 * WTN * 4 <= 4 * (BM + BN) * BK,
                 "epilogue staging must fit in the operand stages");
 };
