@@ -76,12 +76,17 @@ __device__ __forceinline__ float c_value(const GemmParams& p, int m, int n) {
   return 0.0f;
 }
 
+// Stores of D are non-temporal (the `nt` cache policy): D is written once
+// and never read back by the kernel, and leaving it out of the L2s shortens
+// the write-back at the end of the kernel (about 1 % at 4096^3).
+constexpr int kNtStore = 2;   // cache-policy operand of the buffer-store builtins: nt
+
 template <int DK>
 __device__ __forceinline__ void d_store(const GemmParams& p, int m, int n, float x) {
   if constexpr (DK == 1)
-    ((_Float16*)p.D)[(int64_t)m * p.ldd + n] = (_Float16)x;   // v_cvt_f16_f32, RNE
+    __builtin_nontemporal_store((_Float16)x, (_Float16*)p.D + (int64_t)m * p.ldd + n);   // RNE
   else
-    ((float*)p.D)[(int64_t)m * p.ldd + n] = x;
+    __builtin_nontemporal_store(x, (float*)p.D + (int64_t)m * p.ldd + n);
 }
 
 // Register epilogue: acc[i][j] value v -> (m, n) from the accumulator TV
@@ -118,11 +123,13 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, int w, int lane, i
           // (the element is copied to a scalar first: a bit cast applied to
           // a vector element directly read element 0 with this compiler)
           const float x = acc[i][j][v];
+          // kNtStore: D is written once and not read back by this kernel
           if constexpr (DK == 1)
             __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (_Float16)x),
-                                                  rsrc, voff + dn, soff, 0);
+                                                  rsrc, voff + dn, soff, kNtStore);
           else
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), rsrc, voff + dn, soff, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), rsrc, voff + dn, soff,
+                                                  kNtStore);
         }
     return;
   }
@@ -171,9 +178,11 @@ __device__ __forceinline__ void store_d4(const GemmParams& p, int m, int n, floa
     if constexpr (DK == 1) {
       typedef _Float16 half4v __attribute__((ext_vector_type(4)));
       const half4v h = {(_Float16)x.x, (_Float16)x.y, (_Float16)x.z, (_Float16)x.w};
-      *(half4v*)((_Float16*)p.D + (int64_t)m * p.ldd + n) = h;
+      __builtin_nontemporal_store(h, (half4v*)((_Float16*)p.D + (int64_t)m * p.ldd + n));
     } else {
-      *(float4*)((float*)p.D + (int64_t)m * p.ldd + n) = x;
+      typedef float float4v __attribute__((ext_vector_type(4)));
+      const float4v v = {x.x, x.y, x.z, x.w};
+      __builtin_nontemporal_store(v, (float4v*)((float*)p.D + (int64_t)m * p.ldd + n));
     }
   } else {
     d_store<DK>(p, m, n, x.x);
