@@ -58,7 +58,8 @@ typedef enum { MFL_A_KMAJOR = 0, MFL_A_MMAJOR = 1 } mfl_a_order;
  * 128x128x32 block tiles through LDS (the block tile of "CuTe Layout 到
  * Tensor Core" §4) with 4 waves of 64x64.  LDS_256 stages 256x256x64 block
  * tiles with 8 waves of 128x64; LDS_256_W4 the same tile with 4 waves of
- * 128x128.  The LDS kernels fetch each K-contiguous operand straight into
+ * 128x128.  LDS_128_W1 stages 128x128x32 tiles owned by one wave each (a
+ * workgroup of 64 threads, four per CU).  The LDS kernels fetch each K-contiguous operand straight into
  * LDS (global_load_lds_dwordx4) when its base and leading dimension are
  * 16-byte aligned, else through registers with 16-byte loads at any 2-byte
  * alignment.  An M-contiguous A goes straight into an M-contiguous LDS tile
@@ -72,7 +73,8 @@ typedef enum {
   MFL_ALGO_LDS_128 = 2,
   MFL_ALGO_LDS_256 = 3,
   MFL_ALGO_LDS_256_W4 = 4,
-  MFL_ALGO_COUNT = 5,
+  MFL_ALGO_LDS_128_W1 = 5,
+  MFL_ALGO_COUNT = 6,
   MFL_ALGO_MASK = 0xff,
   MFL_ALGO_REG_FETCH = 0x100
 } mfl_algo;

@@ -483,6 +483,8 @@ int mfl_lds_tile_offsets(int32_t algo, int32_t operand, int32_t* out, int64_t ca
     case mfl::kAlgoLds256: return lds_offsets<mfl::CfgLds256>(operand, out, cap, outer, inner);
     case mfl::kAlgoLds256W4:
       return lds_offsets<mfl::CfgLds256W4>(operand, out, cap, outer, inner);
+    case mfl::kAlgoLds128W1:
+      return lds_offsets<mfl::CfgLds128W1>(operand, out, cap, outer, inner);
     default: return mfl::kLayoutBadIndex;
   }
 }
@@ -505,6 +507,7 @@ int mfl_fragment_coords(int32_t algo, int32_t operand, int32_t* out, int64_t cap
     case mfl::kAlgoLds128: return frag_coords<mfl::CfgLds128>(operand, out, cap, threads, slots);
     case mfl::kAlgoLds256: return frag_coords<mfl::CfgLds256>(operand, out, cap, threads, slots);
     case mfl::kAlgoLds256W4: return frag_coords<mfl::CfgLds256W4>(operand, out, cap, threads, slots);
+    case mfl::kAlgoLds128W1: return frag_coords<mfl::CfgLds128W1>(operand, out, cap, threads, slots);
     default: return mfl::kLayoutBadIndex;
   }
 }

@@ -8,6 +8,7 @@ namespace mfl {
 const void* tiled_symbol_128(int fa, int fb, int ck, int dk);
 const void* tiled_symbol_256(int fa, int fb, int ck, int dk);
 const void* tiled_symbol_256w4(int fa, int fb, int ck, int dk);
+const void* tiled_symbol_128w1(int fa, int fb, int ck, int dk);
 const void* direct_symbol(int ck, int dk);
 
 namespace {
@@ -23,6 +24,7 @@ KernelInfo kernel_info(int algo) {
     case kAlgoLds128: return info_of<CfgLds128>(algo);
     case kAlgoLds256: return info_of<CfgLds256>(algo);
     case kAlgoLds256W4: return info_of<CfgLds256W4>(algo);
+    case kAlgoLds128W1: return info_of<CfgLds128W1>(algo);
     default: return KernelInfo{-1, 0, 0, 0, 0};
   }
 }
@@ -34,6 +36,7 @@ const void* kernel_symbol(int algo, int fetch_a, int fetch_b, int c_kind, int d_
     case kAlgoLds128: return tiled_symbol_128(fetch_a, fetch_b, c_kind, d_kind);
     case kAlgoLds256: return tiled_symbol_256(fetch_a, fetch_b, c_kind, d_kind);
     case kAlgoLds256W4: return tiled_symbol_256w4(fetch_a, fetch_b, c_kind, d_kind);
+    case kAlgoLds128W1: return tiled_symbol_128w1(fetch_a, fetch_b, c_kind, d_kind);
     default: return nullptr;
   }
 }

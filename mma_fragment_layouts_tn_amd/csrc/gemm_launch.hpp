@@ -29,7 +29,8 @@ enum Algo : int {
   kAlgoLds128 = 2,
   kAlgoLds256 = 3,      // 8 waves of 128x64
   kAlgoLds256W4 = 4,    // 4 waves of 128x128
-  kAlgoCount = 5
+  kAlgoLds128W1 = 5,    // 1 wave of 128x128 per workgroup, 4 workgroups per CU
+  kAlgoCount = 6
 };
 
 // how an operand tile travels from global memory to LDS
@@ -50,6 +51,9 @@ using CfgLds256 = TileCfg<256, 256, 64, 2, 4>;
 // 256x256x64 block tile, 2x2 waves of 128x128 (one wave per SIMD); with a
 // single wave per SIMD the fragments are read two K sub-steps ahead
 using CfgLds256W4 = TileCfg<256, 256, 64, 2, 2, 2>;
+// 128x128x32 block tile owned by a single wave (128x128, 4x4 atoms): no
+// workgroup barrier to wait on, and four such workgroups share a CU
+using CfgLds128W1 = TileCfg<128, 128, 32, 1, 1>;
 
 struct KernelInfo {
   int algo, bm, bn, bk, threads;

@@ -20,8 +20,8 @@ from gpu_helpers import (freivalds_exact, oracle_full, oracle_sampled, run_gemm,
 
 pytestmark = pytest.mark.gpu
 
-ALGOS = ["direct", "lds128", "lds256", "lds256w4"]
-LDS_ALGOS = ["lds128", "lds256", "lds256w4"]
+ALGOS = ["direct", "lds128", "lds256", "lds256w4", "lds128w1"]
+LDS_ALGOS = ["lds128", "lds256", "lds256w4", "lds128w1"]
 
 
 def _assert_checks(checks):
@@ -121,7 +121,9 @@ def test_kernel_properties():
     assert mfl.kernel_info("lds128")["lds_bytes"] == 2 * (128 + 128) * 32 * 2
     assert mfl.kernel_info("lds256")["lds_bytes"] == 2 * (256 + 256) * 64 * 2
     assert mfl.kernel_info("lds256w4")["lds_bytes"] == 2 * (256 + 256) * 64 * 2
+    assert mfl.kernel_info("lds128w1")["lds_bytes"] == 2 * (128 + 128) * 32 * 2
     assert mfl.kernel_info("lds256")["threads"] == 512
+    assert mfl.kernel_info("lds128w1")["threads"] == 64
     say("[gpu] kernel info", {a: mfl.kernel_info(a) for a in ALGOS})
 
 
@@ -129,9 +131,9 @@ def test_kernel_properties():
 NAMED = [
     ("tiny_32x16x16", ["direct", "lds128", "lds256"], False),
     ("direct_256", ["direct"], True),
-    ("lds_4096", ["lds128", "lds256", "lds256w4", "lds256+reg"], True),
+    ("lds_4096", ["lds128", "lds256", "lds256w4", "lds256+reg", "lds128w1"], True),
     ("accum_mmajor_8192x8192x2048", ["auto", "lds128", "lds256+reg"], True),
-    ("ragged_8191x6143x4097", ["auto", "lds128", "lds256w4"], True),
+    ("ragged_8191x6143x4097", ["auto", "lds128", "lds256w4", "lds128w1"], True),
 ]
 
 

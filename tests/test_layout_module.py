@@ -157,7 +157,8 @@ def test_mfma_tv_layouts_equal_oracle_closed_forms(op):
 
 # --------------------------------------------- kernel fragment addressing
 KERNEL_TILES = {"direct": (128, 128, 32, 2, 2), "lds128": (128, 128, 32, 2, 2),
-                "lds256": (256, 256, 64, 2, 4), "lds256w4": (256, 256, 64, 2, 2)}
+                "lds256": (256, 256, 64, 2, 4), "lds256w4": (256, 256, 64, 2, 2),
+                "lds128w1": (128, 128, 32, 1, 1)}
 
 
 @pytest.mark.parametrize("algo", sorted(KERNEL_TILES))
@@ -212,7 +213,7 @@ def test_fragment_multiplicities(algo):
 
 
 # ------------------------------------------------ LDS tile layout, tile order
-@pytest.mark.parametrize("algo", ["lds128", "lds256", "lds256w4"])
+@pytest.mark.parametrize("algo", ["lds128", "lds256", "lds256w4", "lds128w1"])
 @pytest.mark.parametrize("operand", ["A", "B"])
 def test_lds_tile_layout_bijective_and_conflict_free(algo, operand):
     """The swizzled tile is a permutation of rows*BK halves that keeps each
@@ -247,7 +248,7 @@ def test_tile_order_keeps_xcd_blocks_compact():
 
 
 # ----------------------------------------- M-contiguous A: transposing reads
-@pytest.mark.parametrize("algo", ["lds128", "lds256", "lds256w4"])
+@pytest.mark.parametrize("algo", ["lds128", "lds256", "lds256w4", "lds128w1"])
 def test_mmajor_tile_and_transposed_reads_conflict_free(algo):
     """The M-contiguous A tile is a permutation keeping 8-half chunks whole,
     and every transposing read (64 lanes x 8 bytes, served 32 lanes per pass)
@@ -271,7 +272,7 @@ def test_mmajor_tile_and_transposed_reads_conflict_free(algo):
                     assert sorted(banks) == list(range(64)), (algo, t0, slot, h, half)
 
 
-@pytest.mark.parametrize("algo", ["lds128", "lds256", "lds256w4"])
+@pytest.mark.parametrize("algo", ["lds128", "lds256", "lds256w4", "lds128w1"])
 def test_transposed_reads_give_the_operand_fragments(algo):
     """Applying the transposing read's lane regrouping (pinned on the GPU by
     test_gpu_probe) to the kernel's source coordinates yields exactly the A
