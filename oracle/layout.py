@@ -74,6 +74,16 @@ def parse(text: str) -> Tuple[Nested, Nested]:
     return shape, stride
 
 
+def format_layout(layout) -> str:
+    """shape:stride text of a layout, in the form ``parse`` reads."""
+    def f(t):
+        if isinstance(t, int):
+            return str(t)
+        return "(" + ",".join(f(x) for x in t) + ")"
+    shape, stride = layout
+    return f(shape) + ":" + f(stride)
+
+
 def congruent(a: Nested, b: Nested) -> bool:
     if isinstance(a, int):
         return isinstance(b, int)
