@@ -16,7 +16,7 @@
  *     "把编号接到原来的存储上"); the result has one mode per mode of B;
  *     inputs whose leaves of B would interact through carries in A's shape
  *     are rejected (-11): every returned layout equals A(B(c)) at every c,
- *     checked by brute force (size(B) <= 2^22);
+ *     checked by brute force (size(B) <= 2^22, else -10);
  *   - right_inverse(L) = R with L(R(j)) = j for j < size(R), over the
  *     longest prefix 0..n-1 that L reaches (retile page, section
  *     "先确定要从哪些 fragment 位置取值"; route page "ldmatrix 怎样对上 MMA
@@ -46,6 +46,76 @@ int mfl_layout_table(const char* layout, int64_t* out, int64_t cap);
 int mfl_layout_coalesce(const char* layout, char* out, int64_t cap);
 int mfl_layout_compose(const char* a, const char* b, char* out, int64_t cap);
 int mfl_layout_right_inverse(const char* layout, char* out, int64_t cap);
+
+/* Tiling algebra (the operations partition_C and retile are built from:
+ * TiledMMA page "读懂 CuTe 的 make_tiled_mma", section "partition_C 怎样把分工
+ * 应用到一个 Tensor"; retile page "读懂 CuTe 的 retile_D", sections "带着 8 和
+ * 2，读一遍 retile 的源码" and "两个 K fragment 怎样连成一组").  Text in and out
+ * as above; results nesting deeper than modes of leaves keep their leaves
+ * flattened inside a top-level mode (the same function).
+ *   complement(L, M): the layout R, strides increasing, filling the gaps
+ *     between L's strides so that (L, R) tiles [0, M).  -11 when L's leaves
+ *     overlap or do not divide each other.
+ *   logical_divide(A, tiler): tiler is one layout B (A o (B, complement(B,
+ *     |A|)), result (tile, rest)) or "T0;T1;..." dividing mode m by Tm ("_"
+ *     keeps the mode; "T0;" for a single entry; result mode m = (tile_m,
+ *     rest_m)).
+ *   zipped_divide(A, tiler): as logical_divide, then all tile parts in mode
+ *     0 and all rest parts in mode 1.
+ *   logical_product(A, B): (A, complement(A, |A| cosize(B)) o B).
+ *   upcast(L, n): each leaf (s, d) -> (s / (n / d), d / n), 1 where the unit
+ *     exceeds the extent; -11 when the sizes do not divide.
+ *   with_shape(L, shape): L o make_layout(shape); shape text like
+ *     "(8,(2,4,2))" must have L's size.
+ *   tiled_product(A, B): logical_product with B's top-level modes kept
+ *     apart, (A, (C o B)_0, (C o B)_1, ...), C = complement(A, |A| cosize(B));
+ *     with A the atom's thread ids and B the atoms' arrangement over M, N, K
+ *     it is the tiled MMA's thread layout (TiledMMA page, section "第二个参数
+ *     怎样把一个 warp 扩展成四个").
+ * Compositions inside these are checked against A(B(c)) at every c; -11 when
+ * the shape:stride form would not equal it. */
+int mfl_layout_complement(const char* layout, int64_t cotarget, char* out, int64_t cap);
+int mfl_layout_logical_divide(const char* a, const char* tiler, char* out, int64_t cap);
+int mfl_layout_zipped_divide(const char* a, const char* tiler, char* out, int64_t cap);
+int mfl_layout_logical_product(const char* a, const char* b, char* out, int64_t cap);
+int mfl_layout_upcast(const char* layout, int64_t n, char* out, int64_t cap);
+int mfl_layout_with_shape(const char* layout, const char* shape, char* out, int64_t cap);
+int mfl_layout_tiled_product(const char* a, const char* b, char* out, int64_t cap);
+
+/* partition_C of a tiled MMA, derived with the operations above in the four
+ * steps of the TiledMMA page, section "partition_C 怎样把分工应用到一个 Tensor":
+ * the output tensor `c` (two modes, M then N: its storage layout) is divided
+ * by the tile, then by the atom (atom_m, atom_n); the atom block (index
+ * m + atom_m*n) is composed with the atom's C TV layout `atom_tv` (lane +
+ * nlanes*value -> m + atom_m*n); the remaining blocks are divided by the
+ * warp counts (warps_m, warps_n).  `tile` is "" (compact atom*warps per
+ * direction) or "Lm;Ln", the tiled MMA's M and N permutations (section "用
+ * Layout 改变 M 方向的坐标顺序"; "_" for an unpermuted direction).
+ * Outputs, each `cap` bytes: thr_out, one mode, thread lane + nlanes*(wm +
+ * warps_m*wn) -> storage offset of that thread's first value; val_out,
+ * (value, rest M, rest N) -> offset relative to it.  The view of thread t
+ * is the layout val_out starting at offset thr_out(t).  -13 when c is not
+ * rank 2, the tile does not divide c, the atom the tile, or the warp counts
+ * the atom blocks. */
+int mfl_layout_partition_c(const char* c, const char* tile, const char* atom_tv, int64_t atom_m,
+                           int64_t atom_n, int64_t warps_m, int64_t warps_n, char* thr_out,
+                           char* val_out, int64_t cap);
+
+/* retile_D's regrouping of a register fragment (retile page, sections "带着 8
+ * 和 2，读一遍 retile 的源码" and "两个 K fragment 怎样连成一组"): `frag` is
+ * one thread's fragment layout (mode 0 the V values of one MMA, then one mode
+ * per repeat direction, values = register slots), `tv` the copy's tiled TV
+ * layout over the reference tile of shape `tile_shape` (thread + nthr*value
+ * -> position, first coordinate fastest; it must cover the tile exactly) and
+ * atom_nval the values one copy instruction writes per thread.  Computes
+ *   mn = upcast<nthr*V>(right_inverse(tv).with_shape(tile_shape)),
+ *   fv = logical_divide(logical_product(V:1, right_inverse(mn)), atom_nval:1),
+ *   the fragment divided by (V, product_each(mn)...),
+ * and returns (tile o fv, rest modes 1..): mode 0 = (values of one copy,
+ * copy groups) -> register slot, then the repeats the copy leaves.  -13 when
+ * frag's rank is not rank(tile_shape)+1 or the value mode is not taken whole. */
+int mfl_layout_retile(const char* frag, const char* tv, const char* tile_shape, int64_t nthr,
+                      int64_t atom_nval, char* out, int64_t cap);
 
 /* Thread/value layout of a gfx950 matrix instruction operand.
  * op: 0 v_mfma_f32_32x32x16_f16, 1 v_mfma_f32_16x16x32_f16,

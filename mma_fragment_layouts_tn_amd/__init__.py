@@ -92,6 +92,16 @@ def _load() -> ctypes.CDLL:
         getattr(lib, name).argtypes = [cp, ctypes.c_char_p, i64]
         getattr(lib, name).restype = ctypes.c_int
     lib.mfl_layout_compose.argtypes = [cp, cp, ctypes.c_char_p, i64]
+    lib.mfl_layout_complement.argtypes = [cp, i64, ctypes.c_char_p, i64]
+    lib.mfl_layout_logical_divide.argtypes = [cp, cp, ctypes.c_char_p, i64]
+    lib.mfl_layout_zipped_divide.argtypes = [cp, cp, ctypes.c_char_p, i64]
+    lib.mfl_layout_logical_product.argtypes = [cp, cp, ctypes.c_char_p, i64]
+    lib.mfl_layout_upcast.argtypes = [cp, i64, ctypes.c_char_p, i64]
+    lib.mfl_layout_with_shape.argtypes = [cp, cp, ctypes.c_char_p, i64]
+    lib.mfl_layout_tiled_product.argtypes = [cp, cp, ctypes.c_char_p, i64]
+    lib.mfl_layout_partition_c.argtypes = [cp, cp, cp, i64, i64, i64, i64, ctypes.c_char_p,
+                                           ctypes.c_char_p, i64]
+    lib.mfl_layout_retile.argtypes = [cp, cp, cp, i64, i64, ctypes.c_char_p, i64]
     lib.mfl_layout_compose.restype = ctypes.c_int
     lib.mfl_layout_mfma_tv.argtypes = [i32, i32, ctypes.c_char_p, i64]
     lib.mfl_layout_mfma_tv.restype = ctypes.c_int
@@ -268,6 +278,57 @@ def layout_compose(a: str, b: str) -> str:
 
 def layout_right_inverse(text: str) -> str:
     return _text_op(_lib.mfl_layout_right_inverse, text)
+
+
+def _tiler_text(tiler) -> str:
+    """One layout text, or a sequence with one entry per mode (None = keep)."""
+    if isinstance(tiler, str):
+        return tiler
+    text = ";".join("_" if t is None else t for t in tiler)
+    return text + ";" if len(tiler) == 1 else text     # one entry: still per mode
+
+
+def layout_complement(text: str, cotarget: int) -> str:
+    return _text_op(_lib.mfl_layout_complement, text, cotarget)
+
+
+def layout_logical_divide(a: str, tiler) -> str:
+    return _text_op(_lib.mfl_layout_logical_divide, a, _tiler_text(tiler))
+
+
+def layout_zipped_divide(a: str, tiler) -> str:
+    return _text_op(_lib.mfl_layout_zipped_divide, a, _tiler_text(tiler))
+
+
+def layout_logical_product(a: str, b: str) -> str:
+    return _text_op(_lib.mfl_layout_logical_product, a, b)
+
+
+def layout_upcast(text: str, n: int) -> str:
+    return _text_op(_lib.mfl_layout_upcast, text, n)
+
+
+def layout_with_shape(text: str, shape: str) -> str:
+    return _text_op(_lib.mfl_layout_with_shape, text, shape)
+
+
+def layout_tiled_product(a: str, b: str) -> str:
+    return _text_op(_lib.mfl_layout_tiled_product, a, b)
+
+
+def layout_partition_c(c: str, atom_tv: str, atom_mn, warps_mn, tile=None) -> Tuple[str, str]:
+    """(thread layout, value layout) of partition_C; ``tile`` = None or the
+    (M, N) permutation layouts (None entries unpermuted)."""
+    thr, val = ctypes.create_string_buffer(1024), ctypes.create_string_buffer(1024)
+    tile_txt = "" if tile is None else ";".join("_" if t is None else t for t in tile)
+    _lay_check(_lib.mfl_layout_partition_c(c.encode(), tile_txt.encode(), atom_tv.encode(),
+                                           atom_mn[0], atom_mn[1], warps_mn[0], warps_mn[1],
+                                           thr, val, 1024), c)
+    return thr.value.decode(), val.value.decode()
+
+
+def layout_retile(frag: str, tv: str, tile_shape: str, nthr: int, atom_nval: int) -> str:
+    return _text_op(_lib.mfl_layout_retile, frag, tv, tile_shape, nthr, atom_nval)
 
 
 def mfma_tv(op: str, operand: str) -> str:

@@ -248,6 +248,78 @@ int emit(const mfl::Layout& L, char* out, int64_t cap) {
   return 0;
 }
 
+// a shape alone, "(8,(2,4,2))": modes of leaves with unit strides
+int parse_shape(const char* text, mfl::Layout& S) {
+  if (!text) return mfl::kLayoutBadText;
+  int64_t sh[mfl::kMaxLeaves];
+  int n = 0, ml[mfl::kMaxModes], nm = 0;
+  Parser p{text};
+  if (!p.top(sh, n, ml, nm)) return mfl::kLayoutBadText;
+  p.ws();
+  if (p.s[p.pos] != 0) return mfl::kLayoutBadText;
+  S = mfl::Layout{};
+  int k = 0;
+  for (int m = 0; m < nm; ++m) {
+    S.open_mode();
+    for (int i = 0; i < ml[m]; ++i, ++k) {
+      if (sh[k] <= 0) return mfl::kLayoutBadText;
+      S.push_leaf(sh[k], 1);
+    }
+  }
+  return S.status;
+}
+
+// Tiler text: one layout (divide the whole layout), or "T0;T1;..." with one
+// entry per top-level mode, "_" keeping that mode whole ("T0;" for a single
+// per-mode entry).  `whole` tells which form was given.
+int parse_tiler(const char* tiler, mfl::Layout* tl, bool* has, int& nt, bool& whole) {
+  if (!tiler) return mfl::kLayoutBadText;
+  const std::string t(tiler);
+  nt = 0;
+  whole = t.find(';') == std::string::npos && t.find('_') == std::string::npos;
+  if (whole) {
+    has[0] = true;
+    nt = 1;
+    return parse_layout(tiler, tl[0]);
+  }
+  size_t pos = 0;
+  for (;;) {
+    const size_t e = t.find(';', pos);
+    std::string item = t.substr(pos, e == std::string::npos ? std::string::npos : e - pos);
+    item.erase(0, item.find_first_not_of(' '));
+    item.erase(item.find_last_not_of(' ') + 1);
+    if (item.empty() && e == std::string::npos && nt > 0) break;   // "T0;": one entry
+    if (nt >= mfl::kMaxModes) return mfl::kLayoutTooLarge;
+    if (item == "_") {
+      has[nt++] = false;
+    } else {
+      const int rc = parse_layout(item.c_str(), tl[nt]);
+      if (rc) return rc;
+      has[nt++] = true;
+    }
+    if (e == std::string::npos) break;
+    pos = e + 1;
+  }
+  return 0;
+}
+
+int divide_text(const char* a, const char* tiler, bool zipped, char* out, int64_t cap) {
+  mfl::Layout A;
+  int rc = parse_layout(a, A);
+  if (rc) return rc;
+  mfl::Layout tl[mfl::kMaxModes];
+  bool has[mfl::kMaxModes] = {};
+  int nt = 0;
+  bool whole = false;
+  rc = parse_tiler(tiler, tl, has, nt, whole);
+  if (rc) return rc;
+  if (whole) return emit(mfl::logical_divide(A, tl[0], true), out, cap);
+  if (nt > A.nmodes) return mfl::kLayoutBadIndex;
+  return emit(zipped ? mfl::zipped_divide(A, tl, has, nt, true)
+                     : mfl::logical_divide_modes(A, tl, has, nt, true),
+              out, cap);
+}
+
 template <class Cfg>
 int lds_offsets(int operand, int32_t* out, int64_t cap, int32_t* outer, int32_t* inner) {
   if (operand < 0 || operand > 2) return mfl::kLayoutBadIndex;
@@ -455,12 +527,101 @@ int mfl_layout_compose(const char* a, const char* b, char* out, int64_t cap) {
   if (rc) return rc;
   rc = parse_layout(b, B);
   if (rc) return rc;
-  const mfl::Layout AB = mfl::compose(A, B);
-  if (AB.status != mfl::kLayoutOk) return AB.status;
-  // reject inputs whose leaves interact (the result would not be A o B)
-  if (mfl::size(B) > ((int64_t)1 << 22) || !mfl::compose_is_exact(A, B, AB))
-    return mfl::kLayoutNotComposable;
-  return emit(AB, out, cap);
+  // inputs whose leaves interact (the result would not be A o B) are rejected
+  return emit(mfl::compose_v(A, B, true), out, cap);
+}
+
+int mfl_layout_complement(const char* layout, int64_t cotarget, char* out, int64_t cap) {
+  mfl::Layout L;
+  const int rc = parse_layout(layout, L);
+  if (rc) return rc;
+  if (cotarget < 1 || cotarget > ((int64_t)1 << 40)) return mfl::kLayoutBadIndex;
+  return emit(mfl::complement(L, cotarget), out, cap);
+}
+
+int mfl_layout_logical_divide(const char* a, const char* tiler, char* out, int64_t cap) {
+  return divide_text(a, tiler, false, out, cap);
+}
+
+int mfl_layout_zipped_divide(const char* a, const char* tiler, char* out, int64_t cap) {
+  return divide_text(a, tiler, true, out, cap);
+}
+
+int mfl_layout_logical_product(const char* a, const char* b, char* out, int64_t cap) {
+  mfl::Layout A, B;
+  int rc = parse_layout(a, A);
+  if (rc) return rc;
+  rc = parse_layout(b, B);
+  if (rc) return rc;
+  return emit(mfl::logical_product(A, B, true), out, cap);
+}
+
+int mfl_layout_tiled_product(const char* a, const char* b, char* out, int64_t cap) {
+  mfl::Layout A, B;
+  int rc = parse_layout(a, A);
+  if (rc) return rc;
+  rc = parse_layout(b, B);
+  if (rc) return rc;
+  return emit(mfl::tiled_product(A, B, true), out, cap);
+}
+
+int mfl_layout_upcast(const char* layout, int64_t n, char* out, int64_t cap) {
+  mfl::Layout L;
+  const int rc = parse_layout(layout, L);
+  if (rc) return rc;
+  if (n < 1) return mfl::kLayoutBadIndex;
+  return emit(mfl::upcast(L, n), out, cap);
+}
+
+int mfl_layout_with_shape(const char* layout, const char* shape, char* out, int64_t cap) {
+  mfl::Layout L, S;
+  int rc = parse_layout(layout, L);
+  if (rc) return rc;
+  rc = parse_shape(shape, S);
+  if (rc) return rc;
+  if (mfl::size(S) != mfl::size(L)) return mfl::kLayoutBadIndex;
+  return emit(mfl::with_shape(L, S, true), out, cap);
+}
+
+int mfl_layout_partition_c(const char* c, const char* tile, const char* atom_tv, int64_t atom_m,
+                           int64_t atom_n, int64_t warps_m, int64_t warps_n, char* thr_out,
+                           char* val_out, int64_t cap) {
+  mfl::Layout C, TV;
+  int rc = parse_layout(c, C);
+  if (rc) return rc;
+  rc = parse_layout(atom_tv, TV);
+  if (rc) return rc;
+  if (C.nmodes != 2 || atom_m < 1 || atom_n < 1 || warps_m < 1 || warps_n < 1)
+    return mfl::kLayoutBadIndex;
+  mfl::Layout tl[mfl::kMaxModes];
+  const mfl::Layout* tp = nullptr;
+  if (tile && *tile) {
+    bool has[mfl::kMaxModes] = {}, whole = false;
+    int nt = 0;
+    rc = parse_tiler(tile, tl, has, nt, whole);
+    if (rc) return rc;
+    if (whole || nt != 2) return mfl::kLayoutBadText;
+    for (int m = 0; m < 2; ++m)
+      if (!has[m]) tl[m] = mfl::unit_leaf(m == 0 ? atom_m * warps_m : atom_n * warps_n);
+    tp = tl;
+  }
+  const mfl::CPartition p = mfl::partition_c(C, tp, TV, atom_m, atom_n, warps_m, warps_n, true);
+  rc = emit(p.thr, thr_out, cap);
+  if (rc) return rc;
+  return emit(p.val, val_out, cap);
+}
+
+int mfl_layout_retile(const char* frag, const char* tv, const char* tile_shape, int64_t nthr,
+                      int64_t atom_nval, char* out, int64_t cap) {
+  mfl::Layout F, TV, S;
+  int rc = parse_layout(frag, F);
+  if (rc) return rc;
+  rc = parse_layout(tv, TV);
+  if (rc) return rc;
+  rc = parse_shape(tile_shape, S);
+  if (rc) return rc;
+  if (nthr < 1 || atom_nval < 1) return mfl::kLayoutBadIndex;
+  return emit(mfl::retile(F, TV, S, nthr, atom_nval, true), out, cap);
 }
 
 int mfl_layout_right_inverse(const char* layout, char* out, int64_t cap) {

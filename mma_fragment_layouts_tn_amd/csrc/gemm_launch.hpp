@@ -55,6 +55,10 @@ using CfgLds256W4 = TileCfg<256, 256, 64, 2, 2, 2>;
 // workgroup barrier to wait on, and four such workgroups share a CU
 using CfgLds128W1 = TileCfg<128, 128, 32, 1, 1>;
 
+static_assert(frag_c_is_partition_c<CfgLds128>() && frag_c_is_partition_c<CfgLds256>() &&
+                  frag_c_is_partition_c<CfgLds256W4>() && frag_c_is_partition_c<CfgLds128W1>(),
+              "accumulator coordinates must be the tiled MMA's partition_C");
+
 struct KernelInfo {
   int algo, bm, bn, bk, threads;
 };

@@ -211,6 +211,42 @@ MFL_HD constexpr RowK frag_c_coord(int w, int lane, int i, int j, int v) {
               wn * Cfg::WTN + j * Cfg::kAtomN + c.k};
 }
 
+// frag_c_coord is the tiled MMA's partition_C written out in closed form.
+// Derived with the layout algebra (TiledMMA page, "partition_C 怎样把分工应用
+// 到一个 Tensor", with the tile permutations of "用 Layout 改变 M 方向的坐标
+// 顺序"): a BM x BN tile stored M-contiguous, divided per direction by the
+// permutation (32, WAVES, R):(1, 32R, 32) -- wave w takes R adjacent atom
+// blocks instead of every WAVES-th one -- then by the 32x32 atom, composed
+// with the atom's C TV layout and split over the wave grid.  Thread lane +
+// 64 w's view is thr(t) + val(v + 16 (i + RM j)).  Every thread's base and
+// thread 0's values are compared; with the atom layout separable (asserted
+// above) that covers every (thread, value).
+template <class Cfg>
+constexpr bool frag_c_is_partition_c() {
+  Layout C;
+  C.open_mode();
+  C.push_leaf(Cfg::BM, 1);
+  C.open_mode();
+  C.push_leaf(Cfg::BN, Cfg::BM);
+  const int64_t pm_s[3] = {32, Cfg::WAVES_M, Cfg::RM}, pm_d[3] = {1, 32 * Cfg::RM, 32};
+  const int64_t pn_s[3] = {32, Cfg::WAVES_N, Cfg::RN}, pn_d[3] = {1, 32 * Cfg::RN, 32};
+  const Layout tile[2] = {make_flat(3, pm_s, pm_d), make_flat(3, pn_s, pn_d)};
+  const CPartition p =
+      partition_c(C, tile, atom_c_tv(), 32, 32, Cfg::WAVES_M, Cfg::WAVES_N);
+  if (p.thr.status != kLayoutOk || p.val.status != kLayoutOk) return false;
+  for (int t = 0; t < Cfg::kThreads; ++t) {
+    const RowK c = frag_c_coord<Cfg>(t / 64, t % 64, 0, 0, 0);
+    if (eval(p.thr, t) != c.row + int64_t(Cfg::BM) * c.k) return false;
+  }
+  for (int j = 0; j < Cfg::RN; ++j)
+    for (int i = 0; i < Cfg::RM; ++i)
+      for (int v = 0; v < 16; ++v) {
+        const RowK c = frag_c_coord<Cfg>(0, 0, i, j, v);
+        if (eval(p.val, v + 16 * (i + Cfg::RM * j)) != c.row + int64_t(Cfg::BM) * c.k) return false;
+      }
+  return true;
+}
+
 // Workgroup -> output tile.  Workgroups are handed to the 8 XCDs round-robin
 // (XCD = id % 8); regrouping ids so each XCD gets a contiguous run, then
 // walking that run in GROUP_M-tall column bands, keeps the A rows and B

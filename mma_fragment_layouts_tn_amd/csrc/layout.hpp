@@ -20,6 +20,24 @@
 //   right_inverse(L)    R with L(R(j)) = j on the longest prefix 0..n-1 the
 //                       layout covers (retile page, section "先确定要从哪些
 //                       fragment 位置取值")
+//   complement(L, M)    the layout R, strides increasing, that fills the gaps
+//                       between L's strides so (L, R) tiles [0, M)
+//   logical_divide      A o (B, complement(B, |A|)): (tile, rest), whole
+//                       layout or mode by mode (partition_C's first step,
+//                       TiledMMA page "先按第三个参数划分 M、N")
+//   zipped_divide       mode-by-mode divide with all tile parts gathered in
+//                       mode 0 and all rest parts in mode 1 ("再切出单条指令
+//                       的输出块")
+//   logical_product     (A, complement(A, |A| cosize(B)) o B) (retile page,
+//                       "建立 Copy 的分组编号")
+//   upcast(L, N)        L viewed in units of N elements, leaf by leaf
+//   with_shape(L, S)    L o make_layout(S): the same function on a domain
+//                       reshaped to S
+//   tiled_product       logical_product with B's modes kept apart
+//   partition_c         the four steps of a tiled MMA's C partition
+//   retile              retile_D's regrouping of a register fragment
+// Results that would nest three levels deep keep their leaves flattened
+// inside a top-level mode; as functions they are unchanged.
 // All functions are constexpr so kernels can fold them at compile time.
 #pragma once
 
@@ -248,13 +266,30 @@ MFL_HD constexpr Layout compose(const Layout& A, const Layout& B) {
 }
 
 // true when compose(A, B) equals A(B(c)) at every c (brute force; for
-// host-side checks of arbitrary inputs)
-inline bool compose_is_exact(const Layout& A, const Layout& B, const Layout& AB) {
+// checks of arbitrary inputs)
+MFL_HD constexpr bool compose_is_exact(const Layout& A, const Layout& B, const Layout& AB) {
   const int64_t n = size(B);
   if (size(AB) != n) return false;
   for (int64_t i = 0; i < n; ++i)
     if (eval(AB, i) != eval_unbounded(A, eval(B, i))) return false;
   return true;
+}
+
+// largest domain compose_v checks point by point
+constexpr int64_t kVerifyMax = int64_t(1) << 22;
+
+// compose; with `verify`, a result that differs from A(B(c)) anywhere is
+// marked not composable (and a domain too large to check, too large).  The
+// operations below take the same flag: callers with arbitrary input set it,
+// kernels folding known-good layouts at compile time leave it off.
+MFL_HD constexpr Layout compose_v(const Layout& A, const Layout& B, bool verify) {
+  Layout AB = compose(A, B);
+  if (!verify || AB.status != kLayoutOk) return AB;
+  if (size(B) > kVerifyMax)
+    AB.status = kLayoutTooLarge;
+  else if (!compose_is_exact(A, B, AB))
+    AB.status = kLayoutNotComposable;
+  return AB;
 }
 
 // -------------------------------------------------------- right inverse
@@ -289,6 +324,350 @@ MFL_HD constexpr Layout right_inverse(const Layout& L) {
   }
   if (out.nleaves == 0) out.push_leaf(1, 0);
   out.status = c.status;
+  return out;
+}
+
+// ------------------------------------------------------------ complement
+MFL_HD constexpr Layout complement(const Layout& L, int64_t cotarget) {
+  // leaves that move (shape > 1, stride != 0), sorted by stride
+  int64_t sh[kMaxLeaves] = {}, st[kMaxLeaves] = {};
+  int n = 0;
+  Layout out;
+  out.open_mode();
+  for (int i = 0; i < L.nleaves; ++i) {
+    if (L.shape[i] == 1 || L.stride[i] == 0) continue;
+    if (L.stride[i] < 0) {
+      out.status = kLayoutNegativeStride;
+      return out;
+    }
+    int j = n++;
+    while (j > 0 && st[j - 1] > L.stride[i]) {
+      sh[j] = sh[j - 1];
+      st[j] = st[j - 1];
+      --j;
+    }
+    sh[j] = L.shape[i];
+    st[j] = L.stride[i];
+  }
+  int64_t cur = 1;   // extent covered so far
+  for (int i = 0; i < n; ++i) {
+    if (st[i] < cur || st[i] % cur != 0) {   // overlapping or non-divisible leaves
+      out.status = kLayoutNotComposable;
+      return out;
+    }
+    if (st[i] / cur > 1) out.push_leaf(st[i] / cur, cur);
+    cur = sh[i] * st[i];
+  }
+  const int64_t rest = (cotarget + cur - 1) / cur;
+  if (rest > 1) out.push_leaf(rest, cur);
+  Layout c = coalesce(out);
+  if (L.status != kLayoutOk) c.status = L.status;
+  return c;
+}
+
+// one top-level mode of L as a layout of its own
+MFL_HD constexpr Layout mode_of(const Layout& L, int m) {
+  Layout out;
+  out.open_mode();
+  for (int i = L.mode_begin(m); i < L.mode_end[m]; ++i) out.push_leaf(L.shape[i], L.stride[i]);
+  out.status = L.status;
+  return out;
+}
+
+// append all leaves of `src` to the last mode of `dst`
+MFL_HD constexpr void append_leaves(Layout& dst, const Layout& src) {
+  for (int i = 0; i < src.nleaves; ++i) dst.push_leaf(src.shape[i], src.stride[i]);
+  if (src.status != kLayoutOk) dst.status = src.status;
+}
+
+// -------------------------------------------------------------- divides
+// A divided by the single layout B over A's whole domain: mode 0 the tile
+// (B's leaves composed into A), mode 1 the rest (B's complement)
+MFL_HD constexpr Layout logical_divide(const Layout& A, const Layout& B, bool verify = false) {
+  const Layout R = complement(B, size(A));
+  Layout BR;
+  BR.open_mode();
+  append_leaves(BR, B);
+  BR.open_mode();
+  append_leaves(BR, R);
+  const Layout q = compose_v(A, BR, verify);
+  Layout out;
+  for (int m = 0; m < q.nmodes; ++m) {
+    out.open_mode();
+    append_leaves(out, mode_of(q, m));
+  }
+  if (q.status != kLayoutOk) out.status = q.status;
+  return out;
+}
+
+// Mode-by-mode tilers: tilers[m] divides mode m of A (has_tiler[m] false or
+// m >= ntilers: the mode is kept whole as the tile, rest 1).  `tile[m]` and
+// `rest[m]` receive the parts.
+MFL_HD constexpr void divide_modes(const Layout& A, const Layout* tilers, const bool* has_tiler,
+                                   int ntilers, Layout* tile, Layout* rest, bool verify = false) {
+  for (int m = 0; m < A.nmodes; ++m) {
+    const Layout am = mode_of(A, m);
+    if (m < ntilers && has_tiler[m]) {
+      const Layout q = logical_divide(am, tilers[m], verify);
+      tile[m] = mode_of(q, 0);
+      rest[m] = mode_of(q, 1);
+      if (q.status != kLayoutOk) tile[m].status = q.status;
+    } else {
+      tile[m] = am;
+      Layout one;
+      one.open_mode();
+      one.push_leaf(1, 0);
+      rest[m] = one;
+    }
+  }
+}
+
+// mode m of the result is (tile_m, rest_m), flattened into one mode; modes
+// without a tiler are returned unchanged
+MFL_HD constexpr Layout logical_divide_modes(const Layout& A, const Layout* tilers,
+                                             const bool* has_tiler, int ntilers,
+                                             bool verify = false) {
+  Layout tile[kMaxModes], rest[kMaxModes];
+  divide_modes(A, tilers, has_tiler, ntilers, tile, rest, verify);
+  Layout out;
+  for (int m = 0; m < A.nmodes; ++m) {
+    out.open_mode();
+    append_leaves(out, tile[m]);
+    if (m < ntilers && has_tiler[m]) append_leaves(out, rest[m]);
+  }
+  if (A.status != kLayoutOk) out.status = A.status;
+  return out;
+}
+
+// ((tile_0, tile_1, ...), (rest_0, rest_1, ...)), each part flattened
+MFL_HD constexpr Layout zipped_divide(const Layout& A, const Layout* tilers, const bool* has_tiler,
+                                      int ntilers, bool verify = false) {
+  Layout tile[kMaxModes], rest[kMaxModes];
+  divide_modes(A, tilers, has_tiler, ntilers, tile, rest, verify);
+  Layout out;
+  out.open_mode();
+  for (int m = 0; m < A.nmodes; ++m) append_leaves(out, tile[m]);
+  out.open_mode();
+  for (int m = 0; m < A.nmodes; ++m) append_leaves(out, rest[m]);
+  if (A.status != kLayoutOk) out.status = A.status;
+  return out;
+}
+
+// ------------------------------------------------------------- product
+MFL_HD constexpr Layout logical_product(const Layout& A, const Layout& B, bool verify = false) {
+  const Layout C = complement(A, size(A) * cosize(B));
+  const Layout CB = compose_v(C, B, verify);
+  Layout out;
+  out.open_mode();
+  append_leaves(out, A);
+  out.open_mode();
+  append_leaves(out, CB);
+  if (A.status != kLayoutOk) out.status = A.status;
+  return out;
+}
+
+// logical_product with B's top-level modes kept apart: (A, (C o B)_0,
+// (C o B)_1, ...).  With A the atom's thread ids and B the arrangement of
+// atoms over M, N, K this is the tiled MMA's thread layout (TiledMMA page,
+// "第二个参数怎样把一个 warp 扩展成四个")
+MFL_HD constexpr Layout tiled_product(const Layout& A, const Layout& B, bool verify = false) {
+  const Layout C = complement(A, size(A) * cosize(B));
+  const Layout CB = compose_v(C, B, verify);
+  Layout out;
+  out.open_mode();
+  append_leaves(out, A);
+  for (int m = 0; m < CB.nmodes; ++m) {
+    out.open_mode();
+    append_leaves(out, mode_of(CB, m));
+  }
+  if (A.status != kLayoutOk) out.status = A.status;
+  if (C.status != kLayoutOk) out.status = C.status;
+  return out;
+}
+
+// ------------------------------------------------------------- upcast
+// a / b when b divides a, 1 when a divides b, else not representable
+MFL_HD constexpr int64_t shape_div(int64_t a, int64_t b, int& status) {
+  if (b != 0 && a % b == 0) return a / b;
+  if (a != 0 && b % a == 0) return 1;
+  status = kLayoutNotComposable;
+  return 1;
+}
+
+// leaf (s, d) -> (s / (N / d), d / N), 1 where the unit exceeds the extent;
+// stride-0 leaves unchanged
+MFL_HD constexpr Layout upcast(const Layout& L, int64_t n) {
+  Layout out;
+  for (int m = 0; m < L.nmodes; ++m) {
+    out.open_mode();
+    for (int i = L.mode_begin(m); i < L.mode_end[m]; ++i) {
+      const int64_t s = L.shape[i], d = L.stride[i];
+      if (d == 0) {
+        out.push_leaf(s, 0);
+        continue;
+      }
+      int st = kLayoutOk;
+      const int64_t ad = d < 0 ? -d : d;
+      const int64_t ns = shape_div(s, shape_div(n, ad, st), st);
+      const int64_t nd = shape_div(ad, n, st) * (d < 0 ? -1 : 1);
+      out.push_leaf(ns, nd);
+      if (st != kLayoutOk) out.status = st;
+    }
+  }
+  if (L.status != kLayoutOk) out.status = L.status;
+  return out;
+}
+
+// --------------------------------------------------------- with_shape
+// make_layout(shape) for a shape given as modes of leaves: column-major
+MFL_HD constexpr Layout compact(const Layout& shape_only) {
+  Layout out;
+  int64_t d = 1;
+  for (int m = 0; m < shape_only.nmodes; ++m) {
+    out.open_mode();
+    for (int i = shape_only.mode_begin(m); i < shape_only.mode_end[m]; ++i) {
+      out.push_leaf(shape_only.shape[i], d);
+      d *= shape_only.shape[i];
+    }
+  }
+  out.status = shape_only.status;
+  return out;
+}
+
+MFL_HD constexpr Layout with_shape(const Layout& L, const Layout& shape_only, bool verify = false) {
+  return compose_v(L, compact(shape_only), verify);
+}
+
+MFL_HD constexpr Layout unit_leaf(int64_t n) {
+  Layout out;
+  out.open_mode();
+  out.push_leaf(n, n == 1 ? 0 : 1);
+  return out;
+}
+
+// all leaves of the listed layouts, in order, as one top-level mode
+MFL_HD constexpr Layout flat_join(const Layout* parts, int n) {
+  Layout out;
+  out.open_mode();
+  for (int i = 0; i < n; ++i) append_leaves(out, parts[i]);
+  return out;
+}
+
+// ------------------------------------------------------------ partition_C
+// The C partition of a tiled MMA (TiledMMA page, "partition_C 怎样把分工应
+// 用到一个 Tensor"): the output tensor C (mode 0 = M, mode 1 = N) is
+//   1. divided mode by mode by the tile (tile_m, tile_n): the tiled MMA's
+//      permutations, or compact (atom_m * warps_m):1 where none is given;
+//   2. divided again by the atom (atom_m:1, atom_n:1), tile parts together;
+//   3. the atom block (index m + atom_m * n) composed with the atom's C TV
+//      layout: (lane, value) -> offset;
+//   4. the remaining blocks divided by the warps (warps_m:1, warps_n:1).
+// Result `thr`: one mode, thread lane + nlanes * (wm + warps_m * wn) -> offset
+// of the thread's first value; `val`: (value, rest M, rest N) -> offset from
+// it.  The view of thread t is offset thr(t) with layout val.
+struct CPartition {
+  Layout thr;
+  Layout val;
+};
+
+MFL_HD constexpr CPartition partition_c(const Layout& C, const Layout* tile, const Layout& atom_tv,
+                                        int64_t atom_m, int64_t atom_n, int64_t warps_m,
+                                        int64_t warps_n, bool verify = false) {
+  CPartition r;
+  Layout t2[2] = {unit_leaf(atom_m * warps_m), unit_leaf(atom_n * warps_n)};
+  if (tile) {
+    t2[0] = tile[0];
+    t2[1] = tile[1];
+  }
+  const bool all[2] = {true, true};
+  const Layout t_tensor = logical_divide_modes(C, t2, all, 2, verify);
+  const Layout a2[2] = {unit_leaf(atom_m), unit_leaf(atom_n)};
+  Layout atile[2], arest[2];
+  divide_modes(t_tensor, a2, all, 2, atile, arest, verify);
+  const Layout block = flat_join(atile, 2);
+  const Layout tv = compose_v(block, atom_tv, verify);
+  const Layout w2[2] = {unit_leaf(warps_m), unit_leaf(warps_n)};
+  Layout q0 = logical_divide(arest[0], w2[0], verify), q1 = logical_divide(arest[1], w2[1], verify);
+  const Layout thr_parts[3] = {mode_of(tv, 0), mode_of(q0, 0), mode_of(q1, 0)};
+  r.thr = flat_join(thr_parts, 3);
+  r.val.open_mode();
+  append_leaves(r.val, mode_of(tv, 1));
+  r.val.open_mode();
+  append_leaves(r.val, mode_of(q0, 1));
+  r.val.open_mode();
+  append_leaves(r.val, mode_of(q1, 1));
+  int st = kLayoutOk;
+  const Layout* chk[] = {&C, &t_tensor, &atile[0], &atile[1], &arest[0], &arest[1], &tv, &q0, &q1};
+  for (const Layout* l : chk)
+    if (l->status != kLayoutOk) st = l->status;
+  // the tile must divide C, the atom the tile and the warps the atom blocks
+  if (C.nmodes != 2 || size_mode(C, 0) % size(t2[0]) != 0 ||
+      size_mode(C, 1) % size(t2[1]) != 0 || size(t2[0]) % atom_m != 0 ||
+      size(t2[1]) % atom_n != 0 || size(arest[0]) % warps_m != 0 ||
+      size(arest[1]) % warps_n != 0 || size(atom_tv) != atom_m * atom_n)
+    st = kLayoutBadIndex;
+  r.thr.status = r.val.status = st;
+  return r;
+}
+
+// ----------------------------------------------------------------- retile
+// retile_D (retile page, "带着 8 和 2，读一遍 retile 的源码" and "两个 K
+// fragment 怎样连成一组"): the register fragment `frag` of one thread (mode 0
+// the V values of one MMA, then one mode per repeat direction) regrouped for a
+// copy atom that writes `atom_nval` values per thread, given the copy's tiled
+// TV layout `tv` (thread + nthr * value -> position in the reference tile,
+// first coordinate fastest) and the tile's shape:
+//   frg_layout_mn = upcast<nthr*V>(right_inverse(tv).with_shape(tile_shape))
+//   frg_layout_v  = divide(logical_product(V:1, right_inverse(frg_layout_mn)),
+//                          atom_nval:1)
+//   t_tensor      = zipped_divide(frag, (V, product_each(frg_layout_mn)...))
+//   result        = (t_tensor's tile o frg_layout_v, rest modes 1..)
+// The value mode's own rest has size 1 and is dropped.  Mode 0 of the result
+// is (copy values, copy groups) flattened: a copy group takes values
+// across fragments wherever frg_layout_mn keeps more than one position.
+MFL_HD constexpr Layout retile(const Layout& frag, const Layout& tv, const Layout& tile_shape,
+                               int64_t nthr, int64_t atom_nval, bool verify = false) {
+  Layout out;
+  const int64_t V = size_mode(frag, 0);
+  const Layout ri = right_inverse(tv);
+  if (size(ri) != size(tile_shape)) {   // tv must cover the tile exactly
+    out.status = kLayoutBadIndex;
+    return out;
+  }
+  const Layout inv = with_shape(ri, tile_shape, verify);
+  const Layout mn = upcast(inv, nthr * V);
+  const Layout G = right_inverse(mn);
+  const Layout prod = logical_product(unit_leaf(V), G, verify);
+  const Layout fv = logical_divide(prod, unit_leaf(atom_nval), verify);
+  if (frag.nmodes != mn.nmodes + 1 || frag.nmodes > kMaxModes) {
+    out.status = kLayoutBadIndex;
+    return out;
+  }
+  Layout tilers[kMaxModes];
+  bool all[kMaxModes] = {};
+  tilers[0] = unit_leaf(V);
+  all[0] = true;
+  for (int m = 1; m < frag.nmodes; ++m) {
+    tilers[m] = unit_leaf(size_mode(mn, m - 1));
+    all[m] = true;
+  }
+  Layout tile[kMaxModes], rest[kMaxModes];
+  divide_modes(frag, tilers, all, frag.nmodes, tile, rest, verify);
+  const Layout t0 = flat_join(tile, frag.nmodes);
+  const Layout vt = compose_v(t0, fv, verify);
+  out.open_mode();
+  append_leaves(out, vt);
+  for (int m = 1; m < frag.nmodes; ++m) {
+    out.open_mode();
+    append_leaves(out, rest[m]);
+  }
+  const Layout* chk[] = {&tv, &inv, &mn, &G, &prod, &fv, &t0, &vt};
+  for (const Layout* l : chk)
+    if (l->status != kLayoutOk) out.status = l->status;
+  for (int m = 0; m < frag.nmodes; ++m)
+    if (tile[m].status != kLayoutOk) out.status = tile[m].status;
+  if (size(rest[0]) != 1 || size(prod) % atom_nval != 0)
+    out.status = kLayoutBadIndex;
   return out;
 }
 
