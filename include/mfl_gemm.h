@@ -52,14 +52,21 @@ typedef enum { MFL_A_KMAJOR = 0, MFL_A_MMAJOR = 1 } mfl_a_order;
 
 /* Kernel choice (low 8 bits of gemm_dtypes_t.algo).  AUTO picks per shape:
  * LDS_256 (LDS_256_W4 when both operands go straight into LDS and C is
- * absent) once the grid has at least 192 tiles of 256x256, else LDS_128.
+ * absent) once the grid has at least 192 tiles of 256x256; else LDS_SPLITK
+ * when the grid has fewer than 256 tiles of 128x128 and K >= 1024; else
+ * LDS_128.
  * DIRECT reads fragments straight from global memory into registers (no
  * LDS; the simple-GEMM page's "不用 Shared Memory" kernel).  LDS_128 stages
  * 128x128x32 block tiles through LDS (the block tile of "CuTe Layout 到
  * Tensor Core" §4) with 4 waves of 64x64.  LDS_256 stages 256x256x64 block
  * tiles with 8 waves of 128x64; LDS_256_W4 the same tile with 4 waves of
  * 128x128.  LDS_128_W1 stages 128x128x32 tiles owned by one wave each (a
- * workgroup of 64 threads, four per CU).  The LDS kernels fetch each K-contiguous operand straight into
+ * workgroup of 64 threads, four per CU).  LDS_SPLITK stages 128x64x128
+ * tiles with 4 waves that each compute the whole 128x64 tile over their own
+ * quarter of every stage's K (the K-direction thread groups of the TiledMMA
+ * page, section "K 方向的线程组，与 K 方向的循环"); the four partial tiles are
+ * reduced through LDS, every wave finishing a quarter of the tile and adding
+ * C once.  The LDS kernels fetch each K-contiguous operand straight into
  * LDS (global_load_lds_dwordx4) when its base and leading dimension are
  * 16-byte aligned, else through registers with 16-byte loads at any 2-byte
  * alignment.  An M-contiguous A goes straight into an M-contiguous LDS tile
@@ -74,7 +81,8 @@ typedef enum {
   MFL_ALGO_LDS_256 = 3,
   MFL_ALGO_LDS_256_W4 = 4,
   MFL_ALGO_LDS_128_W1 = 5,
-  MFL_ALGO_COUNT = 6,
+  MFL_ALGO_LDS_SPLITK = 6,
+  MFL_ALGO_COUNT = 7,
   MFL_ALGO_MASK = 0xff,
   MFL_ALGO_REG_FETCH = 0x100
 } mfl_algo;

@@ -126,7 +126,9 @@ int mfl_layout_mfma_tv(int32_t op, int32_t operand, char* out, int64_t cap);
 
 /* Per-lane fragment addressing of a GEMM kernel, computed by the same code
  * the kernel runs: for every thread t of one workgroup and every fragment
- * slot s of one K-step, the (row, k) (operand 0 A, 1 B) or (m, n)
+ * slot s of the K sub-steps it takes from one stage (all of them, or its
+ * K-group's share when the tile splits K), the (row, k) (operand 0 A, 1 B)
+ * or (m, n)
  * (operand 2, accumulators) within the workgroup tile, written as pairs into
  * out[2*(t*slots + s) + {0,1}].  Operand 3: for an M-contiguous A, the
  * (m, k) each lane addresses with the first of the two transposing LDS reads

@@ -37,10 +37,15 @@ bool span_fits(int64_t rows, int64_t ld, int64_t cols) {
 // start must be 16-byte aligned
 bool dma_ok(const void* X, int64_t ld) { return ((uintptr_t)X % 16 == 0) && (ld % 8 == 0); }
 
+// Large outputs take the 256x256 tile.  Below that the 128x128 tile, unless
+// its grid leaves CUs idle (fewer tiles than the 256 CUs) while K is long:
+// then the split-K tile (128x64, four K-groups per workgroup) runs twice as
+// many workgroups, each with four waves.
 int pick_algo(int64_t M, int64_t N, int64_t K) {
-  (void)K;
   const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
-  return t256 >= 192 ? mfl::kAlgoLds256 : mfl::kAlgoLds128;
+  if (t256 >= 192) return mfl::kAlgoLds256;
+  const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
+  return t128 < 256 && K >= 1024 ? mfl::kAlgoLdsSplitK : mfl::kAlgoLds128;
 }
 
 struct Plan {
@@ -339,11 +344,13 @@ int lds_offsets(int operand, int32_t* out, int64_t cap, int32_t* outer, int32_t*
 
 template <class Cfg>
 int frag_coords(int operand, int32_t* out, int64_t cap, int32_t* threads, int32_t* slots) {
+  // per thread: its own K sub-steps of one stage (KSUB_W; all of them unless
+  // the tile splits K between groups of waves)
   int ns = 0;
-  if (operand == 0) ns = Cfg::KSUB * Cfg::RM * 8;
-  else if (operand == 1) ns = Cfg::KSUB * Cfg::RN * 8;
+  if (operand == 0) ns = Cfg::KSUB_W * Cfg::RM * 8;
+  else if (operand == 1) ns = Cfg::KSUB_W * Cfg::RN * 8;
   else if (operand == 2) ns = Cfg::RM * Cfg::RN * 16;
-  else if (operand == 3) ns = Cfg::KSUB * Cfg::RM;
+  else if (operand == 3) ns = Cfg::KSUB_W * Cfg::RM;
   else return mfl::kLayoutBadIndex;
   if (threads) *threads = Cfg::kThreads;
   if (slots) *slots = ns;
@@ -358,7 +365,7 @@ int frag_coords(int operand, int32_t* out, int64_t cap, int32_t* threads, int32_
       ++s;
     };
     if (operand == 3) {
-      for (int kk = 0; kk < Cfg::KSUB; ++kk)
+      for (int kk = 0; kk < Cfg::KSUB_W; ++kk)
         for (int i = 0; i < Cfg::RM; ++i) {
           const mfl::RowK c = mfl::frag_a_tr_coord<Cfg>(w, lane, i, kk);
           put(c.row, c.k);
@@ -372,7 +379,7 @@ int frag_coords(int operand, int32_t* out, int64_t cap, int32_t* threads, int32_
           }
     } else {
       const int R = operand == 0 ? Cfg::RM : Cfg::RN;
-      for (int kk = 0; kk < Cfg::KSUB; ++kk)
+      for (int kk = 0; kk < Cfg::KSUB_W; ++kk)
         for (int i = 0; i < R; ++i)
           for (int v = 0; v < 8; ++v) {
             const mfl::RowK c = operand == 0 ? mfl::frag_a_coord<Cfg>(w, lane, i, kk)
@@ -646,6 +653,8 @@ int mfl_lds_tile_offsets(int32_t algo, int32_t operand, int32_t* out, int64_t ca
       return lds_offsets<mfl::CfgLds256W4>(operand, out, cap, outer, inner);
     case mfl::kAlgoLds128W1:
       return lds_offsets<mfl::CfgLds128W1>(operand, out, cap, outer, inner);
+    case mfl::kAlgoLdsSplitK:
+      return lds_offsets<mfl::CfgLdsSplitK>(operand, out, cap, outer, inner);
     default: return mfl::kLayoutBadIndex;
   }
 }
@@ -669,6 +678,7 @@ int mfl_fragment_coords(int32_t algo, int32_t operand, int32_t* out, int64_t cap
     case mfl::kAlgoLds256: return frag_coords<mfl::CfgLds256>(operand, out, cap, threads, slots);
     case mfl::kAlgoLds256W4: return frag_coords<mfl::CfgLds256W4>(operand, out, cap, threads, slots);
     case mfl::kAlgoLds128W1: return frag_coords<mfl::CfgLds128W1>(operand, out, cap, threads, slots);
+    case mfl::kAlgoLdsSplitK: return frag_coords<mfl::CfgLdsSplitK>(operand, out, cap, threads, slots);
     default: return mfl::kLayoutBadIndex;
   }
 }

@@ -9,6 +9,7 @@ const void* tiled_symbol_128(int fa, int fb, int ck, int dk);
 const void* tiled_symbol_256(int fa, int fb, int ck, int dk);
 const void* tiled_symbol_256w4(int fa, int fb, int ck, int dk);
 const void* tiled_symbol_128w1(int fa, int fb, int ck, int dk);
+const void* tiled_symbol_splitk(int fa, int fb, int ck, int dk);
 const void* direct_symbol(int ck, int dk);
 
 namespace {
@@ -25,6 +26,7 @@ KernelInfo kernel_info(int algo) {
     case kAlgoLds256: return info_of<CfgLds256>(algo);
     case kAlgoLds256W4: return info_of<CfgLds256W4>(algo);
     case kAlgoLds128W1: return info_of<CfgLds128W1>(algo);
+    case kAlgoLdsSplitK: return info_of<CfgLdsSplitK>(algo);
     default: return KernelInfo{-1, 0, 0, 0, 0};
   }
 }
@@ -37,6 +39,7 @@ const void* kernel_symbol(int algo, int fetch_a, int fetch_b, int c_kind, int d_
     case kAlgoLds256: return tiled_symbol_256(fetch_a, fetch_b, c_kind, d_kind);
     case kAlgoLds256W4: return tiled_symbol_256w4(fetch_a, fetch_b, c_kind, d_kind);
     case kAlgoLds128W1: return tiled_symbol_128w1(fetch_a, fetch_b, c_kind, d_kind);
+    case kAlgoLdsSplitK: return tiled_symbol_splitk(fetch_a, fetch_b, c_kind, d_kind);
     default: return nullptr;
   }
 }

@@ -91,16 +91,21 @@ __device__ __forceinline__ void d_store(const GemmParams& p, int m, int n, float
 
 // Register epilogue: acc[i][j] value v -> (m, n) from the accumulator TV
 // layout, one element per store (for a fixed value the 64 lanes cover two
-// 128-byte row runs).  Interior tiles without C store through a buffer
+// 128-byte row runs), for the blocks (i, j) that own(i, j) accepts.  Interior tiles without C store through a buffer
 // descriptor based at the wave's tile origin: the lane part of the layout is
 // one per-lane offset, the row part of (repeat, value) a uniform scalar
 // offset and the column part the instruction's immediate, so each element is
 // one store instruction with no address arithmetic on the vector side.  Edge
 // tiles (and C reads, which only the direct kernel does here) check and
 // address each element.
-template <class Cfg, int CK, int DK>
+struct AllBlocks {
+  __device__ bool operator()(int, int) const { return true; }
+};
+
+template <class Cfg, int CK, int DK, class Own = AllBlocks>
 __device__ __forceinline__ void epilogue(const GemmParams& p, int w, int lane, int m0,
-                                         int n0, const floatx16 (&acc)[Cfg::RM][Cfg::RN]) {
+                                         int n0, const floatx16 (&acc)[Cfg::RM][Cfg::RN],
+                                         Own own = Own()) {
   constexpr int ES = DK == 1 ? 2 : 4;
   if (CK == 0 && m0 + Cfg::BM <= p.M && n0 + Cfg::BN <= p.N &&
       (int64_t)Cfg::BM * p.ldd * ES < ((int64_t)1 << 31)) {
@@ -114,7 +119,8 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, int w, int lane, i
 #pragma unroll
     for (int i = 0; i < Cfg::RM; ++i)
 #pragma unroll
-      for (int j = 0; j < Cfg::RN; ++j)
+      for (int j = 0; j < Cfg::RN; ++j) {
+        if (!own(i, j)) continue;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const RowK cv = atom_c_coord(0, v);
@@ -131,18 +137,79 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, int w, int lane, i
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), rsrc, voff + dn, soff,
                                                   kNtStore);
         }
+      }
     return;
   }
 #pragma unroll
   for (int i = 0; i < Cfg::RM; ++i)
 #pragma unroll
-    for (int j = 0; j < Cfg::RN; ++j)
+    for (int j = 0; j < Cfg::RN; ++j) {
+      if (!own(i, j)) continue;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const RowK c = frag_c_coord<Cfg>(w, lane, i, j, v);
         const int m = m0 + c.row, n = n0 + c.k;
         if (m < p.M && n < p.N) d_store<DK>(p, m, n, acc[i][j][v] + c_value<CK>(p, m, n));
       }
+    }
+}
+
+// Split-K reduction (the K-direction thread groups of the TiledMMA page,
+// section "K 方向的线程组，与 K 方向的循环": several groups hold partial sums
+// for the same outputs and one of them must add the others, C once).  Atom
+// block b = i*RN + j of a wave is finished by the member of its K-group set
+// with wave_k == b % WAVES_K; each other member writes its partial block into
+// the freed operand stages and the owner adds them, so every member finishes
+// RM*RN/WAVES_K blocks (a reduce-scatter inside the workgroup).  A block is
+// 16 values x 64 lanes, laid out [v/4][lane][v%4]: each lane moves 16-byte
+// pieces and the 64 lanes of one access cover 1 KB contiguously.
+template <class Cfg>
+struct OwnedBlocks {
+  int wk;
+  __device__ bool operator()(int i, int j) const {
+    return (i * Cfg::RN + j) % Cfg::WAVES_K == wk;
+  }
+};
+
+template <class Cfg>
+__device__ __forceinline__ void reduce_k_groups(float* red, int w, int lane,
+                                                floatx16 (&acc)[Cfg::RM][Cfg::RN]) {
+  constexpr int RN = Cfg::RN, WK = Cfg::WAVES_K, NB = Cfg::RM * RN;
+  const int wg = w % Cfg::kGroupWaves, wk = wave_k<Cfg>(w);
+  auto block = [&](int b, int writer) {
+    const int owner = b % WK;
+    const int slot = (writer - owner - 1 + WK) % WK;    // 0 .. WK-2
+    return red + ((wg * NB + b) * (WK - 1) + slot) * (16 * 64) + lane * 4;
+  };
+  __syncthreads();   // every wave is done with the operand stages
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    if (b % WK == wk) continue;
+    float* dst = block(b, wk);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const floatx16& a = acc[b / RN][b % RN];
+      const float4 x = make_float4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
+      *(float4*)(dst + q * 256) = x;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    if (b % WK != wk) continue;
+#pragma unroll
+    for (int m = 1; m < WK; ++m) {
+      const float* src = block(b, (wk + m) % WK);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 x = *(const float4*)(src + q * 256);
+        acc[b / RN][b % RN][4 * q] += x.x;
+        acc[b / RN][b % RN][4 * q + 1] += x.y;
+        acc[b / RN][b % RN][4 * q + 2] += x.z;
+        acc[b / RN][b % RN][4 * q + 3] += x.w;
+      }
+    }
+  }
 }
 
 // LDS-staged epilogue of the LDS kernels when C is read.  Accumulators leave
@@ -200,7 +267,7 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, float* sm, int
   constexpr int ROWS = IG * 32, V4 = WTN / 4, NV = ROWS * V4 / 64, QB = 8;
   static_assert((ROWS * V4) % 64 == 0 && NV % QB == 0, "runs must divide over the lanes");
   float* reg = sm + w * ROWS * WTN;
-  const int wm = w % Cfg::WAVES_M, wn = w / Cfg::WAVES_M;
+  const int wm = wave_m<Cfg>(w), wn = wave_n<Cfg>(w);
   const int mw = m0 + wm * Cfg::WTM, nw = n0 + wn * WTN;
   const bool interior = m0 + Cfg::BM <= p.M && n0 + Cfg::BN <= p.N;
   __syncthreads();   // every wave is done with the operand stages
@@ -464,21 +531,34 @@ struct BoolC {
   static constexpr bool value = B;
 };
 
+// Wait until at most VM vector-memory operations of this wave are in flight
+// and all its LDS operations are done (s_waitcnt vmcnt(VM) lgkmcnt(0); the
+// export counter is not waited on).  Vector-memory loads complete in issue
+// order, so this leaves exactly the VM most recent ones outstanding.
+template <int VM>
+__device__ __forceinline__ void wait_vm_lds() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt has 6 bits");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | (((VM >> 4) & 3) << 14) | (7 << 4));
+}
+
 // ---------------------------------------------------------------------------
 // LDS-staged pipelined kernel
 // ---------------------------------------------------------------------------
 template <class Cfg, int FA, int FB, int CK, int DK>
 __global__ void __launch_bounds__(Cfg::kThreads, 1) gemm_tiled(const GemmParams p) {
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK;
-  constexpr int RM = Cfg::RM, RN = Cfg::RN, KSUB = Cfg::KSUB;
+  // KSUB: this wave's K sub-steps of each stage (all of them unless the
+  // workgroup splits K between groups of waves)
+  constexpr int RM = Cfg::RM, RN = Cfg::RN, KSUB = Cfg::KSUB_W;
   static_assert(KSUB % 2 == 0, "fragment buffers alternate per K sub-step");
   constexpr int kDist = Cfg::kFragDist;
   constexpr int NBUF = kDist == 1 ? 2 : KSUB;     // fragment register buffers
   static_assert(FB != kFetchRegT && FB != kFetchDmaT, "B is always K-contiguous");
   constexpr bool kAT = FA == kFetchDmaT;   // A tile M-contiguous in LDS
   // stage s: A at smem + s*kStage, B at smem + s*kStage + BM*BK (halves)
+  constexpr int NST = Cfg::kStages;
   constexpr int kStage = (BM + BN) * BK;
-  __shared__ __attribute__((aligned(1024))) _Float16 smem[2 * kStage];
+  __shared__ __attribute__((aligned(1024))) _Float16 smem[NST * kStage];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -622,47 +702,72 @@ __global__ void __launch_bounds__(Cfg::kThreads, 1) gemm_tiled(const GemmParams 
 
   const int nfull = p.K / BK;
   if (nfull > 0) {
+    // tiles 0 .. NST-1 into stages 0 .. NST-1.  Register-staged tiles other
+    // than tile NST-1 are written to LDS at once; tile NST-1 waits in
+    // registers and is written in step 0 (the steps write tile kt+NST-1).
     issue(0, 0);
     if constexpr (kAnyReg) stash(0);
-    if (nfull > 1) issue(1, 1);       // REG operands: held in registers until step 0
-    __builtin_amdgcn_s_waitcnt(0);
+    if (nfull > 1) {
+      issue(1, 1);
+      if constexpr (NST == 3 && kAnyReg) stash(1);
+    }
+    if constexpr (NST == 3) {
+      if (nfull > 2) {
+        issue(2, 2);
+        wait_vm_lds<2 * kVmem>();   // tile 0 has landed; tiles 1 and 2 may be in flight
+      } else {
+        wait_vm_lds<0>();
+      }
+    } else {
+      wait_vm_lds<0>();
+    }
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     frags(bufof(0), 0, 0);
     if constexpr (kDist == 2) frags(bufof(1), 1, 0);
   }
-  // One K-step on tile kt (stage kt&1).  FETCH: tile kt+2 exists and is
-  // fetched; NEXT: tile kt+1 exists.  The last two steps are peeled off the
-  // loop so its body is one straight block.
+  // One K-step on tile kt (stage kt % NST).  FETCH: tile kt+NST exists and is
+  // fetched into this step's stage once every wave is done with it; NEXT:
+  // tile kt+1 exists; LAST: tile kt+NST-1 exists (it was fetched NST-1 steps
+  // ago; with registers as staging it is written to its stage in this step).
+  // The last NST steps are peeled off the loop so its body is one straight
+  // block.
   //
   // Fragment distance 1: sub-steps 0..KSUB-2 read sub-step kk+1 of stage cur;
-  // the barrier; sub-step KSUB-1 fetches tile kt+2 and reads sub-step 0 of
+  // the barrier; sub-step KSUB-1 fetches tile kt+NST and reads sub-step 0 of
   // the next stage.  Distance 2: sub-steps 0..KSUB-3 read sub-step kk+2; the
   // barrier; sub-steps KSUB-2 and KSUB-1 share the fetch and read sub-steps 0
-  // and 1 of the next stage.  Either way register-staged tile kt+1 goes to
-  // the idle stage in the last group before the barrier, and the groups after
-  // the barrier run on fragments already in registers.
-  auto step = [&](const int kt, auto fetch, auto next) {
-    constexpr bool kNext = decltype(next)::value;
-    const int cur = kt & 1;
+  // and 1 of the next stage.  Either way register-staged tile kt+NST-1 goes to
+  // its stage in the last group before the barrier, and the groups after the
+  // barrier run on fragments already in registers.  Before the barrier each
+  // wave waits for its fetch of tile kt+1; with three stages the fetch of
+  // tile kt+2 (the most recent kVmem loads) stays in flight.
+  auto step = [&](const int kt, auto fetch, auto next, auto last) {
+    constexpr bool kLast = decltype(last)::value;
+    const int cur = NST == 2 ? (kt & 1) : kt % NST;
+    const int nxt = cur + 1 == NST ? 0 : cur + 1;
+    const int prv = cur == 0 ? NST - 1 : cur - 1;   // stage of tile kt+NST-1
     constexpr int kPre = KSUB - kDist;   // groups before the barrier
 #pragma unroll
     for (int kk = 0; kk + 1 < kPre; ++kk)
       group(bufof(kk), Yes(), bufof(kk + kDist), kk + kDist, cur, No(), 0, 0, No(), 0, 0, 0);
     group(bufof(kPre - 1), Yes(), bufof(KSUB - 1), KSUB - 1, cur, No(), 0, 0,
-          BoolC<kAnyReg && kNext>(), cur ^ 1, 0, 0);
-    __builtin_amdgcn_s_waitcnt(0);        // own reads, stores and fetch of tile kt+1 done
-    __builtin_amdgcn_s_barrier();         // ... in every wave: stage cur is free
+          BoolC<kAnyReg && kLast>(), prv, 0, 0);
+    wait_vm_lds<(NST == 3 && kLast) ? kVmem : 0>();   // own reads, stores, fetch of tile kt+1
+    __builtin_amdgcn_s_barrier();                     // ... in every wave: stage cur is free
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int d = 0; d < kDist; ++d)
-      group(bufof(kPre + d), next, bufof(d), d, cur ^ 1, fetch, kt + 2, cur, No(), 0,
+      group(bufof(kPre + d), next, bufof(d), d, nxt, fetch, kt + NST, cur, No(), 0,
             d * kVmem / kDist, (d + 1) * kVmem / kDist);
   };
   int kt = 0;
-  for (; kt + 2 < nfull; ++kt) step(kt, Yes(), Yes());
-  if (kt + 1 < nfull) step(kt++, No(), Yes());
-  if (kt < nfull) step(kt, No(), No());
+  for (; kt + NST < nfull; ++kt) step(kt, Yes(), Yes(), Yes());
+  if constexpr (NST == 3) {
+    if (kt + 2 < nfull) step(kt++, No(), Yes(), Yes());
+  }
+  if (kt + 1 < nfull) step(kt++, No(), Yes(), BoolC<NST == 2>());
+  if (kt < nfull) step(kt, No(), No(), No());
 
   // K remainder: one step staged element by element with zero fill
   if (p.K % BK != 0) {
@@ -695,10 +800,14 @@ __global__ void __launch_bounds__(Cfg::kThreads, 1) gemm_tiled(const GemmParams 
       mma(0);
     }
   }
-  if constexpr (CK != 0)
+  if constexpr (Cfg::WAVES_K > 1) {
+    reduce_k_groups<Cfg>((float*)smem, w, lane, acc);
+    epilogue<Cfg, CK, DK>(p, w, lane, m0, n0, acc, OwnedBlocks<Cfg>{wave_k<Cfg>(w)});
+  } else if constexpr (CK != 0) {
     epilogue_lds<Cfg, CK, DK>(p, (float*)smem, w, lane, m0, n0, acc);
-  else
+  } else {
     epilogue<Cfg, CK, DK>(p, w, lane, m0, n0, acc);
+  }
 }
 
 // ---------------------------------------------------------------------------

@@ -30,7 +30,8 @@ enum Algo : int {
   kAlgoLds256 = 3,      // 8 waves of 128x64
   kAlgoLds256W4 = 4,    // 4 waves of 128x128
   kAlgoLds128W1 = 5,    // 1 wave of 128x128 per workgroup, 4 workgroups per CU
-  kAlgoCount = 6
+  kAlgoLdsSplitK = 6,   // 128x64 tile, 4 waves each taking a quarter of every K stage
+  kAlgoCount = 7
 };
 
 // how an operand tile travels from global memory to LDS
@@ -54,9 +55,17 @@ using CfgLds256W4 = TileCfg<256, 256, 64, 2, 2, 2>;
 // 128x128x32 block tile owned by a single wave (128x128, 4x4 atoms): no
 // workgroup barrier to wait on, and four such workgroups share a CU
 using CfgLds128W1 = TileCfg<128, 128, 32, 1, 1>;
+// 128x64x128 block tile, 4 K-groups of one wave each: every wave computes
+// the whole 128x64 tile over 32 of each stage's 128 k, then the four partial
+// tiles are reduced through LDS.  256 workgroups of 4 waves fill the chip
+// when the output has only 256 such tiles (small M x N, long K).  A step is
+// only 16 MFMAs per wave, so tiles are fetched two steps ahead (three
+// stages, 144 KB of LDS).
+using CfgLdsSplitK = TileCfg<128, 64, 128, 1, 1, 1, 4, 3>;
 
 static_assert(frag_c_is_partition_c<CfgLds128>() && frag_c_is_partition_c<CfgLds256>() &&
-                  frag_c_is_partition_c<CfgLds256W4>() && frag_c_is_partition_c<CfgLds128W1>(),
+                  frag_c_is_partition_c<CfgLds256W4>() && frag_c_is_partition_c<CfgLds128W1>() &&
+                  frag_c_is_partition_c<CfgLdsSplitK>(),
               "accumulator coordinates must be the tiled MMA's partition_C");
 
 struct KernelInfo {

@@ -5,9 +5,13 @@
 //  * a workgroup owns a BM x BN block of D and walks K in BK steps, the CTA
 //    tiling of "CuTe Layout 到 Tensor Core" §4 (local_tile with cta_tiler
 //    (128,128,32)) and of the simple-GEMM page ("cute(7) simple_gemm" §3.1);
-//  * the workgroup's waves are arranged WAVES_M x WAVES_N, wave id
-//    w = wm + WAVES_M*wn (M fastest, the compact arrangement of the TiledMMA
-//    page, section "第二个参数怎样把一个 warp 扩展成四个");
+//  * the workgroup's waves are arranged WAVES_M x WAVES_N x WAVES_K, wave id
+//    w = wm + WAVES_M*wn + WAVES_M*WAVES_N*wk (M fastest, the compact
+//    arrangement of the TiledMMA page, section "第二个参数怎样把一个 warp 扩
+//    展成四个").  The WAVES_K K-groups ("K 方向的线程组，与 K 方向的循环") hold
+//    the same accumulator positions and split every stage's K sub-steps
+//    between them; their partial sums are reduced through LDS at the end, C
+//    added once;
 //  * each wave repeats the MFMA atom RM x RN times over its WTM x WTN tile
 //    and KSUB times along BK (the repeat modes of the TiledMMA page, section
 //    "输入扩大以后，后两个 mode 怎样工作", and the register reuse of the
@@ -32,19 +36,27 @@ namespace mfl {
 
 // DIST: how many K sub-steps ahead the operand fragments are read from LDS
 // (1: two register buffers; 2: one buffer per sub-step, the step's barrier
-// one sub-step earlier).
-template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int DIST_ = 1>
+// one sub-step earlier).  WAVES_K: K-groups splitting each stage's sub-steps.
+// STAGES: LDS stages; a tile is fetched STAGES-1 steps before it is used.
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int DIST_ = 1, int WAVES_K_ = 1,
+          int STAGES_ = 2>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_;
   static constexpr int kFragDist = DIST_;
-  static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
-  static constexpr int kWaves = WAVES_M * WAVES_N;
+  static constexpr int kStages = STAGES_;
+  static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, WAVES_K = WAVES_K_;
+  static constexpr int kGroupWaves = WAVES_M * WAVES_N;   // waves of one K-group
+  static constexpr int kWaves = kGroupWaves * WAVES_K;
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
   static constexpr int kAtomM = 32, kAtomN = 32, kAtomK = 16;   // 32x32x16 f16
   static constexpr int RM = WTM / kAtomM, RN = WTN / kAtomN;
-  static constexpr int KSUB = BK / kAtomK;
+  static constexpr int KSUB = BK / kAtomK;        // K sub-steps per stage
+  static constexpr int KSUB_W = KSUB / WAVES_K;   // ... taken by each wave
   static constexpr int CH = BK / 8;               // 16-byte chunks per LDS row
+  // split-K: one 16 x 64 fp32 block per (wave of a K-group, atom block,
+  // other member), written into the operand stages once they are free
+  static constexpr int kRedBytes = kGroupWaves * RM * RN * (WAVES_K - 1) * 16 * 64 * 4;
   static constexpr int kLdsA = BM * BK;           // halves per stage
   static constexpr int kLdsB = BN * BK;
   // epilogue: accumulator rows of 32 staged through LDS per pass (fp32,
@@ -57,8 +69,16 @@ struct TileCfg {
   static_assert(BK % kAtomK == 0, "BK must be a multiple of the atom K");
   static_assert((BM * CH) % kThreads == 0 && (BN * CH) % kThreads == 0,
                 "operand tile chunks must divide evenly over the threads");
-  static_assert(CH == 4 || CH == 8, "swizzle defined for 4 or 8 chunks per row");
-  static_assert(DIST_ == 1 || (DIST_ == 2 && KSUB >= 4), "fragment distance 1, or 2 with 4+ sub-steps");
+  static_assert(CH == 4 || CH == 8 || CH == 16, "swizzle defined for 4, 8 or 16 chunks per row");
+  static_assert(DIST_ == 1 || (DIST_ == 2 && KSUB_W >= 4),
+                "fragment distance 1, or 2 with 4+ sub-steps per wave");
+  static_assert(KSUB % WAVES_K == 0 && KSUB_W % 2 == 0,
+                "each K-group takes an even number of the stage's sub-steps");
+  static_assert(WAVES_K == 1 || ((RM * RN) % WAVES_K == 0 &&
+                                 kRedBytes <= kStages * 2 * (BM + BN) * BK),
+                "split-K: blocks divide over the K-groups, partials fit in the stages");
+  static_assert((kStages == 2 || kStages == 3) && kStages * 2 * (BM + BN) * BK <= 160 * 1024,
+                "two or three stages within the 160 KB of LDS");
   static_assert(kWaves * kEpiRows * 32 * WTN * 4 <= 4 * (BM + BN) * BK,
                 "epilogue staging must fit in the operand stages");
 };
@@ -78,10 +98,11 @@ MFL_HD constexpr int epi_offset(int r, int n) {
 // the 16 rows that 16 consecutive lanes read (same logical chunk) must land
 // on 16 different 16-byte bank groups: (row*CH + chunk') mod 16 distinct.
 // For CH = 8 that is parity(row) and (row>>1)&7; for CH = 4, row&3 and
-// (row>>2)&3.
+// (row>>2)&3; for CH = 16 a row spans all 64 banks and the chunk alone
+// decides, so the XOR is row&15.
 template <int CH>
 MFL_HD constexpr int swz(int row) {
-  return CH == 8 ? ((row >> 1) & 7) : ((row >> 2) & 3);
+  return CH == 16 ? (row & 15) : CH == 8 ? ((row >> 1) & 7) : ((row >> 2) & 3);
 }
 
 struct RowK {
@@ -177,13 +198,26 @@ static_assert(eval2(atom_ab_tv(), 0, 1) - eval2(atom_ab_tv(), 0, 0) == 32,
 static_assert(size(atom_ab_tv()) == 32 * 16 && size(atom_c_tv()) == 32 * 32,
               "atom layouts must cover the atom");
 
-// Operand fragment of wave `w`, repeat i (along M or N), K sub-step kk:
-// (row, k) of value 0 within the workgroup tile.
+// Wave w of the workgroup: (wm, wn) within its K-group, and the K-group.
+template <class Cfg>
+MFL_HD constexpr int wave_m(int w) { return (w % Cfg::kGroupWaves) % Cfg::WAVES_M; }
+template <class Cfg>
+MFL_HD constexpr int wave_n(int w) { return (w % Cfg::kGroupWaves) / Cfg::WAVES_M; }
+template <class Cfg>
+MFL_HD constexpr int wave_k(int w) { return w / Cfg::kGroupWaves; }
+
+// K offset within a stage of wave w's sub-step kk (0 <= kk < KSUB_W)
+template <class Cfg>
+MFL_HD constexpr int sub_k(int w, int kk) {
+  return (wave_k<Cfg>(w) * Cfg::KSUB_W + kk) * Cfg::kAtomK;
+}
+
+// Operand fragment of wave `w`, repeat i (along M or N), the wave's K
+// sub-step kk: (row, k) of value 0 within the workgroup tile.
 template <class Cfg>
 MFL_HD constexpr RowK frag_a_coord(int w, int lane, int i, int kk) {
   const RowK a = atom_ab_coord(lane);
-  const int wm = w % Cfg::WAVES_M;
-  return RowK{wm * Cfg::WTM + i * Cfg::kAtomM + a.row, kk * Cfg::kAtomK + a.k};
+  return RowK{wave_m<Cfg>(w) * Cfg::WTM + i * Cfg::kAtomM + a.row, sub_k<Cfg>(w, kk) + a.k};
 }
 
 // Source (m, k) within the workgroup tile of the first transposed read that
@@ -192,23 +226,22 @@ MFL_HD constexpr RowK frag_a_coord(int w, int lane, int i, int kk) {
 template <class Cfg>
 MFL_HD constexpr RowK frag_a_tr_coord(int w, int lane, int i, int kk) {
   const RowK t = atom_a_tr_source(lane);
-  const int wm = w % Cfg::WAVES_M;
-  return RowK{wm * Cfg::WTM + i * Cfg::kAtomM + t.row, kk * Cfg::kAtomK + t.k};
+  return RowK{wave_m<Cfg>(w) * Cfg::WTM + i * Cfg::kAtomM + t.row, sub_k<Cfg>(w, kk) + t.k};
 }
 
 template <class Cfg>
 MFL_HD constexpr RowK frag_b_coord(int w, int lane, int j, int kk) {
   const RowK b = atom_ab_coord(lane);
-  const int wn = w / Cfg::WAVES_M;
-  return RowK{wn * Cfg::WTN + j * Cfg::kAtomN + b.row, kk * Cfg::kAtomK + b.k};
+  return RowK{wave_n<Cfg>(w) * Cfg::WTN + j * Cfg::kAtomN + b.row, sub_k<Cfg>(w, kk) + b.k};
 }
 
+// Accumulator value v of repeat (i, j): (m, n) within the workgroup tile;
+// the same for every K-group.
 template <class Cfg>
 MFL_HD constexpr RowK frag_c_coord(int w, int lane, int i, int j, int v) {
   const RowK c = atom_c_coord(lane, v);
-  const int wm = w % Cfg::WAVES_M, wn = w / Cfg::WAVES_M;
-  return RowK{wm * Cfg::WTM + i * Cfg::kAtomM + c.row,
-              wn * Cfg::WTN + j * Cfg::kAtomN + c.k};
+  return RowK{wave_m<Cfg>(w) * Cfg::WTM + i * Cfg::kAtomM + c.row,
+              wave_n<Cfg>(w) * Cfg::WTN + j * Cfg::kAtomN + c.k};
 }
 
 // frag_c_coord is the tiled MMA's partition_C written out in closed form.
@@ -234,9 +267,11 @@ constexpr bool frag_c_is_partition_c() {
   const CPartition p =
       partition_c(C, tile, atom_c_tv(), 32, 32, Cfg::WAVES_M, Cfg::WAVES_N);
   if (p.thr.status != kLayoutOk || p.val.status != kLayoutOk) return false;
+  // partition_C selects (lane, wm, wn) only: every K-group sees the view of
+  // the thread with the same (lane, wm, wn)
   for (int t = 0; t < Cfg::kThreads; ++t) {
     const RowK c = frag_c_coord<Cfg>(t / 64, t % 64, 0, 0, 0);
-    if (eval(p.thr, t) != c.row + int64_t(Cfg::BM) * c.k) return false;
+    if (eval(p.thr, t % (64 * Cfg::kGroupWaves)) != c.row + int64_t(Cfg::BM) * c.k) return false;
   }
   for (int j = 0; j < Cfg::RN; ++j)
     for (int i = 0; i < Cfg::RM; ++i)

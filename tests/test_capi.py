@@ -113,6 +113,11 @@ def test_auto_choice():
     assert _v(M=4096, N=4096, K=4096, lda=4100)[1] == mfl.ALGOS["lds256"]
     assert _v(M=256, N=256, K=256)[1] == mfl.ALGOS["lds128"]
     assert _v(M=32, N=16, K=16, algo=1)[1] == mfl.ALGOS["direct"]
+    # fewer 128x128 tiles than CUs and a long K: split K inside the workgroup
+    assert _v(M=512, N=4096, K=4096)[1] == mfl.ALGOS["splitk"]
+    assert _v(M=256, N=4096, K=8192)[1] == mfl.ALGOS["splitk"]
+    assert _v(M=512, N=4096, K=512)[1] == mfl.ALGOS["lds128"]       # K too short
+    assert _v(M=1024, N=4096, K=4096)[1] == mfl.ALGOS["lds128"]     # 256 tiles fill the CUs
 
 
 def test_binding_rejects_cpu_tensors():

@@ -20,8 +20,8 @@ from gpu_helpers import (freivalds_exact, oracle_full, oracle_sampled, run_gemm,
 
 pytestmark = pytest.mark.gpu
 
-ALGOS = ["direct", "lds128", "lds256", "lds256w4", "lds128w1"]
-LDS_ALGOS = ["lds128", "lds256", "lds256w4", "lds128w1"]
+ALGOS = ["direct", "lds128", "lds256", "lds256w4", "lds128w1", "splitk"]
+LDS_ALGOS = ["lds128", "lds256", "lds256w4", "lds128w1", "splitk"]
 
 
 def _assert_checks(checks):
@@ -46,6 +46,28 @@ def test_small_integer_bit_exact(algo, shape):
         w = W.custom(M, N, K, c=c, d=d, dist="int", seed=M * 7 + N * 3 + K, lda=lda, ldb=ldb)
         x = W.make_inputs(w)
         D, checks = run_gemm(w, x, algo)
+        _assert_checks(checks)
+        v = verdict(D, oracle_full(w, x), w, True)
+        assert v.ok, (w.name, c, d, str(v))
+
+
+# Split-K (K-groups of waves, partial tiles reduced through LDS): K from one
+# 128-deep stage to several, with and without a K tail, ragged M and N, every
+# C/D combination, both fetch paths
+SPLITK_SHAPES = [(128, 64, 128), (128, 64, 256), (200, 100, 384), (257, 129, 1000),
+                 (64, 200, 4097), (130, 70, 640), (1, 1, 300), (300, 260, 129)]
+
+
+@pytest.mark.parametrize("shape", SPLITK_SHAPES)
+def test_splitk_integer_bit_exact(shape):
+    M, N, K = shape
+    ld16 = (K + 7) // 8 * 8 + 8
+    for (c, d), lda, ldb in (((None, "f32"), ld16, ld16), (("f16", "f16"), K + 1, ld16),
+                             (("f32", "f32"), ld16, K + 3), ((None, "f16"), K + 1, K + 1)):
+        w = W.custom(M, N, K, c=c, d=d, dist="int", seed=M + 3 * N + 7 * K, lda=lda, ldb=ldb)
+        x = W.make_inputs(w)
+        say(f"[gpu] splitk {w.name} c={c} d={d} lda={lda} ldb={ldb}")
+        D, checks = run_gemm(w, x, "splitk")
         _assert_checks(checks)
         v = verdict(D, oracle_full(w, x), w, True)
         assert v.ok, (w.name, c, d, str(v))
@@ -124,6 +146,8 @@ def test_kernel_properties():
     assert mfl.kernel_info("lds128w1")["lds_bytes"] == 2 * (128 + 128) * 32 * 2
     assert mfl.kernel_info("lds256")["threads"] == 512
     assert mfl.kernel_info("lds128w1")["threads"] == 64
+    assert mfl.kernel_info("splitk")["lds_bytes"] == 3 * (128 + 64) * 128 * 2   # three stages
+    assert mfl.kernel_info("splitk")["threads"] == 256
     say("[gpu] kernel info", {a: mfl.kernel_info(a) for a in ALGOS})
 
 
@@ -133,7 +157,8 @@ NAMED = [
     ("direct_256", ["direct"], True),
     ("lds_4096", ["lds128", "lds256", "lds256w4", "lds256+reg", "lds128w1"], True),
     ("accum_mmajor_8192x8192x2048", ["auto", "lds128", "lds256+reg"], True),
-    ("ragged_8191x6143x4097", ["auto", "lds128", "lds256w4", "lds128w1"], True),
+    ("ragged_8191x6143x4097", ["auto", "lds128", "lds256w4", "lds128w1", "splitk"], True),
+    ("shard_512x4096x4096", ["auto", "splitk", "lds128"], True),
 ]
 
 
@@ -160,8 +185,8 @@ def test_named_workload(name, algo, integer):
         v = verdict(D, ref, w, x.integer)
         assert v.ok, str(v)
         return
-    ms, ns = W.sample_indices(w.M, w.N, 20000, seed=w.seed,
-                              tile=128 if algo.startswith(("lds128", "direct")) else 256)
+    tile = 64 if algo == "splitk" else 128 if algo.startswith(("lds128", "direct")) else 256
+    ms, ns = W.sample_indices(w.M, w.N, 20000, seed=w.seed, tile=tile)
     ref = oracle_sampled(w, x, ms, ns)
     v = verdict(D[ms, ns], ref, w, x.integer)
     say(f"[gpu] {w.name} sampled {len(ms)}: {v}")

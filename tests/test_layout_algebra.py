@@ -16,8 +16,10 @@ from helpers import keyed
 P = L.parse
 F = L.format_layout
 
-KERNEL_TILES = {"lds128": (128, 128, 32, 2, 2), "lds256": (256, 256, 64, 2, 4),
-                "lds256w4": (256, 256, 64, 2, 2), "lds128w1": (128, 128, 32, 1, 1)}
+# BM, BN, BK, waves along M, N and K
+KERNEL_TILES = {"lds128": (128, 128, 32, 2, 2, 1), "lds256": (256, 256, 64, 2, 4, 1),
+                "lds256w4": (256, 256, 64, 2, 2, 1), "lds128w1": (128, 128, 32, 1, 1, 1),
+                "splitk": (128, 64, 128, 1, 1, 4)}
 
 
 def _tab(text):
@@ -308,8 +310,9 @@ def test_error_codes():
 def test_kernel_accumulators_are_partition_c(algo):
     """The kernels' accumulator coordinates are partition_C of the block tile
     for the 32x32x16 atom, with wave-contiguous repeats: tile permutation
-    (32, W, R):(1, 32R, 32) per direction."""
-    BM, BN, BK, WM, WN = KERNEL_TILES[algo]
+    (32, W, R):(1, 32R, 32) per direction.  partition_C selects (lane, wm,
+    wn) only, so every K-group of a split-K tile holds the same view."""
+    BM, BN, BK, WM, WN, WK = KERNEL_TILES[algo]
     RM, RN = BM // WM // 32, BN // WN // 32
     tile = (F(((32, WM, RM), (1, 32 * RM, 32))), F(((32, WN, RN), (1, 32 * RN, 32))))
     c = F(((BM, BN), (1, BM)))
@@ -320,7 +323,9 @@ def test_kernel_accumulators_are_partition_c(algo):
     want = fc[..., 0] + BM * fc[..., 1]
     i, j, v = np.meshgrid(np.arange(RM), np.arange(RN), np.arange(16), indexing="ij")
     order = (v + 16 * (i + RM * j)).reshape(-1)        # value layout index of each slot
-    assert np.array_equal(T[:, None] + V[None, order], want)
+    thr = np.arange(want.shape[0]) % (64 * WM * WN)      # the thread's (lane, wm, wn)
+    assert want.shape[0] == 64 * WM * WN * WK
+    assert np.array_equal(T[thr][:, None] + V[None, order], want)
     # the oracle's chain gives the same
     _check_partition(c, _mfma_tv("f32_32x32x16_f16", "C"), (32, 32), 64, (WM, WN), tile)
 

@@ -156,37 +156,41 @@ def test_mfma_tv_layouts_equal_oracle_closed_forms(op):
 
 
 # --------------------------------------------- kernel fragment addressing
-KERNEL_TILES = {"direct": (128, 128, 32, 2, 2), "lds128": (128, 128, 32, 2, 2),
-                "lds256": (256, 256, 64, 2, 4), "lds256w4": (256, 256, 64, 2, 2),
-                "lds128w1": (128, 128, 32, 1, 1)}
+# BM, BN, BK, waves along M, N and K (K-groups split each stage's sub-steps)
+KERNEL_TILES = {"direct": (128, 128, 32, 2, 2, 1), "lds128": (128, 128, 32, 2, 2, 1),
+                "lds256": (256, 256, 64, 2, 4, 1), "lds256w4": (256, 256, 64, 2, 2, 1),
+                "lds128w1": (128, 128, 32, 1, 1, 1), "splitk": (128, 64, 128, 1, 1, 4)}
+LDS_KERNELS = ["lds128", "lds256", "lds256w4", "lds128w1", "splitk"]
 
 
 @pytest.mark.parametrize("algo", sorted(KERNEL_TILES))
 def test_fragment_coords_follow_the_atom_layout(algo):
-    BM, BN, BK, WM, WN = KERNEL_TILES[algo]
+    BM, BN, BK, WM, WN, WK = KERNEL_TILES[algo]
     op = "f32_32x32x16_f16"
     fa = mfl.fragment_coords(algo, "A")
     fb = mfl.fragment_coords(algo, "B")
     fc = mfl.fragment_coords(algo, "C")
-    T = 64 * WM * WN
+    T = 64 * WM * WN * WK
     assert fa.shape[0] == fb.shape[0] == fc.shape[0] == T
-    RM, RN = BM // WM // 32, BN // WN // 32
+    RM, RN, KW = BM // WM // 32, BN // WN // 32, BK // 16 // WK
     for t in range(T):
         w, lane = divmod(t, 64)
-        wm, wn = w % WM, w // WM
+        wm, wn, wk = w % WM, (w // WM) % WN, w // (WM * WN)
         s = 0
-        for kk in range(BK // 16):
+        for kk in range(KW):
             for i in range(RM):
                 for v in range(8):
                     r, k = L.mfma_ab_coord(op, lane, v)
-                    assert tuple(fa[t, s]) == (wm * (BM // WM) + 32 * i + r, 16 * kk + k)
+                    assert tuple(fa[t, s]) == (wm * (BM // WM) + 32 * i + r,
+                                               16 * (wk * KW + kk) + k)
                     s += 1
         s = 0
-        for kk in range(BK // 16):
+        for kk in range(KW):
             for j in range(RN):
                 for v in range(8):
                     r, k = L.mfma_ab_coord(op, lane, v)
-                    assert tuple(fb[t, s]) == (wn * (BN // WN) + 32 * j + r, 16 * kk + k)
+                    assert tuple(fb[t, s]) == (wn * (BN // WN) + 32 * j + r,
+                                               16 * (wk * KW + kk) + k)
                     s += 1
         s = 0
         for i in range(RM):
@@ -200,8 +204,9 @@ def test_fragment_coords_follow_the_atom_layout(algo):
 
 @pytest.mark.parametrize("algo", sorted(KERNEL_TILES))
 def test_fragment_multiplicities(algo):
-    """A held WAVES_N times, B WAVES_M times, C once (the pages' 2/2/1)."""
-    BM, BN, BK, WM, WN = KERNEL_TILES[algo]
+    """A held WAVES_N times, B WAVES_M times, C once per K-group (the pages'
+    2/2/1, and C twice for two K-direction warp groups)."""
+    BM, BN, BK, WM, WN, WK = KERNEL_TILES[algo]
     for operand, rows, mult in (("A", BM, WN), ("B", BN, WM)):
         f = mfl.fragment_coords(algo, operand).reshape(-1, 2)
         idx = f[:, 0] * BK + f[:, 1]
@@ -209,11 +214,11 @@ def test_fragment_multiplicities(algo):
         assert counts.shape[0] == rows * BK and (counts == mult).all()
     f = mfl.fragment_coords(algo, "C").reshape(-1, 2)
     counts = np.bincount(f[:, 0] * BN + f[:, 1], minlength=BM * BN)
-    assert (counts == 1).all()
+    assert (counts == WK).all()
 
 
 # ------------------------------------------------ LDS tile layout, tile order
-@pytest.mark.parametrize("algo", ["lds128", "lds256", "lds256w4", "lds128w1"])
+@pytest.mark.parametrize("algo", LDS_KERNELS)
 @pytest.mark.parametrize("operand", ["A", "B"])
 def test_lds_tile_layout_bijective_and_conflict_free(algo, operand):
     """The swizzled tile is a permutation of rows*BK halves that keeps each
@@ -248,7 +253,7 @@ def test_tile_order_keeps_xcd_blocks_compact():
 
 
 # ----------------------------------------- M-contiguous A: transposing reads
-@pytest.mark.parametrize("algo", ["lds128", "lds256", "lds256w4", "lds128w1"])
+@pytest.mark.parametrize("algo", LDS_KERNELS)
 def test_mmajor_tile_and_transposed_reads_conflict_free(algo):
     """The M-contiguous A tile is a permutation keeping 8-half chunks whole,
     and every transposing read (64 lanes x 8 bytes, served 32 lanes per pass)
@@ -272,7 +277,7 @@ def test_mmajor_tile_and_transposed_reads_conflict_free(algo):
                     assert sorted(banks) == list(range(64)), (algo, t0, slot, h, half)
 
 
-@pytest.mark.parametrize("algo", ["lds128", "lds256", "lds256w4", "lds128w1"])
+@pytest.mark.parametrize("algo", LDS_KERNELS)
 def test_transposed_reads_give_the_operand_fragments(algo):
     """Applying the transposing read's lane regrouping (pinned on the GPU by
     test_gpu_probe) to the kernel's source coordinates yields exactly the A

@@ -101,6 +101,10 @@ WORKLOADS = {
         "ragged_8191x6143x4097", 8191, 6143, 4097, c="f16", d="f16", dist="unif",
         c_dist="unif", seed=5, twin_seed=105,
         note="partial tiles in M, N and K; odd leading dimensions; fp16 C and D"),
+    "shard_512x4096x4096": Workload(
+        "shard_512x4096x4096", 512, 4096, 4096, d="f32", dist="unif", seed=6, twin_seed=106,
+        note="one GPU's share of an 8-way M split of the 4096^3 GEMM: 256 tiles of "
+             "128x64, long K"),
 }
 
 
