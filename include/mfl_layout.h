@@ -125,7 +125,10 @@ int mfl_layout_retile(const char* frag, const char* tv, const char* tile_shape, 
 int mfl_layout_mfma_tv(int32_t op, int32_t operand, char* out, int64_t cap);
 
 /* Per-lane fragment addressing of a GEMM kernel, computed by the same code
- * the kernel runs: for every thread t of one workgroup and every fragment
+ * the kernel runs.  B coordinates are LDS rows: the kernels store B in
+ * N-permuted row order (LDS row r of a wave's WTN rows holds tile row
+ * RN*(r % 32) + r / 32, RN = WTN / 32), and accumulator coordinates are the
+ * physical (m, n).  For every thread t of one workgroup and every fragment
  * slot s of the K sub-steps it takes from one stage (all of them, or its
  * K-group's share when the tile splits K), the (row, k) (operand 0 A, 1 B)
  * or (m, n)

@@ -437,6 +437,7 @@ int gemm_tn(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const v
   p.tiles_n = (int)((N + ki.bn - 1) / ki.bn);
   p.group_m = ki.bm >= 256 ? 4 : 8;
   p.d_vec = ((uintptr_t)D % (uintptr_t)(4 * elem_size(dtypes.d)) == 0) && (ldd % 4 == 0);
+  p.c_vec = C && ((uintptr_t)C % (uintptr_t)(4 * elem_size(dtypes.c)) == 0) && (ldc % 4 == 0);
   p.A = A;
   p.B = B;
   p.C = C;

@@ -89,86 +89,245 @@ __device__ __forceinline__ void d_store(const GemmParams& p, int m, int n, float
     __builtin_nontemporal_store(x, (float*)p.D + (int64_t)m * p.ldd + n);
 }
 
-// Register epilogue: acc[i][j] value v -> (m, n) from the accumulator TV
-// layout, one element per store (for a fixed value the 64 lanes cover two
-// 128-byte row runs), for the blocks (i, j) that own(i, j) accepts.  Interior tiles without C store through a buffer
-// descriptor based at the wave's tile origin: the lane part of the layout is
-// one per-lane offset, the row part of (repeat, value) a uniform scalar
-// offset and the column part the instruction's immediate, so each element is
-// one store instruction with no address arithmetic on the vector side.  Edge
-// tiles (and C reads, which only the direct kernel does here) check and
-// address each element.
-struct AllBlocks {
-  __device__ bool operator()(int, int) const { return true; }
+// Register epilogue.  The N permutation gives each lane, for a row block i
+// and value v, its RN accumulators acc[i][0..RN-1][v] on RN adjacent columns
+// of one row: one RN-element vector of D per (i, v), and for a fixed (i, v)
+// the 64 lanes cover two rows of 32*RN consecutive columns.  Interior tiles
+// with vector-aligned D (and C) go through buffer descriptors based at the
+// wave's tile origin: the lane part of the accumulator layout is one per-lane
+// offset and the row part of (i, v) a uniform scalar offset, so there is no
+// vector address arithmetic and no per-element branch; C's 16 vectors of a
+// row block are loaded before any of them is used.  Other tiles address each
+// vector and fall back to elements where a vector would cross the right edge
+// or the rows are not vector-aligned.  Only the row blocks own(i) accepts
+// are written.
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+struct AllRows {
+  __device__ bool operator()(int) const { return true; }
 };
 
-template <class Cfg, int CK, int DK, class Own = AllBlocks>
-__device__ __forceinline__ void epilogue(const GemmParams& p, int w, int lane, int m0,
-                                         int n0, const floatx16 (&acc)[Cfg::RM][Cfg::RN],
-                                         Own own = Own()) {
-  constexpr int ES = DK == 1 ? 2 : 4;
-  if (CK == 0 && m0 + Cfg::BM <= p.M && n0 + Cfg::BN <= p.N &&
-      (int64_t)Cfg::BM * p.ldd * ES < ((int64_t)1 << 31)) {
+__device__ __forceinline__ unsigned pack_half2(float a, float b) {   // RNE
+  return (unsigned)__builtin_bit_cast(unsigned short, (_Float16)a) |
+         ((unsigned)__builtin_bit_cast(unsigned short, (_Float16)b) << 16);
+}
+
+__device__ __forceinline__ float half_lo(unsigned u) {
+  return (float)__builtin_bit_cast(_Float16, (unsigned short)(u & 0xffffu));
+}
+__device__ __forceinline__ float half_hi(unsigned u) {
+  return (float)__builtin_bit_cast(_Float16, (unsigned short)(u >> 16));
+}
+
+// RN values -> one D vector through a buffer descriptor (kNtStore: D is
+// written once and not read back by this kernel)
+template <int DK, int RN>
+__device__ __forceinline__ void buffer_store_d(const float (&x)[RN], __amdgpu_buffer_rsrc_t r,
+                                               int voff, int soff) {
+  static_assert(RN == 2 || RN == 4, "vectors of 2 or 4 columns");
+  if constexpr (DK == 2 && RN == 4) {
+    const u32x4 d = {__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]),
+                     __float_as_uint(x[3])};
+    __builtin_amdgcn_raw_buffer_store_b128(d, r, voff, soff, kNtStore);
+  } else if constexpr (DK == 2) {
+    const u32x2 d = {__float_as_uint(x[0]), __float_as_uint(x[1])};
+    __builtin_amdgcn_raw_buffer_store_b64(d, r, voff, soff, kNtStore);
+  } else if constexpr (RN == 4) {
+    const u32x2 d = {pack_half2(x[0], x[1]), pack_half2(x[2], x[3])};
+    __builtin_amdgcn_raw_buffer_store_b64(d, r, voff, soff, kNtStore);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b32(pack_half2(x[0], x[1]), r, voff, soff, kNtStore);
+  }
+}
+
+template <int CK, int RN>
+__device__ __forceinline__ void buffer_load_c(float (&c)[RN], __amdgpu_buffer_rsrc_t r, int voff,
+                                              int soff) {
+  if constexpr (CK == 2 && RN == 4) {
+    const u32x4 d = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c[e] = __uint_as_float(d[e]);
+  } else if constexpr (CK == 2) {
+    const u32x2 d = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+    c[0] = __uint_as_float(d[0]);
+    c[1] = __uint_as_float(d[1]);
+  } else if constexpr (RN == 4) {
+    const u32x2 d = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+    c[0] = half_lo(d[0]);
+    c[1] = half_hi(d[0]);
+    c[2] = half_lo(d[1]);
+    c[3] = half_hi(d[1]);
+  } else {
+    const unsigned d = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+    c[0] = half_lo(d);
+    c[1] = half_hi(d);
+  }
+}
+
+// the same through a plain address (rows not in reach of one descriptor, or
+// edge tiles)
+template <int DK, int RN>
+__device__ __forceinline__ void store_d_vec(const GemmParams& p, int m, int n,
+                                            const float (&x)[RN]) {
+  if constexpr (DK == 2) {
+    typedef float fv __attribute__((ext_vector_type(RN)));
+    fv v;
+#pragma unroll
+    for (int e = 0; e < RN; ++e) v[e] = x[e];
+    __builtin_nontemporal_store(v, (fv*)((float*)p.D + (int64_t)m * p.ldd + n));
+  } else {
+    typedef _Float16 hv __attribute__((ext_vector_type(RN)));
+    hv v;
+#pragma unroll
+    for (int e = 0; e < RN; ++e) v[e] = (_Float16)x[e];
+    __builtin_nontemporal_store(v, (hv*)((_Float16*)p.D + (int64_t)m * p.ldd + n));
+  }
+}
+
+template <int CK, int RN>
+__device__ __forceinline__ void load_c_vec(const GemmParams& p, int m, int n, float (&c)[RN]) {
+  if constexpr (CK == 2) {
+    typedef float fv __attribute__((ext_vector_type(RN)));
+    fv v;
+    __builtin_memcpy(&v, (const float*)p.C + (int64_t)m * p.ldc + n, sizeof(v));
+#pragma unroll
+    for (int e = 0; e < RN; ++e) c[e] = v[e];
+  } else {
+    typedef _Float16 hv __attribute__((ext_vector_type(RN)));
+    hv v;
+    __builtin_memcpy(&v, (const _Float16*)p.C + (int64_t)m * p.ldc + n, sizeof(v));
+#pragma unroll
+    for (int e = 0; e < RN; ++e) c[e] = (float)v[e];
+  }
+}
+
+// every value of a lane lies in the lane's own column of the atom, so the
+// column of acc[i][j][v] depends on (lane, j) only
+MFL_HD constexpr bool c_columns_per_lane() {
+  for (int v = 0; v < 16; ++v)
+    if (atom_c_coord(0, v).k != 0) return false;
+  return true;
+}
+static_assert(c_columns_per_lane(), "accumulator column must not depend on the value");
+
+// whole tile inside D, vector-aligned rows, and every row of the tile within
+// reach of one buffer descriptor
+template <class Cfg, int CK, int DK>
+__device__ __forceinline__ bool register_epilogue_ok(const GemmParams& p, int m0, int n0) {
+  constexpr int ES = DK == 1 ? 2 : 4, CS = CK == 1 ? 2 : 4;
+  return p.d_vec && (CK == 0 || p.c_vec) && m0 + Cfg::BM <= p.M && n0 + Cfg::BN <= p.N &&
+         (int64_t)Cfg::BM * p.ldd * ES < ((int64_t)1 << 31) &&
+         (CK == 0 || (int64_t)Cfg::BM * p.ldc * CS < ((int64_t)1 << 31));
+}
+
+// the buffer-descriptor path alone (one straight block: the kernels with one
+// wave per SIMD have no registers for a second path)
+template <class Cfg, int CK, int DK, class Own = AllRows>
+__device__ __forceinline__ void epilogue_regs(const GemmParams& p, int w, int lane, int m0,
+                                              int n0, const floatx16 (&acc)[Cfg::RM][Cfg::RN],
+                                              Own own = Own()) {
+  constexpr int RM = Cfg::RM, RN = Cfg::RN;
+  constexpr int ES = DK == 1 ? 2 : 4, CS = CK == 1 ? 2 : 4;
+  {
     const RowK cl = atom_c_coord(lane, 0);
-    const RowK w0 = frag_c_coord<Cfg>(w, 0, 0, 0, 0);
-    char* tile = (char*)p.D + ((int64_t)(m0 + w0.row) * p.ldd + (n0 + w0.k)) * ES;
-    // raw buffer (stride 0), records up to 2^31 bytes, 32-bit data format
-    const __amdgpu_buffer_rsrc_t rsrc =
-        __builtin_amdgcn_make_buffer_rsrc(tile, (short)0, 0x7fffffff, 0x00020000);
-    const int voff = (cl.row * p.ldd + cl.k) * ES;
+    const RowK w0 = frag_c_coord<Cfg>(w, 0, 0, 0, 0);     // the wave's tile origin
+    // raw buffers (stride 0), records up to 2^31 bytes, 32-bit data format
+    const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(
+        (char*)p.D + ((int64_t)(m0 + w0.row) * p.ldd + (n0 + w0.k)) * ES, (short)0, 0x7fffffff,
+        0x00020000);
+    const int voff = (cl.row * p.ldd + RN * cl.k) * ES;
+    __amdgpu_buffer_rsrc_t rc = rd;
+    int cvoff = 0;
+    if constexpr (CK != 0) {
+      rc = __builtin_amdgcn_make_buffer_rsrc(
+          (char*)p.C + ((int64_t)(m0 + w0.row) * p.ldc + (n0 + w0.k)) * CS, (short)0, 0x7fffffff,
+          0x00020000);
+      cvoff = (cl.row * p.ldc + RN * cl.k) * CS;
+    }
+    constexpr int QB = 8;   // C vectors loaded before the first is used
 #pragma unroll
-    for (int i = 0; i < Cfg::RM; ++i)
+    for (int i = 0; i < RM; ++i) {
+      if (!own(i)) continue;
 #pragma unroll
-      for (int j = 0; j < Cfg::RN; ++j) {
-        if (!own(i, j)) continue;
+      for (int v0 = 0; v0 < 16; v0 += QB) {
+        float c[QB][RN];
+        if constexpr (CK != 0) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const RowK cv = atom_c_coord(0, v);
-          const int soff = (i * Cfg::kAtomM + cv.row) * p.ldd * ES;
-          const int dn = (j * Cfg::kAtomN + cv.k) * ES;
-          // (the element is copied to a scalar first: a bit cast applied to
-          // a vector element directly read element 0 with this compiler)
-          const float x = acc[i][j][v];
-          // kNtStore: D is written once and not read back by this kernel
-          if constexpr (DK == 1)
-            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (_Float16)x),
-                                                  rsrc, voff + dn, soff, kNtStore);
-          else
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), rsrc, voff + dn, soff,
-                                                  kNtStore);
+          for (int q = 0; q < QB; ++q)
+            buffer_load_c<CK, RN>(c[q], rc, cvoff,
+                                  (i * Cfg::kAtomM + atom_c_coord(0, v0 + q).row) * p.ldc * CS);
+        }
+#pragma unroll
+        for (int q = 0; q < QB; ++q) {
+          const int v = v0 + q;
+          float x[RN];
+#pragma unroll
+          for (int j = 0; j < RN; ++j) {
+            // (copied to a scalar first: a bit cast applied to a vector element
+            // directly read element 0 with this compiler)
+            x[j] = acc[i][j][v];
+            if constexpr (CK != 0) x[j] += c[q][j];
+          }
+          buffer_store_d<DK, RN>(x, rd, voff,
+                                 (i * Cfg::kAtomM + atom_c_coord(0, v).row) * p.ldd * ES);
         }
       }
-    return;
+    }
   }
+}
+
+// any tile: one vector per (i, v) where it fits inside D and the rows are
+// vector-aligned, elements otherwise
+template <class Cfg, int CK, int DK, class Own = AllRows>
+__device__ __forceinline__ void epilogue_any(const GemmParams& p, int w, int lane, int m0,
+                                             int n0, const floatx16 (&acc)[Cfg::RM][Cfg::RN],
+                                             Own own = Own()) {
+  constexpr int RM = Cfg::RM, RN = Cfg::RN;
+  const bool vec = p.d_vec && (CK == 0 || p.c_vec);
 #pragma unroll
-  for (int i = 0; i < Cfg::RM; ++i)
+  for (int i = 0; i < RM; ++i) {
+    if (!own(i)) continue;
 #pragma unroll
-    for (int j = 0; j < Cfg::RN; ++j) {
-      if (!own(i, j)) continue;
+    for (int v = 0; v < 16; ++v) {
+      const RowK c0 = frag_c_coord<Cfg>(w, lane, i, 0, v);   // columns n .. n+RN-1
+      const int m = m0 + c0.row, n = n0 + c0.k;
+      if (m >= p.M) continue;
+      float x[RN];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const RowK c = frag_c_coord<Cfg>(w, lane, i, j, v);
-        const int m = m0 + c.row, n = n0 + c.k;
-        if (m < p.M && n < p.N) d_store<DK>(p, m, n, acc[i][j][v] + c_value<CK>(p, m, n));
+      for (int j = 0; j < RN; ++j) x[j] = acc[i][j][v];
+      if (vec && n + RN <= p.N) {
+        if constexpr (CK != 0) {
+          float c[RN];
+          load_c_vec<CK, RN>(p, m, n, c);
+#pragma unroll
+          for (int j = 0; j < RN; ++j) x[j] += c[j];
+        }
+        store_d_vec<DK, RN>(p, m, n, x);
+      } else {
+#pragma unroll
+        for (int j = 0; j < RN; ++j)
+          if (n + j < p.N) d_store<DK>(p, m, n + j, x[j] + c_value<CK>(p, m, n + j));
       }
     }
+  }
 }
 
 // Split-K reduction (the K-direction thread groups of the TiledMMA page,
 // section "K 方向的线程组，与 K 方向的循环": several groups hold partial sums
-// for the same outputs and one of them must add the others, C once).  Atom
-// block b = i*RN + j of a wave is finished by the member of its K-group set
-// with wave_k == b % WAVES_K; each other member writes its partial block into
-// the freed operand stages and the owner adds them, so every member finishes
-// RM*RN/WAVES_K blocks (a reduce-scatter inside the workgroup).  A block is
+// for the same outputs and one of them must add the others, C once).  Row
+// block i (atom blocks i*RN .. i*RN+RN-1, whole rows so the epilogue's
+// vectors stay with one wave) of a wave is finished by the member of its
+// K-group set with wave_k == i % WAVES_K; each other member writes its
+// partial blocks into the freed operand stages and the owner adds them, so
+// every member finishes RM/WAVES_K row blocks (a reduce-scatter inside the
+// workgroup).  A block is
 // 16 values x 64 lanes, laid out [v/4][lane][v%4]: each lane moves 16-byte
 // pieces and the 64 lanes of one access cover 1 KB contiguously.
 template <class Cfg>
-struct OwnedBlocks {
+struct OwnedRows {
   int wk;
-  __device__ bool operator()(int i, int j) const {
-    return (i * Cfg::RN + j) % Cfg::WAVES_K == wk;
-  }
+  __device__ bool operator()(int i) const { return i % Cfg::WAVES_K == wk; }
 };
 
 template <class Cfg>
@@ -177,14 +336,14 @@ __device__ __forceinline__ void reduce_k_groups(float* red, int w, int lane,
   constexpr int RN = Cfg::RN, WK = Cfg::WAVES_K, NB = Cfg::RM * RN;
   const int wg = w % Cfg::kGroupWaves, wk = wave_k<Cfg>(w);
   auto block = [&](int b, int writer) {
-    const int owner = b % WK;
+    const int owner = (b / RN) % WK;
     const int slot = (writer - owner - 1 + WK) % WK;    // 0 .. WK-2
     return red + ((wg * NB + b) * (WK - 1) + slot) * (16 * 64) + lane * 4;
   };
   __syncthreads();   // every wave is done with the operand stages
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    if (b % WK == wk) continue;
+    if ((b / RN) % WK == wk) continue;
     float* dst = block(b, wk);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -196,7 +355,7 @@ __device__ __forceinline__ void reduce_k_groups(float* red, int w, int lane,
   __syncthreads();
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    if (b % WK != wk) continue;
+    if ((b / RN) % WK != wk) continue;
 #pragma unroll
     for (int m = 1; m < WK; ++m) {
       const float* src = block(b, (wk + m) % WK);
@@ -273,16 +432,19 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, float* sm, int
   __syncthreads();   // every wave is done with the operand stages
 #pragma unroll
   for (int i0 = 0; i0 < RM; i0 += IG) {
-    // accumulators -> this wave's staging tile (rows i0*32 .. +ROWS)
+    // accumulators -> this wave's staging tile (rows i0*32 .. +ROWS), at
+    // their physical columns: a lane's RN repeats are adjacent, one vector
 #pragma unroll
     for (int ii = 0; ii < IG; ++ii)
 #pragma unroll
-      for (int j = 0; j < RN; ++j)
+      for (int v = 0; v < 16; ++v) {
+        const RowK c = atom_c_coord(lane, v);
+        typedef float fv __attribute__((ext_vector_type(RN)));
+        fv x;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const RowK c = atom_c_coord(lane, v);
-          reg[epi_offset<WTN>(ii * 32 + c.row, j * 32 + c.k)] = acc[i0 + ii][j][v];
-        }
+        for (int j = 0; j < RN; ++j) x[j] = acc[i0 + ii][j][v];
+        *(fv*)&reg[epi_offset<WTN>(ii * 32 + c.row, RN * c.k)] = x;
+      }
     // A wave's LDS operations complete in order, so the reads below see the
     // stores above, and the next pass's stores follow these reads.
 #pragma unroll
@@ -354,7 +516,9 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, float* sm, int
 // LDS after M0, lane l at byte 16 l.  A 1 KB run holds RUN = 512/BK rows; lane
 // l takes row RUN*run + l/CH, physical chunk l%CH, so it fetches logical chunk
 // (l%CH) ^ swz(row) of that row.
-template <class Cfg, int ROWS>
+// PERM: the operand's rows carry the N permutation (B): LDS row r holds
+// global row row0 + perm_n(r).
+template <class Cfg, int ROWS, bool PERM>
 struct FetchDma {
   static constexpr int BK = Cfg::BK, CH = Cfg::CH, RUN = 512 / BK;
   static constexpr int kRuns = ROWS / RUN / Cfg::kWaves;
@@ -369,8 +533,9 @@ struct FetchDma {
 #pragma unroll
     for (int i = 0; i < kRuns; ++i) {
       const int row = RUN * (run0 + i) + rsub;
+      const int grow = PERM ? perm_n<Cfg>(row) : row;
       const int kc = ((lane % CH) ^ swz<CH>(row)) * 8;
-      off[i] = (unsigned)((int64_t)min(row0 + row, row0 + rows_valid - 1) * ld * 2) + kc * 2;
+      off[i] = (unsigned)((int64_t)min(row0 + grow, row0 + rows_valid - 1) * ld * 2) + kc * 2;
     }
   }
   __device__ void issue_one(int i, const void* base, int kt, _Float16* stage) {
@@ -382,7 +547,7 @@ struct FetchDma {
 };
 
 // REG: K-contiguous rows, 16-byte chunks q = tid + i*T (row q/CH, chunk q%CH)
-template <class Cfg, int ROWS>
+template <class Cfg, int ROWS, bool PERM>
 struct FetchReg {
   static constexpr int BK = Cfg::BK, CH = Cfg::CH, T = Cfg::kThreads;
   static constexpr int kChunks = ROWS * CH / T;
@@ -396,7 +561,8 @@ struct FetchReg {
 #pragma unroll
     for (int i = 0; i < kChunks; ++i) {
       const int q = tid + i * T, row = q / CH, c = q % CH;
-      off[i] = (int)((int64_t)min(row0 + row, row0 + rows_valid - 1) * ld * 2) + c * 16;
+      const int grow = PERM ? perm_n<Cfg>(row) : row;
+      off[i] = (int)((int64_t)min(row0 + grow, row0 + rows_valid - 1) * ld * 2) + c * 16;
       lds[i] = lds_offset<BK>(row, c * 8);
     }
   }
@@ -495,22 +661,22 @@ struct FetchDmaT {
   __device__ void stash_one(int, _Float16*) {}
 };
 
-template <class Cfg, int ROWS, int POLICY>
+template <class Cfg, int ROWS, int POLICY, bool PERM>
 struct FetchSel;
-template <class Cfg, int ROWS>
-struct FetchSel<Cfg, ROWS, kFetchDma> {
-  using type = FetchDma<Cfg, ROWS>;
+template <class Cfg, int ROWS, bool PERM>
+struct FetchSel<Cfg, ROWS, kFetchDma, PERM> {
+  using type = FetchDma<Cfg, ROWS, PERM>;
+};
+template <class Cfg, int ROWS, bool PERM>
+struct FetchSel<Cfg, ROWS, kFetchReg, PERM> {
+  using type = FetchReg<Cfg, ROWS, PERM>;
 };
 template <class Cfg, int ROWS>
-struct FetchSel<Cfg, ROWS, kFetchReg> {
-  using type = FetchReg<Cfg, ROWS>;
-};
-template <class Cfg, int ROWS>
-struct FetchSel<Cfg, ROWS, kFetchRegT> {
+struct FetchSel<Cfg, ROWS, kFetchRegT, false> {   // A only
   using type = FetchRegT<Cfg, ROWS>;
 };
 template <class Cfg, int ROWS>
-struct FetchSel<Cfg, ROWS, kFetchDmaT> {
+struct FetchSel<Cfg, ROWS, kFetchDmaT, false> {   // A only
   using type = FetchDmaT<Cfg, ROWS>;
 };
 
@@ -565,8 +731,8 @@ __global__ void __launch_bounds__(Cfg::kThreads, 1) gemm_tiled(const GemmParams 
   const TileIndex ti = tile_of_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m);
   const int m0 = ti.tm * BM, n0 = ti.tn * BN;
 
-  using FetchA = typename FetchSel<Cfg, BM, FA>::type;
-  using FetchB = typename FetchSel<Cfg, BN, FB>::type;
+  using FetchA = typename FetchSel<Cfg, BM, FA, false>::type;
+  using FetchB = typename FetchSel<Cfg, BN, FB, true>::type;   // rows in N-permuted order
   FetchA fa_;
   FetchB fb_;
   fa_.init(m0, p.M - m0, p.lda, tid, w, lane);
@@ -790,7 +956,7 @@ __global__ void __launch_bounds__(Cfg::kThreads, 1) gemm_tiled(const GemmParams 
     }
     for (int e = tid; e < BN * BK; e += Cfg::kThreads) {
       const int row = e / BK, k = e % BK, gk = k0 + k;
-      const int gn = min(n0 + row, p.N - 1);
+      const int gn = min(n0 + perm_n<Cfg>(row), p.N - 1);
       sb[lds_offset<BK>(row, k)] = gk < p.K ? B[(int64_t)gn * p.ldb + gk] : (_Float16)0.0f;
     }
     __syncthreads();
@@ -800,13 +966,22 @@ __global__ void __launch_bounds__(Cfg::kThreads, 1) gemm_tiled(const GemmParams 
       mma(0);
     }
   }
+  // Interior tiles with vector-aligned rows: vectors straight from the
+  // registers.  Other tiles: split-K owners address each vector; the other
+  // kernels stage through LDS into row runs of 4 (one code path less in the
+  // kernels that hold every register).
   if constexpr (Cfg::WAVES_K > 1) {
     reduce_k_groups<Cfg>((float*)smem, w, lane, acc);
-    epilogue<Cfg, CK, DK>(p, w, lane, m0, n0, acc, OwnedBlocks<Cfg>{wave_k<Cfg>(w)});
-  } else if constexpr (CK != 0) {
-    epilogue_lds<Cfg, CK, DK>(p, (float*)smem, w, lane, m0, n0, acc);
+    const OwnedRows<Cfg> own{wave_k<Cfg>(w)};
+    if (register_epilogue_ok<Cfg, CK, DK>(p, m0, n0))
+      epilogue_regs<Cfg, CK, DK>(p, w, lane, m0, n0, acc, own);
+    else
+      epilogue_any<Cfg, CK, DK>(p, w, lane, m0, n0, acc, own);
   } else {
-    epilogue<Cfg, CK, DK>(p, w, lane, m0, n0, acc);
+    if (register_epilogue_ok<Cfg, CK, DK>(p, m0, n0))
+      epilogue_regs<Cfg, CK, DK>(p, w, lane, m0, n0, acc);
+    else
+      epilogue_lds<Cfg, CK, DK>(p, (float*)smem, w, lane, m0, n0, acc);
   }
 }
 
@@ -850,7 +1025,7 @@ __global__ void __launch_bounds__(Cfg::kThreads, 1) gemm_direct(const GemmParams
 #pragma unroll
       for (int j = 0; j < Cfg::RN; ++j) {
         const RowK b = frag_b_coord<Cfg>(w, lane, j, kk);
-        const int n = min(n0 + b.row, p.N - 1);
+        const int n = min(n0 + perm_n<Cfg>(b.row), p.N - 1);   // N-permuted rows
         const int k = kt * BK + b.k;
         const _Float16* src = B + (int64_t)n * p.ldb + k;
         const int valid = p.K - k;
@@ -865,7 +1040,10 @@ __global__ void __launch_bounds__(Cfg::kThreads, 1) gemm_direct(const GemmParams
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
     }
   }
-  epilogue<Cfg, CK, DK>(p, w, lane, m0, n0, acc);
+  if (register_epilogue_ok<Cfg, CK, DK>(p, m0, n0))
+    epilogue_regs<Cfg, CK, DK>(p, w, lane, m0, n0, acc);
+  else
+    epilogue_any<Cfg, CK, DK>(p, w, lane, m0, n0, acc);
 }
 
 // ---------------------------------------------------------------------------

@@ -16,6 +16,7 @@ struct GemmParams {
   int lda, ldb, ldc, ldd;
   int tiles_m, tiles_n, group_m;
   int d_vec;   // 1: D rows take aligned 4-element vector stores (base and ldd)
+  int c_vec;   // 1: C rows take aligned 4-element vector loads (base and ldc)
   const void* A;
   const void* B;
   const void* C;

@@ -16,6 +16,13 @@
 //    and KSUB times along BK (the repeat modes of the TiledMMA page, section
 //    "输入扩大以后，后两个 mode 怎样工作", and the register reuse of the
 //    simple-GEMM page §2.4);
+//  * the N direction carries a tile permutation (TiledMMA page, section "用
+//    Layout 改变 M 方向的坐标顺序", applied to N): repeat j of atom column c
+//    of a wave's tile is physical column RN*c + j of that tile, so each lane's
+//    RN accumulators of one row are adjacent columns and D is written in
+//    RN-element vectors.  B's rows are permuted the same way when they are
+//    fetched (global row P(r) goes to LDS row r), so LDS and the fragment
+//    reads are unchanged;
 //  * operand (row, k) of lane/value comes from the atom's TV layout
 //    (mfma_atoms.hpp), composed with the LDS tile layout below, the role the
 //    route page ("ldmatrix 怎样对上 MMA 的寄存器") gives F o right_inverse(R)
@@ -74,9 +81,9 @@ struct TileCfg {
                 "fragment distance 1, or 2 with 4+ sub-steps per wave");
   static_assert(KSUB % WAVES_K == 0 && KSUB_W % 2 == 0,
                 "each K-group takes an even number of the stage's sub-steps");
-  static_assert(WAVES_K == 1 || ((RM * RN) % WAVES_K == 0 &&
+  static_assert(WAVES_K == 1 || (RM % WAVES_K == 0 &&
                                  kRedBytes <= kStages * 2 * (BM + BN) * BK),
-                "split-K: blocks divide over the K-groups, partials fit in the stages");
+                "split-K: row blocks divide over the K-groups, partials fit in the stages");
   static_assert((kStages == 2 || kStages == 3) && kStages * 2 * (BM + BN) * BK <= 160 * 1024,
                 "two or three stages within the 160 KB of LDS");
   static_assert(kWaves * kEpiRows * 32 * WTN * 4 <= 4 * (BM + BN) * BK,
@@ -235,22 +242,34 @@ MFL_HD constexpr RowK frag_b_coord(int w, int lane, int j, int kk) {
   return RowK{wave_n<Cfg>(w) * Cfg::WTN + j * Cfg::kAtomN + b.row, sub_k<Cfg>(w, kk) + b.k};
 }
 
-// Accumulator value v of repeat (i, j): (m, n) within the workgroup tile;
-// the same for every K-group.
+// N permutation of the block tile: logical column n = wn*WTN + 32 j + c
+// (wave, repeat, atom column; the LDS row of B) is physical column
+// wn*WTN + RN*c + j.
+template <class Cfg>
+MFL_HD constexpr int perm_n(int n) {
+  const int r = n % Cfg::WTN;
+  return n - r + Cfg::RN * (r % Cfg::kAtomN) + r / Cfg::kAtomN;
+}
+
+// Accumulator value v of repeat (i, j): physical (m, n) within the workgroup
+// tile; the same for every K-group.  For a fixed (i, v) a lane's RN repeats
+// are adjacent columns.
 template <class Cfg>
 MFL_HD constexpr RowK frag_c_coord(int w, int lane, int i, int j, int v) {
   const RowK c = atom_c_coord(lane, v);
   return RowK{wave_m<Cfg>(w) * Cfg::WTM + i * Cfg::kAtomM + c.row,
-              wave_n<Cfg>(w) * Cfg::WTN + j * Cfg::kAtomN + c.k};
+              perm_n<Cfg>(wave_n<Cfg>(w) * Cfg::WTN + j * Cfg::kAtomN + c.k)};
 }
 
 // frag_c_coord is the tiled MMA's partition_C written out in closed form.
 // Derived with the layout algebra (TiledMMA page, "partition_C 怎样把分工应用
 // 到一个 Tensor", with the tile permutations of "用 Layout 改变 M 方向的坐标
-// 顺序"): a BM x BN tile stored M-contiguous, divided per direction by the
-// permutation (32, WAVES, R):(1, 32R, 32) -- wave w takes R adjacent atom
-// blocks instead of every WAVES-th one -- then by the 32x32 atom, composed
-// with the atom's C TV layout and split over the wave grid.  Thread lane +
+// 顺序"): a BM x BN tile stored M-contiguous, divided per direction by a
+// permutation -- M: (32, WAVES_M, RM):(1, 32 RM, 32), wave wm takes RM
+// adjacent atom blocks instead of every WAVES_M-th one; N: (32, WAVES_N,
+// RN):(RN, 32 RN, 1), the same wave-contiguous blocks with the repeats
+// interleaved column by column -- then by the 32x32 atom, composed with the
+// atom's C TV layout and split over the wave grid.  Thread lane +
 // 64 w's view is thr(t) + val(v + 16 (i + RM j)).  Every thread's base and
 // thread 0's values are compared; with the atom layout separable (asserted
 // above) that covers every (thread, value).
@@ -262,7 +281,7 @@ constexpr bool frag_c_is_partition_c() {
   C.open_mode();
   C.push_leaf(Cfg::BN, Cfg::BM);
   const int64_t pm_s[3] = {32, Cfg::WAVES_M, Cfg::RM}, pm_d[3] = {1, 32 * Cfg::RM, 32};
-  const int64_t pn_s[3] = {32, Cfg::WAVES_N, Cfg::RN}, pn_d[3] = {1, 32 * Cfg::RN, 32};
+  const int64_t pn_s[3] = {32, Cfg::WAVES_N, Cfg::RN}, pn_d[3] = {Cfg::RN, 32 * Cfg::RN, 1};
   const Layout tile[2] = {make_flat(3, pm_s, pm_d), make_flat(3, pn_s, pn_d)};
   const CPartition p =
       partition_c(C, tile, atom_c_tv(), 32, 32, Cfg::WAVES_M, Cfg::WAVES_N);

@@ -309,12 +309,14 @@ def test_error_codes():
 @pytest.mark.parametrize("algo", sorted(KERNEL_TILES))
 def test_kernel_accumulators_are_partition_c(algo):
     """The kernels' accumulator coordinates are partition_C of the block tile
-    for the 32x32x16 atom, with wave-contiguous repeats: tile permutation
-    (32, W, R):(1, 32R, 32) per direction.  partition_C selects (lane, wm,
+    for the 32x32x16 atom with tile permutations: M (32, WM, RM):(1, 32RM, 32)
+    (wave-contiguous repeats), N (32, WN, RN):(RN, 32RN, 1) (the same, with a
+    lane's repeats on adjacent columns for vector stores).  A
+    lane's RN accumulators of a row are adjacent columns.  partition_C selects (lane, wm,
     wn) only, so every K-group of a split-K tile holds the same view."""
     BM, BN, BK, WM, WN, WK = KERNEL_TILES[algo]
     RM, RN = BM // WM // 32, BN // WN // 32
-    tile = (F(((32, WM, RM), (1, 32 * RM, 32))), F(((32, WN, RN), (1, 32 * RN, 32))))
+    tile = (F(((32, WM, RM), (1, 32 * RM, 32))), F(((32, WN, RN), (RN, 32 * RN, 1))))
     c = F(((BM, BN), (1, BM)))
     thr, val = mfl.layout_partition_c(c, _mfma_tv("f32_32x32x16_f16", "C"), (32, 32),
                                       (WM, WN), tile=tile)

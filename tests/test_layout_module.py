@@ -196,10 +196,38 @@ def test_fragment_coords_follow_the_atom_layout(algo):
         for i in range(RM):
             for j in range(RN):
                 for v in range(16):
+                    # the N permutation: repeat j of atom column n is column RN*n + j
                     m, n = L.mfma_c_coord(op, lane, v)
                     assert tuple(fc[t, s]) == (wm * (BM // WM) + 32 * i + m,
-                                               wn * (BN // WN) + 32 * j + n)
+                                               wn * (BN // WN) + RN * n + j)
                     s += 1
+
+
+def _perm_n(n, WTN, RN):
+    """Logical column (wave, repeat, atom column) -> physical column."""
+    w, r = divmod(n, WTN)
+    return w * WTN + RN * (r % 32) + r // 32
+
+
+@pytest.mark.parametrize("algo", sorted(KERNEL_TILES))
+def test_output_columns_are_the_permuted_b_rows(algo):
+    """Each lane's accumulator column for repeat j is the B row it multiplies
+    (lane % 32 of the fragment for repeat j), through the N permutation that
+    the B fetch applies: LDS row r holds global row perm(r).  A transposed or
+    unpermuted pairing fails this for every lane but the first."""
+    BM, BN, BK, WM, WN, WK = KERNEL_TILES[algo]
+    RM, RN, KW = BM // WM // 32, BN // WN // 32, BK // 16 // WK
+    fb = mfl.fragment_coords(algo, "B")            # (T, KW*RN*8, 2): LDS rows
+    fc = mfl.fragment_coords(algo, "C")            # (T, RM*RN*16, 2): physical
+    for t in range(fb.shape[0]):
+        lane = t % 64
+        for j in range(RN):
+            brow = fb[t, (0 * RN + j) * 8, 0]      # kk = 0, repeat j, value 0
+            for i in range(RM):
+                for v in range(16):
+                    col = fc[t, (i * RN + j) * 16 + v, 1]
+                    assert col == _perm_n(brow, BN // WN, RN), (algo, t, j)
+    assert sorted({_perm_n(n, BN // WN, RN) for n in range(BN)}) == list(range(BN))
 
 
 @pytest.mark.parametrize("algo", sorted(KERNEL_TILES))
