@@ -151,6 +151,12 @@ int mfl_fragment_coords(int32_t algo, int32_t operand, int32_t* out, int64_t cap
 int mfl_lds_tile_offsets(int32_t algo, int32_t operand, int32_t* out, int64_t cap,
                          int32_t* outer, int32_t* inner);
 
+/* The back-to-back GEMM's K order (mfl_chain.h): out[p] = N1 column (0..31
+ * within a 32-wide chunk) of the first product's accumulator that feeds K
+ * position p of the second product's operand, derived at compile time from
+ * the 32x32x16 atom's accumulator and operand TV layouts.  Pure host code. */
+int mfl_chain_k_perm(int32_t* out);
+
 /* Workgroup -> output tile order the kernels use for a grid of
  * tiles_m x tiles_n tiles (XCD-aware grouping, band height group_m):
  * tm[b], tn[b] for every workgroup id b < tiles_m*tiles_n.  Pure host code. */

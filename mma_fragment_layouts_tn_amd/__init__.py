@@ -49,6 +49,7 @@ ERRORS = {
     -4: "MFL_E_UNSUPPORTED", -5: "MFL_E_LAUNCH", -6: "MFL_E_ALGO_CASE",
     -7: "MFL_E_MISALIGNED", -8: "MFL_E_ALIAS", -9: "MFL_E_TOO_LARGE",
 }
+ERR = {v.replace("MFL_E_", "").replace("MFL_", ""): k for k, v in ERRORS.items()}
 
 
 class GemmDtypes(ctypes.Structure):
@@ -80,6 +81,10 @@ def _load() -> ctypes.CDLL:
     lib.gemm_tn_plan.restype = ctypes.c_int
     lib.gemm_strerror.argtypes = [ctypes.c_int]
     lib.gemm_strerror.restype = cp
+    lib.gemm_tn_chain.argtypes = [i64] * 5 + [vp, i64, i64] * 4 + [i32, vp]
+    lib.gemm_tn_chain.restype = ctypes.c_int
+    lib.gemm_tn_chain_validate.argtypes = [i64] * 5 + [vp, i64, i64] * 4 + [i32]
+    lib.gemm_tn_chain_validate.restype = ctypes.c_int
     lib.mfl_kernel_info.argtypes = [i32, GemmDtypes] + [P(i32)] * 6
     lib.mfl_kernel_info.restype = ctypes.c_int
     for name in ("mfl_layout_size", "mfl_layout_cosize"):
@@ -110,6 +115,8 @@ def _load() -> ctypes.CDLL:
     lib.mfl_fragment_coords.restype = ctypes.c_int
     lib.mfl_lds_tile_offsets.argtypes = [i32, i32, vp, i64, P(i32), P(i32)]
     lib.mfl_lds_tile_offsets.restype = ctypes.c_int
+    lib.mfl_chain_k_perm.argtypes = [vp]
+    lib.mfl_chain_k_perm.restype = ctypes.c_int
     lib.mfl_tile_order.argtypes = [i32, i32, i32, vp, vp]
     lib.mfl_tile_order.restype = ctypes.c_int
     lib.mfl_probe_mfma.argtypes = [i32, vp, vp, vp, vp, vp]
@@ -214,6 +221,64 @@ def gemm_tn(A: torch.Tensor, B: torch.Tensor, C: Optional[torch.Tensor] = None,
         stream = torch.cuda.current_stream(A.device).cuda_stream
     rc = gemm_tn_raw(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb,
                      None if C is None else C.data_ptr(), ldc, D.data_ptr(), ldd, dt, stream)
+    _check(rc)
+    return D
+
+
+# ------------------------------------------------------- back-to-back GEMM
+def gemm_chain_raw(batch, M, N1, N2, K, A, lda, sa, B, ldb, sb, W, ldw, sw, D, ldd, sd,
+                   d_dtype: int, stream: int) -> int:
+    """Direct call of gemm_tn_chain with integer pointers; returns the code."""
+    return _lib.gemm_tn_chain(batch, M, N1, N2, K, A, lda, sa, B, ldb, sb, W, ldw, sw, D, ldd,
+                              sd, d_dtype, stream)
+
+
+def gemm_chain_validate(batch, M, N1, N2, K, A, lda, sa, B, ldb, sb, W, ldw, sw, D, ldd, sd,
+                        d_dtype: int) -> int:
+    return _lib.gemm_tn_chain_validate(batch, M, N1, N2, K, A, lda, sa, B, ldb, sb, W, ldw, sw,
+                                       D, ldd, sd, d_dtype)
+
+
+def _rows_view(X: torch.Tensor, name: str):
+    """(batch, rows, cols, ld, batch stride) of a 2-D or 3-D view whose rows
+    are contiguous."""
+    if X.dim() == 2:
+        X = X.unsqueeze(0)
+    if X.dim() != 3:
+        raise ValueError(f"{name} must be 2-D or 3-D")
+    bt, r, c = X.shape
+    if c > 1 and X.stride(2) != 1:
+        raise ValueError(f"{name} rows must be contiguous")
+    ld = max(X.stride(1), max(c, 1)) if r > 1 else max(c, 1)
+    sb = X.stride(0) if bt > 1 else 0
+    return bt, r, c, ld, sb
+
+
+def gemm_chain(A: torch.Tensor, B: torch.Tensor, W: torch.Tensor,
+               out_dtype: torch.dtype = torch.float16, stream=None) -> torch.Tensor:
+    """D = rne16(A @ B.T) @ W.T per batch on the GPU.  A (batch,M,K),
+    B (batch,N1,K), W (batch,N2,N1), fp16 with contiguous rows (2-D views are
+    one batch; a batch of 1 broadcasts).  Returns D (batch,M,N2)."""
+    for X in (A, B, W):
+        if X.dtype != torch.float16:
+            raise TypeError("A, B and W must be float16")
+        if not X.is_cuda:
+            raise ValueError("A, B and W must be device tensors (no CPU path)")
+    ba, M, K, lda, sa = _rows_view(A, "A")
+    bb, N1, K2, ldb, sb = _rows_view(B, "B")
+    bw, N2, N1w, ldw, sw = _rows_view(W, "W")
+    if K2 != K or N1w != N1:
+        raise ValueError("A, B and W disagree on K or N1")
+    batch = max(ba, bb, bw)
+    if any(x not in (1, batch) for x in (ba, bb, bw)):
+        raise ValueError("batch sizes disagree")
+    D = torch.empty((batch, M, N2), dtype=out_dtype, device=A.device)
+    dk = _kind(D)
+    if stream is None:
+        stream = torch.cuda.current_stream(A.device).cuda_stream
+    rc = gemm_chain_raw(batch, M, N1, N2, K, A.data_ptr(), lda, sa, B.data_ptr(), ldb, sb,
+                        W.data_ptr(), ldw, sw, D.data_ptr(), max(N2, 1), M * max(N2, 1), dk,
+                        stream)
     _check(rc)
     return D
 
@@ -358,6 +423,14 @@ def lds_tile_offsets(algo: str, operand: str) -> np.ndarray:
     out = np.empty((r.value, k.value), dtype=np.int32)
     _lay_check(_lib.mfl_lds_tile_offsets(algo_code(algo), opnd, out.ctypes.data, out.size,
                                          ctypes.byref(r), ctypes.byref(k)), algo)
+    return out
+
+
+def chain_k_perm() -> np.ndarray:
+    """pi of the back-to-back GEMM: K position p of the second product over a
+    32-wide N1 chunk -> N1 column of the first accumulator."""
+    out = np.empty(32, dtype=np.int32)
+    _lay_check(_lib.mfl_chain_k_perm(out.ctypes.data), "chain_k_perm")
     return out
 
 

@@ -9,7 +9,9 @@
 #include <string>
 
 #include "../../include/mfl_gemm.h"
+#include "../../include/mfl_chain.h"
 #include "../../include/mfl_layout.h"
+#include "chain.hpp"
 #include "gemm_launch.hpp"
 #include "gemm_tile.hpp"
 #include "layout.hpp"
@@ -393,6 +395,31 @@ int frag_coords(int operand, int32_t* out, int64_t cap, int32_t* threads, int32_
 
 }  // namespace
 
+// back-to-back GEMM: argument checks shared by launch and validate
+int chain_check(int64_t batch, int64_t M, int64_t N1, int64_t N2, int64_t K, const void* A,
+                int64_t lda, int64_t sa, const void* B, int64_t ldb, int64_t sb, const void* W,
+                int64_t ldw, int64_t sw, const void* D, int64_t ldd, int64_t sd, int32_t dk) {
+  if (batch < 0 || M < 0 || N1 < 0 || N2 < 0 || K < 0) return MFL_E_NEGATIVE_DIM;
+  if (K != 32 && K != 64 && K != 128 && K != 256) return MFL_E_UNSUPPORTED;
+  if (dk != MFL_F16 && dk != MFL_F32) return MFL_E_UNSUPPORTED;
+  const int64_t one = 1;
+  if (lda < K || ldb < K || ldw < (N1 > one ? N1 : one) || ldd < (N2 > one ? N2 : one))
+    return MFL_E_LEADING_DIM;
+  if (sa < 0 || sb < 0 || sw < 0 || sd < 0) return MFL_E_LEADING_DIM;
+  if (batch > 1 && M > 0 && N2 > 0 && sd < M * ldd) return MFL_E_ALIAS;
+  const bool work = batch > 0 && M > 0 && N2 > 0;
+  if (work && !D) return MFL_E_NULL_POINTER;
+  if (work && N1 > 0 && (!A || !B || !W)) return MFL_E_NULL_POINTER;
+  if (((uintptr_t)A & 1) || ((uintptr_t)B & 1) || ((uintptr_t)W & 1)) return MFL_E_MISALIGNED;
+  if (D && ((uintptr_t)D % (uintptr_t)elem_size(dk))) return MFL_E_MISALIGNED;
+  if (M > INT_MAX / 2 || N1 > INT_MAX / 2 || N2 > INT_MAX / 2 || batch > INT_MAX)
+    return MFL_E_TOO_LARGE;
+  const int64_t tiles = batch * ((M + mfl::chain::BM - 1) / mfl::chain::BM) *
+                        ((N2 + mfl::chain::BN - 1) / mfl::chain::BN);
+  if (tiles > INT_MAX) return MFL_E_TOO_LARGE;
+  return MFL_OK;
+}
+
 extern "C" {
 
 int gemm_tn_validate(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
@@ -660,6 +687,14 @@ int mfl_lds_tile_offsets(int32_t algo, int32_t operand, int32_t* out, int64_t ca
   }
 }
 
+int mfl_chain_k_perm(int32_t* out) {
+  constexpr mfl::ChainPerm pi = mfl::chain_k_perm();
+  static_assert(pi.ok, "accumulator -> operand map");
+  if (!out) return mfl::kLayoutBadIndex;
+  for (int p = 0; p < 32; ++p) out[p] = pi.n1[p];
+  return 0;
+}
+
 int mfl_tile_order(int32_t tiles_m, int32_t tiles_n, int32_t group_m, int32_t* tm, int32_t* tn) {
   if (tiles_m <= 0 || tiles_n <= 0 || group_m <= 0 || !tm || !tn) return mfl::kLayoutBadIndex;
   const int nb = tiles_m * tiles_n;
@@ -682,6 +717,54 @@ int mfl_fragment_coords(int32_t algo, int32_t operand, int32_t* out, int64_t cap
     case mfl::kAlgoLdsSplitK: return frag_coords<mfl::CfgLdsSplitK>(operand, out, cap, threads, slots);
     default: return mfl::kLayoutBadIndex;
   }
+}
+
+int gemm_tn_chain_validate(int64_t batch, int64_t M, int64_t N1, int64_t N2, int64_t K,
+                           const void* A, int64_t lda, int64_t stride_a, const void* B,
+                           int64_t ldb, int64_t stride_b, const void* W, int64_t ldw,
+                           int64_t stride_w, const void* D, int64_t ldd, int64_t stride_d,
+                           int32_t d_dtype) {
+  return chain_check(batch, M, N1, N2, K, A, lda, stride_a, B, ldb, stride_b, W, ldw, stride_w,
+                     D, ldd, stride_d, d_dtype);
+}
+
+int gemm_tn_chain(int64_t batch, int64_t M, int64_t N1, int64_t N2, int64_t K, const void* A,
+                  int64_t lda, int64_t stride_a, const void* B, int64_t ldb, int64_t stride_b,
+                  const void* W, int64_t ldw, int64_t stride_w, void* D, int64_t ldd,
+                  int64_t stride_d, int32_t d_dtype, void* stream) {
+  const int rc = chain_check(batch, M, N1, N2, K, A, lda, stride_a, B, ldb, stride_b, W, ldw,
+                             stride_w, D, ldd, stride_d, d_dtype);
+  if (rc != MFL_OK) return rc;
+  if (batch == 0 || M == 0 || N2 == 0) return MFL_OK;
+  const void* fn = mfl::chain_symbol((int)K, d_dtype);
+  if (!fn) return MFL_E_UNSUPPORTED;
+  mfl::ChainParams p{};
+  p.batch = (int)batch;
+  p.M = (int)M;
+  p.N1 = (int)N1;
+  p.N2 = (int)N2;
+  p.lda = lda;
+  p.ldb = ldb;
+  p.ldw = ldw;
+  p.ldd = ldd;
+  p.sa = stride_a;
+  p.sb = stride_b;
+  p.sw = stride_w;
+  p.sd = stride_d;
+  p.tiles_m = (int)(batch * ((M + mfl::chain::BM - 1) / mfl::chain::BM));
+  p.tiles_n = (int)((N2 + mfl::chain::BN - 1) / mfl::chain::BN);
+  p.group_m = 8;
+  p.d_vec = ((uintptr_t)D % (uintptr_t)(4 * elem_size(d_dtype)) == 0) && (ldd % 4 == 0) &&
+            (stride_d % 4 == 0);
+  p.A = A;
+  p.B = B;
+  p.W = W;
+  p.D = D;
+  void* args[] = {(void*)&p};
+  const int64_t nb = (int64_t)p.tiles_m * p.tiles_n;
+  const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)nb), dim3(mfl::chain::THREADS), args, 0,
+                                       (hipStream_t)stream);
+  return e == hipSuccess ? MFL_OK : MFL_E_LAUNCH;
 }
 
 }  // extern "C"

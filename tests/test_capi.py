@@ -125,3 +125,64 @@ def test_binding_rejects_cpu_tensors():
     a = torch.zeros(4, 4, dtype=torch.float16)
     with pytest.raises(ValueError):
         mfl.gemm_tn(a, a)
+
+
+# ------------------------------------------------------- back-to-back GEMM
+def _cv(batch=2, M=100, N1=300, N2=128, K=128, A=P, lda=None, sa=None, B=P, ldb=None, sb=None,
+        W=P, ldw=None, sw=None, D=P, ldd=None, sd=None, d=mfl.F16):
+    lda = K if lda is None else lda
+    ldb = K if ldb is None else ldb
+    ldw = max(N1, 1) if ldw is None else ldw
+    ldd = max(N2, 1) if ldd is None else ldd
+    sa = M * lda if sa is None else sa
+    sb = N1 * ldb if sb is None else sb
+    sw = N2 * ldw if sw is None else sw
+    sd = M * ldd if sd is None else sd
+    return mfl.gemm_chain_validate(batch, M, N1, N2, K, A, lda, sa, B, ldb, sb, W, ldw, sw,
+                                   D, ldd, sd, d)
+
+
+def test_chain_validation():
+    assert _cv() == 0
+    assert _cv(d=mfl.F32) == 0
+    for K in (32, 64, 128, 256):
+        assert _cv(K=K) == 0
+    assert _cv(N1=0) == 0                          # D = 0
+    assert _cv(batch=0, D=None) == 0
+    assert _cv(sa=0, sb=0, sw=0) == 0              # shared operands
+    assert _cv(M=-1) == mfl.ERR["NEGATIVE_DIM"]
+    for K in (0, 16, 96, 512):
+        assert _cv(K=K) == mfl.ERR["UNSUPPORTED"], K
+    assert _cv(d=0) == mfl.ERR["UNSUPPORTED"]
+    assert _cv(lda=100) == mfl.ERR["LEADING_DIM"]
+    assert _cv(ldw=299) == mfl.ERR["LEADING_DIM"]
+    assert _cv(ldd=127) == mfl.ERR["LEADING_DIM"]
+    assert _cv(sb=-1) == mfl.ERR["LEADING_DIM"]
+    assert _cv(sd=100 * 128 - 1) == mfl.ERR["ALIAS"]   # D batches overlap
+    assert _cv(D=None) == mfl.ERR["NULL_POINTER"]
+    assert _cv(W=None) == mfl.ERR["NULL_POINTER"]
+    assert _cv(A=P + 1) == mfl.ERR["MISALIGNED"]
+    assert _cv(D=P + 2, d=mfl.F32) == mfl.ERR["MISALIGNED"]
+
+
+def test_chain_perm_is_derived_from_the_atoms():
+    """The N1 order the kernel stores W in: position p = 16 kc + 8 h + v of
+    the second product's K is column 8 (2 kc + v / 4) + 4 h + v % 4 of the
+    first accumulator (closed form from the 32x32x16 maps of the oracle)."""
+    from oracle import layout as OL
+    op = "f32_32x32x16_f16"
+    pi = {}
+    for lane in range(64):
+        row, k0 = OL.mfma_ab_coord(op, lane, 0)
+        for kc in range(2):
+            for v in range(8):
+                m_c, n_c = OL.mfma_c_coord(op, lane, 8 * kc + v)
+                # transposed first product: accumulator row = n1, column = m
+                assert n_c == row
+                pi.setdefault(16 * kc + k0 + v, set()).add(m_c)
+    assert all(len(s) == 1 for s in pi.values()) and len(pi) == 32
+    got = [next(iter(pi[p])) for p in range(32)]
+    assert got == [8 * (2 * (p // 16) + (p % 8) // 4) + 4 * ((p % 16) // 8) + p % 4
+                   for p in range(32)]
+    assert sorted(got) == list(range(32))
+    assert mfl.chain_k_perm().tolist() == got          # the kernel's compile-time map

@@ -1,0 +1,159 @@
+"""Back-to-back GEMM on the GPU (gemm_tn_chain through the C ABI) against
+the oracle chain (oracle/chain.py): D_b = rne16(A_b B_b^T) W_b^T.
+
+* integer inputs: bit-exact (S stays exact in fp16, D in fp32; fp16 D is
+  the nearest-even rounding of the exact D);
+* random inputs: every element within the bound ``chain_tolerance`` derives
+  from fp32 summation and the two roundings of S (fp16 D: plus one rounding);
+* the attention-shaped workload at full size, sampled rows of every batch;
+* ragged M, N1 and N2, N1 not a multiple of the 32-wide chunk, N1 = 0,
+  padded rows, shared (stride 0) operands, guard canaries after every buffer.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mma_fragment_layouts_tn_amd as mfl
+import workloads as W
+from gpu_helpers import GUARD, Guarded, out_buffer, say
+from oracle import chain as CH
+from oracle import fp16
+
+pytestmark = pytest.mark.gpu
+
+
+def run_chain(x: W.ChainInputs, d: str, share=(False, False, False)):
+    """Upload, call gemm_tn_chain, download.  share[i]: operand i (A, B, W)
+    is passed with batch stride 0 (its batch 0 serves every batch)."""
+    w = x.w
+    say(f"[gpu] chain {w.name} batch={w.batch} M={w.M} N1={w.N1} N2={w.N2} K={w.K} d={d} "
+        f"share={share} int={x.integer}")
+    bufs = []
+    args = []
+    for X, sh in zip((x.A, x.B, x.W), share):
+        g = Guarded(X[:1] if sh else X)
+        bufs.append(g)
+        args += [g.ptr, X.shape[2], 0 if sh else X.shape[1] * X.shape[2]]
+    ldd = max(w.N2, 1)
+    Dt = out_buffer(w.batch * w.M, ldd, d)
+    dk = mfl.F16 if d == "f16" else mfl.F32
+    rc = mfl.gemm_chain_raw(w.batch, w.M, w.N1, w.N2, w.K, *args, Dt.data_ptr(), ldd,
+                            w.M * ldd, dk, torch.cuda.current_stream().cuda_stream)
+    assert rc == 0, mfl.strerror(rc)
+    torch.cuda.synchronize()
+    n = w.batch * w.M * ldd
+    raw = Dt.cpu()
+    if d == "f16":
+        D = raw[:n].numpy().view(np.float16).astype(np.float64)
+    else:
+        D = raw[:n].numpy().view(np.float32).astype(np.float64)
+    guard_ok = torch.equal(raw[n:], out_buffer(0, 0, d, dev="cpu")[:GUARD]) if GUARD else True
+    checks = {"D guard": guard_ok, "inputs unchanged": all(g.unchanged() for g in bufs)}
+    return D.reshape(w.batch, w.M, ldd)[:, :, :w.N2], checks
+
+
+def oracle_chain(x: W.ChainInputs, share=(False, False, False), with_s=False):
+    w = x.w
+    ops = []
+    for X, sh in zip((x.A, x.B, x.W), share):
+        ops += [X, X.shape[2], 0 if sh else X.shape[1] * X.shape[2]]
+    return CH.chain_f64(w.batch, w.M, w.N1, w.N2, w.K, *ops, with_s=with_s)
+
+
+def _logical(X, cols):
+    return X[:, :, :cols].astype(np.float64)
+
+
+SHAPES = [  # batch, M, N1, N2, K
+    (1, 32, 32, 32, 32), (1, 256, 64, 128, 64), (2, 300, 100, 130, 128),
+    (3, 257, 33, 129, 256), (1, 1, 1, 1, 32), (2, 512, 1000, 64, 128), (1, 70, 31, 200, 64),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("d", ["f32", "f16"])
+def test_integer_bit_exact(shape, d):
+    bt, M, N1, N2, K = shape
+    w = W.ChainWorkload("int", bt, M, N1, N2, K, d=d, dist="int", seed=sum(shape),
+                        lda=K + 8, ldw=N1 + 3)
+    x = W.make_chain_inputs(w)
+    D, checks = run_chain(x, d)
+    assert all(checks.values()), checks
+    ref = oracle_chain(x)
+    want = fp16.rne16_array(ref) if d == "f16" else ref
+    bad = np.argwhere(D != want)
+    assert bad.size == 0, (shape, d, bad[:5], D[tuple(bad[0])], want[tuple(bad[0])])
+
+
+def test_n1_zero_gives_zero():
+    w = W.ChainWorkload("n1zero", 2, 40, 0, 70, 64, d="f32", dist="int", seed=3)
+    x = W.make_chain_inputs(w)
+    D, checks = run_chain(x, "f32")
+    assert all(checks.values()), checks
+    assert (D == 0).all()
+
+
+@pytest.mark.parametrize("share", [(True, False, False), (False, True, True), (True, True, True)])
+def test_shared_operands(share):
+    w = W.ChainWorkload("share", 3, 130, 96, 100, 128, d="f32", dist="int", seed=5)
+    x = W.make_chain_inputs(w)
+    D, checks = run_chain(x, "f32", share)
+    assert all(checks.values()), checks
+    assert np.array_equal(D, oracle_chain(x, share))
+
+
+def _float_bound(x, S, P, d, D_ref):
+    w = x.w
+    tol = np.stack([CH.chain_tolerance(_logical(x.A[b:b + 1], w.K)[0],
+                                       _logical(x.B[b:b + 1], w.K)[0],
+                                       _logical(x.W[b:b + 1], w.N1)[0], S[b], P[b])
+                    for b in range(w.batch)])
+    if d == "f16":
+        tol = tol + fp16.ulp16_array(np.abs(D_ref) + tol)
+    return tol
+
+
+@pytest.mark.parametrize("shape", [(2, 300, 200, 130, 128), (1, 256, 1024, 128, 64),
+                                   (1, 100, 77, 60, 256)])
+@pytest.mark.parametrize("d", ["f32", "f16"])
+def test_float_within_derived_bound(shape, d):
+    bt, M, N1, N2, K = shape
+    w = W.ChainWorkload("float", bt, M, N1, N2, K, d=d, dist="unif", seed=sum(shape) + 1)
+    x = W.make_chain_inputs(w)
+    D, checks = run_chain(x, d)
+    assert all(checks.values()), checks
+    ref, S, P = oracle_chain(x, with_s=True)
+    want = fp16.rne16_array(ref) if d == "f16" else ref
+    tol = _float_bound(x, S, P, d, ref)
+    err = np.abs(D - want)
+    assert np.isfinite(D).all()
+    assert (err <= tol).all(), (shape, d, float((err - tol).max()))
+    say(f"[gpu] chain float {shape} {d}: max err {err.max():.3g}, max bound {tol.max():.3g}, "
+        f"max |D| {np.abs(ref).max():.3g}")
+
+
+@pytest.mark.parametrize("integer", [False, True])
+def test_named_workload_sampled(integer):
+    """The attention-shaped workload at full size, in the launch the bench
+    times: rows (first, last, tile seams and random ones) of every batch
+    checked against the oracle on those rows."""
+    w = W.CHAIN_WORKLOADS["chain_b32_2048x2048_k128_n128"]
+    if integer:
+        w = w.twin()
+    x = W.make_chain_inputs(w)
+    D, checks = run_chain(x, w.d)
+    assert all(checks.values()), checks
+    assert np.isfinite(D).all()
+    rng = np.random.default_rng(w.seed)
+    rows = sorted({0, 1, 255, 256, w.M - 1, *rng.integers(0, w.M, 12).tolist()})
+    for b in range(w.batch):
+        sub = W.ChainInputs(W.ChainWorkload("rows", 1, len(rows), w.N1, w.N2, w.K, d=w.d),
+                            x.A[b:b + 1, rows], x.B[b:b + 1], x.W[b:b + 1], x.integer)
+        ref, S, P = oracle_chain(sub, with_s=True)
+        want = fp16.rne16_array(ref) if w.d == "f16" else ref
+        got = D[b:b + 1, rows]
+        if integer:
+            assert np.array_equal(got, want), b
+        else:
+            tol = _float_bound(sub, S, P, w.d, ref)
+            assert (np.abs(got - want) <= tol).all(), b

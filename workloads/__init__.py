@@ -196,3 +196,80 @@ def sample_indices(M: int, N: int, n_random: int, seed: int, tile: int = 128,
         ms_set.add(p)
     arr = np.array(sorted(ms_set), dtype=np.int64).reshape(-1, 2)
     return arr[:, 0].copy(), arr[:, 1].copy()
+
+
+# --------------------------------------------------------- back-to-back GEMM
+@dataclass(frozen=True)
+class ChainWorkload:
+    """D_b = rne16(A_b B_b^T) W_b^T per batch b: A (M,K), B (N1,K), W (N2,N1),
+    stored as 3-D arrays (batch, rows, ld) with contiguous rows and padding
+    (fp16 NaN) past the logical columns when ld exceeds them."""
+    name: str
+    batch: int
+    M: int
+    N1: int
+    N2: int
+    K: int
+    d: str = "f16"
+    dist: str = "unif"
+    seed: int = 0
+    twin_seed: Optional[int] = None
+    lda: Optional[int] = None
+    ldb: Optional[int] = None
+    ldw: Optional[int] = None
+    note: str = ""
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.batch * self.M * self.N1 * (self.K + self.N2)
+
+    def algorithmic_bytes(self) -> int:
+        """A, B and W read once, D written once."""
+        e = 2 if self.d == "f16" else 4
+        return self.batch * (2 * (self.M * self.K + self.N1 * self.K + self.N2 * self.N1)
+                             + e * self.M * self.N2)
+
+    def twin(self) -> "ChainWorkload":
+        return replace(self, name=self.name + "_int", dist="int",
+                       seed=self.twin_seed if self.twin_seed is not None else self.seed + 100)
+
+
+@dataclass
+class ChainInputs:
+    w: ChainWorkload
+    A: np.ndarray   # (batch, M, lda) fp16
+    B: np.ndarray   # (batch, N1, ldb)
+    W: np.ndarray   # (batch, N2, ldw)
+    integer: bool
+
+
+def make_chain_inputs(w: ChainWorkload) -> ChainInputs:
+    """Draw order A, B, W (each (batch, rows, cols) in C order); "int" draws
+    from {-2..2} for A and B and {-1, 0, 1} for W so that S stays exact in
+    fp16 and D in fp32 (and in fp16 where |D| <= 2048)."""
+    rng = np.random.default_rng(w.seed)
+
+    def draw(shape, ld, lo_hi=(-2, 2)):
+        if w.dist == "int":
+            v = rng.integers(lo_hi[0], lo_hi[1] + 1, size=shape).astype(np.float16)
+        else:
+            v = _draw(rng, w.dist, shape).astype(np.float16)
+        if ld == shape[2]:
+            return v
+        out = np.full(shape[:2] + (ld,), F16_NAN, dtype=np.float16)
+        out[:, :, :shape[2]] = v
+        return out
+
+    A = draw((w.batch, w.M, w.K), w.lda or w.K)
+    B = draw((w.batch, w.N1, w.K), w.ldb or w.K)
+    W = draw((w.batch, w.N2, w.N1), w.ldw or max(w.N1, 1), (-1, 1))
+    return ChainInputs(w, A, B, W, integer=(w.dist == "int"))
+
+
+CHAIN_WORKLOADS = {
+    "chain_b32_2048x2048_k128_n128": ChainWorkload(
+        "chain_b32_2048x2048_k128_n128", 32, 2048, 2048, 128, 128, d="f16", seed=7,
+        twin_seed=107,
+        note="attention-shaped: 32 batch x heads, sequence 2048 for queries and keys, "
+             "head dimension 128 for both products, fp16 out"),
+}
