@@ -11,6 +11,10 @@ per-launch kernel time from HIP events on the launch stream, the roofline
 entry of the GEMM kernel (MFMA bound, dense fp16 peak of the chip), the
 shader clock the chip holds under sustained load with the peak scaled to it,
 and the float64 CPU oracle timed on a bounded row sample of the same workload.
+
+``--workload chain_b32_2048x2048_k128_n128`` measures the back-to-back GEMM
+(D = rne16(A B^T) W^T per batch, one kernel launch per step) the same way,
+counting 2 batch M N1 (K + N2) FLOP per step.
 """
 from __future__ import annotations
 
@@ -30,17 +34,19 @@ METRIC = "TFLOP/s for fp16 TN GEMM at 4096³ (fp32 acc) and % of dense FP16 MFMA
 KERNEL_SOURCES = ["mma_fragment_layouts_tn_amd/csrc/gemm_kernels.hpp",
                   "mma_fragment_layouts_tn_amd/csrc/gemm_tile.hpp",
                   "mma_fragment_layouts_tn_amd/csrc/gemm_launch.hpp"]
+CHAIN_SOURCES = ["mma_fragment_layouts_tn_amd/csrc/chain.hpp",
+                 "mma_fragment_layouts_tn_amd/csrc/gemm_tile.hpp"]
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=None) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources or KERNEL_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload: str, algo: str):
+def load_traffic(workload: str, algo: str, sources=None):
     """HBM bytes per launch measured with rocprofv3 counters (committed under
     profiles/), or None when absent or taken on a different kernel source."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}_{algo}.json")
@@ -48,7 +54,7 @@ def load_traffic(workload: str, algo: str):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_hash") != kernel_source_hash():
+    if rec.get("source_hash") != kernel_source_hash(sources):
         return None
     return rec.get("bytes_per_launch")
 
@@ -104,6 +110,163 @@ def cpu_baseline(w, x, target_s: float):
                       f"float64 loop incl. fp16 decode, {cores} threads)"}
 
 
+def time_steps(step, stream, args):
+    """W untimed steps, then K back-to-back launches on the launch stream,
+    bracketed by synchronize and by one pair of HIP events recorded on that
+    stream (events between launches would serialise them and distort the
+    time); then a short pass with an event pair per launch for the spread.
+    Returns (wall ms per step, event ms per launch, per-launch ms array)."""
+    import numpy as np
+    import torch
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    kern_ms = ev0.elapsed_time(ev1) / args.steps          # average launch duration
+    nper = min(20, args.steps)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(nper)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(nper)]
+    for i in range(nper):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    per = np.array([st.elapsed_time(en) for st, en in zip(starts, ends)])   # ms
+    print(f"[bench] avg launch {kern_ms:.4f} ms (events over {args.steps} launches); "
+          f"wall/step {ms_per_step:.4f} ms; single-launch median {np.median(per):.4f} "
+          f"min {per.min():.4f} p90 {np.percentile(per, 90):.4f}", file=sys.stderr, flush=True)
+    return ms_per_step, kern_ms, per
+
+
+def cpu_baseline_chain(w, x, target_s: float):
+    """The float64 oracle chain, as it stands, on whole batches of the
+    workload: as many as a one-batch calibration says fit in target_s."""
+    from oracle import chain as CH
+    from oracle import gemm as G
+    cores = G.max_threads()
+
+    def run(nb):
+        CH.chain_f64(nb, w.M, w.N1, w.N2, w.K, x.A, x.A.shape[2], x.A.shape[1] * x.A.shape[2],
+                     x.B, x.B.shape[2], x.B.shape[1] * x.B.shape[2],
+                     x.W, x.W.shape[2], x.W.shape[1] * x.W.shape[2])
+
+    t0 = time.perf_counter()
+    run(1)
+    t_cal = time.perf_counter() - t0
+    nb = max(1, min(w.batch, int(target_s / max(t_cal, 1e-3))))
+    t0 = time.perf_counter()
+    run(nb)
+    t = time.perf_counter() - t0
+    flops = 2.0 * nb * w.M * w.N1 * (w.K + w.N2)
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{nb} of the {w.batch} batches of the {w.M}x{w.N1}x{w.K} / "
+                      f"{w.M}x{w.N2}x{w.N1} chain ({flops / 1e9:.1f} GFLOP in {t:.2f} s, "
+                      f"float64 loops incl. fp16 decode and the rounding of S, "
+                      f"{cores} threads)"}
+
+
+def main_chain(args) -> int:
+    import numpy as np
+    import torch
+
+    import mma_fragment_layouts_tn_amd as mfl
+    import workloads as W
+
+    w = W.CHAIN_WORKLOADS[args.workload]
+    x = W.make_chain_inputs(w)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    A, B, Wt = (torch.from_numpy(np.ascontiguousarray(t)).to(dev) for t in (x.A, x.B, x.W))
+    dk = mfl.F16 if w.d == "f16" else mfl.F32
+    D = torch.empty((w.batch, w.M, w.N2), dtype=torch.float16 if w.d == "f16" else torch.float32,
+                    device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+    args_c = (w.batch, w.M, w.N1, w.N2, w.K,
+              A.data_ptr(), x.A.shape[2], x.A.shape[1] * x.A.shape[2],
+              B.data_ptr(), x.B.shape[2], x.B.shape[1] * x.B.shape[2],
+              Wt.data_ptr(), x.W.shape[2], x.W.shape[1] * x.W.shape[2],
+              D.data_ptr(), w.N2, w.M * w.N2, dk)
+    rc = mfl.gemm_chain_validate(*args_c[:14], D.data_ptr(), w.N2, w.M * w.N2, dk)
+    if rc != 0:
+        print(f"invalid arguments: {mfl.strerror(rc)}", file=sys.stderr)
+        return 1
+    copy_src = copy_dst = None
+    if args.copy_mib:
+        copy_src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
+        copy_dst = torch.empty_like(copy_src)
+
+    def step():
+        r = mfl.gemm_chain_raw(*args_c, sptr)
+        if r != 0:
+            raise RuntimeError(mfl.strerror(r))
+        if copy_dst is not None:
+            copy_dst.copy_(copy_src)
+
+    print(f"[bench] {w.name} back-to-back GEMM batch={w.batch} M={w.M} N1={w.N1} N2={w.N2} "
+          f"K={w.K} warmup={args.warmup} steps={args.steps}", file=sys.stderr, flush=True)
+    ms_per_step, kern_ms, per = time_steps(step, stream, args)
+    flops = float(w.flops)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+    sclk = None
+    if args.clock_seconds > 0:
+        sclk = sustained_clock(step, torch.cuda.synchronize, args.clock_seconds)
+        print(f"[bench] shader clock under sustained load: {sclk} MHz", file=sys.stderr, flush=True)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "M": w.M, "N1": w.N1, "N2": w.N2,
+                   "K": w.K, "a": "f16 K-contiguous", "b": "f16 K-contiguous",
+                   "w": "f16 N1-contiguous", "d": w.d, "accumulate": "f32",
+                   "intermediate": "S rounded once to f16",
+                   "kernel": "gemm_chain 256x128 tile, N1 chunks of 32"},
+        "pct_of_peak": round(100.0 * value / PEAK_FP16_DENSE_TFLOPS, 2),
+        "kernel_ms": {"avg_back_to_back": round(kern_ms, 5),
+                      "single_median": round(float(np.median(per)), 5),
+                      "single_min": round(float(per.min()), 5),
+                      "single_p90": round(float(np.percentile(per, 90)), 5)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_FP16_DENSE_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_FP16_DENSE_TFLOPS, 4),
+                     "traffic": load_traffic(w.name, "chain", CHAIN_SOURCES)},
+        "cpu_baseline": None,
+        "kernel_source_hash": kernel_source_hash(CHAIN_SOURCES),
+    }
+    if sclk:
+        adj = PEAK_FP16_DENSE_TFLOPS * sclk / 2400.0
+        out["clock"] = {"sclk_mhz_sustained": sclk, "peak_at_sclk": round(adj, 1),
+                        "pct_of_peak_at_sclk": round(100.0 * value / adj, 2),
+                        "how": f"rocm-smi during {args.clock_seconds:g} s of back-to-back steps"}
+    if args.copy_mib:
+        out["config"]["copy_mib_per_step"] = args.copy_mib
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a batch sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline_chain(w, x, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -138,6 +301,8 @@ def main() -> int:
     import mma_fragment_layouts_tn_amd as mfl
     import workloads as W
 
+    if args.workload in W.CHAIN_WORKLOADS:
+        return main_chain(args)
     w = W.WORKLOADS[args.workload]
     x = W.make_inputs(w)
     dev = torch.device("cuda", 0)
@@ -178,40 +343,10 @@ def main() -> int:
     print(f"[bench] {w.name} algo={algo_name} fetch A:{mfl.FETCH_NAMES[fetch_a]} "
           f"B:{mfl.FETCH_NAMES[fetch_b]} tile={info['bm']}x{info['bn']}x{info['bk']} "
           f"warmup={args.warmup} steps={args.steps}", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    # Timed region: K back-to-back launches on the launch stream, bracketed
-    # by synchronize and by one pair of HIP events recorded on that stream
-    # (events between launches would serialise them and distort the time).
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for i in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
+    ms_per_step, kern_ms, per = time_steps(step, stream, args)
     flops = float(w.flops)
     value = flops / (ms_per_step * 1e-3) / 1e12
-    kern_ms = ev0.elapsed_time(ev1) / args.steps          # average launch duration
     achieved = flops / (kern_ms * 1e-3) / 1e12
-    # a second, short pass with an event pair per launch gives the spread
-    nper = min(20, args.steps)
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(nper)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(nper)]
-    for i in range(nper):
-        starts[i].record(stream)
-        step()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])   # ms
-    print(f"[bench] avg launch {kern_ms:.4f} ms (events over {args.steps} launches); "
-          f"wall/step {ms_per_step:.4f} ms; single-launch median {np.median(per):.4f} "
-          f"min {per.min():.4f} p90 {np.percentile(per, 90):.4f}", file=sys.stderr, flush=True)
 
     sclk = None
     if args.clock_seconds > 0:
