@@ -52,6 +52,20 @@ int gemm_tn_chain_validate(int64_t batch, int64_t M, int64_t N1, int64_t N2, int
                            const void* W, int64_t ldw, int64_t stride_w,
                            const void* D, int64_t ldd, int64_t stride_d, int32_t d_dtype);
 
+/* how gemm_tn_chain stages B and W for these arguments: the same checks,
+ * then *staging = MFL_CHAIN_STAGE_DMA (direct global-to-LDS loads: N1 a
+ * multiple of 32, B and W 16-byte aligned with ldb, ldw, stride_b, stride_w
+ * multiples of 8) or MFL_CHAIN_STAGE_REGS (through registers, any layout);
+ * staging may be NULL.  Both give the same D. */
+#define MFL_CHAIN_STAGE_REGS 0
+#define MFL_CHAIN_STAGE_DMA 1
+int gemm_tn_chain_plan(int64_t batch, int64_t M, int64_t N1, int64_t N2, int64_t K,
+                       const void* A, int64_t lda, int64_t stride_a,
+                       const void* B, int64_t ldb, int64_t stride_b,
+                       const void* W, int64_t ldw, int64_t stride_w,
+                       const void* D, int64_t ldd, int64_t stride_d, int32_t d_dtype,
+                       int32_t* staging);
+
 #ifdef __cplusplus
 }
 #endif

@@ -85,6 +85,8 @@ def _load() -> ctypes.CDLL:
     lib.gemm_tn_chain.restype = ctypes.c_int
     lib.gemm_tn_chain_validate.argtypes = [i64] * 5 + [vp, i64, i64] * 4 + [i32]
     lib.gemm_tn_chain_validate.restype = ctypes.c_int
+    lib.gemm_tn_chain_plan.argtypes = [i64] * 5 + [vp, i64, i64] * 4 + [i32, vp]
+    lib.gemm_tn_chain_plan.restype = ctypes.c_int
     lib.mfl_kernel_info.argtypes = [i32, GemmDtypes] + [P(i32)] * 6
     lib.mfl_kernel_info.restype = ctypes.c_int
     for name in ("mfl_layout_size", "mfl_layout_cosize"):
@@ -237,6 +239,18 @@ def gemm_chain_validate(batch, M, N1, N2, K, A, lda, sa, B, ldb, sb, W, ldw, sw,
                         d_dtype: int) -> int:
     return _lib.gemm_tn_chain_validate(batch, M, N1, N2, K, A, lda, sa, B, ldb, sb, W, ldw, sw,
                                        D, ldd, sd, d_dtype)
+
+
+CHAIN_STAGING = {0: "regs", 1: "dma"}
+
+
+def gemm_chain_plan(batch, M, N1, N2, K, A, lda, sa, B, ldb, sb, W, ldw, sw, D, ldd, sd,
+                    d_dtype: int):
+    """(code, staging name) gemm_tn_chain would take for these arguments."""
+    st = ctypes.c_int32(-1)
+    rc = _lib.gemm_tn_chain_plan(batch, M, N1, N2, K, A, lda, sa, B, ldb, sb, W, ldw, sw,
+                                 D, ldd, sd, d_dtype, ctypes.byref(st))
+    return rc, CHAIN_STAGING.get(st.value)
 
 
 def _rows_view(X: torch.Tensor, name: str):

@@ -76,8 +76,8 @@ MFL_HD constexpr ChainPerm chain_k_perm() {
   return r;
 }
 
-// runs of 4 consecutive N1 columns stay together under pi, so an 8-element
-// global chunk is stored as two 8-byte pieces
+// runs of 4 consecutive N1 columns stay together under pi, so pi^-1 is
+// known from its values at the run starts
 MFL_HD constexpr bool chain_runs_of_4() {
   const ChainPerm r = chain_k_perm();
   for (int n = 0; n < 32; ++n)
@@ -92,29 +92,55 @@ static_assert(chain_runs_of_4(), "pi must keep runs of 4 N1 columns");
 // Workgroup: 4 waves, 256 rows of M (64 per wave, RM = 2 atom rows) x 128
 // columns of N2 (RN = 4 atom columns, N-permuted: repeat j of atom column c
 // is column 4 c + j, so D leaves in 4-element vectors).  N1 is consumed in
-// 32-wide chunks; the B chunk (32 x KD) and W chunk (128 x 32, pi order)
-// of chunk c+1 are loaded into registers while chunk c computes and written
-// to the other LDS stage.
+// 32-wide chunks.
+//
+// Where pi goes: LDS row r of a B chunk holds N1 row pi^-1(r) of it, so the
+// first product's accumulator value at atom row r is N1 column pi^-1(r), and
+// lane l's values 8 kc .. 8 kc + 7 become K positions 16 kc + 8 (l / 32) + v
+// = N1 columns in natural order.  W is then staged as it is in memory.
+//
+// Software pipeline: iteration c issues the second product of chunk c (its
+// P in registers) interleaved with the first product of chunk c+1, so the
+// matrix core never waits for a first product before the second can start.
+// Slot c of the LDS ring (stage c mod 3) holds B of chunk c+1 and W of chunk
+// c, the operands of iteration c; slot -1 holds B of chunk 0 for the
+// prologue.  Slot c+2 is fetched during iteration c into the stage read in
+// iteration c-1.  Fetch: direct global-to-LDS loads when B and W are 16-byte
+// aligned and N1 fills whole chunks (slot c+2 may land as late as the end of
+// iteration c+1); otherwise through registers with zero fill, loaded at the
+// start of iteration c and written at its end.
 namespace chain {
-constexpr int BM = 256, BN = 128, RM = 2, RN = 4, WAVES = 4, THREADS = 256;
+constexpr int BM = 256, BN = 128, RM = 2, RN = 4, WAVES = 4, THREADS = 256, NST = 3;
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+using lds_t = __attribute__((address_space(3))) void*;
 
 // B chunk tile: 32 rows x KD halves, 16-byte chunks XOR-swizzled as the GEMM
 // tiles (16 consecutive rows at one chunk land on distinct bank groups)
 template <int KD>
+MFL_HD constexpr int b_swz(int row) {
+  return KD / 8 >= 16 ? (row & 15) : swz<KD / 8>(row);
+}
+template <int KD>
 __device__ __forceinline__ int b_off(int row, int k) {
-  constexpr int CH = KD / 8;
-  const int s = CH >= 16 ? (row & 15) : swz<CH>(row);
-  return row * KD + (((k >> 3) ^ s) << 3) + (k & 7);
+  return row * KD + (((k >> 3) ^ b_swz<KD>(row)) << 3) + (k & 7);
 }
 
-// W chunk tile: 128 rows x 32 halves (positions p in pi order), the four
+// W chunk tile: 128 rows x 32 halves (N1 in natural order), the four
 // 16-byte chunks of a row XOR-swizzled by (row >> 2) & 3
-__device__ __forceinline__ int w_off(int row, int p) {
-  return row * 32 + (((p >> 3) ^ ((row >> 2) & 3)) << 3) + (p & 7);
+MFL_HD constexpr int w_swz(int row) { return (row >> 2) & 3; }
+__device__ __forceinline__ int w_off(int row, int n) {
+  return row * 32 + (((n >> 3) ^ w_swz(row)) << 3) + (n & 7);
 }
+
+// the N2 column held by W's LDS row r (the N permutation of the tile)
+__device__ __forceinline__ int w_col(int r) { return RN * (r % 32) + r / 32; }
+
+template <bool V>
+struct BoolC {
+  static constexpr bool value = V;
+};
 
 __device__ __forceinline__ uint4 load16(const _Float16* p) {
   uint4 v;
@@ -122,37 +148,49 @@ __device__ __forceinline__ uint4 load16(const _Float16* p) {
   return v;
 }
 
-__device__ __forceinline__ uint4 load8_valid(const _Float16* p, int valid) {
-  if (valid >= 8) return load16(p);
+// n (1..7) leading halves of p, the rest zero
+__device__ __forceinline__ uint4 load_partial(const _Float16* p, int n) {
   union {
     uint4 u;
     _Float16 h[8];
   } r;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) r.h[e] = e < valid ? p[e] : (_Float16)0.0f;
+  for (int e = 0; e < 8; ++e) r.h[e] = e < n ? p[e] : (_Float16)0.0f;
   return r.u;
+}
+
+// LDS reads and writes of this wave done, then the workgroup barrier (no
+// memory fence: direct-to-LDS loads still in flight are waited for by count)
+__device__ __forceinline__ void barrier() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));   // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+}
+
+// wait until at most VM vector-memory operations of this wave are in flight
+template <int VM>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt has 6 bits");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | (((VM >> 4) & 3) << 14) | (7 << 4) | (15 << 8));
 }
 }  // namespace chain
 
-template <int KD, int DK>
+template <int KD, int DK, bool DMA>
 __global__ void __launch_bounds__(chain::THREADS, 1) gemm_chain(const ChainParams p) {
   using namespace chain;
   static_assert(KD == 32 || KD == 64 || KD == 128 || KD == 256, "K is 32, 64, 128 or 256");
-  constexpr int KSUB = KD / 16;
+  constexpr int KSUB = KD / 16, CH = KD / 8;
   constexpr int BSTAGE = 32 * KD, WSTAGE = BN * 32, STAGE = BSTAGE + WSTAGE;   // halves
-  constexpr int BCH = 32 * KD / 8, WCH = BN * 4;                              // 16-byte chunks
-  constexpr int BPT = (BCH + THREADS - 1) / THREADS, WPT = WCH / THREADS;     // per thread
-  static_assert(WCH % THREADS == 0, "W chunk divides over the threads");
-  __shared__ __attribute__((aligned(1024))) _Float16 smem[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) _Float16 smem[NST * STAGE];
   constexpr ChainPerm kPi = chain_k_perm();
-  // pi^-1 at a run start n (a multiple of 4): a select over the table's
-  // compile-time entries, no indexed memory
-  auto pi_pos = [&](int n) {
-    int r = kPi.pos[0];
+  // pi^-1 of an LDS row: runs of 4 keep their order, the run start is a
+  // select over the table's compile-time entries (no indexed memory)
+  auto pi_inv = [&](int r) {
+    const int r0 = r & ~3;
+    int q = kPi.pos[0];
 #pragma unroll
     for (int e = 4; e < 32; e += 4)
-      if (n == e) r = kPi.pos[e];
-    return r;
+      if (r0 == e) q = kPi.pos[e];
+    return q + (r & 3);
   };
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -164,6 +202,7 @@ __global__ void __launch_bounds__(chain::THREADS, 1) gemm_chain(const ChainParam
   const _Float16* A = (const _Float16*)p.A + (int64_t)b * p.sa;
   const _Float16* B = (const _Float16*)p.B + (int64_t)b * p.sb;
   const _Float16* Wm = (const _Float16*)p.W + (int64_t)b * p.sw;
+  const int nch = (p.N1 + 31) / 32;
 
   // this wave's A rows as the second operand of the first product:
   // fragment (i, kk) of lane l: row m0 + 64 w + 32 i + l % 32, k = 16 kk + 8 (l / 32)
@@ -179,46 +218,125 @@ __global__ void __launch_bounds__(chain::THREADS, 1) gemm_chain(const ChainParam
     }
   }
 
-  // staging: thread's 16-byte chunks of the B chunk (row r, k chunk q) and of
-  // the W chunk (LDS row r = 32 j + c holds N2 column n0 + 4 c + j; N1 piece q)
-  uint4 rb[BPT], rw[WPT];
-  auto load_chunk = [&](int c) {
-    const int n1b = 32 * c;
+  // ---- staging of slot s: B of chunk s+1 and W of chunk s, when they exist
+  // DMA: one instruction moves 64 lanes x SZ bytes into consecutive LDS bytes;
+  // each lane fetches the element its LDS bytes stand for
+  constexpr int SZB = KD >= 64 ? 16 : 4;
+  constexpr int NB = 64 * KD / (64 * SZB) / WAVES, NW = 64 * BN / 1024 / WAVES;
+  static_assert(NB >= 1 && NW >= 1, "every wave issues B and W loads");
+  // registers: 16-byte chunks q = tid + t * THREADS of each tile
+  constexpr int BCH = 32 * CH, WCH = BN * 4;
+  constexpr int BPT = (BCH + THREADS - 1) / THREADS, WPT = WCH / THREADS;
+  static_assert(WCH % THREADS == 0, "W chunks divide over the threads");
+  constexpr int NBI = DMA ? NB : BPT, NWI = DMA ? NW : WPT;
+  int64_t boff[NBI], woff[NWI];   // element offsets within chunk 0
+  int brow[NBI], wn1[NWI];        // (registers) N1 row / column within a chunk
+  uint4 rb[DMA ? 1 : BPT], rw[DMA ? 1 : WPT];
+  if constexpr (DMA) {
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int byte = (w * NB + i) * 64 * SZB + SZB * lane;
+      const int r = byte / (2 * KD), rb_ = byte % (2 * KD);
+      const int k = 8 * ((rb_ / 16) ^ b_swz<KD>(r)) + (rb_ % 16) / 2;
+      brow[i] = pi_inv(r);
+      boff[i] = (int64_t)brow[i] * p.ldb + k;
+    }
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      const int byte = (w * NW + i) * 1024 + 16 * lane;
+      const int r = byte / 64, q = (byte % 64) / 16;
+      const int n2 = min(n0 + w_col(r), p.N2 - 1);
+      wn1[i] = 8 * (q ^ w_swz(r));
+      woff[i] = (int64_t)n2 * p.ldw + wn1[i];
+    }
+  } else {
 #pragma unroll
     for (int t = 0; t < BPT; ++t) {
-      const int q = tid + t * THREADS;
-      if (q < BCH) {
-        const int row = q / (KD / 8), kq = q % (KD / 8);
-        const int n1 = n1b + row;
-        rb[t] = n1 < p.N1 ? load16(B + (int64_t)n1 * p.ldb + 8 * kq) : make_uint4(0, 0, 0, 0);
-      }
+      const int q = min(tid + t * THREADS, BCH - 1), r = q / CH;
+      brow[t] = pi_inv(r);
+      boff[t] = 8 * (q % CH);
     }
 #pragma unroll
     for (int t = 0; t < WPT; ++t) {
-      const int q = tid + t * THREADS, row = q / 4, kq = q % 4;
-      const int n2 = min(n0 + RN * (row % 32) + row / 32, p.N2 - 1);
-      const int n1 = n1b + 8 * kq;
-      rw[t] = n1 < p.N1 ? load8_valid(Wm + (int64_t)n2 * p.ldw + n1, p.N1 - n1)
-                        : make_uint4(0, 0, 0, 0);
+      const int q = tid + t * THREADS, r = q / 4;
+      const int n2 = min(n0 + w_col(r), p.N2 - 1);
+      wn1[t] = 8 * (q % 4);
+      woff[t] = (int64_t)n2 * p.ldw + wn1[t];
+    }
+  }
+  auto stage_of = [](int slot) { return (slot + NST) % NST; };
+  // issue the loads of slot s (DMA: straight into its stage)
+  auto issue = [&](int s) {
+    _Float16* st = smem + stage_of(s) * STAGE;
+    const int cb = s + 1, cw = s;
+    if (cb < nch) {
+      if constexpr (DMA) {
+        const _Float16* base = B + (int64_t)(32 * cb) * p.ldb;
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+          const void* g = base + boff[i];
+          const lds_t l = (lds_t)(st + (w * NB + i) * 32 * SZB);
+          if constexpr (SZB == 16)
+            __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+          else
+            __builtin_amdgcn_global_load_lds(g, l, 4, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < BPT; ++t) {
+          const int n1 = min(32 * cb + brow[t], p.N1 - 1);   // zeroed when written
+          rb[t] = load16(B + (int64_t)n1 * p.ldb + boff[t]);
+        }
+      }
+    }
+    if (cw >= 0 && cw < nch) {
+      if constexpr (DMA) {
+        const _Float16* base = Wm + 32 * cw;
+#pragma unroll
+        for (int i = 0; i < NW; ++i)
+          __builtin_amdgcn_global_load_lds((const void*)(base + woff[i]),
+                                           (lds_t)(st + BSTAGE + (w * NW + i) * 512), 16, 0, 0);
+      } else {
+#pragma unroll
+        for (int t = 0; t < WPT; ++t)
+          if (32 * cw + wn1[t] + 8 <= p.N1) rw[t] = load16(Wm + 32 * cw + woff[t]);
+      }
     }
   };
-  auto store_chunk = [&](int s) {
-    _Float16* sb = smem + s * STAGE;
-    _Float16* sw = sb + BSTAGE;
+  // registers: write slot s to its stage, zero beyond N1
+  auto stash = [&](int s) {
+    if constexpr (!DMA) {
+      _Float16* st = smem + stage_of(s) * STAGE;
+      const int cb = s + 1, cw = s;
+      if (cb < nch) {
 #pragma unroll
-    for (int t = 0; t < BPT; ++t) {
-      const int q = tid + t * THREADS;
-      if (q < BCH) {
-        const int row = q / (KD / 8), kq = q % (KD / 8);
-        *(uint4*)&sb[b_off<KD>(row, 8 * kq)] = rb[t];
+        for (int t = 0; t < BPT; ++t) {
+          const int q = tid + t * THREADS;
+          if (BCH % THREADS == 0 || q < BCH) {
+            const uint4 v = 32 * cb + brow[t] < p.N1 ? rb[t] : make_uint4(0, 0, 0, 0);
+            *(uint4*)&st[b_off<KD>(q / CH, (int)boff[t])] = v;
+          }
+        }
+      }
+      if (cw >= 0 && cw < nch) {
+#pragma unroll
+        for (int t = 0; t < WPT; ++t) {
+          const int q = tid + t * THREADS, left = p.N1 - 32 * cw - wn1[t];
+          uint4 v = rw[t];
+          if (left < 8)
+            v = left > 0 ? load_partial(Wm + 32 * cw + woff[t], left) : make_uint4(0, 0, 0, 0);
+          *(uint4*)&st[BSTAGE + w_off(q / 4, wn1[t])] = v;
+        }
       }
     }
-#pragma unroll
-    for (int t = 0; t < WPT; ++t) {
-      const int q = tid + t * THREADS, row = q / 4, kq = q % 4;
-      // N1 columns 8 kq .. 8 kq + 3 and 8 kq + 4 .. + 7 go to their pi positions
-      *(uint2*)&sw[w_off(row, pi_pos(8 * kq))] = make_uint2(rw[t].x, rw[t].y);
-      *(uint2*)&sw[w_off(row, pi_pos(8 * kq + 4))] = make_uint2(rw[t].z, rw[t].w);
+  };
+  // DMA: wait until every slot before s has landed (slot s may be in flight)
+  auto wait_before = [&](int s) {
+    if constexpr (DMA) {
+      const bool hb = s + 1 < nch, hw = s < nch;
+      if (hb && hw) wait_vm<NB + NW>();
+      else if (hw) wait_vm<NW>();
+      else wait_vm<0>();
     }
   };
 
@@ -230,43 +348,37 @@ __global__ void __launch_bounds__(chain::THREADS, 1) gemm_chain(const ChainParam
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  const int nch = (p.N1 + 31) / 32;
-  if (nch > 0) {
-    load_chunk(0);
-    store_chunk(0);
-    if (nch > 1) load_chunk(1);
-  }
-  __syncthreads();
-  for (int c = 0; c < nch; ++c) {
-    const int s = c & 1;
-    const _Float16* sb = smem + s * STAGE;
-    const _Float16* sw = sb + BSTAGE;
-    // first product, transposed: S^T (32 N1 x 32 M per atom row i)
-    floatx16 st[RM];
-#pragma unroll
-    for (int i = 0; i < RM; ++i)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) st[i][v] = 0.0f;
-#pragma unroll
-    for (int kk = 0; kk < KSUB; ++kk) {
-      const half8 bf = *(const half8*)&sb[b_off<KD>(al.row, 16 * kk + al.k)];
-#pragma unroll
-      for (int i = 0; i < RM; ++i)
-        st[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf, af[i][kk], st[i], 0, 0, 0);
-    }
-    // the accumulator, rounded once to fp16, is the next operand: values
-    // 8 kc .. 8 kc + 7 are K chunk kc (pi order)
-    half8 pf[RM][2];
+  // the accumulator, rounded once to fp16, is the next operand: values
+  // 8 kc .. 8 kc + 7 are K chunk kc
+  half8 pf[RM][2];
+  auto convert = [&](const floatx16 (&st)[RM]) {
 #pragma unroll
     for (int i = 0; i < RM; ++i)
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
-        for (int v = 0; v < 8; ++v) {
-          const float x = st[i][8 * kc + v];
-          pf[i][kc][v] = (_Float16)x;   // RNE
-        }
-    // second product: D += P W^T over this chunk's 32 N1 columns
+        for (int v = 0; v < 8; ++v) pf[i][kc][v] = (_Float16)st[i][8 * kc + v];   // RNE
+  };
+  // first product of the B chunk in stage sb (S^T), K sub-step kk
+  auto first_step = [&](floatx16 (&st)[RM], const _Float16* sb, int kk) {
+    const half8 bf = *(const half8*)&sb[b_off<KD>(al.row, 16 * kk + al.k)];
+#pragma unroll
+    for (int i = 0; i < RM; ++i)
+      st[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf, af[i][kk], st[i], 0, 0, 0);
+  };
+  // iteration c on slot c: per K sub-step of the first product (chunk c+1),
+  // its RM MFMAs, then G of the second product's RM x RN (chunk c).  The last
+  // chunk has no first product; it is peeled so no MFMA sits under a branch.
+  constexpr int HALF = KSUB / 2, G = (RM * RN) / HALF;
+  static_assert((RM * RN) % HALF == 0, "second-product MFMAs spread over the sub-steps");
+  auto iteration = [&](int c, auto more) {
+    const _Float16* sb = smem + stage_of(c) * STAGE;
+    const _Float16* sw = sb + BSTAGE;
+    floatx16 st[RM];
+#pragma unroll
+    for (int i = 0; i < RM; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) st[i][v] = 0.0f;
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
       half8 wf[RN];
@@ -274,14 +386,48 @@ __global__ void __launch_bounds__(chain::THREADS, 1) gemm_chain(const ChainParam
       for (int j = 0; j < RN; ++j)
         wf[j] = *(const half8*)&sw[w_off(32 * j + al.row, 16 * kc + al.k)];
 #pragma unroll
+      for (int h = 0; h < HALF; ++h) {
+        if constexpr (decltype(more)::value) first_step(st, sb, kc * HALF + h);
+#pragma unroll
+        for (int g = h * G; g < (h + 1) * G; ++g)
+          acc[g / RN][g % RN] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+              pf[g / RN][kc], wf[g % RN], acc[g / RN][g % RN], 0, 0, 0);
+      }
+    }
+    if constexpr (decltype(more)::value) convert(st);
+  };
+
+  // the whole main loop sits under this test, so on every path into it the
+  // prologue has waited for A's fragments
+  if (nch > 0) {
+    issue(-1);
+    stash(-1);
+    issue(0);
+    stash(0);
+    issue(1);
+    stash(1);
+    wait_before(1);
+    barrier();
+    {
+      floatx16 st[RM];
+#pragma unroll
       for (int i = 0; i < RM; ++i)
 #pragma unroll
-        for (int j = 0; j < RN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pf[i][kc], wf[j], acc[i][j], 0, 0, 0);
+        for (int v = 0; v < 16; ++v) st[i][v] = 0.0f;
+      const _Float16* sb = smem + stage_of(-1) * STAGE;
+#pragma unroll
+      for (int kk = 0; kk < KSUB; ++kk) first_step(st, sb, kk);
+      convert(st);
     }
-    if (c + 1 < nch) store_chunk(s ^ 1);   // stage s^1 was last read before the previous barrier
-    if (c + 2 < nch) load_chunk(c + 2);
-    __syncthreads();
+    barrier();   // slot 2 reuses the prologue's stage
+    for (int c = 0; c + 1 < nch; ++c) {
+      issue(c + 2);
+      iteration(c, BoolC<true>{});
+      stash(c + 2);
+      wait_before(c + 2);
+      barrier();
+    }
+    iteration(nch - 1, BoolC<false>{});
   }
 
   // epilogue: acc[i][j][v] of lane l is D(m0 + 64 w + 32 i + atom_c(l, v).row,
@@ -321,7 +467,8 @@ __global__ void __launch_bounds__(chain::THREADS, 1) gemm_chain(const ChainParam
     }
 }
 
-// host: kernel symbol for K and the D type (1 fp16, 2 fp32); nullptr if none
-const void* chain_symbol(int kd, int dk);
+// host: kernel symbol for K, the D type (1 fp16, 2 fp32) and the staging
+// (direct-to-LDS or through registers); nullptr if none
+const void* chain_symbol(int kd, int dk, bool dma);
 
 }  // namespace mfl

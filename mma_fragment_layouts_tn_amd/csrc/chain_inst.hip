@@ -1,16 +1,25 @@
-// Kernel instances of the back-to-back GEMM: K in {32, 64, 128, 256}, D fp16 or fp32.
+// Kernel instances of the back-to-back GEMM: K in {32, 64, 128, 256}, D fp16
+// or fp32, operands staged direct-to-LDS or through registers.
 #include <hip/hip_runtime.h>
 
 #include "chain.hpp"
 
 namespace mfl {
-const void* chain_symbol(int kd, int dk) {
+namespace {
+template <int KD>
+const void* pick(int dk, bool dma) {
+  if (dma) return dk == 1 ? (const void*)gemm_chain<KD, 1, true> : (const void*)gemm_chain<KD, 2, true>;
+  return dk == 1 ? (const void*)gemm_chain<KD, 1, false> : (const void*)gemm_chain<KD, 2, false>;
+}
+}  // namespace
+
+const void* chain_symbol(int kd, int dk, bool dma) {
   if (dk != 1 && dk != 2) return nullptr;
   switch (kd) {
-    case 32: return dk == 1 ? (const void*)gemm_chain<32, 1> : (const void*)gemm_chain<32, 2>;
-    case 64: return dk == 1 ? (const void*)gemm_chain<64, 1> : (const void*)gemm_chain<64, 2>;
-    case 128: return dk == 1 ? (const void*)gemm_chain<128, 1> : (const void*)gemm_chain<128, 2>;
-    case 256: return dk == 1 ? (const void*)gemm_chain<256, 1> : (const void*)gemm_chain<256, 2>;
+    case 32: return pick<32>(dk, dma);
+    case 64: return pick<64>(dk, dma);
+    case 128: return pick<128>(dk, dma);
+    case 256: return pick<256>(dk, dma);
     default: return nullptr;
   }
 }

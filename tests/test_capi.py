@@ -165,10 +165,39 @@ def test_chain_validation():
     assert _cv(D=P + 2, d=mfl.F32) == mfl.ERR["MISALIGNED"]
 
 
+def _cplan(**kw):
+    args = dict(batch=2, M=100, N1=256, N2=128, K=128, A=P, lda=128, sa=100 * 128, B=P, ldb=128,
+                sb=256 * 128, W=P, ldw=256, sw=128 * 256, D=P, ldd=128, sd=100 * 128, d=mfl.F16)
+    args.update(kw)
+    a = args
+    return mfl.gemm_chain_plan(a["batch"], a["M"], a["N1"], a["N2"], a["K"], a["A"], a["lda"],
+                               a["sa"], a["B"], a["ldb"], a["sb"], a["W"], a["ldw"], a["sw"],
+                               a["D"], a["ldd"], a["sd"], a["d"])
+
+
+def test_chain_staging_rule():
+    """Direct-to-LDS staging only for whole N1 chunks and 16-byte rows."""
+    assert _cplan() == (0, "dma")
+    assert _cplan(K=32) == (0, "dma")
+    assert _cplan(sa=0, sb=0, sw=0) == (0, "dma")
+    assert _cplan(N1=250, ldw=256) == (0, "regs")        # ragged last chunk
+    assert _cplan(ldw=260) == (0, "regs")                # W rows 8-byte aligned
+    assert _cplan(ldb=136) == (0, "dma")
+    assert _cplan(ldb=130) == (0, "regs")
+    assert _cplan(B=P + 8) == (0, "regs")
+    assert _cplan(W=P + 2) == (0, "regs")
+    assert _cplan(sw=128 * 256 + 4) == (0, "regs")
+    assert _cplan(sb=256 * 128 + 2) == (0, "regs")
+    assert _cplan(A=P + 2, lda=130) == (0, "dma")        # A is read through registers
+    assert _cplan(K=96)[0] == mfl.ERR["UNSUPPORTED"]
+
+
 def test_chain_perm_is_derived_from_the_atoms():
-    """The N1 order the kernel stores W in: position p = 16 kc + 8 h + v of
-    the second product's K is column 8 (2 kc + v / 4) + 4 h + v % 4 of the
-    first accumulator (closed form from the 32x32x16 maps of the oracle)."""
+    """The map behind the kernel's B row order: position p = 16 kc + 8 h + v
+    of the second product's K is accumulator row 8 (2 kc + v / 4) + 4 h +
+    v % 4 of the first (closed form from the 32x32x16 maps of the oracle); the
+    kernel puts N1 row pi^-1(r) of a chunk in LDS row r, so P arrives in
+    natural N1 order."""
     from oracle import layout as OL
     op = "f32_32x32x16_f16"
     pi = {}

@@ -21,6 +21,8 @@ from oracle import fp16
 
 pytestmark = pytest.mark.gpu
 
+STAGINGS_SEEN = set()   # (staging, K) of every launch in this module
+
 
 def run_chain(x: W.ChainInputs, d: str, share=(False, False, False)):
     """Upload, call gemm_tn_chain, download.  share[i]: operand i (A, B, W)
@@ -37,6 +39,11 @@ def run_chain(x: W.ChainInputs, d: str, share=(False, False, False)):
     ldd = max(w.N2, 1)
     Dt = out_buffer(w.batch * w.M, ldd, d)
     dk = mfl.F16 if d == "f16" else mfl.F32
+    rc, staging = mfl.gemm_chain_plan(w.batch, w.M, w.N1, w.N2, w.K, *args, Dt.data_ptr(), ldd,
+                                      w.M * ldd, dk)
+    assert rc == 0, mfl.strerror(rc)
+    say(f"[gpu]   staging {staging}")
+    STAGINGS_SEEN.add((staging, w.K))
     rc = mfl.gemm_chain_raw(w.batch, w.M, w.N1, w.N2, w.K, *args, Dt.data_ptr(), ldd,
                             w.M * ldd, dk, torch.cuda.current_stream().cuda_stream)
     assert rc == 0, mfl.strerror(rc)
@@ -67,15 +74,19 @@ def _logical(X, cols):
 SHAPES = [  # batch, M, N1, N2, K
     (1, 32, 32, 32, 32), (1, 256, 64, 128, 64), (2, 300, 100, 130, 128),
     (3, 257, 33, 129, 256), (1, 1, 1, 1, 32), (2, 512, 1000, 64, 128), (1, 70, 31, 200, 64),
+    (2, 300, 96, 130, 256), (1, 130, 160, 70, 32), (2, 256, 288, 256, 128),
 ]
 
 
 @pytest.mark.parametrize("shape", SHAPES)
 @pytest.mark.parametrize("d", ["f32", "f16"])
-def test_integer_bit_exact(shape, d):
+@pytest.mark.parametrize("rows", ["padded", "aligned"])
+def test_integer_bit_exact(shape, d, rows):
+    """padded: A and W rows off 16-byte alignment (register staging);
+    aligned: 16-byte rows, direct-to-LDS staging wherever N1 % 32 == 0."""
     bt, M, N1, N2, K = shape
-    w = W.ChainWorkload("int", bt, M, N1, N2, K, d=d, dist="int", seed=sum(shape),
-                        lda=K + 8, ldw=N1 + 3)
+    ld = dict(lda=K + 8, ldw=N1 + 3) if rows == "padded" else dict(ldw=-(-N1 // 8) * 8 or 8)
+    w = W.ChainWorkload("int", bt, M, N1, N2, K, d=d, dist="int", seed=sum(shape), **ld)
     x = W.make_chain_inputs(w)
     D, checks = run_chain(x, d)
     assert all(checks.values()), checks
@@ -157,3 +168,10 @@ def test_named_workload_sampled(integer):
         else:
             tol = _float_bound(sub, S, P, w.d, ref)
             assert (np.abs(got - want) <= tol).all(), b
+
+
+def test_both_stagings_ran_for_every_k():
+    """Collected after the cases above: each K ran through both stagings."""
+    for K in (32, 64, 128, 256):
+        for staging in ("dma", "regs"):
+            assert (staging, K) in STAGINGS_SEEN, (staging, K, sorted(STAGINGS_SEEN))
