@@ -54,8 +54,9 @@ int gemm_tn_chain_validate(int64_t batch, int64_t M, int64_t N1, int64_t N2, int
 
 /* how gemm_tn_chain stages B and W for these arguments: the same checks,
  * then *staging = MFL_CHAIN_STAGE_DMA (direct global-to-LDS loads: N1 a
- * multiple of 32, B and W 16-byte aligned with ldb, ldw, stride_b, stride_w
- * multiples of 8) or MFL_CHAIN_STAGE_REGS (through registers, any layout);
+ * multiple of the kernel's N1 chunk, 64 columns, 32 at K = 256; B and W
+ * 16-byte aligned with ldb, ldw, stride_b, stride_w multiples of 8) or
+ * MFL_CHAIN_STAGE_REGS (through registers, any layout);
  * staging may be NULL.  Both give the same D. */
 #define MFL_CHAIN_STAGE_REGS 0
 #define MFL_CHAIN_STAGE_DMA 1

@@ -420,11 +420,12 @@ int chain_check(int64_t batch, int64_t M, int64_t N1, int64_t N2, int64_t K, con
   return MFL_OK;
 }
 
-// direct-to-LDS staging: whole 32-wide N1 chunks and 16-byte aligned rows
-// of B and W in every batch
-bool chain_dma(int64_t N1, const void* B, int64_t ldb, int64_t sb, const void* W, int64_t ldw,
-               int64_t sw) {
-  return N1 % 32 == 0 && dma_ok(B, ldb) && dma_ok(W, ldw) && sb % 8 == 0 && sw % 8 == 0;
+// direct-to-LDS staging: whole N1 chunks (64 columns, 32 at K = 256) and
+// 16-byte aligned rows of B and W in every batch
+bool chain_dma(int64_t K, int64_t N1, const void* B, int64_t ldb, int64_t sb, const void* W,
+               int64_t ldw, int64_t sw) {
+  return N1 % mfl::chain::chunk_width((int)K) == 0 && dma_ok(B, ldb) && dma_ok(W, ldw) &&
+         sb % 8 == 0 && sw % 8 == 0;
 }
 
 extern "C" {
@@ -743,7 +744,7 @@ int gemm_tn_chain_plan(int64_t batch, int64_t M, int64_t N1, int64_t N2, int64_t
   const int rc = chain_check(batch, M, N1, N2, K, A, lda, stride_a, B, ldb, stride_b, W, ldw,
                              stride_w, D, ldd, stride_d, d_dtype);
   if (rc == MFL_OK && staging)
-    *staging = chain_dma(N1, B, ldb, stride_b, W, ldw, stride_w) ? MFL_CHAIN_STAGE_DMA
+    *staging = chain_dma(K, N1, B, ldb, stride_b, W, ldw, stride_w) ? MFL_CHAIN_STAGE_DMA
                                                                   : MFL_CHAIN_STAGE_REGS;
   return rc;
 }
@@ -756,7 +757,7 @@ int gemm_tn_chain(int64_t batch, int64_t M, int64_t N1, int64_t N2, int64_t K, c
                              stride_w, D, ldd, stride_d, d_dtype);
   if (rc != MFL_OK) return rc;
   if (batch == 0 || M == 0 || N2 == 0) return MFL_OK;
-  const void* fn = mfl::chain_symbol((int)K, d_dtype, chain_dma(N1, B, ldb, stride_b, W, ldw, stride_w));
+  const void* fn = mfl::chain_symbol((int)K, d_dtype, chain_dma(K, N1, B, ldb, stride_b, W, ldw, stride_w));
   if (!fn) return MFL_E_UNSUPPORTED;
   mfl::ChainParams p{};
   p.batch = (int)batch;

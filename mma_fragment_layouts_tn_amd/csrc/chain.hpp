@@ -92,12 +92,13 @@ static_assert(chain_runs_of_4(), "pi must keep runs of 4 N1 columns");
 // Workgroup: 4 waves, 256 rows of M (64 per wave, RM = 2 atom rows) x 128
 // columns of N2 (RN = 4 atom columns, N-permuted: repeat j of atom column c
 // is column 4 c + j, so D leaves in 4-element vectors).  N1 is consumed in
-// 32-wide chunks.
+// chunks of CW = 32 H columns, H blocks of 32.
 //
-// Where pi goes: LDS row r of a B chunk holds N1 row pi^-1(r) of it, so the
-// first product's accumulator value at atom row r is N1 column pi^-1(r), and
-// lane l's values 8 kc .. 8 kc + 7 become K positions 16 kc + 8 (l / 32) + v
-// = N1 columns in natural order.  W is then staged as it is in memory.
+// Where pi goes: LDS row 32 h + r of a B chunk holds N1 row 32 h + pi^-1(r)
+// of it, so the first product's accumulator value at atom row r of block h
+// is N1 column 32 h + pi^-1(r), and lane l's values 8 kc .. 8 kc + 7 of that
+// block become K positions 32 h + 16 kc + 8 (l / 32) + v = N1 columns in
+// natural order.  W is then staged as it is in memory.
 //
 // Software pipeline: iteration c issues the second product of chunk c (its
 // P in registers) interleaved with the first product of chunk c+1, so the
@@ -111,12 +112,16 @@ static_assert(chain_runs_of_4(), "pi must keep runs of 4 N1 columns");
 // start of iteration c and written at its end.
 namespace chain {
 constexpr int BM = 256, BN = 128, RM = 2, RN = 4, WAVES = 4, THREADS = 256, NST = 3;
+// N1 columns per iteration (H = CW / 32 atom blocks): 64 halves the
+// iterations' fixed costs (barrier, conversion); at K = 256 the register
+// budget keeps it at 32
+MFL_HD constexpr int chunk_width(int kd) { return kd >= 256 ? 32 : 64; }
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 using lds_t = __attribute__((address_space(3))) void*;
 
-// B chunk tile: 32 rows x KD halves, 16-byte chunks XOR-swizzled as the GEMM
+// B chunk tile: CW rows x KD halves, 16-byte chunks XOR-swizzled as the GEMM
 // tiles (16 consecutive rows at one chunk land on distinct bank groups)
 template <int KD>
 MFL_HD constexpr int b_swz(int row) {
@@ -127,11 +132,16 @@ __device__ __forceinline__ int b_off(int row, int k) {
   return row * KD + (((k >> 3) ^ b_swz<KD>(row)) << 3) + (k & 7);
 }
 
-// W chunk tile: 128 rows x 32 halves (N1 in natural order), the four
-// 16-byte chunks of a row XOR-swizzled by (row >> 2) & 3
-MFL_HD constexpr int w_swz(int row) { return (row >> 2) & 3; }
+// W chunk tile: 128 rows x CW halves (N1 in natural order), the CW / 8
+// 16-byte chunks of a row XOR-swizzled so that 16 consecutive rows at one
+// chunk fall on distinct bank groups
+template <int CW>
+MFL_HD constexpr int w_swz(int row) {
+  return CW == 32 ? (row >> 2) & 3 : (row >> 1) & 7;
+}
+template <int CW>
 __device__ __forceinline__ int w_off(int row, int n) {
-  return row * 32 + (((n >> 3) ^ w_swz(row)) << 3) + (n & 7);
+  return row * CW + (((n >> 3) ^ w_swz<CW>(row)) << 3) + (n & 7);
 }
 
 // the N2 column held by W's LDS row r (the N permutation of the tile)
@@ -179,18 +189,20 @@ __global__ void __launch_bounds__(chain::THREADS, 1) gemm_chain(const ChainParam
   using namespace chain;
   static_assert(KD == 32 || KD == 64 || KD == 128 || KD == 256, "K is 32, 64, 128 or 256");
   constexpr int KSUB = KD / 16, CH = KD / 8;
-  constexpr int BSTAGE = 32 * KD, WSTAGE = BN * 32, STAGE = BSTAGE + WSTAGE;   // halves
+  constexpr int CW = chunk_width(KD), H = CW / 32;
+  static_assert(CW == 32 || CW == 64, "chunks of 32 or 64 N1 columns");
+  constexpr int BSTAGE = CW * KD, WSTAGE = BN * CW, STAGE = BSTAGE + WSTAGE;   // halves
   __shared__ __attribute__((aligned(1024))) _Float16 smem[NST * STAGE];
   constexpr ChainPerm kPi = chain_k_perm();
   // pi^-1 of an LDS row: runs of 4 keep their order, the run start is a
   // select over the table's compile-time entries (no indexed memory)
   auto pi_inv = [&](int r) {
-    const int r0 = r & ~3;
+    const int r0 = r & 28;
     int q = kPi.pos[0];
 #pragma unroll
     for (int e = 4; e < 32; e += 4)
       if (r0 == e) q = kPi.pos[e];
-    return q + (r & 3);
+    return (r & ~31) + q + (r & 3);   // within each 32-row block
   };
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -202,7 +214,7 @@ __global__ void __launch_bounds__(chain::THREADS, 1) gemm_chain(const ChainParam
   const _Float16* A = (const _Float16*)p.A + (int64_t)b * p.sa;
   const _Float16* B = (const _Float16*)p.B + (int64_t)b * p.sb;
   const _Float16* Wm = (const _Float16*)p.W + (int64_t)b * p.sw;
-  const int nch = (p.N1 + 31) / 32;
+  const int nch = (p.N1 + CW - 1) / CW;
 
   // this wave's A rows as the second operand of the first product:
   // fragment (i, kk) of lane l: row m0 + 64 w + 32 i + l % 32, k = 16 kk + 8 (l / 32)
@@ -221,11 +233,11 @@ __global__ void __launch_bounds__(chain::THREADS, 1) gemm_chain(const ChainParam
   // ---- staging of slot s: B of chunk s+1 and W of chunk s, when they exist
   // DMA: one instruction moves 64 lanes x SZ bytes into consecutive LDS bytes;
   // each lane fetches the element its LDS bytes stand for
-  constexpr int SZB = KD >= 64 ? 16 : 4;
-  constexpr int NB = 64 * KD / (64 * SZB) / WAVES, NW = 64 * BN / 1024 / WAVES;
+  constexpr int SZB = KD * H >= 64 ? 16 : 4;
+  constexpr int NB = 2 * CW * KD / (64 * SZB) / WAVES, NW = 2 * CW * BN / 1024 / WAVES;
   static_assert(NB >= 1 && NW >= 1, "every wave issues B and W loads");
   // registers: 16-byte chunks q = tid + t * THREADS of each tile
-  constexpr int BCH = 32 * CH, WCH = BN * 4;
+  constexpr int BCH = CW * CH, WCH = BN * CW / 8;
   constexpr int BPT = (BCH + THREADS - 1) / THREADS, WPT = WCH / THREADS;
   static_assert(WCH % THREADS == 0, "W chunks divide over the threads");
   constexpr int NBI = DMA ? NB : BPT, NWI = DMA ? NW : WPT;
@@ -244,9 +256,9 @@ __global__ void __launch_bounds__(chain::THREADS, 1) gemm_chain(const ChainParam
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
       const int byte = (w * NW + i) * 1024 + 16 * lane;
-      const int r = byte / 64, q = (byte % 64) / 16;
+      const int r = byte / (2 * CW), q = (byte % (2 * CW)) / 16;
       const int n2 = min(n0 + w_col(r), p.N2 - 1);
-      wn1[i] = 8 * (q ^ w_swz(r));
+      wn1[i] = 8 * (q ^ w_swz<CW>(r));
       woff[i] = (int64_t)n2 * p.ldw + wn1[i];
     }
   } else {
@@ -258,9 +270,9 @@ __global__ void __launch_bounds__(chain::THREADS, 1) gemm_chain(const ChainParam
     }
 #pragma unroll
     for (int t = 0; t < WPT; ++t) {
-      const int q = tid + t * THREADS, r = q / 4;
+      const int q = tid + t * THREADS, r = q / (CW / 8);
       const int n2 = min(n0 + w_col(r), p.N2 - 1);
-      wn1[t] = 8 * (q % 4);
+      wn1[t] = 8 * (q % (CW / 8));
       woff[t] = (int64_t)n2 * p.ldw + wn1[t];
     }
   }
@@ -271,7 +283,7 @@ __global__ void __launch_bounds__(chain::THREADS, 1) gemm_chain(const ChainParam
     const int cb = s + 1, cw = s;
     if (cb < nch) {
       if constexpr (DMA) {
-        const _Float16* base = B + (int64_t)(32 * cb) * p.ldb;
+        const _Float16* base = B + (int64_t)(CW * cb) * p.ldb;
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
           const void* g = base + boff[i];
@@ -284,14 +296,14 @@ __global__ void __launch_bounds__(chain::THREADS, 1) gemm_chain(const ChainParam
       } else {
 #pragma unroll
         for (int t = 0; t < BPT; ++t) {
-          const int n1 = min(32 * cb + brow[t], p.N1 - 1);   // zeroed when written
+          const int n1 = min(CW * cb + brow[t], p.N1 - 1);   // zeroed when written
           rb[t] = load16(B + (int64_t)n1 * p.ldb + boff[t]);
         }
       }
     }
     if (cw >= 0 && cw < nch) {
       if constexpr (DMA) {
-        const _Float16* base = Wm + 32 * cw;
+        const _Float16* base = Wm + CW * cw;
 #pragma unroll
         for (int i = 0; i < NW; ++i)
           __builtin_amdgcn_global_load_lds((const void*)(base + woff[i]),
@@ -299,7 +311,7 @@ __global__ void __launch_bounds__(chain::THREADS, 1) gemm_chain(const ChainParam
       } else {
 #pragma unroll
         for (int t = 0; t < WPT; ++t)
-          if (32 * cw + wn1[t] + 8 <= p.N1) rw[t] = load16(Wm + 32 * cw + woff[t]);
+          if (CW * cw + wn1[t] + 8 <= p.N1) rw[t] = load16(Wm + CW * cw + woff[t]);
       }
     }
   };
@@ -313,7 +325,7 @@ __global__ void __launch_bounds__(chain::THREADS, 1) gemm_chain(const ChainParam
         for (int t = 0; t < BPT; ++t) {
           const int q = tid + t * THREADS;
           if (BCH % THREADS == 0 || q < BCH) {
-            const uint4 v = 32 * cb + brow[t] < p.N1 ? rb[t] : make_uint4(0, 0, 0, 0);
+            const uint4 v = CW * cb + brow[t] < p.N1 ? rb[t] : make_uint4(0, 0, 0, 0);
             *(uint4*)&st[b_off<KD>(q / CH, (int)boff[t])] = v;
           }
         }
@@ -321,11 +333,11 @@ __global__ void __launch_bounds__(chain::THREADS, 1) gemm_chain(const ChainParam
       if (cw >= 0 && cw < nch) {
 #pragma unroll
         for (int t = 0; t < WPT; ++t) {
-          const int q = tid + t * THREADS, left = p.N1 - 32 * cw - wn1[t];
+          const int q = tid + t * THREADS, left = p.N1 - CW * cw - wn1[t];
           uint4 v = rw[t];
           if (left < 8)
-            v = left > 0 ? load_partial(Wm + 32 * cw + woff[t], left) : make_uint4(0, 0, 0, 0);
-          *(uint4*)&st[BSTAGE + w_off(q / 4, wn1[t])] = v;
+            v = left > 0 ? load_partial(Wm + CW * cw + woff[t], left) : make_uint4(0, 0, 0, 0);
+          *(uint4*)&st[BSTAGE + w_off<CW>(q / (CW / 8), wn1[t])] = v;
         }
       }
     }
@@ -349,42 +361,50 @@ __global__ void __launch_bounds__(chain::THREADS, 1) gemm_chain(const ChainParam
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
   // the accumulator, rounded once to fp16, is the next operand: values
-  // 8 kc .. 8 kc + 7 are K chunk kc
-  half8 pf[RM][2];
-  auto convert = [&](const floatx16 (&st)[RM]) {
+  // 8 kc' .. 8 kc' + 7 of block h are K chunk kc = 2 h + kc'
+  half8 pf[RM][2 * H];
+  auto convert = [&](const floatx16 (&st)[RM][H]) {
 #pragma unroll
     for (int i = 0; i < RM; ++i)
 #pragma unroll
-      for (int kc = 0; kc < 2; ++kc)
+      for (int kc = 0; kc < 2 * H; ++kc)
 #pragma unroll
-        for (int v = 0; v < 8; ++v) pf[i][kc][v] = (_Float16)st[i][8 * kc + v];   // RNE
+        for (int v = 0; v < 8; ++v) pf[i][kc][v] = (_Float16)st[i][kc / 2][8 * (kc % 2) + v];   // RNE
   };
-  // first product of the B chunk in stage sb (S^T), K sub-step kk
-  auto first_step = [&](floatx16 (&st)[RM], const _Float16* sb, int kk) {
-    const half8 bf = *(const half8*)&sb[b_off<KD>(al.row, 16 * kk + al.k)];
+  auto zero_st = [&](floatx16 (&st)[RM][H]) {
 #pragma unroll
     for (int i = 0; i < RM; ++i)
-      st[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf, af[i][kk], st[i], 0, 0, 0);
+#pragma unroll
+      for (int h = 0; h < H; ++h)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) st[i][h][v] = 0.0f;
   };
-  // iteration c on slot c: per K sub-step of the first product (chunk c+1),
-  // its RM MFMAs, then G of the second product's RM x RN (chunk c).  The last
-  // chunk has no first product; it is peeled so no MFMA sits under a branch.
+  // first product of the B chunk in stage sb (S^T), step s: block h = s / KSUB,
+  // K sub-step kk = s % KSUB
+  auto first_step = [&](floatx16 (&st)[RM][H], const _Float16* sb, int s) {
+    const int h = s / KSUB, kk = s % KSUB;
+    const half8 bf = *(const half8*)&sb[b_off<KD>(32 * h + al.row, 16 * kk + al.k)];
+#pragma unroll
+    for (int i = 0; i < RM; ++i)
+      st[i][h] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf, af[i][kk], st[i][h], 0, 0, 0);
+  };
+  // iteration c on slot c: per K chunk kc of the second product (chunk c),
+  // HALF steps of the first product (chunk c+1), each followed by G of the
+  // second product's RM x RN MFMAs.  The last chunk has no first product; it
+  // is peeled so no MFMA sits under a branch.
   constexpr int HALF = KSUB / 2, G = (RM * RN) / HALF;
   static_assert((RM * RN) % HALF == 0, "second-product MFMAs spread over the sub-steps");
   auto iteration = [&](int c, auto more) {
     const _Float16* sb = smem + stage_of(c) * STAGE;
     const _Float16* sw = sb + BSTAGE;
-    floatx16 st[RM];
+    floatx16 st[RM][H];
+    zero_st(st);
 #pragma unroll
-    for (int i = 0; i < RM; ++i)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) st[i][v] = 0.0f;
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
+    for (int kc = 0; kc < 2 * H; ++kc) {
       half8 wf[RN];
 #pragma unroll
       for (int j = 0; j < RN; ++j)
-        wf[j] = *(const half8*)&sw[w_off(32 * j + al.row, 16 * kc + al.k)];
+        wf[j] = *(const half8*)&sw[w_off<CW>(32 * j + al.row, 16 * kc + al.k)];
 #pragma unroll
       for (int h = 0; h < HALF; ++h) {
         if constexpr (decltype(more)::value) first_step(st, sb, kc * HALF + h);
@@ -409,14 +429,11 @@ __global__ void __launch_bounds__(chain::THREADS, 1) gemm_chain(const ChainParam
     wait_before(1);
     barrier();
     {
-      floatx16 st[RM];
-#pragma unroll
-      for (int i = 0; i < RM; ++i)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) st[i][v] = 0.0f;
+      floatx16 st[RM][H];
+      zero_st(st);
       const _Float16* sb = smem + stage_of(-1) * STAGE;
 #pragma unroll
-      for (int kk = 0; kk < KSUB; ++kk) first_step(st, sb, kk);
+      for (int s1 = 0; s1 < KSUB * H; ++s1) first_step(st, sb, s1);
       convert(st);
     }
     barrier();   // slot 2 reuses the prologue's stage

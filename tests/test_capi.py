@@ -181,6 +181,8 @@ def test_chain_staging_rule():
     assert _cplan(K=32) == (0, "dma")
     assert _cplan(sa=0, sb=0, sw=0) == (0, "dma")
     assert _cplan(N1=250, ldw=256) == (0, "regs")        # ragged last chunk
+    assert _cplan(N1=96, ldw=96) == (0, "regs")          # chunks of 64 at K = 128
+    assert _cplan(N1=96, ldw=96, K=256, lda=256, ldb=256) == (0, "dma")   # 32 at K = 256
     assert _cplan(ldw=260) == (0, "regs")                # W rows 8-byte aligned
     assert _cplan(ldb=136) == (0, "dma")
     assert _cplan(ldb=130) == (0, "regs")

@@ -75,6 +75,7 @@ SHAPES = [  # batch, M, N1, N2, K
     (1, 32, 32, 32, 32), (1, 256, 64, 128, 64), (2, 300, 100, 130, 128),
     (3, 257, 33, 129, 256), (1, 1, 1, 1, 32), (2, 512, 1000, 64, 128), (1, 70, 31, 200, 64),
     (2, 300, 96, 130, 256), (1, 130, 160, 70, 32), (2, 256, 288, 256, 128),
+    (1, 130, 192, 70, 32), (2, 256, 128, 256, 128),
 ]
 
 
@@ -83,7 +84,8 @@ SHAPES = [  # batch, M, N1, N2, K
 @pytest.mark.parametrize("rows", ["padded", "aligned"])
 def test_integer_bit_exact(shape, d, rows):
     """padded: A and W rows off 16-byte alignment (register staging);
-    aligned: 16-byte rows, direct-to-LDS staging wherever N1 % 32 == 0."""
+    aligned: 16-byte rows, direct-to-LDS staging wherever N1 fills whole
+    chunks (64 columns, 32 at K = 256)."""
     bt, M, N1, N2, K = shape
     ld = dict(lda=K + 8, ldw=N1 + 3) if rows == "padded" else dict(ldw=-(-N1 // 8) * 8 or 8)
     w = W.ChainWorkload("int", bt, M, N1, N2, K, d=d, dist="int", seed=sum(shape), **ld)
