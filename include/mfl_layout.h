@@ -151,10 +151,12 @@ int mfl_fragment_coords(int32_t algo, int32_t operand, int32_t* out, int64_t cap
 int mfl_lds_tile_offsets(int32_t algo, int32_t operand, int32_t* out, int64_t cap,
                          int32_t* outer, int32_t* inner);
 
-/* The back-to-back GEMM's K order (mfl_chain.h): out[p] = N1 column (0..31
- * within a 32-wide chunk) of the first product's accumulator that feeds K
- * position p of the second product's operand, derived at compile time from
- * the 32x32x16 atom's accumulator and operand TV layouts.  Pure host code. */
+/* The back-to-back GEMM's accumulator -> operand map (mfl_chain.h): out[p]
+ * = row (0..31 within a 32-row block) of the first, transposed product's
+ * accumulator that feeds K position p of the second product's operand,
+ * derived at compile time from the 32x32x16 atom's accumulator and operand
+ * TV layouts.  The kernel stages B's rows by its inverse, so the operand
+ * arrives in natural N1 order.  Pure host code. */
 int mfl_chain_k_perm(int32_t* out);
 
 /* Workgroup -> output tile order the kernels use for a grid of

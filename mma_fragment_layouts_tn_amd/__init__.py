@@ -441,8 +441,8 @@ def lds_tile_offsets(algo: str, operand: str) -> np.ndarray:
 
 
 def chain_k_perm() -> np.ndarray:
-    """pi of the back-to-back GEMM: K position p of the second product over a
-    32-wide N1 chunk -> N1 column of the first accumulator."""
+    """pi of the back-to-back GEMM: K position p of the second product's
+    operand over a 32-row block -> row of the first (transposed) accumulator."""
     out = np.empty(32, dtype=np.int32)
     _lay_check(_lib.mfl_chain_k_perm(out.ctypes.data), "chain_k_perm")
     return out

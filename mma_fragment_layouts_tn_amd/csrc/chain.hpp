@@ -13,11 +13,12 @@
 // accumulators hold row m = l % 32 of S.  The second MMA's A operand wants
 // row m = l % 32 as well, 8 values per 16-wide K chunk.  The accumulators
 // 8 kc .. 8 kc + 7 of a lane become chunk kc of that operand as they are
-// (converted to fp16); the sum over N1 does not care about order, so W's
-// N1 axis takes the same permutation pi: K position p = 16 kc + 8 h + v of
-// the second MMA is N1 column pi(p) of the first accumulator.  pi is derived
-// below from the two atom TV layouts and checked at compile time; W is stored
-// in LDS in pi order, so every lane reads its 8 values with one 16-byte read.
+// (converted to fp16): K position p = 16 kc + 8 h + v of the second MMA is
+// row pi(p) of the first (transposed) accumulator.  pi is derived below from
+// the two atom TV layouts and checked at compile time.  The kernel absorbs it
+// in the order it stages B: LDS row r of a 32-row block holds N1 row
+// pi^-1(r), so P arrives in natural N1 order and W is staged as it lies in
+// memory, every lane reading its 8 values with one 16-byte read.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -39,15 +40,16 @@ struct ChainParams {
 };
 
 // ---------------------------------------------------------------- the pi map
-// K position p (0..31) of the second MMA over one 32-wide N1 chunk -> N1
-// column: lane l, chunk kc, value v of the operand (row atom_ab(l).row, k =
-// 16 kc + atom_ab(l).k + v) takes accumulator value 8 kc + v of the same lane,
-// which sits at (row n1, column m) = atom_c(l, 8 kc + v) of the transposed
-// first product.  Requires: the accumulator's column is the operand's row (so
-// the values stay in their lane), and every lane with the same k agrees on
-// the N1 column (pi is a function of p) and pi is a bijection.
+// K position p (0..31) of the second MMA over one 32-row block -> row of the
+// first accumulator: lane l, chunk kc, value v of the operand (row
+// atom_ab(l).row, k = 16 kc + atom_ab(l).k + v) takes accumulator value
+// 8 kc + v of the same lane, which sits at (row r, column m) =
+// atom_c(l, 8 kc + v) of the transposed first product (row r: the B row in
+// LDS row r of the block).  Requires: the accumulator's column is the
+// operand's row (so the values stay in their lane), every lane with the same
+// k agrees on the row (pi is a function of p), and pi is a bijection.
 struct ChainPerm {
-  int n1[32];     // pi
+  int n1[32];     // pi: accumulator row feeding K position p
   int pos[32];    // pi^-1
   bool ok;
 };

@@ -107,8 +107,9 @@ def test_n1_zero_gives_zero():
 
 
 @pytest.mark.parametrize("share", [(True, False, False), (False, True, True), (True, True, True)])
-def test_shared_operands(share):
-    w = W.ChainWorkload("share", 3, 130, 96, 100, 128, d="f32", dist="int", seed=5)
+@pytest.mark.parametrize("N1", [96, 128])   # register / direct-to-LDS staging at K = 128
+def test_shared_operands(share, N1):
+    w = W.ChainWorkload("share", 3, 130, N1, 100, 128, d="f32", dist="int", seed=5)
     x = W.make_chain_inputs(w)
     D, checks = run_chain(x, "f32", share)
     assert all(checks.values()), checks
@@ -127,7 +128,7 @@ def _float_bound(x, S, P, d, D_ref):
 
 
 @pytest.mark.parametrize("shape", [(2, 300, 200, 130, 128), (1, 256, 1024, 128, 64),
-                                   (1, 100, 77, 60, 256)])
+                                   (1, 100, 77, 60, 256), (2, 260, 128, 200, 256)])
 @pytest.mark.parametrize("d", ["f32", "f16"])
 def test_float_within_derived_bound(shape, d):
     bt, M, N1, N2, K = shape
