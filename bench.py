@@ -60,8 +60,9 @@ def load_traffic(workload: str, algo: str, sources=None):
 
 
 def sustained_clock(step, sync, seconds: float):
-    """Shader clock (MHz) read with rocm-smi, in a child process, while the
-    step runs back to back for `seconds`; None when rocm-smi is unavailable."""
+    """(shader clock in MHz, package power in W) read with rocm-smi, in child
+    processes, while the step runs back to back for `seconds`; None for what
+    rocm-smi does not report."""
     import re
     import subprocess
     import threading
@@ -77,6 +78,14 @@ def sustained_clock(step, sync, seconds: float):
         m = re.search(r"sclk clock level: \d+: \((\d+)Mhz\)", out)
         if m:
             found["sclk"] = int(m.group(1))
+        try:
+            out = subprocess.run(["rocm-smi", "--showpower"], capture_output=True, text=True,
+                                 timeout=20).stdout
+        except (OSError, subprocess.SubprocessError):
+            return
+        m = re.search(r"Power \(W\):\s*([0-9.]+)", out)
+        if m:
+            found["power"] = float(m.group(1))
 
     th = threading.Thread(target=sample)
     t0 = time.perf_counter()
@@ -86,7 +95,7 @@ def sustained_clock(step, sync, seconds: float):
             step()
         sync()
     th.join()
-    return found.get("sclk")
+    return found.get("sclk"), found.get("power")
 
 
 def cpu_baseline(w, x, target_s: float):
@@ -142,10 +151,23 @@ def time_steps(step, stream, args):
         ends[i].record(stream)
     torch.cuda.synchronize()
     per = np.array([st.elapsed_time(en) for st, en in zip(starts, ends)])   # ms
+    # cold caches: 512 MiB written between launches (more than the L2s and the
+    # 256 MB Infinity Cache hold), so the inputs come from HBM
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=stream.device)
+    for i in range(nper):
+        with torch.cuda.stream(stream):
+            scratch.fill_(i & 0xff)
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    cold = np.array([st.elapsed_time(en) for st, en in zip(starts, ends)])   # ms
+    del scratch
     print(f"[bench] avg launch {kern_ms:.4f} ms (events over {args.steps} launches); "
           f"wall/step {ms_per_step:.4f} ms; single-launch median {np.median(per):.4f} "
-          f"min {per.min():.4f} p90 {np.percentile(per, 90):.4f}", file=sys.stderr, flush=True)
-    return ms_per_step, kern_ms, per
+          f"min {per.min():.4f} p90 {np.percentile(per, 90):.4f}; cold-cache median "
+          f"{np.median(cold):.4f} p90 {np.percentile(cold, 90):.4f}", file=sys.stderr, flush=True)
+    return ms_per_step, kern_ms, per, cold
 
 
 def cpu_baseline_chain(w, x, target_s: float):
@@ -215,14 +237,15 @@ def main_chain(args) -> int:
 
     print(f"[bench] {w.name} back-to-back GEMM batch={w.batch} M={w.M} N1={w.N1} N2={w.N2} "
           f"K={w.K} warmup={args.warmup} steps={args.steps}", file=sys.stderr, flush=True)
-    ms_per_step, kern_ms, per = time_steps(step, stream, args)
+    ms_per_step, kern_ms, per, cold = time_steps(step, stream, args)
     flops = float(w.flops)
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (kern_ms * 1e-3) / 1e12
-    sclk = None
+    sclk = power = None
     if args.clock_seconds > 0:
-        sclk = sustained_clock(step, torch.cuda.synchronize, args.clock_seconds)
-        print(f"[bench] shader clock under sustained load: {sclk} MHz", file=sys.stderr, flush=True)
+        sclk, power = sustained_clock(step, torch.cuda.synchronize, args.clock_seconds)
+        print(f"[bench] shader clock under sustained load: {sclk} MHz, power {power} W",
+              file=sys.stderr, flush=True)
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -240,12 +263,14 @@ def main_chain(args) -> int:
                    "K": w.K, "a": "f16 K-contiguous", "b": "f16 K-contiguous",
                    "w": "f16 N1-contiguous", "d": w.d, "accumulate": "f32",
                    "intermediate": "S rounded once to f16",
-                   "kernel": "gemm_chain 256x128 tile, N1 chunks of 32"},
+                   "kernel": f"gemm_chain 256x128 tile, N1 chunks of {32 if w.K >= 256 else 64}"},
         "pct_of_peak": round(100.0 * value / PEAK_FP16_DENSE_TFLOPS, 2),
         "kernel_ms": {"avg_back_to_back": round(kern_ms, 5),
                       "single_median": round(float(np.median(per)), 5),
                       "single_min": round(float(per.min()), 5),
-                      "single_p90": round(float(np.percentile(per, 90)), 5)},
+                      "single_p90": round(float(np.percentile(per, 90)), 5),
+                      "cold_median": round(float(np.median(cold)), 5),
+                      "cold_p90": round(float(np.percentile(cold, 90)), 5)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_FP16_DENSE_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_FP16_DENSE_TFLOPS, 4),
@@ -257,6 +282,7 @@ def main_chain(args) -> int:
         adj = PEAK_FP16_DENSE_TFLOPS * sclk / 2400.0
         out["clock"] = {"sclk_mhz_sustained": sclk, "peak_at_sclk": round(adj, 1),
                         "pct_of_peak_at_sclk": round(100.0 * value / adj, 2),
+                        "power_w": power,
                         "how": f"rocm-smi during {args.clock_seconds:g} s of back-to-back steps"}
     if args.copy_mib:
         out["config"]["copy_mib_per_step"] = args.copy_mib
@@ -343,15 +369,16 @@ def main() -> int:
     print(f"[bench] {w.name} algo={algo_name} fetch A:{mfl.FETCH_NAMES[fetch_a]} "
           f"B:{mfl.FETCH_NAMES[fetch_b]} tile={info['bm']}x{info['bn']}x{info['bk']} "
           f"warmup={args.warmup} steps={args.steps}", file=sys.stderr, flush=True)
-    ms_per_step, kern_ms, per = time_steps(step, stream, args)
+    ms_per_step, kern_ms, per, cold = time_steps(step, stream, args)
     flops = float(w.flops)
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (kern_ms * 1e-3) / 1e12
 
-    sclk = None
+    sclk = power = None
     if args.clock_seconds > 0:
-        sclk = sustained_clock(step, torch.cuda.synchronize, args.clock_seconds)
-        print(f"[bench] shader clock under sustained load: {sclk} MHz", file=sys.stderr, flush=True)
+        sclk, power = sustained_clock(step, torch.cuda.synchronize, args.clock_seconds)
+        print(f"[bench] shader clock under sustained load: {sclk} MHz, power {power} W",
+              file=sys.stderr, flush=True)
 
     traffic = load_traffic(w.name, algo_name + "_" + mfl.FETCH_NAMES[fetch_a] + mfl.FETCH_NAMES[fetch_b])
     out = {
@@ -377,7 +404,9 @@ def main() -> int:
         "kernel_ms": {"avg_back_to_back": round(kern_ms, 5),
                       "single_median": round(float(np.median(per)), 5),
                       "single_min": round(float(per.min()), 5),
-                      "single_p90": round(float(np.percentile(per, 90)), 5)},
+                      "single_p90": round(float(np.percentile(per, 90)), 5),
+                      "cold_median": round(float(np.median(cold)), 5),
+                      "cold_p90": round(float(np.percentile(cold, 90)), 5)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_FP16_DENSE_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_FP16_DENSE_TFLOPS, 4),
@@ -390,6 +419,7 @@ def main() -> int:
         adj = PEAK_FP16_DENSE_TFLOPS * sclk / 2400.0
         out["clock"] = {"sclk_mhz_sustained": sclk, "peak_at_sclk": round(adj, 1),
                         "pct_of_peak_at_sclk": round(100.0 * value / adj, 2),
+                        "power_w": power,
                         "how": f"rocm-smi during {args.clock_seconds:g} s of back-to-back steps"}
     if args.copy_mib:
         out["config"]["copy_mib_per_step"] = args.copy_mib
