@@ -107,11 +107,14 @@ static_assert(chain_runs_of_4(), "pi must keep runs of 4 N1 columns");
 // matrix core never waits for a first product before the second can start.
 // Slot c of the LDS ring (stage c mod 3) holds B of chunk c+1 and W of chunk
 // c, the operands of iteration c; slot -1 holds B of chunk 0 for the
-// prologue.  Slot c+2 is fetched during iteration c into the stage read in
-// iteration c-1.  Fetch: direct global-to-LDS loads when B and W are 16-byte
-// aligned and N1 fills whole chunks (slot c+2 may land as late as the end of
-// iteration c+1); otherwise through registers with zero fill, loaded at the
-// start of iteration c and written at its end.
+// prologue.  One barrier per iteration, before the second product's last K
+// chunk: after it every wave is done with slot c-1 and can read slot c+1,
+// and the last K chunk runs on registers while the next slot's first
+// fragments are read and slot c+2 is fetched into slot c-1's stage.  Fetch:
+// direct global-to-LDS loads when B and W are 16-byte aligned and N1 fills
+// whole chunks (slot c+2 lands before the barrier of iteration c+1);
+// otherwise through registers with zero fill, loaded after the barrier of
+// iteration c and written to LDS before that of iteration c+1.
 namespace chain {
 constexpr int BM = 256, BN = 128, RM = 2, RN = 4, WAVES = 4, THREADS = 256, NST = 3;
 // N1 columns per iteration (H = CW / 32 atom blocks): 64 halves the
@@ -364,14 +367,14 @@ __global__ void __launch_bounds__(chain::THREADS, 1) gemm_chain(const ChainParam
 
   // the accumulator, rounded once to fp16, is the next operand: values
   // 8 kc' .. 8 kc' + 7 of block h are K chunk kc = 2 h + kc'
-  half8 pf[RM][2 * H];
-  auto convert = [&](const floatx16 (&st)[RM][H]) {
+  typedef half8 Frag[RM][2 * H];
+  auto convert = [&](const floatx16 (&st)[RM][H], Frag& out) {
 #pragma unroll
     for (int i = 0; i < RM; ++i)
 #pragma unroll
       for (int kc = 0; kc < 2 * H; ++kc)
 #pragma unroll
-        for (int v = 0; v < 8; ++v) pf[i][kc][v] = (_Float16)st[i][kc / 2][8 * (kc % 2) + v];   // RNE
+        for (int v = 0; v < 8; ++v) out[i][kc][v] = (_Float16)st[i][kc / 2][8 * (kc % 2) + v];   // RNE
   };
   auto zero_st = [&](floatx16 (&st)[RM][H]) {
 #pragma unroll
@@ -381,42 +384,85 @@ __global__ void __launch_bounds__(chain::THREADS, 1) gemm_chain(const ChainParam
 #pragma unroll
         for (int v = 0; v < 16; ++v) st[i][h][v] = 0.0f;
   };
-  // first product of the B chunk in stage sb (S^T), step s: block h = s / KSUB,
-  // K sub-step kk = s % KSUB
-  auto first_step = [&](floatx16 (&st)[RM][H], const _Float16* sb, int s) {
+  auto read_b = [&](const _Float16* sb, int s) {   // step s: block s / KSUB, sub-step s % KSUB
+    return *(const half8*)&sb[b_off<KD>(32 * (s / KSUB) + al.row, 16 * (s % KSUB) + al.k)];
+  };
+  auto read_w = [&](const _Float16* sw, int kc, half8 (&wf)[RN]) {
+#pragma unroll
+    for (int j = 0; j < RN; ++j)
+      wf[j] = *(const half8*)&sw[w_off<CW>(32 * j + al.row, 16 * kc + al.k)];
+  };
+  // first product of B's block s / KSUB (S^T), K sub-step s % KSUB
+  auto first_step = [&](floatx16 (&st)[RM][H], const half8& bf, int s) {
     const int h = s / KSUB, kk = s % KSUB;
-    const half8 bf = *(const half8*)&sb[b_off<KD>(32 * h + al.row, 16 * kk + al.k)];
 #pragma unroll
     for (int i = 0; i < RM; ++i)
       st[i][h] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf, af[i][kk], st[i][h], 0, 0, 0);
   };
-  // iteration c on slot c: per K chunk kc of the second product (chunk c),
-  // HALF steps of the first product (chunk c+1), each followed by G of the
-  // second product's RM x RN MFMAs.  The last chunk has no first product; it
-  // is peeled so no MFMA sits under a branch.
-  constexpr int HALF = KSUB / 2, G = (RM * RN) / HALF;
-  static_assert((RM * RN) % HALF == 0, "second-product MFMAs spread over the sub-steps");
+  auto second = [&](const Frag& pf, int kc, int g, const half8 (&wf)[RN]) {
+    acc[g / RN][g % RN] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pf[g / RN][kc], wf[g % RN],
+                                                                 acc[g / RN][g % RN], 0, 0, 0);
+  };
+
+  // Iteration c on slot c: the second product of chunk c over its 2H K
+  // chunks (P in registers) with the FS steps of the first product of chunk
+  // c+1 spread over all but the last K chunk.  P of chunk c+1 is converted
+  // before the barrier that closes the slot; after it the last K chunk runs
+  // on fragments already in registers while the first fragments of slot c+1
+  // are read and slot c+2 is fetched into the stage slot c-1 used (every wave
+  // is past it).  So the matrix core has work on both sides of the barrier.
+  constexpr int FS = KSUB * H, NPRE = (2 * H - 1) * RM * RN;
+  Frag pf, pn;
+  half8 wf0[RN], bf0;   // carried: W of the next chunk, K chunk 0; its B, step 0
   auto iteration = [&](int c, auto more) {
+    constexpr bool MORE = decltype(more)::value;
     const _Float16* sb = smem + stage_of(c) * STAGE;
     const _Float16* sw = sb + BSTAGE;
     floatx16 st[RM][H];
     zero_st(st);
+    half8 wf[RN];
 #pragma unroll
     for (int kc = 0; kc < 2 * H; ++kc) {
-      half8 wf[RN];
+      if (kc == 0) {
 #pragma unroll
-      for (int j = 0; j < RN; ++j)
-        wf[j] = *(const half8*)&sw[w_off<CW>(32 * j + al.row, 16 * kc + al.k)];
+        for (int j = 0; j < RN; ++j) wf[j] = wf0[j];
+      } else {
+        read_w(sw, kc, wf);
+      }
+      if (kc == 2 * H - 1) {
+        if constexpr (MORE) {
+          convert(st, pn);
+          stash(c + 1);          // registers: slot c+1, loaded one iteration ago
+          wait_vm<0>();          // direct-to-LDS: slot c+1 has landed
+          barrier();             // ... in every wave; slot c-1 is free
+        }
+      }
 #pragma unroll
-      for (int h = 0; h < HALF; ++h) {
-        if constexpr (decltype(more)::value) first_step(st, sb, kc * HALF + h);
+      for (int g = 0; g < RM * RN; ++g) {
+        if constexpr (MORE) {
+          if (kc < 2 * H - 1) {
 #pragma unroll
-        for (int g = h * G; g < (h + 1) * G; ++g)
-          acc[g / RN][g % RN] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-              pf[g / RN][kc], wf[g % RN], acc[g / RN][g % RN], 0, 0, 0);
+            for (int s1 = 0; s1 < FS; ++s1)
+              if (s1 * NPRE / FS == kc * RM * RN + g) first_step(st, s1 == 0 ? bf0 : read_b(sb, s1), s1);
+          } else if (g == 0) {
+            // after the barrier: the next slot's first fragments, the fetch
+            // of slot c+2 (B of chunk c+2 may not exist: its value is then
+            // stale and unused, the last iteration has no first product)
+            const _Float16* nb = smem + stage_of(c + 1) * STAGE;
+            read_w(nb + BSTAGE, 0, wf0);
+            bf0 = read_b(nb, 0);
+            issue(c + 2);
+          }
+        }
+        second(pf, kc, g, wf);
       }
     }
-    if constexpr (decltype(more)::value) convert(st);
+    if constexpr (MORE) {
+#pragma unroll
+      for (int i = 0; i < RM; ++i)
+#pragma unroll
+        for (int kc = 0; kc < 2 * H; ++kc) pf[i][kc] = pn[i][kc];
+    }
   };
 
   // the whole main loop sits under this test, so on every path into it the
@@ -426,8 +472,7 @@ __global__ void __launch_bounds__(chain::THREADS, 1) gemm_chain(const ChainParam
     stash(-1);
     issue(0);
     stash(0);
-    issue(1);
-    stash(1);
+    issue(1);                        // registers: written in iteration 0
     wait_before(1);
     barrier();
     {
@@ -435,17 +480,13 @@ __global__ void __launch_bounds__(chain::THREADS, 1) gemm_chain(const ChainParam
       zero_st(st);
       const _Float16* sb = smem + stage_of(-1) * STAGE;
 #pragma unroll
-      for (int s1 = 0; s1 < KSUB * H; ++s1) first_step(st, sb, s1);
-      convert(st);
+      for (int s1 = 0; s1 < FS; ++s1) first_step(st, read_b(sb, s1), s1);
+      convert(st, pf);
+      const _Float16* s0 = smem + stage_of(0) * STAGE;
+      read_w(s0 + BSTAGE, 0, wf0);
+      bf0 = read_b(s0, 0);           // B of chunk 1, used only if it exists
     }
-    barrier();   // slot 2 reuses the prologue's stage
-    for (int c = 0; c + 1 < nch; ++c) {
-      issue(c + 2);
-      iteration(c, BoolC<true>{});
-      stash(c + 2);
-      wait_before(c + 2);
-      barrier();
-    }
+    for (int c = 0; c + 1 < nch; ++c) iteration(c, BoolC<true>{});
     iteration(nch - 1, BoolC<false>{});
   }
 
