@@ -62,9 +62,9 @@ def load_traffic(workload: str, algo: str, sources=None):
 
 
 def sustained_clock(step, sync, seconds: float):
-    """(shader clock in MHz, package power in W) read with rocm-smi, in child
-    processes, while the step runs back to back for `seconds`; None for what
-    rocm-smi does not report."""
+    """(shader clock MHz, memory clock MHz, package power W) read with
+    rocm-smi, in child processes, while the step runs back to back for
+    `seconds`; None for what rocm-smi does not report."""
     import re
     import subprocess
     import threading
@@ -80,6 +80,9 @@ def sustained_clock(step, sync, seconds: float):
         m = re.search(r"sclk clock level: \d+: \((\d+)Mhz\)", out)
         if m:
             found["sclk"] = int(m.group(1))
+        m = re.search(r"mclk clock level: \d+: \((\d+)Mhz\)", out)
+        if m:
+            found["mclk"] = int(m.group(1))
         try:
             out = subprocess.run(["rocm-smi", "--showpower"], capture_output=True, text=True,
                                  timeout=20).stdout
@@ -97,7 +100,7 @@ def sustained_clock(step, sync, seconds: float):
             step()
         sync()
     th.join()
-    return found.get("sclk"), found.get("power")
+    return found.get("sclk"), found.get("mclk"), found.get("power")
 
 
 def cpu_baseline(w, x, target_s: float):
@@ -243,11 +246,11 @@ def main_chain(args) -> int:
     flops = float(w.flops)
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (kern_ms * 1e-3) / 1e12
-    sclk = power = None
+    sclk = mclk = power = None
     if args.clock_seconds > 0:
-        sclk, power = sustained_clock(step, torch.cuda.synchronize, args.clock_seconds)
-        print(f"[bench] shader clock under sustained load: {sclk} MHz, power {power} W",
-              file=sys.stderr, flush=True)
+        sclk, mclk, power = sustained_clock(step, torch.cuda.synchronize, args.clock_seconds)
+        print(f"[bench] under sustained load: shader clock {sclk} MHz, memory clock {mclk} MHz, "
+              f"power {power} W", file=sys.stderr, flush=True)
     out = {
         "metric": METRIC_CHAIN,
         "value": round(value, 2),
@@ -284,7 +287,7 @@ def main_chain(args) -> int:
         adj = PEAK_FP16_DENSE_TFLOPS * sclk / 2400.0
         out["clock"] = {"sclk_mhz_sustained": sclk, "peak_at_sclk": round(adj, 1),
                         "pct_of_peak_at_sclk": round(100.0 * value / adj, 2),
-                        "power_w": power,
+                        "mclk_mhz": mclk, "power_w": power,
                         "how": f"rocm-smi during {args.clock_seconds:g} s of back-to-back steps"}
     if args.copy_mib:
         out["config"]["copy_mib_per_step"] = args.copy_mib
@@ -376,11 +379,11 @@ def main() -> int:
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (kern_ms * 1e-3) / 1e12
 
-    sclk = power = None
+    sclk = mclk = power = None
     if args.clock_seconds > 0:
-        sclk, power = sustained_clock(step, torch.cuda.synchronize, args.clock_seconds)
-        print(f"[bench] shader clock under sustained load: {sclk} MHz, power {power} W",
-              file=sys.stderr, flush=True)
+        sclk, mclk, power = sustained_clock(step, torch.cuda.synchronize, args.clock_seconds)
+        print(f"[bench] under sustained load: shader clock {sclk} MHz, memory clock {mclk} MHz, "
+              f"power {power} W", file=sys.stderr, flush=True)
 
     traffic = load_traffic(w.name, algo_name + "_" + mfl.FETCH_NAMES[fetch_a] + mfl.FETCH_NAMES[fetch_b])
     out = {
@@ -421,7 +424,7 @@ def main() -> int:
         adj = PEAK_FP16_DENSE_TFLOPS * sclk / 2400.0
         out["clock"] = {"sclk_mhz_sustained": sclk, "peak_at_sclk": round(adj, 1),
                         "pct_of_peak_at_sclk": round(100.0 * value / adj, 2),
-                        "power_w": power,
+                        "mclk_mhz": mclk, "power_w": power,
                         "how": f"rocm-smi during {args.clock_seconds:g} s of back-to-back steps"}
     if args.copy_mib:
         out["config"]["copy_mib_per_step"] = args.copy_mib
