@@ -935,7 +935,10 @@ __global__ void __launch_bounds__(Cfg::kThreads, 1) gemm_tiled(const GemmParams 
   if (kt + 1 < nfull) step(kt++, No(), Yes(), BoolC<NST == 2>());
   if (kt < nfull) step(kt, No(), No(), No());
 
-  // K remainder: one step staged element by element with zero fill
+  // K remainder: one step staged with zero fill past K.  K-contiguous rows go
+  // by 16-byte chunks (a whole chunk in one load, the chunk that holds K's
+  // edge element by element, zeros past it); M-contiguous A element by
+  // element.
   if (p.K % BK != 0) {
     const int k0 = nfull * BK;
     __syncthreads();
@@ -943,22 +946,40 @@ __global__ void __launch_bounds__(Cfg::kThreads, 1) gemm_tiled(const GemmParams 
     _Float16* sb = stage_b(0);
     const _Float16* A = (const _Float16*)p.A;
     const _Float16* B = (const _Float16*)p.B;
-    for (int e = tid; e < BM * BK; e += Cfg::kThreads) {
-      const int row = e / BK, k = e % BK, gk = k0 + k;
-      const int gm = min(m0 + row, p.M - 1);
-      _Float16 v = (_Float16)0.0f;
-      if (gk < p.K)
-        v = (FA == kFetchRegT || kAT) ? A[(int64_t)gk * p.lda + gm] : A[(int64_t)gm * p.lda + gk];
-      if constexpr (kAT)
-        sa[lds_offset_mn<BM>(row, k)] = v;
-      else
-        sa[lds_offset<BK>(row, k)] = v;
+    auto stage_rows = [&](const _Float16* X, int64_t ld, int rows, auto grow, _Float16* dst) {
+      constexpr int CHK = BK / 8;
+      for (int q = tid; q < rows * CHK; q += Cfg::kThreads) {
+        const int row = q / CHK, c = q % CHK, gk = k0 + 8 * c;
+        const _Float16* src = X + (int64_t)grow(row) * ld + gk;
+        union {
+          uint4 u;
+          _Float16 h[8];
+        } v;
+        v.u = make_uint4(0, 0, 0, 0);
+        if (gk + 8 <= p.K) {
+          __builtin_memcpy(&v.u, src, 16);
+        } else if (gk < p.K) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (gk + e < p.K) v.h[e] = src[e];
+        }
+        *(uint4*)&dst[lds_offset<BK>(row, 8 * c)] = v.u;
+      }
+    };
+    if constexpr (FA == kFetchRegT || kAT) {
+      for (int e = tid; e < BM * BK; e += Cfg::kThreads) {
+        const int row = e / BK, k = e % BK, gk = k0 + k;
+        const int gm = min(m0 + row, p.M - 1);
+        const _Float16 v = gk < p.K ? A[(int64_t)gk * p.lda + gm] : (_Float16)0.0f;
+        if constexpr (kAT)
+          sa[lds_offset_mn<BM>(row, k)] = v;
+        else
+          sa[lds_offset<BK>(row, k)] = v;
+      }
+    } else {
+      stage_rows(A, p.lda, BM, [&](int row) { return min(m0 + row, p.M - 1); }, sa);
     }
-    for (int e = tid; e < BN * BK; e += Cfg::kThreads) {
-      const int row = e / BK, k = e % BK, gk = k0 + k;
-      const int gn = min(n0 + perm_n<Cfg>(row), p.N - 1);
-      sb[lds_offset<BK>(row, k)] = gk < p.K ? B[(int64_t)gn * p.ldb + gk] : (_Float16)0.0f;
-    }
+    stage_rows(B, p.ldb, BN, [&](int row) { return min(n0 + perm_n<Cfg>(row), p.N - 1); }, sb);
     __syncthreads();
 #pragma unroll
     for (int kk = 0; kk < KSUB; ++kk) {
