@@ -981,10 +981,14 @@ __global__ void __launch_bounds__(Cfg::kThreads, 1) gemm_tiled(const GemmParams 
     }
     stage_rows(B, p.ldb, BN, [&](int row) { return min(n0 + perm_n<Cfg>(row), p.N - 1); }, sb);
     __syncthreads();
+    // this wave's sub-steps that start at or past K hold only zeros: skipped
+    const int krem = p.K % BK;
 #pragma unroll
     for (int kk = 0; kk < KSUB; ++kk) {
-      frags(0, kk, 0);
-      mma(0);
+      if (sub_k<Cfg>(w, kk) < krem) {
+        frags(0, kk, 0);
+        mma(0);
+      }
     }
   }
   // Interior tiles with vector-aligned rows: vectors straight from the

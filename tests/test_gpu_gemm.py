@@ -51,6 +51,27 @@ def test_small_integer_bit_exact(algo, shape):
         assert v.ok, (w.name, c, d, str(v))
 
 
+# K remainders of every size class for every stage depth (BK 32, 64, 128):
+# the last, partial K-step is staged by 16-byte chunks with zero fill and
+# runs only the sub-steps that hold some k < K
+K_TAILS = [65, 79, 80, 81, 97, 113, 127, 143, 193]
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("K", K_TAILS)
+def test_k_remainder_integer_bit_exact(algo, K):
+    M, N = 130, 96
+    ld16 = (K + 7) // 8 * 8 + 8
+    for (c, d), lda, ldb in (((None, "f32"), K, K), (("f16", "f16"), ld16, K + 1),
+                             (("f32", "f16"), K + 3, ld16)):
+        w = W.custom(M, N, K, c=c, d=d, dist="int", seed=K * 11 + lda, lda=lda, ldb=ldb)
+        x = W.make_inputs(w)
+        D, checks = run_gemm(w, x, algo)
+        _assert_checks(checks)
+        v = verdict(D, oracle_full(w, x), w, True)
+        assert v.ok, (w.name, algo, c, d, lda, ldb, str(v))
+
+
 # Split-K (K-groups of waves, partial tiles reduced through LDS): K from one
 # 128-deep stage to several, with and without a K tail, ragged M and N, every
 # C/D combination, both fetch paths
