@@ -56,8 +56,9 @@ int gemm_tn_chain_validate(int64_t batch, int64_t M, int64_t N1, int64_t N2, int
  * then *staging = MFL_CHAIN_STAGE_DMA (direct global-to-LDS loads: N1 a
  * multiple of the kernel's N1 chunk, 64 columns, 32 at K = 256; B and W
  * 16-byte aligned with ldb, ldw, stride_b, stride_w multiples of 8) or
- * MFL_CHAIN_STAGE_REGS (through registers, any layout);
- * staging may be NULL.  Both give the same D. */
+ * MFL_CHAIN_STAGE_REGS (through registers, any layout), and *tile_n = the
+ * N2 columns per workgroup (64 when N2 <= 64, else 128); either pointer may
+ * be NULL.  Every choice gives the same D. */
 #define MFL_CHAIN_STAGE_REGS 0
 #define MFL_CHAIN_STAGE_DMA 1
 int gemm_tn_chain_plan(int64_t batch, int64_t M, int64_t N1, int64_t N2, int64_t K,
@@ -65,7 +66,7 @@ int gemm_tn_chain_plan(int64_t batch, int64_t M, int64_t N1, int64_t N2, int64_t
                        const void* B, int64_t ldb, int64_t stride_b,
                        const void* W, int64_t ldw, int64_t stride_w,
                        const void* D, int64_t ldd, int64_t stride_d, int32_t d_dtype,
-                       int32_t* staging);
+                       int32_t* staging, int32_t* tile_n);
 
 #ifdef __cplusplus
 }

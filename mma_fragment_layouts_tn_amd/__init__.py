@@ -85,7 +85,7 @@ def _load() -> ctypes.CDLL:
     lib.gemm_tn_chain.restype = ctypes.c_int
     lib.gemm_tn_chain_validate.argtypes = [i64] * 5 + [vp, i64, i64] * 4 + [i32]
     lib.gemm_tn_chain_validate.restype = ctypes.c_int
-    lib.gemm_tn_chain_plan.argtypes = [i64] * 5 + [vp, i64, i64] * 4 + [i32, vp]
+    lib.gemm_tn_chain_plan.argtypes = [i64] * 5 + [vp, i64, i64] * 4 + [i32, vp, vp]
     lib.gemm_tn_chain_plan.restype = ctypes.c_int
     lib.mfl_kernel_info.argtypes = [i32, GemmDtypes] + [P(i32)] * 6
     lib.mfl_kernel_info.restype = ctypes.c_int
@@ -246,11 +246,12 @@ CHAIN_STAGING = {0: "regs", 1: "dma"}
 
 def gemm_chain_plan(batch, M, N1, N2, K, A, lda, sa, B, ldb, sb, W, ldw, sw, D, ldd, sd,
                     d_dtype: int):
-    """(code, staging name) gemm_tn_chain would take for these arguments."""
-    st = ctypes.c_int32(-1)
+    """(code, staging name, N2 tile width) gemm_tn_chain would take for these
+    arguments."""
+    st, tn = ctypes.c_int32(-1), ctypes.c_int32(-1)
     rc = _lib.gemm_tn_chain_plan(batch, M, N1, N2, K, A, lda, sa, B, ldb, sb, W, ldw, sw,
-                                 D, ldd, sd, d_dtype, ctypes.byref(st))
-    return rc, CHAIN_STAGING.get(st.value)
+                                 D, ldd, sd, d_dtype, ctypes.byref(st), ctypes.byref(tn))
+    return rc, CHAIN_STAGING.get(st.value), (tn.value if rc == 0 else None)
 
 
 def _rows_view(X: torch.Tensor, name: str):

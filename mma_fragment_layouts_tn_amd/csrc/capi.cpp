@@ -414,8 +414,8 @@ int chain_check(int64_t batch, int64_t M, int64_t N1, int64_t N2, int64_t K, con
   if (D && ((uintptr_t)D % (uintptr_t)elem_size(dk))) return MFL_E_MISALIGNED;
   if (M > INT_MAX / 2 || N1 > INT_MAX / 2 || N2 > INT_MAX / 2 || batch > INT_MAX)
     return MFL_E_TOO_LARGE;
-  const int64_t tiles = batch * ((M + mfl::chain::BM - 1) / mfl::chain::BM) *
-                        ((N2 + mfl::chain::BN - 1) / mfl::chain::BN);
+  const int64_t bn = mfl::chain::tile_n(N2);
+  const int64_t tiles = batch * ((M + mfl::chain::BM - 1) / mfl::chain::BM) * ((N2 + bn - 1) / bn);
   if (tiles > INT_MAX) return MFL_E_TOO_LARGE;
   return MFL_OK;
 }
@@ -740,12 +740,13 @@ int gemm_tn_chain_plan(int64_t batch, int64_t M, int64_t N1, int64_t N2, int64_t
                        const void* A, int64_t lda, int64_t stride_a, const void* B, int64_t ldb,
                        int64_t stride_b, const void* W, int64_t ldw, int64_t stride_w,
                        const void* D, int64_t ldd, int64_t stride_d, int32_t d_dtype,
-                       int32_t* staging) {
+                       int32_t* staging, int32_t* tile_n) {
   const int rc = chain_check(batch, M, N1, N2, K, A, lda, stride_a, B, ldb, stride_b, W, ldw,
                              stride_w, D, ldd, stride_d, d_dtype);
   if (rc == MFL_OK && staging)
     *staging = chain_dma(K, N1, B, ldb, stride_b, W, ldw, stride_w) ? MFL_CHAIN_STAGE_DMA
                                                                   : MFL_CHAIN_STAGE_REGS;
+  if (rc == MFL_OK && tile_n) *tile_n = mfl::chain::tile_n(N2);
   return rc;
 }
 
@@ -757,7 +758,9 @@ int gemm_tn_chain(int64_t batch, int64_t M, int64_t N1, int64_t N2, int64_t K, c
                              stride_w, D, ldd, stride_d, d_dtype);
   if (rc != MFL_OK) return rc;
   if (batch == 0 || M == 0 || N2 == 0) return MFL_OK;
-  const void* fn = mfl::chain_symbol((int)K, d_dtype, chain_dma(K, N1, B, ldb, stride_b, W, ldw, stride_w));
+  const int bn = mfl::chain::tile_n(N2);
+  const void* fn =
+      mfl::chain_symbol((int)K, d_dtype, chain_dma(K, N1, B, ldb, stride_b, W, ldw, stride_w), bn);
   if (!fn) return MFL_E_UNSUPPORTED;
   mfl::ChainParams p{};
   p.batch = (int)batch;
@@ -773,7 +776,7 @@ int gemm_tn_chain(int64_t batch, int64_t M, int64_t N1, int64_t N2, int64_t K, c
   p.sw = stride_w;
   p.sd = stride_d;
   p.tiles_m = (int)(batch * ((M + mfl::chain::BM - 1) / mfl::chain::BM));
-  p.tiles_n = (int)((N2 + mfl::chain::BN - 1) / mfl::chain::BN);
+  p.tiles_n = (int)((N2 + bn - 1) / bn);
   p.group_m = 8;
   p.d_vec = ((uintptr_t)D % (uintptr_t)(4 * elem_size(d_dtype)) == 0) && (ldd % 4 == 0) &&
             (stride_d % 4 == 0);

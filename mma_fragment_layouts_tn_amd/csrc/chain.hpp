@@ -91,9 +91,9 @@ static_assert(chain_k_perm().ok, "the accumulator must read as the next operand"
 static_assert(chain_runs_of_4(), "pi must keep runs of 4 N1 columns");
 
 // ------------------------------------------------------------------ kernel
-// Workgroup: 4 waves, 256 rows of M (64 per wave, RM = 2 atom rows) x 128
-// columns of N2 (RN = 4 atom columns, N-permuted: repeat j of atom column c
-// is column 4 c + j, so D leaves in 4-element vectors).  N1 is consumed in
+// Workgroup: 4 waves, 256 rows of M (64 per wave, RM = 2 atom rows) x BN
+// columns of N2 (RN = BN / 32 atom columns, N-permuted: repeat j of atom
+// column c is column RN c + j, so D leaves in RN-element vectors).  N1 is consumed in
 // chunks of CW = 32 H columns, H blocks of 32.
 //
 // Where pi goes: LDS row 32 h + r of a B chunk holds N1 row 32 h + pi^-1(r)
@@ -116,7 +116,10 @@ static_assert(chain_runs_of_4(), "pi must keep runs of 4 N1 columns");
 // otherwise through registers with zero fill, loaded after the barrier of
 // iteration c and written to LDS before that of iteration c+1.
 namespace chain {
-constexpr int BM = 256, BN = 128, RM = 2, RN = 4, WAVES = 4, THREADS = 256, NST = 3;
+constexpr int BM = 256, RM = 2, WAVES = 4, THREADS = 256, NST = 3;
+// N2 columns per workgroup: 128 (RN = 4 atom columns per wave), 64 when N2
+// fits in it (RN = 2: no MFMAs on columns past N2)
+MFL_HD constexpr int tile_n(int64_t n2) { return n2 <= 64 ? 64 : 128; }
 // N1 columns per iteration (H = CW / 32 atom blocks): 64 halves the
 // iterations' fixed costs (barrier, conversion); at K = 256 the register
 // budget keeps it at 32
@@ -137,7 +140,7 @@ __device__ __forceinline__ int b_off(int row, int k) {
   return row * KD + (((k >> 3) ^ b_swz<KD>(row)) << 3) + (k & 7);
 }
 
-// W chunk tile: 128 rows x CW halves (N1 in natural order), the CW / 8
+// W chunk tile: BN rows x CW halves (N1 in natural order), the CW / 8
 // 16-byte chunks of a row XOR-swizzled so that 16 consecutive rows at one
 // chunk fall on distinct bank groups
 template <int CW>
@@ -150,6 +153,7 @@ __device__ __forceinline__ int w_off(int row, int n) {
 }
 
 // the N2 column held by W's LDS row r (the N permutation of the tile)
+template <int RN>
 __device__ __forceinline__ int w_col(int r) { return RN * (r % 32) + r / 32; }
 
 template <bool V>
@@ -189,10 +193,12 @@ __device__ __forceinline__ void wait_vm() {
 }
 }  // namespace chain
 
-template <int KD, int DK, bool DMA>
+template <int KD, int DK, bool DMA, int BN>
 __global__ void __launch_bounds__(chain::THREADS, 1) gemm_chain(const ChainParams p) {
   using namespace chain;
   static_assert(KD == 32 || KD == 64 || KD == 128 || KD == 256, "K is 32, 64, 128 or 256");
+  static_assert(BN == 64 || BN == 128, "N2 tiles of 64 or 128 columns");
+  constexpr int RN = BN / 32;
   constexpr int KSUB = KD / 16, CH = KD / 8;
   constexpr int CW = chunk_width(KD), H = CW / 32;
   static_assert(CW == 32 || CW == 64, "chunks of 32 or 64 N1 columns");
@@ -262,7 +268,7 @@ __global__ void __launch_bounds__(chain::THREADS, 1) gemm_chain(const ChainParam
     for (int i = 0; i < NW; ++i) {
       const int byte = (w * NW + i) * 1024 + 16 * lane;
       const int r = byte / (2 * CW), q = (byte % (2 * CW)) / 16;
-      const int n2 = min(n0 + w_col(r), p.N2 - 1);
+      const int n2 = min(n0 + w_col<RN>(r), p.N2 - 1);
       wn1[i] = 8 * (q ^ w_swz<CW>(r));
       woff[i] = (int64_t)n2 * p.ldw + wn1[i];
     }
@@ -276,7 +282,7 @@ __global__ void __launch_bounds__(chain::THREADS, 1) gemm_chain(const ChainParam
 #pragma unroll
     for (int t = 0; t < WPT; ++t) {
       const int q = tid + t * THREADS, r = q / (CW / 8);
-      const int n2 = min(n0 + w_col(r), p.N2 - 1);
+      const int n2 = min(n0 + w_col<RN>(r), p.N2 - 1);
       wn1[t] = 8 * (q % (CW / 8));
       woff[t] = (int64_t)n2 * p.ldw + wn1[t];
     }
@@ -506,13 +512,17 @@ __global__ void __launch_bounds__(chain::THREADS, 1) gemm_chain(const ChainParam
       const int64_t row = (int64_t)b * p.sd + (int64_t)m * p.ldd;
       if (p.d_vec && n + RN <= p.N2) {
         if constexpr (DK == 2) {
-          typedef float f4 __attribute__((ext_vector_type(4)));
-          const f4 y = {x[0], x[1], x[2], x[3]};
-          __builtin_nontemporal_store(y, (f4*)((float*)p.D + row + n));
+          typedef float fv __attribute__((ext_vector_type(RN)));
+          fv y;
+#pragma unroll
+          for (int j = 0; j < RN; ++j) y[j] = x[j];
+          __builtin_nontemporal_store(y, (fv*)((float*)p.D + row + n));
         } else {
-          typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-          const h4 y = {(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]};
-          __builtin_nontemporal_store(y, (h4*)((_Float16*)p.D + row + n));
+          typedef _Float16 hv __attribute__((ext_vector_type(RN)));
+          hv y;
+#pragma unroll
+          for (int j = 0; j < RN; ++j) y[j] = (_Float16)x[j];
+          __builtin_nontemporal_store(y, (hv*)((_Float16*)p.D + row + n));
         }
       } else {
 #pragma unroll
@@ -527,8 +537,8 @@ __global__ void __launch_bounds__(chain::THREADS, 1) gemm_chain(const ChainParam
     }
 }
 
-// host: kernel symbol for K, the D type (1 fp16, 2 fp32) and the staging
-// (direct-to-LDS or through registers); nullptr if none
-const void* chain_symbol(int kd, int dk, bool dma);
+// host: kernel symbol for K, the D type (1 fp16, 2 fp32), the staging
+// (direct-to-LDS or through registers) and the N2 tile width; nullptr if none
+const void* chain_symbol(int kd, int dk, bool dma, int bn);
 
 }  // namespace mfl

@@ -172,7 +172,7 @@ def _cplan(**kw):
     a = args
     return mfl.gemm_chain_plan(a["batch"], a["M"], a["N1"], a["N2"], a["K"], a["A"], a["lda"],
                                a["sa"], a["B"], a["ldb"], a["sb"], a["W"], a["ldw"], a["sw"],
-                               a["D"], a["ldd"], a["sd"], a["d"])
+                               a["D"], a["ldd"], a["sd"], a["d"])[:2]
 
 
 def test_chain_staging_rule():
@@ -192,6 +192,14 @@ def test_chain_staging_rule():
     assert _cplan(sb=256 * 128 + 2) == (0, "regs")
     assert _cplan(A=P + 2, lda=130) == (0, "dma")        # A is read through registers
     assert _cplan(K=96)[0] == mfl.ERR["UNSUPPORTED"]
+
+
+def test_chain_n2_tile_rule():
+    """N2 tiles of 64 columns when N2 fits, else 128."""
+    def tile(N2):
+        return mfl.gemm_chain_plan(1, 100, 256, N2, 128, P, 128, 0, P, 128, 0, P, 256, 0,
+                                   P, max(N2, 1), 0, mfl.F16)[2]
+    assert [tile(n) for n in (1, 63, 64, 65, 128, 129, 1000)] == [64, 64, 64, 128, 128, 128, 128]
 
 
 def test_chain_perm_is_derived_from_the_atoms():

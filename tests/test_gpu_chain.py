@@ -39,11 +39,11 @@ def run_chain(x: W.ChainInputs, d: str, share=(False, False, False)):
     ldd = max(w.N2, 1)
     Dt = out_buffer(w.batch * w.M, ldd, d)
     dk = mfl.F16 if d == "f16" else mfl.F32
-    rc, staging = mfl.gemm_chain_plan(w.batch, w.M, w.N1, w.N2, w.K, *args, Dt.data_ptr(), ldd,
-                                      w.M * ldd, dk)
+    rc, staging, tile_n = mfl.gemm_chain_plan(w.batch, w.M, w.N1, w.N2, w.K, *args,
+                                              Dt.data_ptr(), ldd, w.M * ldd, dk)
     assert rc == 0, mfl.strerror(rc)
-    say(f"[gpu]   staging {staging}")
-    STAGINGS_SEEN.add((staging, w.K))
+    say(f"[gpu]   staging {staging}, N2 tile {tile_n}")
+    STAGINGS_SEEN.add((staging, w.K, tile_n))
     rc = mfl.gemm_chain_raw(w.batch, w.M, w.N1, w.N2, w.K, *args, Dt.data_ptr(), ldd,
                             w.M * ldd, dk, torch.cuda.current_stream().cuda_stream)
     assert rc == 0, mfl.strerror(rc)
@@ -76,6 +76,8 @@ SHAPES = [  # batch, M, N1, N2, K
     (3, 257, 33, 129, 256), (1, 1, 1, 1, 32), (2, 512, 1000, 64, 128), (1, 70, 31, 200, 64),
     (2, 300, 96, 130, 256), (1, 130, 160, 70, 32), (2, 256, 288, 256, 128),
     (1, 130, 192, 70, 32), (2, 256, 128, 256, 128),
+    # N2 tiles of 64: whole chunks (direct-to-LDS when aligned) at every K
+    (2, 100, 128, 48, 32), (1, 90, 192, 64, 64), (2, 260, 256, 40, 128), (1, 200, 64, 64, 256),
 ]
 
 
@@ -173,8 +175,11 @@ def test_named_workload_sampled(integer):
             assert (np.abs(got - want) <= tol).all(), b
 
 
-def test_both_stagings_ran_for_every_k():
-    """Collected after the cases above: each K ran through both stagings."""
+def test_every_kernel_variant_ran():
+    """Collected after the cases above: each K ran through both stagings
+    with both N2 tile widths."""
     for K in (32, 64, 128, 256):
         for staging in ("dma", "regs"):
-            assert (staging, K) in STAGINGS_SEEN, (staging, K, sorted(STAGINGS_SEEN))
+            for tile_n in (64, 128):
+                assert (staging, K, tile_n) in STAGINGS_SEEN, (staging, K, tile_n,
+                                                               sorted(STAGINGS_SEEN))
