@@ -202,6 +202,64 @@ def cpu_baseline_chain(w, x, target_s: float):
                       f"{cores} threads)"}
 
 
+def measure_and_report(step, stream, args, flops, metric, config, traffic, source_hash,
+                       cpu_leg):
+    """Time the step (time_steps), read the clocks, print the one JSON line.
+    `cpu_leg()` times the oracle unless --no-cpu-baseline."""
+    import numpy as np
+    import torch
+    ms_per_step, kern_ms, per, cold = time_steps(step, stream, args)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+    sclk = mclk = power = None
+    if args.clock_seconds > 0:
+        sclk, mclk, power = sustained_clock(step, torch.cuda.synchronize, args.clock_seconds)
+        print(f"[bench] under sustained load: shader clock {sclk} MHz, memory clock {mclk} MHz, "
+              f"power {power} W", file=sys.stderr, flush=True)
+    out = {
+        "metric": metric,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": config,
+        "pct_of_peak": round(100.0 * value / PEAK_FP16_DENSE_TFLOPS, 2),
+        "kernel_ms": {"avg_back_to_back": round(kern_ms, 5),
+                      "single_median": round(float(np.median(per)), 5),
+                      "single_min": round(float(per.min()), 5),
+                      "single_p90": round(float(np.percentile(per, 90)), 5),
+                      "cold_median": round(float(np.median(cold)), 5),
+                      "cold_p90": round(float(np.percentile(cold, 90)), 5)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_FP16_DENSE_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_FP16_DENSE_TFLOPS, 4),
+                     "traffic": traffic},
+        "cpu_baseline": None,
+        "kernel_source_hash": source_hash,
+    }
+    if sclk:
+        # the dense peak scales with the shader clock (2400 MHz nominal)
+        adj = PEAK_FP16_DENSE_TFLOPS * sclk / 2400.0
+        out["clock"] = {"sclk_mhz_sustained": sclk, "peak_at_sclk": round(adj, 1),
+                        "pct_of_peak_at_sclk": round(100.0 * value / adj, 2),
+                        "mclk_mhz": mclk, "power_w": power,
+                        "how": f"rocm-smi during {args.clock_seconds:g} s of back-to-back steps"}
+    if args.copy_mib:
+        out["config"]["copy_mib_per_step"] = args.copy_mib
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_leg()
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main_chain(args) -> int:
     import numpy as np
     import torch
@@ -242,60 +300,17 @@ def main_chain(args) -> int:
 
     print(f"[bench] {w.name} back-to-back GEMM batch={w.batch} M={w.M} N1={w.N1} N2={w.N2} "
           f"K={w.K} warmup={args.warmup} steps={args.steps}", file=sys.stderr, flush=True)
-    ms_per_step, kern_ms, per, cold = time_steps(step, stream, args)
-    flops = float(w.flops)
-    value = flops / (ms_per_step * 1e-3) / 1e12
-    achieved = flops / (kern_ms * 1e-3) / 1e12
-    sclk = mclk = power = None
-    if args.clock_seconds > 0:
-        sclk, mclk, power = sustained_clock(step, torch.cuda.synchronize, args.clock_seconds)
-        print(f"[bench] under sustained load: shader clock {sclk} MHz, memory clock {mclk} MHz, "
-              f"power {power} W", file=sys.stderr, flush=True)
-    out = {
-        "metric": METRIC_CHAIN,
-        "value": round(value, 2),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f16",
-        "data": "synthetic",
-        "config": {"workload": w.name, "batch": w.batch, "M": w.M, "N1": w.N1, "N2": w.N2,
-                   "K": w.K, "a": "f16 K-contiguous", "b": "f16 K-contiguous",
-                   "w": "f16 N1-contiguous", "d": w.d, "accumulate": "f32",
-                   "intermediate": "S rounded once to f16",
-                   "kernel": f"gemm_chain 256x128 tile, N1 chunks of {32 if w.K >= 256 else 64}"},
-        "pct_of_peak": round(100.0 * value / PEAK_FP16_DENSE_TFLOPS, 2),
-        "kernel_ms": {"avg_back_to_back": round(kern_ms, 5),
-                      "single_median": round(float(np.median(per)), 5),
-                      "single_min": round(float(per.min()), 5),
-                      "single_p90": round(float(np.percentile(per, 90)), 5),
-                      "cold_median": round(float(np.median(cold)), 5),
-                      "cold_p90": round(float(np.percentile(cold, 90)), 5)},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
-                     "peak": PEAK_FP16_DENSE_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_FP16_DENSE_TFLOPS, 4),
-                     "traffic": load_traffic(w.name, "chain", CHAIN_SOURCES)},
-        "cpu_baseline": None,
-        "kernel_source_hash": kernel_source_hash(CHAIN_SOURCES),
-    }
-    if sclk:
-        adj = PEAK_FP16_DENSE_TFLOPS * sclk / 2400.0
-        out["clock"] = {"sclk_mhz_sustained": sclk, "peak_at_sclk": round(adj, 1),
-                        "pct_of_peak_at_sclk": round(100.0 * value / adj, 2),
-                        "mclk_mhz": mclk, "power_w": power,
-                        "how": f"rocm-smi during {args.clock_seconds:g} s of back-to-back steps"}
-    if args.copy_mib:
-        out["config"]["copy_mib_per_step"] = args.copy_mib
-    if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle on a batch sample", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline_chain(w, x, args.cpu_seconds)
-    print(json.dumps(out), flush=True)
-    return 0
+    rc, staging, tile_n = mfl.gemm_chain_plan(*args_c[:14], D.data_ptr(), w.N2, w.M * w.N2, dk)
+    config = {"workload": w.name, "batch": w.batch, "M": w.M, "N1": w.N1, "N2": w.N2,
+              "K": w.K, "a": "f16 K-contiguous", "b": "f16 K-contiguous",
+              "w": "f16 N1-contiguous", "d": w.d, "accumulate": "f32",
+              "intermediate": "S rounded once to f16",
+              "kernel": f"gemm_chain 256x{tile_n} tile, N1 chunks of {32 if w.K >= 256 else 64}, "
+                        f"{staging} staging"}
+    return measure_and_report(step, stream, args, float(w.flops), METRIC_CHAIN, config,
+                              load_traffic(w.name, "chain", CHAIN_SOURCES),
+                              kernel_source_hash(CHAIN_SOURCES),
+                              lambda: cpu_baseline_chain(w, x, args.cpu_seconds))
 
 
 def main() -> int:
@@ -326,7 +341,6 @@ def main() -> int:
               f"WORLD_SIZE={world}); this GEMM build has no multi-GPU path.", file=sys.stderr)
         return 2
 
-    import numpy as np
     import torch
 
     import mma_fragment_layouts_tn_amd as mfl
@@ -374,65 +388,16 @@ def main() -> int:
     print(f"[bench] {w.name} algo={algo_name} fetch A:{mfl.FETCH_NAMES[fetch_a]} "
           f"B:{mfl.FETCH_NAMES[fetch_b]} tile={info['bm']}x{info['bn']}x{info['bk']} "
           f"warmup={args.warmup} steps={args.steps}", file=sys.stderr, flush=True)
-    ms_per_step, kern_ms, per, cold = time_steps(step, stream, args)
-    flops = float(w.flops)
-    value = flops / (ms_per_step * 1e-3) / 1e12
-    achieved = flops / (kern_ms * 1e-3) / 1e12
-
-    sclk = mclk = power = None
-    if args.clock_seconds > 0:
-        sclk, mclk, power = sustained_clock(step, torch.cuda.synchronize, args.clock_seconds)
-        print(f"[bench] under sustained load: shader clock {sclk} MHz, memory clock {mclk} MHz, "
-              f"power {power} W", file=sys.stderr, flush=True)
-
-    traffic = load_traffic(w.name, algo_name + "_" + mfl.FETCH_NAMES[fetch_a] + mfl.FETCH_NAMES[fetch_b])
-    out = {
-        "metric": METRIC,
-        "value": round(value, 2),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f16",
-        "data": "synthetic",
-        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K,
-                   "a": "f16 K-contiguous" if w.a_order == "k" else f"f16 M-contiguous lda={w.lda_}",
-                   "b": "f16 K-contiguous", "c": w.c, "d": w.d, "accumulate": "f32",
-                   "algo": algo_name, "block_tile": f"{info['bm']}x{info['bn']}x{info['bk']}",
-                   "fetch": f"A:{mfl.FETCH_NAMES[fetch_a]} B:{mfl.FETCH_NAMES[fetch_b]}",
-                   "threads": info["threads"], "lds_bytes": info["lds_bytes"]},
-        "pct_of_peak": round(100.0 * value / PEAK_FP16_DENSE_TFLOPS, 2),
-        "kernel_ms": {"avg_back_to_back": round(kern_ms, 5),
-                      "single_median": round(float(np.median(per)), 5),
-                      "single_min": round(float(per.min()), 5),
-                      "single_p90": round(float(np.percentile(per, 90)), 5),
-                      "cold_median": round(float(np.median(cold)), 5),
-                      "cold_p90": round(float(np.percentile(cold, 90)), 5)},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
-                     "peak": PEAK_FP16_DENSE_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_FP16_DENSE_TFLOPS, 4),
-                     "traffic": traffic},
-        "cpu_baseline": None,
-        "kernel_source_hash": kernel_source_hash(),
-    }
-    if sclk:
-        # the dense peak scales with the shader clock (2400 MHz nominal)
-        adj = PEAK_FP16_DENSE_TFLOPS * sclk / 2400.0
-        out["clock"] = {"sclk_mhz_sustained": sclk, "peak_at_sclk": round(adj, 1),
-                        "pct_of_peak_at_sclk": round(100.0 * value / adj, 2),
-                        "mclk_mhz": mclk, "power_w": power,
-                        "how": f"rocm-smi during {args.clock_seconds:g} s of back-to-back steps"}
-    if args.copy_mib:
-        out["config"]["copy_mib_per_step"] = args.copy_mib
-    if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle on a row sample", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
-    print(json.dumps(out), flush=True)
-    return 0
+    config = {"workload": w.name, "M": w.M, "N": w.N, "K": w.K,
+              "a": "f16 K-contiguous" if w.a_order == "k" else f"f16 M-contiguous lda={w.lda_}",
+              "b": "f16 K-contiguous", "c": w.c, "d": w.d, "accumulate": "f32",
+              "algo": algo_name, "block_tile": f"{info['bm']}x{info['bn']}x{info['bk']}",
+              "fetch": f"A:{mfl.FETCH_NAMES[fetch_a]} B:{mfl.FETCH_NAMES[fetch_b]}",
+              "threads": info["threads"], "lds_bytes": info["lds_bytes"]}
+    traffic = load_traffic(w.name, algo_name + "_" + mfl.FETCH_NAMES[fetch_a] +
+                           mfl.FETCH_NAMES[fetch_b])
+    return measure_and_report(step, stream, args, float(w.flops), METRIC, config, traffic,
+                              kernel_source_hash(), lambda: cpu_baseline(w, x, args.cpu_seconds))
 
 
 if __name__ == "__main__":
