@@ -100,6 +100,18 @@ def test_integer_bit_exact(shape, d, rows):
     assert bad.size == 0, (shape, d, bad[:5], D[tuple(bad[0])], want[tuple(bad[0])])
 
 
+@pytest.mark.parametrize("K", [32, 64, 128, 256])
+def test_odd_leading_dims(K):
+    """Rows of A, B and W only 2-byte aligned (odd leading dimensions): A's
+    fragments and B's register staging use unaligned 16-byte loads."""
+    w = W.ChainWorkload("odd", 2, 140, 100, 70, K, d="f32", dist="int", seed=K,
+                        lda=K + 1, ldb=K + 3, ldw=101)
+    x = W.make_chain_inputs(w)
+    D, checks = run_chain(x, "f32")
+    assert all(checks.values()), checks
+    assert np.array_equal(D, oracle_chain(x))
+
+
 def test_n1_zero_gives_zero():
     w = W.ChainWorkload("n1zero", 2, 40, 0, 70, 64, d="f32", dist="int", seed=3)
     x = W.make_chain_inputs(w)
