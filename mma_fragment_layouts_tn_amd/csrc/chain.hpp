@@ -419,21 +419,25 @@ __global__ void __launch_bounds__(chain::THREADS, 1) gemm_chain(const ChainParam
   // is past it).  So the matrix core has work on both sides of the barrier.
   constexpr int FS = KSUB * H, NPRE = (2 * H - 1) * RM * RN;
   Frag pf, pn;
-  half8 wf0[RN], bf0;   // carried: W of the next chunk, K chunk 0; its B, step 0
+  half8 wf0[RN], bf0, bf1;   // carried: W of the next chunk, K chunk 0; its B, steps 0 and 1
+  // Fragments are read ahead of their use, after the MFMAs of the slot they
+  // follow: W of K chunk kc+1 after the first MFMA of K chunk kc, B of step
+  // s1+2 after the MFMAs of step s1.  A wait for one is then a wait for reads
+  // issued several MFMAs earlier, not for the read just issued.
   auto iteration = [&](int c, auto more) {
     constexpr bool MORE = decltype(more)::value;
     const _Float16* sb = smem + stage_of(c) * STAGE;
     const _Float16* sw = sb + BSTAGE;
     floatx16 st[RM][H];
     zero_st(st);
-    half8 wf[RN];
+    half8 wf[RN], wn[RN], bq[2];
+#pragma unroll
+    for (int j = 0; j < RN; ++j) wf[j] = wf0[j];
 #pragma unroll
     for (int kc = 0; kc < 2 * H; ++kc) {
-      if (kc == 0) {
+      if (kc > 0) {
 #pragma unroll
-        for (int j = 0; j < RN; ++j) wf[j] = wf0[j];
-      } else {
-        read_w(sw, kc, wf);
+        for (int j = 0; j < RN; ++j) wf[j] = wn[j];
       }
       if (kc == 2 * H - 1) {
         if constexpr (MORE) {
@@ -449,7 +453,10 @@ __global__ void __launch_bounds__(chain::THREADS, 1) gemm_chain(const ChainParam
           if (kc < 2 * H - 1) {
 #pragma unroll
             for (int s1 = 0; s1 < FS; ++s1)
-              if (s1 * NPRE / FS == kc * RM * RN + g) first_step(st, s1 == 0 ? bf0 : read_b(sb, s1), s1);
+              if (s1 * NPRE / FS == kc * RM * RN + g) {
+                first_step(st, s1 == 0 ? bf0 : s1 == 1 ? bf1 : bq[s1 % 2], s1);
+                if (s1 + 2 < FS) bq[s1 % 2] = read_b(sb, s1 + 2);
+              }
           } else if (g == 0) {
             // after the barrier: the next slot's first fragments, the fetch
             // of slot c+2 (B of chunk c+2 may not exist: its value is then
@@ -457,10 +464,13 @@ __global__ void __launch_bounds__(chain::THREADS, 1) gemm_chain(const ChainParam
             const _Float16* nb = smem + stage_of(c + 1) * STAGE;
             read_w(nb + BSTAGE, 0, wf0);
             bf0 = read_b(nb, 0);
+            bf1 = read_b(nb, 1);
             issue(c + 2);
           }
         }
         second(pf, kc, g, wf);
+        if (g == 0 && kc + 1 < 2 * H) read_w(sw, kc + 1, wn);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     if constexpr (MORE) {
@@ -491,6 +501,7 @@ __global__ void __launch_bounds__(chain::THREADS, 1) gemm_chain(const ChainParam
       const _Float16* s0 = smem + stage_of(0) * STAGE;
       read_w(s0 + BSTAGE, 0, wf0);
       bf0 = read_b(s0, 0);           // B of chunk 1, used only if it exists
+      bf1 = read_b(s0, 1);
     }
     for (int c = 0; c + 1 < nch; ++c) iteration(c, BoolC<true>{});
     iteration(nch - 1, BoolC<false>{});
