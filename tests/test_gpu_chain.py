@@ -22,6 +22,7 @@ from oracle import fp16
 pytestmark = pytest.mark.gpu
 
 STAGINGS_SEEN = set()   # (staging, K) of every launch in this module
+LAST = {}               # staging and N2 tile of the latest launch
 
 
 def run_chain(x: W.ChainInputs, d: str, share=(False, False, False)):
@@ -44,6 +45,7 @@ def run_chain(x: W.ChainInputs, d: str, share=(False, False, False)):
     assert rc == 0, mfl.strerror(rc)
     say(f"[gpu]   staging {staging}, N2 tile {tile_n}")
     STAGINGS_SEEN.add((staging, w.K, tile_n))
+    LAST.update(staging=staging, tile_n=tile_n)
     rc = mfl.gemm_chain_raw(w.batch, w.M, w.N1, w.N2, w.K, *args, Dt.data_ptr(), ldd,
                             w.M * ldd, dk, torch.cuda.current_stream().cuda_stream)
     assert rc == 0, mfl.strerror(rc)
@@ -185,6 +187,34 @@ def test_named_workload_sampled(integer):
         else:
             tol = _float_bound(sub, S, P, w.d, ref)
             assert (np.abs(got - want) <= tol).all(), b
+
+
+@pytest.mark.parametrize("K", [32, 64, 128, 256])
+def test_float_stagings_bit_identical(K):
+    """The staging path carries data, not arithmetic: with N1 in whole
+    chunks, direct-to-LDS (16-byte rows) and register staging (rows off
+    alignment) put the same fragments in front of the same MFMAs in the same
+    order, so D agrees bit for bit on random inputs, where any change in the
+    order of a sum would show.  Both also sit within the oracle's bound."""
+    bt, M, N1, N2 = 2, 300, 128, 130
+    w = W.ChainWorkload("stg", bt, M, N1, N2, K, d="f32", dist="unif", seed=K + 7)
+    x = W.make_chain_inputs(w)
+
+    def padded(X, cols, extra):
+        out = np.zeros(X.shape[:2] + (cols + extra,), X.dtype)
+        out[:, :, :cols] = X[:, :, :cols]
+        return out
+
+    xp = W.ChainInputs(w, padded(x.A, K, 8), x.B, padded(x.W, N1, 3), x.integer)
+    D_dma, checks = run_chain(x, "f32")
+    assert all(checks.values()), checks
+    assert LAST["staging"] == "dma", LAST
+    D_reg, checks = run_chain(xp, "f32")
+    assert all(checks.values()), checks
+    assert LAST["staging"] == "regs", LAST
+    assert np.array_equal(D_dma, D_reg)
+    ref, S, P = oracle_chain(x, with_s=True)
+    assert (np.abs(D_dma - ref) <= _float_bound(x, S, P, "f32", ref)).all()
 
 
 def test_every_kernel_variant_ran():

@@ -140,6 +140,25 @@ def test_float_inputs_within_tolerance(algo):
         assert v.ok, (w.name, str(v))
 
 
+@pytest.mark.parametrize("algo", LDS_ALGOS)
+def test_float_fetch_paths_bit_identical(algo):
+    """The fetch path carries data, not arithmetic: direct-to-LDS and
+    register fetch fill the same swizzled LDS tiles, so the same fragments
+    meet the same MFMAs in the same order and D agrees bit for bit on random
+    inputs (K remainder and fp16 C included), where any change in the order
+    of a sum would show.  Both also pass the oracle comparison."""
+    for (M, N, K, c, d) in ((513, 384, 320, None, "f32"), (300, 517, 1000, "f16", "f16")):
+        w = W.custom(M, N, K, c=c, d=d, dist="unif", seed=M + N + K, lda=K, ldb=K)
+        x = W.make_inputs(w)
+        D_dma, checks = run_gemm(w, x, algo)
+        _assert_checks(checks)
+        D_reg, checks = run_gemm(w, x, algo + "+reg")
+        _assert_checks(checks)
+        assert np.array_equal(D_dma, D_reg), (algo, M, N, K)
+        v = verdict(D_dma, oracle_full(w, x), w, False)
+        assert v.ok, (w.name, str(v))
+
+
 @pytest.mark.parametrize("algo", ALGOS)
 def test_k_zero_gives_c(algo):
     w = W.custom(70, 50, 0, c="f32", d="f32", dist="int", seed=3, lda=8, ldb=8)
