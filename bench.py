@@ -396,7 +396,9 @@ def main() -> int:
               "threads": info["threads"], "lds_bytes": info["lds_bytes"]}
     traffic = load_traffic(w.name, algo_name + "_" + mfl.FETCH_NAMES[fetch_a] +
                            mfl.FETCH_NAMES[fetch_b])
-    return measure_and_report(step, stream, args, float(w.flops), METRIC, config, traffic,
+    metric = METRIC if (w.M, w.N, w.K) == (4096, 4096, 4096) else (
+        f"TFLOP/s for fp16 TN GEMM at {w.M}x{w.N}x{w.K} (fp32 acc) and % of dense FP16 MFMA peak")
+    return measure_and_report(step, stream, args, float(w.flops), metric, config, traffic,
                               kernel_source_hash(), lambda: cpu_baseline(w, x, args.cpu_seconds))
 
 
