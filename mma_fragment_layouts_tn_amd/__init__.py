@@ -125,6 +125,8 @@ def _load() -> ctypes.CDLL:
     lib.mfl_probe_mfma.restype = ctypes.c_int
     lib.mfl_probe_lds_tr16.argtypes = [vp, vp, vp, vp]
     lib.mfl_probe_lds_tr16.restype = ctypes.c_int
+    lib.mfl_probe_xcc.argtypes = [i32, vp, vp]
+    lib.mfl_probe_xcc.restype = ctypes.c_int
     return lib
 
 
@@ -479,5 +481,13 @@ def probe_lds_tr16(lane_offsets, lds_in: torch.Tensor) -> torch.Tensor:
     out = torch.empty((64, 4), dtype=torch.int16, device=lds_in.device)
     stream = torch.cuda.current_stream(lds_in.device).cuda_stream
     rc = _lib.mfl_probe_lds_tr16(offs, lds_in.data_ptr(), out.data_ptr(), stream)
+    _check(rc)
+    return out
+
+
+def probe_xcc(nblocks: int) -> torch.Tensor:
+    """XCD index (0..7) of each of nblocks workgroups (int32, on the GPU)."""
+    out = torch.full((nblocks,), -1, dtype=torch.int32, device="cuda")
+    rc = _lib.mfl_probe_xcc(nblocks, out.data_ptr(), torch.cuda.current_stream().cuda_stream)
     _check(rc)
     return out

@@ -103,3 +103,18 @@ extern "C" int mfl_probe_mfma(int32_t op, const uint16_t* a_slots, const uint16_
   }
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
+
+// Each workgroup records the XCD (the accelerator die of the 8 on the
+// package) it runs on, read from the XCC_ID hardware register; lane 0 stores
+// it with an ordinary vector store.
+__global__ void __launch_bounds__(64) probe_xcc(int32_t* out) {
+  unsigned id;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(id));
+  if (threadIdx.x == 0) out[blockIdx.x] = (int32_t)(id & 0xf);
+}
+
+extern "C" int mfl_probe_xcc(int32_t nblocks, int32_t* out, void* stream) {
+  if (nblocks <= 0 || nblocks > 65536 || !out) return -4;
+  hipLaunchKernelGGL(probe_xcc, dim3(nblocks), dim3(64), 0, (hipStream_t)stream, out);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}

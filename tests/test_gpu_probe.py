@@ -89,3 +89,18 @@ def test_lds_transposing_read(pattern):
             for e in range(4):
                 m, k = l % 32, 8 * (l // 32) + e
                 assert got[l, e] == values[lay[k, m]], (l, e)
+
+
+def test_workgroups_dealt_round_robin_over_xcds():
+    """The kernels' tile order (tile_of_block) assumes that workgroup b runs
+    on XCD b % 8: the 8 dies are dealt workgroups in turn, so renumbering
+    gives each die a contiguous run of tiles whose operand rows share its
+    L2.  A launch of 4096 small workgroups records where each one ran."""
+    n = 4096
+    x = mfl.probe_xcc(n).cpu().numpy()
+    counts = np.bincount(x[x >= 0], minlength=8)
+    match = float(np.mean(x == np.arange(n) % 8))
+    say(f"[gpu] XCD of workgroup b: first 16 {x[:16].tolist()}, per die {counts.tolist()}, "
+        f"b % 8 matches {100 * match:.1f} %")
+    assert ((x >= 0) & (x < 8)).all()
+    assert np.array_equal(x, np.arange(n) % 8)
