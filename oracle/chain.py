@@ -72,20 +72,56 @@ def chain_py(M, N1, N2, K, A_at, B_at, W_at):
     return D
 
 
+def _gamma(n: int, u: float) -> float:
+    """n u / (1 - n u): the bound on the relative error of n rounded
+    operations, each with unit roundoff u (standard rounding error analysis)."""
+    return n * u / (1.0 - n * u)
+
+
+def _grain(X: np.ndarray) -> float:
+    """Largest power of two g with every element of X an integer multiple of
+    g (X holds binary16 values, so X 2^24 is an exact integer); 1 for an
+    all-zero X."""
+    n = np.abs(np.asarray(X, dtype=np.float64) * 2.0 ** 24).astype(np.int64).reshape(-1)
+    n = n[n != 0]
+    if n.size == 0:
+        return 1.0
+    return float((n & -n).min()) * 2.0 ** -24
+
+
 def chain_tolerance(A32: np.ndarray, B32: np.ndarray, W32: np.ndarray,
                     S: np.ndarray, P: np.ndarray) -> np.ndarray:
     """Per-element bound on |D_gpu - D| for one batch when both sums run in
-    fp32 and P is rounded from the fp32 S (operands as float arrays A (M,K),
-    B (N1,K), W (N2,N1); S and P from ``chain_f64``).  From the arithmetic:
+    fp32 (in any order) and P is rounded from the fp32 S (operands as float
+    arrays A (M,K), B (N1,K), W (N2,N1); S and P from ``chain_f64``).
 
-      |S_gpu - S| <= dS = K u sum_k |A B|        (recursive fp32 summation)
-      |P_gpu - P| <= dS + ulp16(|S| + dS)        (two roundings to binary16)
-      |D_gpu - D| <= sum_n1 |W| (dS + ulp16(|S| + dS)) + N1 u sum_n1 |P W|
+    From the arithmetic, with u32 = 2^-24, u64 = 2^-53 and
+    g(n) = n u / (1 - n u):
 
-    with u = 2^-24.  Matrix products of absolute values are library steps."""
-    u = 2.0 ** -24
+      dS  = (g32(K) + g64(K)) sum_k |A B|      fp32 sum on the GPU, plus the
+                                               float64 sum that produced S;
+      dS  = 0 where every product is a multiple of gA gB (the power-of-two
+            grains of A and B) and sum_k |A B| <= 2^24 gA gB: every partial
+            sum, in any order, is then an integer multiple of gA gB below
+            2^24 of them, which fp32 (and float64) hold exactly;
+      the GPU's S lies in [S - dS, S + dS]; rounding to nearest is monotone,
+      so its P lies in [rne16(S - dS), rne16(S + dS)] and
+      dP  = max(rne16(S + dS) - P, P - rne16(S - dS)),
+      which is 0 wherever no binary16 rounding boundary lies within dS of S
+      (P is then the GPU's P exactly);
+      |D_gpu - D| <= sum_n1 dP |W| + g32(N1) sum_n1 (|P| + dP) |W|
+                     + g64(N1) sum_n1 |P| |W|   (the float64 sum of D).
+
+    Matrix products of absolute values are library steps."""
+    u32, u64 = 2.0 ** -24, 2.0 ** -53
     K = A32.shape[1]
     N1 = B32.shape[0]
-    dS = K * u * (np.abs(A32) @ np.abs(B32).T)
-    dP = dS + fp16.ulp16_array(np.abs(S) + dS)
-    return dP @ np.abs(W32).T + N1 * u * (np.abs(P) @ np.abs(W32).T)
+    sab = np.abs(A32) @ np.abs(B32).T
+    dS = (_gamma(K, u32) + _gamma(K, u64)) * sab
+    dS = np.where(sab <= 2.0 ** 24 * _grain(A32) * _grain(B32), 0.0, dS)
+    lo = fp16.rne16_array(S - dS)
+    hi = fp16.rne16_array(S + dS)
+    dP = np.maximum(hi - P, P - lo)
+    aW = np.abs(W32).T
+    return (dP @ aW + _gamma(N1, u32) * ((np.abs(P) + dP) @ aW)
+            + _gamma(N1, u64) * (np.abs(P) @ aW))

@@ -103,6 +103,21 @@ def oracle_full(w: W.Workload, x: W.Inputs):
     return G.gemm_f64(w.M, w.N, w.K, x.A, w.lda_, w.a_order == "m", x.B, w.ldb_, x.C)
 
 
+_FULL_CACHE = {}
+
+
+def oracle_full_cached(w: W.Workload, x: W.Inputs):
+    """oracle_full, kept for the two most recent workloads (the named
+    workloads' cases run one workload's algorithms and its integer twin in a
+    row, so each full reference is computed once)."""
+    key = w
+    if key not in _FULL_CACHE:
+        while len(_FULL_CACHE) >= 2:
+            _FULL_CACHE.pop(next(iter(_FULL_CACHE)))
+        _FULL_CACHE[key] = oracle_full(w, x)
+    return _FULL_CACHE[key]
+
+
 def oracle_sampled(w: W.Workload, x: W.Inputs, ms, ns):
     return G.gemm_f64_sampled(w.M, w.N, w.K, x.A, w.lda_, w.a_order == "m", x.B, w.ldb_,
                               x.C, ms, ns)

@@ -85,28 +85,188 @@ def test_integer_inputs_are_exact():
     assert np.array_equal(D, (S @ W.astype(np.int64).T).astype(np.float64))
 
 
-def test_tolerance_covers_fp32_arithmetic():
-    """Simulate both sums in fp32 (sequential order) and the fp16 rounding of
-    the fp32 S: the difference stays inside the bound, which is far below
-    the size of D."""
+def _fp32_chain(A, B, W, order="seq", drop=None):
+    """The chain as a GPU computes it: both sums in fp32 (products of two
+    binary16 values are exact in fp32), S rounded once to binary16.  order:
+    "seq" k ascending, "rev" k descending, "blk16" sums of 16 consecutive
+    terms added in turn (the grouping a 16-deep matrix instruction gives).
+    drop=(m, n1, k): leave that product out of S (a planted mistake)."""
+    def fsum(terms):                      # terms (T, ...) float32, summed over axis 0
+        idx = list(range(terms.shape[0]))
+        if order == "rev":
+            idx = idx[::-1]
+        acc = np.zeros(terms.shape[1:], dtype=np.float32)
+        if order == "blk16":
+            for b0 in range(0, len(idx), 16):
+                part = np.zeros(terms.shape[1:], dtype=np.float32)
+                for k in idx[b0:b0 + 16]:
+                    part = part + terms[k]
+                acc = acc + part
+            return acc
+        for k in idx:
+            acc = acc + terms[k]
+        return acc
+
+    A32, B32, W32 = A.astype(np.float32), B.astype(np.float32), W.astype(np.float32)
+    prod = A32.T[:, :, None] * B32.T[:, None, :]          # (K, M, N1), exact
+    if drop is not None:
+        m, n1, k = drop
+        prod[k, m, n1] = 0.0
+    S32 = fsum(prod)
+    P16 = S32.astype(np.float16).astype(np.float32)
+    return fsum(P16.T[:, :, None] * W32.T[:, None, :]), P16   # (M, N2), P
+
+
+def _pin_data(dist="unif"):
+    """Pin shapes M, N1, N2, K = 8, 64, 8, 128.  "unif": binary16 values of
+    uniform [-1, 1); "dyadic": multiples of 2^-6 in [-1, 1] for A and B (so
+    S is exact in fp32 in any order and P's rounding does all the work), W
+    uniform."""
     rng = np.random.default_rng(5)
     M, N1, N2, K = 8, 64, 8, 128
-    A = rng.uniform(-1, 1, (M, K)).astype(np.float16)
-    B = rng.uniform(-1, 1, (N1, K)).astype(np.float16)
+    if dist == "dyadic":
+        A = (rng.integers(-64, 65, (M, K)) / 64.0).astype(np.float16)
+        B = (rng.integers(-64, 65, (N1, K)) / 64.0).astype(np.float16)
+    else:
+        A = rng.uniform(-1, 1, (M, K)).astype(np.float16)
+        B = rng.uniform(-1, 1, (N1, K)).astype(np.float16)
     W = rng.uniform(-1, 1, (N2, N1)).astype(np.float16)
     D, S, P = CH.chain_f64(1, M, N1, N2, K, A, K, 0, B, K, 0, W, N1, 0, with_s=True)
-    S32 = np.zeros((M, N1), dtype=np.float32)
-    for k in range(K):
-        S32 += A[:, k:k + 1].astype(np.float32) * B[:, k].astype(np.float32)[None, :]
-    P16 = S32.astype(np.float16).astype(np.float32)
-    D32 = np.zeros((M, N2), dtype=np.float32)
-    for n1 in range(N1):
-        D32 += P16[:, n1:n1 + 1] * W[:, n1].astype(np.float32)[None, :]
     tol = CH.chain_tolerance(A.astype(np.float64), B.astype(np.float64), W.astype(np.float64),
                              S[0], P[0])
-    err = np.abs(D32.astype(np.float64) - D[0])
+    return A, B, W, D[0], S[0], P[0], tol
+
+
+@pytest.mark.parametrize("dist", ["unif", "dyadic"])
+@pytest.mark.parametrize("order", ["seq", "rev", "blk16"])
+def test_tolerance_covers_fp32_arithmetic(order, dist):
+    """Simulate both sums in fp32 in three orders and the fp16 rounding of
+    the fp32 S: every element of the difference stays inside the bound."""
+    A, B, W, D, S, P, tol = _pin_data(dist)
+    D32, _ = _fp32_chain(A, B, W, order)
+    err = np.abs(D32.astype(np.float64) - D)
     assert (err <= tol).all()
-    assert tol.max() < 0.05 * np.abs(D[0]).max()
+
+
+def test_dyadic_inputs_make_s_exact():
+    """The exactness the bound uses: with A, B multiples of 2^-6 and K = 128,
+    the fp32 S equals the float64 S in every order, so P_gpu = P and the
+    bound charges no flip; one element of finer grain (2^-20) removes the
+    exemption."""
+    A, B, W, D, S, P, tol = _pin_data("dyadic")
+    for order in ("seq", "rev", "blk16"):
+        _, P16 = _fp32_chain(A, B, W, order)
+        assert np.array_equal(P16, P)
+    assert CH._grain(A.astype(np.float64)) == 2.0 ** -6
+    assert (tol <= 64 * 2.0 ** -23 * (np.abs(P) @ np.abs(W.astype(np.float64)).T)).all()
+    A2 = A.copy()
+    A2[3, 7] = np.float16(2.0 ** -20)                # a subnormal: grain 2^-20
+    assert CH._grain(A2.astype(np.float64)) == 2.0 ** -20
+    D2, S2, P2 = CH.chain_f64(1, 8, 64, 8, 128, A2, 128, 0, B, 128, 0, W, 64, 0, with_s=True)
+    tol2 = CH.chain_tolerance(A2.astype(np.float64), B.astype(np.float64), W.astype(np.float64),
+                              S2[0], P2[0])
+    assert (tol2 > 64 * 2.0 ** -23 * (np.abs(P2[0]) @ np.abs(W.astype(np.float64)).T)).any()
+
+
+def _flip_case():
+    """S = 1024 + (1 + 2^-9) 2^-11 - 1024 + 1 = 1 + 2^-11 + 2^-20 exactly, just
+    above the binary16 midpoint 1 + 2^-11 (so P = 1 + 2^-10), while the fp32
+    sum in k order loses the 2^-20 against 1024 and lands on the midpoint,
+    which rounds to even: P_gpu = 1.  W = [[1]], so D = P."""
+    A = np.array([[1024.0, 1.0 + 2.0 ** -9, -1024.0, 1.0]], dtype=np.float16)
+    B = np.array([[1.0, 2.0 ** -11, 1.0, 1.0]], dtype=np.float16)
+    W = np.ones((1, 1), dtype=np.float16)
+    D, S, P = CH.chain_f64(1, 1, 1, 1, 4, A, 4, 0, B, 4, 0, W, 1, 0, with_s=True)
+    tol = CH.chain_tolerance(A.astype(np.float64), B.astype(np.float64), W.astype(np.float64),
+                             S[0], P[0])
+    return A, B, W, D[0], tol
+
+
+def test_flip_case_is_what_it_claims():
+    A, B, W, D, tol = _flip_case()
+    assert D[0, 0] == 1.0 + 2.0 ** -10
+    D32, P16 = _fp32_chain(A, B, W, "seq")
+    assert P16[0, 0] == 1.0 and D32[0, 0] == 1.0
+
+
+def test_bound_is_attained_where_rounding_can_flip():
+    """Tightness: on the flip case the fp32 chain's error is more than half
+    the bound (a bound twice as loose fails this), and on the random pin data
+    the bound charges a flip only to elements whose S lies near a binary16
+    rounding boundary (elsewhere P_gpu must equal P, and does)."""
+    A, B, W, D, tol = _flip_case()
+    D32, _ = _fp32_chain(A, B, W, "seq")
+    err = abs(float(D32[0, 0]) - D[0, 0])
+    assert err <= tol[0, 0] and err > 0.5 * tol[0, 0], (err, tol[0, 0])
+    A, B, W, D, S, P, tol = _pin_data()
+    u = 2.0 ** -24
+    dS = 1.01 * 128 * u * (np.abs(A.astype(np.float64)) @ np.abs(B.astype(np.float64)).T)
+    near = (fp16.rne16_array(S - dS) != P) | (fp16.rne16_array(S + dS) != P)
+    assert 0 < near.sum() < near.size
+    for order in ("seq", "rev", "blk16"):
+        _, P16 = _fp32_chain(A, B, W, order)
+        assert np.array_equal(P16[~near], P[~near])
+
+
+def _old_tolerance(A32, B32, W32, S, P):
+    """The earlier, looser bound: every element charged dS + ulp16(|S| + dS),
+    as if every rounding of S could flip."""
+    u = 2.0 ** -24
+    K, N1 = A32.shape[1], B32.shape[0]
+    dS = K * u * (np.abs(A32) @ np.abs(B32).T)
+    dP = dS + fp16.ulp16_array(np.abs(S) + dS)
+    return dP @ np.abs(W32).T + N1 * u * (np.abs(P) @ np.abs(W32).T)
+
+
+@pytest.mark.parametrize("dist,min_caught", [("dyadic", 0.0), ("unif", 0.05)])
+def test_dropped_product_term_is_caught(dist, min_caught):
+    """A planted mistake in the simulated chain: one product of S left out.
+    Products across the whole range are tried.  Every omission that moves D
+    at all (the rounding of S to binary16 hides the small ones) and that the
+    earlier bound still accepted is rejected by the derived bound: on dyadic
+    inputs whatever its size, on uniform ones from 0.05 up (below that the
+    possible flips of S near binary16 boundaries leave the room a correct
+    fp32 chain needs)."""
+    A, B, W, D, S, P, tol = _pin_data(dist)
+    old = _old_tolerance(A.astype(np.float64), B.astype(np.float64), W.astype(np.float64), S, P)
+    D0, _ = _fp32_chain(A, B, W, "seq")
+    prods = np.abs(A.astype(np.float64)[:, None, :] * B.astype(np.float64)[None, :, :])
+    caught = 0
+    for flat in np.argsort(-prods, axis=None)[::97]:      # products across the range
+        m, n1, k = np.unravel_index(flat, prods.shape)
+        if prods[m, n1, k] < min_caught:
+            continue
+        D32, _ = _fp32_chain(A, B, W, "seq", drop=(m, n1, k))
+        if np.array_equal(D32, D0):
+            continue                                    # absorbed by the rounding of S
+        err = np.abs(D32.astype(np.float64) - D)
+        if (err <= old).all():                          # inside the old bound ...
+            assert not (err <= tol).all(), (m, n1, k, prods[m, n1, k])   # ... not the new
+            caught += 1
+    assert caught >= 5, caught
+
+
+@pytest.mark.parametrize("dist", ["unif", "dyadic"])
+def test_perturbed_element_is_caught(dist):
+    """Any element of D moved by 1e-3 max|D| falls outside the bound."""
+    A, B, W, D, S, P, tol = _pin_data(dist)
+    D32, _ = _fp32_chain(A, B, W, "seq")
+    eps = 1e-3 * np.abs(D).max()
+    for m in range(D.shape[0]):
+        for n in range(D.shape[1]):
+            bad = D32.astype(np.float64).copy()
+            bad[m, n] += eps
+            assert not (np.abs(bad - D) <= tol).all(), (m, n)
+
+
+def test_bound_that_ignores_flips_fails_the_flip_case():
+    """A planted mistake in the bound (no charge for a flipped rounding of S)
+    does not cover the fp32 chain on the flip case."""
+    A, B, W, D, tol = _flip_case()
+    u = 2.0 ** -24
+    no_flip = 1 * u * 1.0 + 0 * tol                    # only the second sum's rounding
+    D32, _ = _fp32_chain(A, B, W, "seq")
+    assert abs(float(D32[0, 0]) - D[0, 0]) > no_flip[0, 0]
 
 
 # ---------------------------------------------------------- planted mistakes

@@ -7,6 +7,8 @@ arithmetic.  Recipe (the pages fix no data, so this is a stated choice):
   * "unif":   float64 uniform on [-1, 1), rounded to the storage dtype;
   * "normal": float64 normal with the given sigma, rounded to storage dtype;
   * "int":    integers drawn uniformly from {-2, -1, 0, 1, 2};
+  * "dyadic": integers drawn uniformly from {-64..64}, divided by 64 (values
+              in [-1, 1] on a 2^-6 grid, exact in fp16);
   * rounding to fp16/fp32 is numpy's cast (round to nearest even);
   * A is stored K-contiguous, A(m,k) = A[m*lda + k], or M-contiguous,
     A(m,k) = A[m + k*lda]; B(n,k) = B[n*ldb + k]; C(m,n) = C[m*ldc + n];
@@ -124,6 +126,8 @@ def _draw(rng, dist: str, shape, sigma: float = 1.0) -> np.ndarray:
         return rng.normal(0.0, sigma, size=shape)
     if dist == "int":
         return rng.integers(-2, 3, size=shape).astype(np.float64)
+    if dist == "dyadic":
+        return rng.integers(-64, 65, size=shape) / 64.0
     raise ValueError(dist)
 
 
@@ -246,14 +250,17 @@ class ChainInputs:
 def make_chain_inputs(w: ChainWorkload) -> ChainInputs:
     """Draw order A, B, W (each (batch, rows, cols) in C order); "int" draws
     from {-2..2} for A and B and {-1, 0, 1} for W so that S stays exact in
-    fp16 and D in fp32 (and in fp16 where |D| <= 2048)."""
+    fp16 and D in fp32 (and in fp16 where |D| <= 2048); "dyadic" draws A and
+    B on the 2^-6 grid (S exact in fp32, its rounding to fp16 not) and W
+    uniform."""
     rng = np.random.default_rng(w.seed)
 
-    def draw(shape, ld, lo_hi=(-2, 2)):
+    def draw(shape, ld, lo_hi=(-2, 2), is_w=False):
         if w.dist == "int":
             v = rng.integers(lo_hi[0], lo_hi[1] + 1, size=shape).astype(np.float16)
         else:
-            v = _draw(rng, w.dist, shape).astype(np.float16)
+            dist = "unif" if (is_w and w.dist == "dyadic") else w.dist
+            v = _draw(rng, dist, shape).astype(np.float16)
         if ld == shape[2]:
             return v
         out = np.full(shape[:2] + (ld,), F16_NAN, dtype=np.float16)
@@ -262,7 +269,7 @@ def make_chain_inputs(w: ChainWorkload) -> ChainInputs:
 
     A = draw((w.batch, w.M, w.K), w.lda or w.K)
     B = draw((w.batch, w.N1, w.K), w.ldb or w.K)
-    W = draw((w.batch, w.N2, w.N1), w.ldw or max(w.N1, 1), (-1, 1))
+    W = draw((w.batch, w.N2, w.N1), w.ldw or max(w.N1, 1), (-1, 1), is_w=True)
     return ChainInputs(w, A, B, W, integer=(w.dist == "int"))
 
 
