@@ -15,6 +15,12 @@ and the float64 CPU oracle timed on a bounded row sample of the same workload.
 ``--workload chain_b32_2048x2048_k128_n128`` measures the back-to-back GEMM
 (D = rne16(A B^T) W^T per batch, one kernel launch per step) the same way,
 counting 2 batch M N1 (K + N2) FLOP per step.
+
+``--workload mfma_rate_32x32x16`` / ``mfma_rate_16x16x32`` (``--data
+random|zero``) and ``lds_read_b128`` (``--threads``) measure the rates the
+GEMM is priced against: the matrix instructions' issue rate with no memory
+traffic, and conflict-free LDS reads, each with the shader clock read inside
+the kernel.
 """
 from __future__ import annotations
 
@@ -260,6 +266,124 @@ def measure_and_report(step, stream, args, flops, metric, config, traffic, sourc
     return 0
 
 
+MICRO_WORKLOADS = {
+    "mfma_rate_32x32x16": ("mfma", 0, "v_mfma_f32_32x32x16_f16"),
+    "mfma_rate_16x16x32": ("mfma", 1, "v_mfma_f32_16x16x32_f16"),
+    "lds_read_b128": ("lds", None, "ds_read_b128"),
+}
+
+
+def main_micro(args) -> int:
+    """The rates the GEMM kernels are priced against, each from one
+    full-chip launch per step with the shader clock read inside the kernel
+    (cycle counter against the real-time counter, per workgroup):
+
+      mfma_rate_*: every wave issues independent matrix instructions on
+        operand registers filled from random (or zero) fp16 data, 2^20 FLOP
+        (32x32x16) or 2^21 FLOP (16x16x32) per wave per iteration, nothing
+        else in the loop;
+      lds_read_b128: every wave issues conflict-free 16-byte LDS reads."""
+    import numpy as np
+    import torch
+
+    import mma_fragment_layouts_tn_amd as mfl
+
+    kind, op, instr = MICRO_WORKLOADS[args.workload]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+    nwg = 256                                   # one workgroup per compute unit
+    clocks = torch.zeros(4 * nwg, dtype=torch.int64, device=dev)
+    if kind == "mfma":
+        n_ops = 1 << 20
+        if args.data == "zero":
+            ops = torch.zeros(n_ops, dtype=torch.float16, device=dev)
+        else:
+            rng = np.random.default_rng(11)
+            ops = torch.from_numpy(rng.uniform(-1.0, 1.0, n_ops).astype(np.float16)).to(dev)
+        sink = torch.empty(nwg * 256, dtype=torch.float32, device=dev)
+        iters = args.iters or 16384
+        threads = 256
+        # per wave per iteration: 2 sets x 16 instructions x 2*32*32*16 FLOP (op 0)
+        # or 2 sets x 64 instructions x 2*16*16*32 FLOP (op 1)
+        flops = float(nwg * 4 * iters * (1 << 20) * (1 if op == 0 else 2))
+
+        def step():
+            r = mfl.bench_mfma_raw(op, ops.data_ptr(), n_ops, iters, nwg, sink.data_ptr(),
+                                   clocks.data_ptr(), sptr)
+            if r != 0:
+                raise RuntimeError(mfl.strerror(r))
+    else:
+        threads = args.threads
+        iters = args.iters or 65536
+        sink = torch.empty(nwg, dtype=torch.int32, device=dev)
+        nbytes = float(nwg * (threads // 64) * iters * 8 * 1024)
+
+        def step():
+            r = mfl.bench_lds_read_raw(threads, iters, nwg, sink.data_ptr(), clocks.data_ptr(),
+                                       sptr)
+            if r != 0:
+                raise RuntimeError(mfl.strerror(r))
+
+    print(f"[bench] {args.workload} ({instr}, data {args.data if kind == 'mfma' else '-'}) "
+          f"{nwg} workgroups x {threads} threads, {iters} iterations; warmup={args.warmup} "
+          f"steps={args.steps}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = ev0.elapsed_time(ev1) / args.steps
+    c = clocks.view(nwg, 4).cpu().numpy().astype(np.float64)   # last launch
+    khz = mfl.wall_clock_khz()
+    mhz = (c[:, 2] - c[:, 0]) / (c[:, 3] - c[:, 1]) * khz / 1e3
+    loop_ms = float(np.median(c[:, 3] - c[:, 1])) / khz
+    sclk = float(np.median(mhz))
+    print(f"[bench] avg launch {kern_ms:.4f} ms; loop {loop_ms:.4f} ms (real-time counter at "
+          f"{khz} kHz); shader clock in the loop: median {sclk:.0f} MHz, min {mhz.min():.0f}, "
+          f"max {mhz.max():.0f}", file=sys.stderr, flush=True)
+    config = {"workload": args.workload, "instruction": instr, "workgroups": nwg,
+              "threads": threads, "iterations": iters}
+    clock = {"sclk_mhz_in_kernel_median": round(sclk, 1), "sclk_mhz_min": round(float(mhz.min()), 1),
+             "sclk_mhz_max": round(float(mhz.max()), 1),
+             "how": "s_memtime cycles / s_memrealtime ticks around the loop, per workgroup, "
+                    "last timed launch"}
+    if kind == "mfma":
+        value = flops / (kern_ms * 1e-3) / 1e12
+        adj = PEAK_FP16_DENSE_TFLOPS * sclk / 2400.0
+        clock.update(peak_at_sclk=round(adj, 1), pct_of_peak_at_sclk=round(100 * value / adj, 2))
+        config["data"] = "zero" if args.data == "zero" else "uniform [-1,1) fp16, seed 11"
+        out = {"metric": f"MFMA issue rate ({instr}, {config['data']} operands), TFLOP/s and % "
+                         f"of dense FP16 MFMA peak",
+               "value": round(value, 2), "unit": "TFLOP/s",
+               "roofline": {"bound": "mfma", "achieved": round(value, 2),
+                            "peak": PEAK_FP16_DENSE_TFLOPS, "unit": "TFLOP/s",
+                            "frac": round(value / PEAK_FP16_DENSE_TFLOPS, 4), "traffic": None},
+               "dtype": "f16"}
+    else:
+        value = nbytes / (kern_ms * 1e-3) / 1e12
+        per_clk = nbytes / (loop_ms * 1e-3) / (sclk * 1e6) / nwg
+        clock["bytes_per_clk_per_cu"] = round(per_clk, 1)
+        out = {"metric": "LDS read rate (ds_read_b128, conflict-free), TB/s over 256 CUs and "
+                         "bytes per clock per CU",
+               "value": round(value, 2), "unit": "TB/s", "roofline": None, "dtype": "u32"}
+    out.update({"n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                "ms_per_step": round(wall * 1e3 / args.steps, 5), "higher_is_better": True,
+                "scaling": "weak", "vs_baseline": None, "data": "synthetic", "config": config,
+                "kernel_ms": {"avg_back_to_back": round(kern_ms, 5)}, "clock": clock,
+                "cpu_baseline": None})
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main_chain(args) -> int:
     import numpy as np
     import torch
@@ -334,6 +458,12 @@ def main() -> int:
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB per step "
                          "(calibration of the HBM byte counters)")
+    ap.add_argument("--data", default="random", choices=["random", "zero"],
+                    help="operand data of the MFMA issue-rate workloads")
+    ap.add_argument("--threads", type=int, default=512,
+                    help="threads per workgroup of the LDS read-rate workload")
+    ap.add_argument("--iters", type=int, default=0,
+                    help="loop iterations of the microbenchmark kernels (0 = default)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -346,6 +476,8 @@ def main() -> int:
     import mma_fragment_layouts_tn_amd as mfl
     import workloads as W
 
+    if args.workload in MICRO_WORKLOADS:
+        return main_micro(args)
     if args.workload in W.CHAIN_WORKLOADS:
         return main_chain(args)
     w = W.WORKLOADS[args.workload]

@@ -46,6 +46,41 @@ int mfl_probe_lds_tr16(const int32_t* lane_offsets, const uint16_t* lds_in, uint
  * -5 on a launch error. */
 int mfl_probe_xcc(int32_t nblocks, int32_t* out, void* stream);
 
+/* Measurement-only entry points: the rates the GEMM kernels are priced
+ * against (a contraction is bound by the matrix cores; the pages' GEMMs, e.g.
+ * "cute(7) simple_gemm" §10, only say the shared-memory version is faster).
+ * Both write, for each workgroup b, clocks[4b .. 4b+4) = (shader-clock cycle
+ * counter, 100 MHz real-time counter) before the timed loop and the same
+ * after it (device memory, 4*nwg uint64), so the shader clock held during the
+ * run is (cycles after - before) / (real time after - before) * 100 MHz.
+ *
+ * mfl_bench_mfma: nwg workgroups of 256 threads (4 waves, one per SIMD when
+ * nwg = 256, the number of compute units); every wave fills 2 sets of operand
+ * fragments from operands[0 .. n_operands) (device, fp16 bit patterns, read
+ * cyclically: random or zero data is the caller's choice), then issues
+ * iters x 32 v_mfma_f32_32x32x16_f16 (op 0; a 4 x 4 grid of 32x32 fp32
+ * tiles, 2^20 FLOP per wave per iteration) or iters x 128
+ * v_mfma_f32_16x16x32_f16 (op 1; 8 x 8 tiles of 16x16, 2^21 FLOP per wave per
+ * iteration), and writes one float per
+ * thread to sink (device, 256*nwg floats) so the work is not removed.
+ * Returns 0, -4 for a bad op, size or NULL pointer, -5 on a launch error.
+ *
+ * mfl_bench_lds_read: nwg workgroups of `threads` threads (a multiple of 64,
+ * at most 1024), each with 96 KB of LDS (one workgroup per compute unit);
+ * every wave issues iters x 8 ds_read_b128, each covering 1 KB contiguously
+ * (64 lanes x 16 bytes, every bank once per 16-lane pass): 8 KB per wave per
+ * iteration.  sink: device, nwg uint32.  Returns 0, -4 for a bad size or NULL
+ * pointer, -5 on a launch error. */
+int mfl_bench_mfma(int32_t op, const uint16_t* operands, int32_t n_operands, int32_t iters,
+                   int32_t nwg, float* sink, uint64_t* clocks, void* stream);
+int mfl_bench_lds_read(int32_t threads, int32_t iters, int32_t nwg, uint32_t* sink,
+                       uint64_t* clocks, void* stream);
+
+/* The rate of the real-time counter the two entry points above record, in
+ * kHz, for the current device (*khz, host memory).  Returns 0, -4 for a NULL
+ * pointer, -5 when the runtime does not report it. */
+int mfl_wall_clock_khz(int32_t* khz);
+
 #ifdef __cplusplus
 }
 #endif

@@ -127,6 +127,12 @@ def _load() -> ctypes.CDLL:
     lib.mfl_probe_lds_tr16.restype = ctypes.c_int
     lib.mfl_probe_xcc.argtypes = [i32, vp, vp]
     lib.mfl_probe_xcc.restype = ctypes.c_int
+    lib.mfl_bench_mfma.argtypes = [i32, vp, i32, i32, i32, vp, vp, vp]
+    lib.mfl_bench_mfma.restype = ctypes.c_int
+    lib.mfl_bench_lds_read.argtypes = [i32, i32, i32, vp, vp, vp]
+    lib.mfl_bench_lds_read.restype = ctypes.c_int
+    lib.mfl_wall_clock_khz.argtypes = [P(i32)]
+    lib.mfl_wall_clock_khz.restype = ctypes.c_int
     return lib
 
 
@@ -491,3 +497,23 @@ def probe_xcc(nblocks: int) -> torch.Tensor:
     rc = _lib.mfl_probe_xcc(nblocks, out.data_ptr(), torch.cuda.current_stream().cuda_stream)
     _check(rc)
     return out
+
+
+# ------------------------------------------------------- microbenchmarks
+def bench_mfma_raw(op: int, operands: int, n_operands: int, iters: int, nwg: int, sink: int,
+                   clocks: int, stream: int) -> int:
+    """Enqueue the MFMA issue-rate kernel (mfl_bench_mfma); raw pointers."""
+    return _lib.mfl_bench_mfma(op, operands, n_operands, iters, nwg, sink, clocks, stream)
+
+
+def bench_lds_read_raw(threads: int, iters: int, nwg: int, sink: int, clocks: int,
+                       stream: int) -> int:
+    """Enqueue the LDS read-rate kernel (mfl_bench_lds_read); raw pointers."""
+    return _lib.mfl_bench_lds_read(threads, iters, nwg, sink, clocks, stream)
+
+
+def wall_clock_khz() -> int:
+    """Rate of the real-time counter the microbenchmarks record (kHz)."""
+    out = ctypes.c_int32(0)
+    _check(_lib.mfl_wall_clock_khz(ctypes.byref(out)))
+    return int(out.value)

@@ -19,7 +19,7 @@ OBJDIR = os.path.join(os.path.dirname(PKG), "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["gemm_inst_256.hip", "gemm_inst_256w4.hip", "gemm_inst_128.hip",
-           "gemm_inst_128w1.hip", "gemm_inst_splitk.hip", "chain_inst.hip", "gemm_dispatch.hip", "probe_kernels.hip", "capi.cpp"]
+           "gemm_inst_128w1.hip", "gemm_inst_splitk.hip", "chain_inst.hip", "gemm_dispatch.hip", "probe_kernels.hip", "microbench.hip", "capi.cpp"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-mcode-object-version=5",
