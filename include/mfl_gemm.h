@@ -51,7 +51,7 @@ typedef enum { MFL_NONE = 0, MFL_F16 = 1, MFL_F32 = 2 } mfl_dtype;
 typedef enum { MFL_A_KMAJOR = 0, MFL_A_MMAJOR = 1 } mfl_a_order;
 
 /* Kernel choice (low 8 bits of gemm_dtypes_t.algo).  AUTO picks per shape:
- * LDS_256 (LDS_256_W4 when both operands go straight into LDS and C is
+ * LDS_256 (LDS_256_16 when both operands go straight into LDS and C is
  * absent) once the grid has at least 192 tiles of 256x256; else LDS_SPLITK
  * when the grid has fewer than 256 tiles of 128x128 and K >= 1024; else
  * LDS_128.
@@ -73,7 +73,15 @@ typedef enum { MFL_A_KMAJOR = 0, MFL_A_MMAJOR = 1 } mfl_a_order;
  * when its base and lda are 16-byte aligned and M % 8 == 0, and its operand
  * fragments are read with the transposing LDS read; otherwise it is
  * transposed in registers.  MFL_ALGO_REG_FETCH or-ed into algo forces
- * register fetch. */
+ * register fetch.
+ * The *_16 kernels run the same block tiles on v_mfma_f32_16x16x32_f16
+ * (the others on v_mfma_f32_32x32x16_f16): LDS_256_W4_16 with 4 waves of
+ * 128x128, LDS_256_16 with 8 waves of 128x64, LDS_128_16 128x128x64 tiles
+ * with 4 waves of 64x64.  They do not transpose an M-contiguous A in
+ * registers, and LDS_256_16 fetches only straight into LDS; LDS_256_W4 does
+ * not combine an M-contiguous A straight into LDS with B through registers.
+ * A forced kernel that does not offer the fetch path a call needs returns
+ * MFL_E_ALGO_CASE. */
 typedef enum {
   MFL_ALGO_AUTO = 0,
   MFL_ALGO_DIRECT = 1,
@@ -82,7 +90,10 @@ typedef enum {
   MFL_ALGO_LDS_256_W4 = 4,
   MFL_ALGO_LDS_128_W1 = 5,
   MFL_ALGO_LDS_SPLITK = 6,
-  MFL_ALGO_COUNT = 7,
+  MFL_ALGO_LDS_256_W4_16 = 7,
+  MFL_ALGO_LDS_256_16 = 8,
+  MFL_ALGO_LDS_128_16 = 9,
+  MFL_ALGO_COUNT = 10,
   MFL_ALGO_MASK = 0xff,
   MFL_ALGO_REG_FETCH = 0x100
 } mfl_algo;

@@ -101,13 +101,18 @@ int check(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const voi
     else
       plan->fetch_a = !force_reg && dma_ok(A, lda) ? mfl::kFetchDma : mfl::kFetchReg;
     plan->fetch_b = !force_reg && dma_ok(B, ldb) ? mfl::kFetchDma : mfl::kFetchReg;
-    // One wave per SIMD (128x128 per wave) reads a third less from LDS and
-    // wins when both operands go straight into LDS and the epilogue only
-    // stores; register fetch or a C read need the second wave per SIMD to
-    // hide their latency.
+    // With both operands straight into LDS and no C, the same 256x256 tile
+    // on v_mfma_f32_16x16x32_f16: the chip holds a higher clock with it under
+    // the power limit (measured by the MFMA issue-rate kernel) and the
+    // eight-wave kernel is the fastest at 4096^3.  Register fetch and C reads
+    // stay on the 32x32x16 kernel, which measured faster there.
     if (auto_algo && algo == mfl::kAlgoLds256 && plan->fetch_a == mfl::kFetchDma &&
         plan->fetch_b == mfl::kFetchDma && dt.c == MFL_NONE)
-      plan->algo = mfl::kAlgoLds256W4;
+      plan->algo = mfl::kAlgoLds256x16;
+    // a forced configuration without an instance for this fetch path
+    if (plan->algo != mfl::kAlgoDirect &&
+        !mfl::kernel_symbol(plan->algo, plan->fetch_a, plan->fetch_b, dt.c, dt.d))
+      return MFL_E_ALGO_CASE;
   }
   return MFL_OK;
 }
@@ -351,7 +356,7 @@ int frag_coords(int operand, int32_t* out, int64_t cap, int32_t* threads, int32_
   int ns = 0;
   if (operand == 0) ns = Cfg::KSUB_W * Cfg::RM * 8;
   else if (operand == 1) ns = Cfg::KSUB_W * Cfg::RN * 8;
-  else if (operand == 2) ns = Cfg::RM * Cfg::RN * 16;
+  else if (operand == 2) ns = Cfg::RM * Cfg::RN * Cfg::kNV;
   else if (operand == 3) ns = Cfg::KSUB_W * Cfg::RM;
   else return mfl::kLayoutBadIndex;
   if (threads) *threads = Cfg::kThreads;
@@ -375,7 +380,7 @@ int frag_coords(int operand, int32_t* out, int64_t cap, int32_t* threads, int32_
     } else if (operand == 2) {
       for (int i = 0; i < Cfg::RM; ++i)
         for (int j = 0; j < Cfg::RN; ++j)
-          for (int v = 0; v < 16; ++v) {
+          for (int v = 0; v < Cfg::kNV; ++v) {
             const mfl::RowK c = mfl::frag_c_coord<Cfg>(w, lane, i, j, v);
             put(c.row, c.k);
           }
@@ -691,6 +696,12 @@ int mfl_lds_tile_offsets(int32_t algo, int32_t operand, int32_t* out, int64_t ca
       return lds_offsets<mfl::CfgLds128W1>(operand, out, cap, outer, inner);
     case mfl::kAlgoLdsSplitK:
       return lds_offsets<mfl::CfgLdsSplitK>(operand, out, cap, outer, inner);
+    case mfl::kAlgoLds256W4x16:
+      return lds_offsets<mfl::CfgLds256W4x16>(operand, out, cap, outer, inner);
+    case mfl::kAlgoLds256x16:
+      return lds_offsets<mfl::CfgLds256x16>(operand, out, cap, outer, inner);
+    case mfl::kAlgoLds128x16:
+      return lds_offsets<mfl::CfgLds128x16>(operand, out, cap, outer, inner);
     default: return mfl::kLayoutBadIndex;
   }
 }
@@ -723,6 +734,12 @@ int mfl_fragment_coords(int32_t algo, int32_t operand, int32_t* out, int64_t cap
     case mfl::kAlgoLds256W4: return frag_coords<mfl::CfgLds256W4>(operand, out, cap, threads, slots);
     case mfl::kAlgoLds128W1: return frag_coords<mfl::CfgLds128W1>(operand, out, cap, threads, slots);
     case mfl::kAlgoLdsSplitK: return frag_coords<mfl::CfgLdsSplitK>(operand, out, cap, threads, slots);
+    case mfl::kAlgoLds256W4x16:
+      return frag_coords<mfl::CfgLds256W4x16>(operand, out, cap, threads, slots);
+    case mfl::kAlgoLds256x16:
+      return frag_coords<mfl::CfgLds256x16>(operand, out, cap, threads, slots);
+    case mfl::kAlgoLds128x16:
+      return frag_coords<mfl::CfgLds128x16>(operand, out, cap, threads, slots);
     default: return mfl::kLayoutBadIndex;
   }
 }

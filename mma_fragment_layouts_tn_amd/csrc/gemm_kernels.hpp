@@ -42,7 +42,79 @@ namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
 using lds_ptr_t = __attribute__((address_space(3))) void*;
+
+// The matrix instruction of a configuration: acc += A B^T on one atom, with
+// one 8-half operand fragment per lane for A and for B.
+//  * 32x32x16: the compiler's builtin.
+//  * 16x16x32: the instruction with its accumulator tied to one AGPR tuple.
+//    With the builtin the compiler does not keep a wave's 64 four-register
+//    accumulator tuples in place across the K loop and copies them around
+//    every iteration (the sixteen-register tuples of the 32x32 form stay in
+//    place).  The compiler cannot see hazards through the tied form: each
+//    instruction carries two wait states ahead of it (operands assembled by
+//    vector instructions), and mma_begin / mma_end below cover the
+//    accumulators' zero fill and the first reads of the results.
+template <int OP>
+struct Mma;
+template <>
+struct Mma<kMfma32x32x16> {
+  using Acc = floatx16;
+  static __device__ __forceinline__ void run(const half8& a, const half8& b, Acc& c) {
+    c = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
+template <>
+struct Mma<kMfma16x16x32> {
+  using Acc = floatx4;
+  static __device__ __forceinline__ void run(const half8& a, const half8& b, Acc& c) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_f16 %0, %1, %2, %0"
+                 : "+a"(c)
+                 : "v"(a), "v"(b));
+  }
+};
+template <class Cfg>
+using AccT = typename Mma<Cfg::kOp>::Acc;
+
+template <class Cfg>
+__device__ __forceinline__ void zero_acc(AccT<Cfg> (&acc)[Cfg::RM][Cfg::RN]) {
+#pragma unroll
+  for (int i = 0; i < Cfg::RM; ++i)
+#pragma unroll
+    for (int j = 0; j < Cfg::RN; ++j)
+#pragma unroll
+      for (int v = 0; v < Cfg::kNV; ++v) acc[i][j][v] = 0.0f;
+}
+
+// Before the first matrix instruction: every accumulator holds its zeros
+// (the empty statements take each tuple as written), then wait states cover
+// the vector writes of those zeros.
+template <class Cfg>
+__device__ __forceinline__ void mma_begin(AccT<Cfg> (&acc)[Cfg::RM][Cfg::RN]) {
+#pragma unroll
+  for (int i = 0; i < Cfg::RM; ++i)
+#pragma unroll
+    for (int j = 0; j < Cfg::RN; ++j) asm volatile("" : "+a"(acc[i][j]));
+  asm volatile("s_nop 4" ::);
+}
+
+// After the last matrix instruction: 24 wait states (more than either
+// instruction's latency), then the empty statements, so no read of an
+// accumulator can be placed before the results are written.  Needed for the
+// tied form, whose hazards the compiler cannot see, and for the builtin as
+// well: where the last instructions sit in a conditional block (the K
+// remainder) this compiler reads an accumulator in the following block, or
+// spills it, with no wait states (measured: a stale value in one register of
+// one tile, through the fp32-C epilogue of the one-wave 128x128 kernel).
+template <class Cfg>
+__device__ __forceinline__ void mma_end(AccT<Cfg> (&acc)[Cfg::RM][Cfg::RN]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::);
+#pragma unroll
+  for (int i = 0; i < Cfg::RM; ++i)
+#pragma unroll
+    for (int j = 0; j < Cfg::RN; ++j) asm volatile("" : "+a"(acc[i][j]));
+}
 
 // 16-byte global load at any 2-byte alignment (gfx9 runs in unaligned access
 // mode, so this is one global_load_dwordx4 either way).
@@ -204,12 +276,14 @@ __device__ __forceinline__ void load_c_vec(const GemmParams& p, int m, int n, fl
 
 // every value of a lane lies in the lane's own column of the atom, so the
 // column of acc[i][j][v] depends on (lane, j) only
+template <int OP>
 MFL_HD constexpr bool c_columns_per_lane() {
-  for (int v = 0; v < 16; ++v)
-    if (atom_c_coord(0, v).k != 0) return false;
+  for (int v = 0; v < AtomTraits<OP>::NV; ++v)
+    if (atom_c_coord_of<OP>(0, v).k != 0) return false;
   return true;
 }
-static_assert(c_columns_per_lane(), "accumulator column must not depend on the value");
+static_assert(c_columns_per_lane<kMfma32x32x16>() && c_columns_per_lane<kMfma16x16x32>(),
+              "accumulator column must not depend on the value");
 
 // whole tile inside D, vector-aligned rows, and every row of the tile within
 // reach of one buffer descriptor
@@ -222,92 +296,107 @@ __device__ __forceinline__ bool register_epilogue_ok(const GemmParams& p, int m0
 }
 
 // the buffer-descriptor path alone (one straight block: the kernels with one
-// wave per SIMD have no registers for a second path)
+// wave per SIMD have no registers for a second path).  A lane's repeats j of
+// row block i sit in RN / V runs g of V adjacent columns (jl = j % V), run g
+// AN V columns after run 0: one V-element vector of D per (i, v, g).
 template <class Cfg, int CK, int DK, class Own = AllRows>
 __device__ __forceinline__ void epilogue_regs(const GemmParams& p, int w, int lane, int m0,
-                                              int n0, const floatx16 (&acc)[Cfg::RM][Cfg::RN],
+                                              int n0, const AccT<Cfg> (&acc)[Cfg::RM][Cfg::RN],
                                               Own own = Own()) {
-  constexpr int RM = Cfg::RM, RN = Cfg::RN;
+  constexpr int RM = Cfg::RM, V = Cfg::kVec, NG = Cfg::RN / V, NV = Cfg::kNV;
+  constexpr int AM = Cfg::kAtomM, AN = Cfg::kAtomN;
   constexpr int ES = DK == 1 ? 2 : 4, CS = CK == 1 ? 2 : 4;
   {
-    const RowK cl = atom_c_coord(lane, 0);
+    const RowK cl = atom_c_coord_of<Cfg::kOp>(lane, 0);
     const RowK w0 = frag_c_coord<Cfg>(w, 0, 0, 0, 0);     // the wave's tile origin
     // raw buffers (stride 0), records up to 2^31 bytes, 32-bit data format
     const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(
         (char*)p.D + ((int64_t)(m0 + w0.row) * p.ldd + (n0 + w0.k)) * ES, (short)0, 0x7fffffff,
         0x00020000);
-    const int voff = (cl.row * p.ldd + RN * cl.k) * ES;
+    const int voff = (cl.row * p.ldd + V * cl.k) * ES;
     __amdgpu_buffer_rsrc_t rc = rd;
     int cvoff = 0;
     if constexpr (CK != 0) {
       rc = __builtin_amdgcn_make_buffer_rsrc(
           (char*)p.C + ((int64_t)(m0 + w0.row) * p.ldc + (n0 + w0.k)) * CS, (short)0, 0x7fffffff,
           0x00020000);
-      cvoff = (cl.row * p.ldc + RN * cl.k) * CS;
+      cvoff = (cl.row * p.ldc + V * cl.k) * CS;
     }
-    constexpr int QB = 8;   // C vectors loaded before the first is used
+    constexpr int QB = NV < 8 ? NV : 8;   // values whose C vectors load before first use
 #pragma unroll
     for (int i = 0; i < RM; ++i) {
       if (!own(i)) continue;
 #pragma unroll
-      for (int v0 = 0; v0 < 16; v0 += QB) {
-        float c[QB][RN];
+      for (int v0 = 0; v0 < NV; v0 += QB) {
+        float c[QB][NG][V];
         if constexpr (CK != 0) {
 #pragma unroll
           for (int q = 0; q < QB; ++q)
-            buffer_load_c<CK, RN>(c[q], rc, cvoff,
-                                  (i * Cfg::kAtomM + atom_c_coord(0, v0 + q).row) * p.ldc * CS);
+#pragma unroll
+            for (int g = 0; g < NG; ++g)
+              buffer_load_c<CK, V>(
+                  c[q][g], rc, cvoff,
+                  (i * AM + atom_c_coord_of<Cfg::kOp>(0, v0 + q).row) * p.ldc * CS +
+                      g * AN * V * CS);
         }
 #pragma unroll
         for (int q = 0; q < QB; ++q) {
           const int v = v0 + q;
-          float x[RN];
 #pragma unroll
-          for (int j = 0; j < RN; ++j) {
-            // (copied to a scalar first: a bit cast applied to a vector element
-            // directly read element 0 with this compiler)
-            x[j] = acc[i][j][v];
-            if constexpr (CK != 0) x[j] += c[q][j];
+          for (int g = 0; g < NG; ++g) {
+            float x[V];
+#pragma unroll
+            for (int jl = 0; jl < V; ++jl) {
+              // (copied to a scalar first: a bit cast applied to a vector
+              // element directly read element 0 with this compiler)
+              x[jl] = acc[i][g * V + jl][v];
+              if constexpr (CK != 0) x[jl] += c[q][g][jl];
+            }
+            buffer_store_d<DK, V>(
+                x, rd, voff,
+                (i * AM + atom_c_coord_of<Cfg::kOp>(0, v).row) * p.ldd * ES + g * AN * V * ES);
           }
-          buffer_store_d<DK, RN>(x, rd, voff,
-                                 (i * Cfg::kAtomM + atom_c_coord(0, v).row) * p.ldd * ES);
         }
       }
     }
   }
 }
 
-// any tile: one vector per (i, v) where it fits inside D and the rows are
-// vector-aligned, elements otherwise
+// any tile: one vector per (i, v, run) where it fits inside D and the rows
+// are vector-aligned, elements otherwise
 template <class Cfg, int CK, int DK, class Own = AllRows>
 __device__ __forceinline__ void epilogue_any(const GemmParams& p, int w, int lane, int m0,
-                                             int n0, const floatx16 (&acc)[Cfg::RM][Cfg::RN],
+                                             int n0, const AccT<Cfg> (&acc)[Cfg::RM][Cfg::RN],
                                              Own own = Own()) {
-  constexpr int RM = Cfg::RM, RN = Cfg::RN;
+  constexpr int RM = Cfg::RM, V = Cfg::kVec, NG = Cfg::RN / V, AN = Cfg::kAtomN;
   const bool vec = p.d_vec && (CK == 0 || p.c_vec);
 #pragma unroll
   for (int i = 0; i < RM; ++i) {
     if (!own(i)) continue;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const RowK c0 = frag_c_coord<Cfg>(w, lane, i, 0, v);   // columns n .. n+RN-1
-      const int m = m0 + c0.row, n = n0 + c0.k;
+    for (int v = 0; v < Cfg::kNV; ++v) {
+      const RowK c0 = frag_c_coord<Cfg>(w, lane, i, 0, v);   // run 0: columns n .. n+V-1
+      const int m = m0 + c0.row;
       if (m >= p.M) continue;
-      float x[RN];
 #pragma unroll
-      for (int j = 0; j < RN; ++j) x[j] = acc[i][j][v];
-      if (vec && n + RN <= p.N) {
-        if constexpr (CK != 0) {
-          float c[RN];
-          load_c_vec<CK, RN>(p, m, n, c);
+      for (int g = 0; g < NG; ++g) {
+        const int n = n0 + c0.k + g * AN * V;
+        float x[V];
 #pragma unroll
-          for (int j = 0; j < RN; ++j) x[j] += c[j];
+        for (int jl = 0; jl < V; ++jl) x[jl] = acc[i][g * V + jl][v];
+        if (vec && n + V <= p.N) {
+          if constexpr (CK != 0) {
+            float c[V];
+            load_c_vec<CK, V>(p, m, n, c);
+#pragma unroll
+            for (int jl = 0; jl < V; ++jl) x[jl] += c[jl];
+          }
+          store_d_vec<DK, V>(p, m, n, x);
+        } else {
+#pragma unroll
+          for (int jl = 0; jl < V; ++jl)
+            if (n + jl < p.N) d_store<DK>(p, m, n + jl, x[jl] + c_value<CK>(p, m, n + jl));
         }
-        store_d_vec<DK, RN>(p, m, n, x);
-      } else {
-#pragma unroll
-        for (int j = 0; j < RN; ++j)
-          if (n + j < p.N) d_store<DK>(p, m, n + j, x[j] + c_value<CK>(p, m, n + j));
       }
     }
   }
@@ -322,7 +411,7 @@ __device__ __forceinline__ void epilogue_any(const GemmParams& p, int w, int lan
 // partial blocks into the freed operand stages and the owner adds them, so
 // every member finishes RM/WAVES_K row blocks (a reduce-scatter inside the
 // workgroup).  A block is
-// 16 values x 64 lanes, laid out [v/4][lane][v%4]: each lane moves 16-byte
+// NV values x 64 lanes, laid out [v/4][lane][v%4]: each lane moves 16-byte
 // pieces and the 64 lanes of one access cover 1 KB contiguously.
 template <class Cfg>
 struct OwnedRows {
@@ -332,13 +421,13 @@ struct OwnedRows {
 
 template <class Cfg>
 __device__ __forceinline__ void reduce_k_groups(float* red, int w, int lane,
-                                                floatx16 (&acc)[Cfg::RM][Cfg::RN]) {
-  constexpr int RN = Cfg::RN, WK = Cfg::WAVES_K, NB = Cfg::RM * RN;
+                                                AccT<Cfg> (&acc)[Cfg::RM][Cfg::RN]) {
+  constexpr int RN = Cfg::RN, WK = Cfg::WAVES_K, NB = Cfg::RM * RN, NV = Cfg::kNV;
   const int wg = w % Cfg::kGroupWaves, wk = wave_k<Cfg>(w);
   auto block = [&](int b, int writer) {
     const int owner = (b / RN) % WK;
     const int slot = (writer - owner - 1 + WK) % WK;    // 0 .. WK-2
-    return red + ((wg * NB + b) * (WK - 1) + slot) * (16 * 64) + lane * 4;
+    return red + ((wg * NB + b) * (WK - 1) + slot) * (NV * 64) + lane * 4;
   };
   __syncthreads();   // every wave is done with the operand stages
 #pragma unroll
@@ -346,8 +435,8 @@ __device__ __forceinline__ void reduce_k_groups(float* red, int w, int lane,
     if ((b / RN) % WK == wk) continue;
     float* dst = block(b, wk);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const floatx16& a = acc[b / RN][b % RN];
+    for (int q = 0; q < NV / 4; ++q) {
+      const AccT<Cfg>& a = acc[b / RN][b % RN];
       const float4 x = make_float4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
       *(float4*)(dst + q * 256) = x;
     }
@@ -360,7 +449,7 @@ __device__ __forceinline__ void reduce_k_groups(float* red, int w, int lane,
     for (int m = 1; m < WK; ++m) {
       const float* src = block(b, (wk + m) % WK);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < NV / 4; ++q) {
         const float4 x = *(const float4*)(src + q * 256);
         acc[b / RN][b % RN][4 * q] += x.x;
         acc[b / RN][b % RN][4 * q + 1] += x.y;
@@ -421,10 +510,11 @@ __device__ __forceinline__ void store_d4(const GemmParams& p, int m, int n, floa
 template <class Cfg, int CK, int DK>
 __device__ __forceinline__ void epilogue_lds(const GemmParams& p, float* sm, int w, int lane,
                                              int m0, int n0,
-                                             const floatx16 (&acc)[Cfg::RM][Cfg::RN]) {
-  constexpr int RM = Cfg::RM, RN = Cfg::RN, WTN = Cfg::WTN, IG = Cfg::kEpiRows;
-  constexpr int ROWS = IG * 32, V4 = WTN / 4, NV = ROWS * V4 / 64, QB = 8;
-  static_assert((ROWS * V4) % 64 == 0 && NV % QB == 0, "runs must divide over the lanes");
+                                             const AccT<Cfg> (&acc)[Cfg::RM][Cfg::RN]) {
+  constexpr int RM = Cfg::RM, WTN = Cfg::WTN, IG = Cfg::kEpiRows, AM = Cfg::kAtomM;
+  constexpr int V = Cfg::kVec, NG = Cfg::RN / V, AN = Cfg::kAtomN;
+  constexpr int ROWS = IG * AM, V4 = WTN / 4, NQ = ROWS * V4 / 64, QB = 8;
+  static_assert((ROWS * V4) % 64 == 0 && NQ % QB == 0, "runs must divide over the lanes");
   float* reg = sm + w * ROWS * WTN;
   const int wm = wave_m<Cfg>(w), wn = wave_n<Cfg>(w);
   const int mw = m0 + wm * Cfg::WTM, nw = n0 + wn * WTN;
@@ -432,23 +522,27 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, float* sm, int
   __syncthreads();   // every wave is done with the operand stages
 #pragma unroll
   for (int i0 = 0; i0 < RM; i0 += IG) {
-    // accumulators -> this wave's staging tile (rows i0*32 .. +ROWS), at
-    // their physical columns: a lane's RN repeats are adjacent, one vector
+    // accumulators -> this wave's staging tile (rows i0*AM .. +ROWS), at
+    // their physical columns: a lane's repeats come in runs of V adjacent
+    // columns, one vector per run
 #pragma unroll
     for (int ii = 0; ii < IG; ++ii)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const RowK c = atom_c_coord(lane, v);
-        typedef float fv __attribute__((ext_vector_type(RN)));
-        fv x;
+      for (int v = 0; v < Cfg::kNV; ++v) {
+        const RowK c = atom_c_coord_of<Cfg::kOp>(lane, v);
+        typedef float fv __attribute__((ext_vector_type(V)));
 #pragma unroll
-        for (int j = 0; j < RN; ++j) x[j] = acc[i0 + ii][j][v];
-        *(fv*)&reg[epi_offset<WTN>(ii * 32 + c.row, RN * c.k)] = x;
+        for (int g = 0; g < NG; ++g) {
+          fv x;
+#pragma unroll
+          for (int jl = 0; jl < V; ++jl) x[jl] = acc[i0 + ii][g * V + jl][v];
+          *(fv*)&reg[epi_offset<WTN>(ii * AM + c.row, g * AN * V + V * c.k)] = x;
+        }
       }
     // A wave's LDS operations complete in order, so the reads below see the
     // stores above, and the next pass's stores follow these reads.
 #pragma unroll
-    for (int q0 = 0; q0 < NV; q0 += QB) {
+    for (int q0 = 0; q0 < NQ; q0 += QB) {
       float4 x[QB], c[QB];
 #pragma unroll
       for (int q = 0; q < QB; ++q) {
@@ -460,7 +554,7 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, float* sm, int
 #pragma unroll
           for (int q = 0; q < QB; ++q) {
             const int t = lane + 64 * (q0 + q);
-            c[q] = load_c4<CK>(p, mw + i0 * 32 + t / V4, nw + 4 * (t % V4));
+            c[q] = load_c4<CK>(p, mw + i0 * AM + t / V4, nw + 4 * (t % V4));
           }
         }
 #pragma unroll
@@ -473,13 +567,13 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, float* sm, int
             y.z += c[q].z;
             y.w += c[q].w;
           }
-          store_d4<DK>(p, mw + i0 * 32 + t / V4, nw + 4 * (t % V4), y);
+          store_d4<DK>(p, mw + i0 * AM + t / V4, nw + 4 * (t % V4), y);
         }
       } else {
 #pragma unroll
         for (int q = 0; q < QB; ++q) {
           const int t = lane + 64 * (q0 + q);
-          const int m = mw + i0 * 32 + t / V4, n = nw + 4 * (t % V4);
+          const int m = mw + i0 * AM + t / V4, n = nw + 4 * (t % V4);
           if (m < p.M) {
             if (n + 3 < p.N) {
               float4 y = x[q];
@@ -630,7 +724,7 @@ struct FetchRegT {
 // DMAT: M-contiguous A straight into an M-contiguous LDS tile (BK rows of
 // ROWS halves, lds_offset_mn).  A 1 KB run holds RUN = 512/ROWS k-rows; lane
 // l takes k-row RUN*run + l/CPR, physical chunk l%CPR, so it fetches logical
-// chunk (l%CPR) ^ 4(krow&3), i.e. m = row0 + 8 * that.  Needs M % 8 == 0
+// chunk (l%CPR) ^ mn_swz(krow), i.e. m = row0 + 8 * that.  Needs M % 8 == 0
 // (chunks are all-valid or all-past-M; the latter are clamped to the last
 // valid chunk and only feed outputs that are never stored).
 template <class Cfg, int ROWS>
@@ -648,7 +742,7 @@ struct FetchDmaT {
 #pragma unroll
     for (int i = 0; i < kRuns; ++i) {
       const int krow = RUN * (run0 + i) + lane / CPR;
-      const int c = (lane % CPR) ^ ((krow & 3) << 2);
+      const int c = (lane % CPR) ^ mn_swz(krow);
       const int m = min(8 * c, rows_valid - 8);
       off[i] = (unsigned)(((int64_t)krow * ld + row0 + m) * 2);
     }
@@ -811,20 +905,15 @@ __global__ void __launch_bounds__(Cfg::kThreads, 1) gemm_tiled(const GemmParams 
     for (int r = 0; r < kReads; ++r) read_one(r, buf, kk, s);
   };
 
-  floatx16 acc[RM][RN];
-#pragma unroll
-  for (int i = 0; i < RM; ++i)
-#pragma unroll
-    for (int j = 0; j < RN; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+  AccT<Cfg> acc[RM][RN];
+  zero_acc<Cfg>(acc);
+  mma_begin<Cfg>(acc);
 
   auto mma = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < RM; ++i)
 #pragma unroll
-      for (int j = 0; j < RN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < RN; ++j) Mma<Cfg::kOp>::run(fa[buf][i], fb[buf][j], acc[i][j]);
   };
 
   // One group: the RM x RN MFMAs on fragment buffer `buf`.  A wave can issue
@@ -842,7 +931,7 @@ __global__ void __launch_bounds__(Cfg::kThreads, 1) gemm_tiled(const GemmParams 
 #pragma unroll
     for (int g = 0; g < kMfma; ++g) {
       const int i = g / RN, j = g % RN;
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
+      Mma<Cfg::kOp>::run(fa[buf][i], fb[buf][j], acc[i][j]);
       if constexpr (kR) {
         if (g < rslots) {
 #pragma unroll
@@ -991,6 +1080,7 @@ __global__ void __launch_bounds__(Cfg::kThreads, 1) gemm_tiled(const GemmParams 
       }
     }
   }
+  mma_end<Cfg>(acc);
   // Interior tiles with vector-aligned rows: vectors straight from the
   // registers.  Other tiles: split-K owners address each vector; the other
   // kernels stage through LDS into row runs of 4 (one code path less in the
@@ -1023,13 +1113,9 @@ __global__ void __launch_bounds__(Cfg::kThreads, 1) gemm_direct(const GemmParams
   const _Float16* A = (const _Float16*)p.A;
   const _Float16* B = (const _Float16*)p.B;
 
-  floatx16 acc[Cfg::RM][Cfg::RN];
-#pragma unroll
-  for (int i = 0; i < Cfg::RM; ++i)
-#pragma unroll
-    for (int j = 0; j < Cfg::RN; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+  AccT<Cfg> acc[Cfg::RM][Cfg::RN];
+  zero_acc<Cfg>(acc);
+  mma_begin<Cfg>(acc);
 
   const int nk = (p.K + BK - 1) / BK;
   for (int kt = 0; kt < nk; ++kt) {
@@ -1061,10 +1147,10 @@ __global__ void __launch_bounds__(Cfg::kThreads, 1) gemm_direct(const GemmParams
 #pragma unroll
       for (int i = 0; i < Cfg::RM; ++i)
 #pragma unroll
-        for (int j = 0; j < Cfg::RN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < Cfg::RN; ++j) Mma<Cfg::kOp>::run(af[i], bf[j], acc[i][j]);
     }
   }
+  mma_end<Cfg>(acc);
   if (register_epilogue_ok<Cfg, CK, DK>(p, m0, n0))
     epilogue_regs<Cfg, CK, DK>(p, w, lane, m0, n0, acc);
   else
@@ -1083,19 +1169,47 @@ constexpr KernelFn tiled_table[3][2] = {
     {gemm_tiled<Cfg, FA, FB, 1, 1>, gemm_tiled<Cfg, FA, FB, 1, 2>},
     {gemm_tiled<Cfg, FA, FB, 2, 1>, gemm_tiled<Cfg, FA, FB, 2, 2>}};
 
+// Fetch policy pairs a configuration offers.  The 16x16x32 configurations
+// issue their instruction with the accumulator tied by hand (Mma above), so
+// the compiler must never move an accumulator between the first and the last
+// instruction; that holds only where registers are not short.  They do not
+// offer the transposing register fetch of an M-contiguous A, and the one with
+// two waves per SIMD (256 registers per lane) offers only direct-to-LDS fetch.
+// The build checks the generated code of every instance for such moves.
+template <class Cfg>
+constexpr bool offers(int fa, int fb) {
+  // The four-wave 256x256 kernel with M-contiguous A straight into LDS and
+  // B through registers: this compiler moves accumulators in a block where
+  // the preceding matrix instructions' results may not be written yet, and
+  // the build's check rejects it; that case runs on the eight-wave kernel.
+  if (Cfg::kOp == kMfma32x32x16)
+    return !(Cfg::BM == 256 && Cfg::kWaves == 4 && fa == kFetchDmaT && fb == kFetchReg);
+  if (fa == kFetchRegT) return false;
+  if (Cfg::kWaves > 4) return fb == kFetchDma && (fa == kFetchDma || fa == kFetchDmaT);
+  return true;
+}
+
+template <class Cfg, int FA, int FB>
+const void* instance(int ck, int dk) {
+  if constexpr (offers<Cfg>(FA, FB))
+    return (const void*)tiled_table<Cfg, FA, FB>[ck][dk - 1];
+  else
+    return nullptr;
+}
+
 // fetch policy pairs used: (A, B) = (DMA, DMA), (REG, REG), (REG, DMA),
 // (DMA, REG), (REGT, DMA), (REGT, REG), (DMAT, DMA), (DMAT, REG)
 template <class Cfg>
 const void* tiled_symbol(int fa, int fb, int ck, int dk) {
   if (ck < 0 || ck > 2 || dk < 1 || dk > 2) return nullptr;
-  if (fa == kFetchDma && fb == kFetchDma) return (const void*)tiled_table<Cfg, kFetchDma, kFetchDma>[ck][dk - 1];
-  if (fa == kFetchReg && fb == kFetchReg) return (const void*)tiled_table<Cfg, kFetchReg, kFetchReg>[ck][dk - 1];
-  if (fa == kFetchReg && fb == kFetchDma) return (const void*)tiled_table<Cfg, kFetchReg, kFetchDma>[ck][dk - 1];
-  if (fa == kFetchDma && fb == kFetchReg) return (const void*)tiled_table<Cfg, kFetchDma, kFetchReg>[ck][dk - 1];
-  if (fa == kFetchRegT && fb == kFetchDma) return (const void*)tiled_table<Cfg, kFetchRegT, kFetchDma>[ck][dk - 1];
-  if (fa == kFetchRegT && fb == kFetchReg) return (const void*)tiled_table<Cfg, kFetchRegT, kFetchReg>[ck][dk - 1];
-  if (fa == kFetchDmaT && fb == kFetchDma) return (const void*)tiled_table<Cfg, kFetchDmaT, kFetchDma>[ck][dk - 1];
-  if (fa == kFetchDmaT && fb == kFetchReg) return (const void*)tiled_table<Cfg, kFetchDmaT, kFetchReg>[ck][dk - 1];
+  if (fa == kFetchDma && fb == kFetchDma) return instance<Cfg, kFetchDma, kFetchDma>(ck, dk);
+  if (fa == kFetchReg && fb == kFetchReg) return instance<Cfg, kFetchReg, kFetchReg>(ck, dk);
+  if (fa == kFetchReg && fb == kFetchDma) return instance<Cfg, kFetchReg, kFetchDma>(ck, dk);
+  if (fa == kFetchDma && fb == kFetchReg) return instance<Cfg, kFetchDma, kFetchReg>(ck, dk);
+  if (fa == kFetchRegT && fb == kFetchDma) return instance<Cfg, kFetchRegT, kFetchDma>(ck, dk);
+  if (fa == kFetchRegT && fb == kFetchReg) return instance<Cfg, kFetchRegT, kFetchReg>(ck, dk);
+  if (fa == kFetchDmaT && fb == kFetchDma) return instance<Cfg, kFetchDmaT, kFetchDma>(ck, dk);
+  if (fa == kFetchDmaT && fb == kFetchReg) return instance<Cfg, kFetchDmaT, kFetchReg>(ck, dk);
   return nullptr;
 }
 

@@ -32,7 +32,10 @@ enum Algo : int {
   kAlgoLds256W4 = 4,    // 4 waves of 128x128
   kAlgoLds128W1 = 5,    // 1 wave of 128x128 per workgroup, 4 workgroups per CU
   kAlgoLdsSplitK = 6,   // 128x64 tile, 4 waves each taking a quarter of every K stage
-  kAlgoCount = 7
+  kAlgoLds256W4x16 = 7,   // 4 waves of 128x128, 16x16x32 instructions
+  kAlgoLds256x16 = 8,     // 8 waves of 128x64, 16x16x32 instructions
+  kAlgoLds128x16 = 9,     // 128x128x64, 4 waves of 64x64, 16x16x32 instructions
+  kAlgoCount = 10
 };
 
 // how an operand tile travels from global memory to LDS
@@ -64,9 +67,18 @@ using CfgLds128W1 = TileCfg<128, 128, 32, 1, 1>;
 // stages, 144 KB of LDS).
 using CfgLdsSplitK = TileCfg<128, 64, 128, 1, 1, 1, 4, 3>;
 
+// The same block tiles on v_mfma_f32_16x16x32_f16, the instruction that
+// holds a higher clock under the power limit on random data (measured with
+// the MFMA issue-rate kernel): one 64-deep stage is two 32-deep sub-steps.
+using CfgLds256W4x16 = TileCfg<256, 256, 64, 2, 2, 1, 1, 2, kMfma16x16x32>;
+using CfgLds256x16 = TileCfg<256, 256, 64, 2, 4, 1, 1, 2, kMfma16x16x32>;
+using CfgLds128x16 = TileCfg<128, 128, 64, 2, 2, 1, 1, 2, kMfma16x16x32>;
+
 static_assert(frag_c_is_partition_c<CfgLds128>() && frag_c_is_partition_c<CfgLds256>() &&
                   frag_c_is_partition_c<CfgLds256W4>() && frag_c_is_partition_c<CfgLds128W1>() &&
-                  frag_c_is_partition_c<CfgLdsSplitK>(),
+                  frag_c_is_partition_c<CfgLdsSplitK>() &&
+                  frag_c_is_partition_c<CfgLds256W4x16>() &&
+                  frag_c_is_partition_c<CfgLds256x16>() && frag_c_is_partition_c<CfgLds128x16>(),
               "accumulator coordinates must be the tiled MMA's partition_C");
 
 struct KernelInfo {

@@ -56,6 +56,31 @@ def out_buffer(M, ldd, d, dev="cuda"):
     return t
 
 
+# configurations that offer only some fetch paths (the 16x16x32 ones, and
+# the four-wave 256x256 one without M-contiguous A straight to LDS with B
+# through registers)
+PARTIAL_FETCH_ALGOS = {"lds256w4_16", "lds256_16", "lds128_16", "lds256w4"}
+
+
+def refused(w: W.Workload, algo: str) -> bool:
+    """True when `algo` does not offer the fetch path this case needs (it is
+    one of PARTIAL_FETCH_ALGOS and the C ABI answers MFL_E_ALGO_CASE); any
+    other refusal fails the calling test."""
+    ckind = {None: mfl.NONE, "f16": mfl.F16, "f32": mfl.F32}[w.c]
+    dkind = {"f16": mfl.F16, "f32": mfl.F32}[w.d]
+    a_order = mfl.A_KMAJOR if w.a_order == "k" else mfl.A_MMAJOR
+    dt = mfl.dtypes(ckind, dkind, a_order, mfl.algo_code(algo))
+    # distinct 256-byte aligned stand-in addresses, aligned as torch's device buffers
+    PA, PB, PC, PD = (k << 20 for k in (1, 2, 3, 4))
+    rc = mfl.validate(w.M, w.N, w.K, PA, w.lda_, PB, w.ldb_, None if w.c is None else PC,
+                      w.ldc_ if w.c is not None else 0, PD, w.ldd_, dt)[0]
+    if rc == -6 and algo.split("+")[0] in PARTIAL_FETCH_ALGOS:
+        say(f"[gpu] {w.name} {algo}: fetch path not offered by this configuration")
+        return True
+    assert rc == 0, (w.name, algo, rc, mfl.strerror(rc))
+    return False
+
+
 def run_gemm(w: W.Workload, x: W.Inputs, algo: str, in_place: bool = False):
     """Upload, call gemm_tn through the C ABI, download.  Returns
     (D as float64 (M,N) array, raw output bits, checks dict)."""

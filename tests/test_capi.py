@@ -60,9 +60,13 @@ def test_valid_cases():
     (dict(A=0), -3), (dict(B=0), -3), (dict(D=0), -3),
     (dict(c=mfl.F32, ldc=64), -3), (dict(C=P + 4096, ldc=64), -3),
     (dict(d=mfl.NONE), -4), (dict(c=7, C=P, ldc=64), -4), (dict(a_order=2), -4),
-    (dict(algo=9), -4),
+    (dict(algo=10), -4),
     (dict(a_order=mfl.A_MMAJOR, algo=1), -6),
-    (dict(algo=0x200), -4), (dict(algo=7), -4),
+    # the 16x16x32 configurations have no register-transposing fetch for an
+    # M-contiguous A: rows off 16-byte alignment need a 32x32x16 one
+    (dict(a_order=mfl.A_MMAJOR, lda=65, algo=7), -6),
+    (dict(a_order=mfl.A_MMAJOR, lda=64, algo=7 | 0x100), -6),
+    (dict(algo=0x200), -4), (dict(algo=12), -4),
     (dict(A=P + 1), -7), (dict(d=mfl.F32, D=P + 2), -7),
     (dict(c=mfl.F16, C=P, ldc=64, d=mfl.F32, D=P), -8),
     (dict(c=mfl.F32, C=P, ldc=128, d=mfl.F32, D=P, ldd=64), -8),
@@ -92,7 +96,7 @@ def _plan(M=64, N=64, K=64, A=P, lda=None, B=P, ldb=None, **kw):
 
 def test_fetch_policy_choice():
     DMA, REG, REGT, DMAT = 0, 1, 2, 3
-    assert _plan(M=4096, N=4096, K=4096)[1:] == (mfl.ALGOS["lds256w4"], DMA, DMA)
+    assert _plan(M=4096, N=4096, K=4096)[1:] == (mfl.ALGOS["lds256_16"], DMA, DMA)
     assert _plan(M=4096, N=4096, K=4097, lda=4097, ldb=4097)[1:] == (mfl.ALGOS["lds256"], REG, REG)
     assert _plan(lda=72, ldb=68)[2:] == (DMA, REG)
     assert _plan(A=P + 2, lda=64)[2:] == (REG, DMA)
@@ -108,7 +112,7 @@ def test_fetch_policy_choice():
 
 
 def test_auto_choice():
-    assert _v(M=4096, N=4096, K=4096)[1] == mfl.ALGOS["lds256w4"]
+    assert _v(M=4096, N=4096, K=4096)[1] == mfl.ALGOS["lds256_16"]
     assert _v(M=4096, N=4096, K=4096, c=mfl.F32, C=P, ldc=4096)[1] == mfl.ALGOS["lds256"]
     assert _v(M=4096, N=4096, K=4096, lda=4100)[1] == mfl.ALGOS["lds256"]
     assert _v(M=256, N=256, K=256)[1] == mfl.ALGOS["lds128"]

@@ -15,13 +15,15 @@ import pytest
 
 import mma_fragment_layouts_tn_amd as mfl
 import workloads as W
-from gpu_helpers import (freivalds_exact, oracle_full, oracle_full_cached, run_gemm, say,
-                         verdict)
+from gpu_helpers import (freivalds_exact, oracle_full, oracle_full_cached, refused, run_gemm,
+                         say, verdict)
 
 pytestmark = pytest.mark.gpu
 
-ALGOS = ["direct", "lds128", "lds256", "lds256w4", "lds128w1", "splitk"]
-LDS_ALGOS = ["lds128", "lds256", "lds256w4", "lds128w1", "splitk"]
+# the 16x16x32 configurations (same block tiles on the other f16 instruction)
+X16 = ["lds256w4_16", "lds256_16", "lds128_16"]
+ALGOS = ["direct", "lds128", "lds256", "lds256w4", "lds128w1", "splitk"] + X16
+LDS_ALGOS = ["lds128", "lds256", "lds256w4", "lds128w1", "splitk"] + X16
 
 
 def _assert_checks(checks):
@@ -44,6 +46,8 @@ def test_small_integer_bit_exact(algo, shape):
              (("f32", "f16"), ld16, ld16))
     for (c, d), lda, ldb in cases:
         w = W.custom(M, N, K, c=c, d=d, dist="int", seed=M * 7 + N * 3 + K, lda=lda, ldb=ldb)
+        if refused(w, algo):
+            continue
         x = W.make_inputs(w)
         D, checks = run_gemm(w, x, algo)
         _assert_checks(checks)
@@ -65,6 +69,8 @@ def test_k_remainder_integer_bit_exact(algo, K):
     for (c, d), lda, ldb in (((None, "f32"), K, K), (("f16", "f16"), ld16, K + 1),
                              (("f32", "f16"), K + 3, ld16)):
         w = W.custom(M, N, K, c=c, d=d, dist="int", seed=K * 11 + lda, lda=lda, ldb=ldb)
+        if refused(w, algo):
+            continue
         x = W.make_inputs(w)
         D, checks = run_gemm(w, x, algo)
         _assert_checks(checks)
@@ -108,6 +114,8 @@ def test_mmajor_a_bit_exact(algo, shape):
     for c, d, ldb in ((None, "f32", K), ("f32", "f32", (K + 7) // 8 * 8), ("f16", "f16", K + 1)):
         w = W.custom(M, N, K, a_order="m", lda=M + 8, ldb=ldb, c=c, d=d, dist="int",
                      seed=M + N + K)
+        if refused(w, algo):
+            continue
         x = W.make_inputs(w)
         D, checks = run_gemm(w, x, algo)
         _assert_checks(checks)
@@ -120,6 +128,8 @@ def test_mmajor_a_float_within_tolerance(algo):
     M, N, K = 520, 264, 700
     w = W.custom(M, N, K, a_order="m", lda=M + 8, ldb=K + 8, c="f32", d="f32", dist="unif",
                  seed=11)
+    if refused(w, algo):
+        return
     x = W.make_inputs(w)
     D, checks = run_gemm(w, x, algo)
     _assert_checks(checks)
@@ -133,6 +143,8 @@ def test_float_inputs_within_tolerance(algo):
                             (256, 256, 256, "f32", "f32")):
         ld = (K + 7) // 8 * 8
         w = W.custom(M, N, K, c=c, d=d, dist="unif", seed=M + K, lda=ld, ldb=ld)
+        if refused(w, algo):
+            continue
         x = W.make_inputs(w)
         D, checks = run_gemm(w, x, algo)
         _assert_checks(checks)
@@ -152,6 +164,8 @@ def test_float_fetch_paths_bit_identical(algo):
         x = W.make_inputs(w)
         D_dma, checks = run_gemm(w, x, algo)
         _assert_checks(checks)
+        if refused(w, algo + "+reg"):
+            continue
         D_reg, checks = run_gemm(w, x, algo + "+reg")
         _assert_checks(checks)
         assert np.array_equal(D_dma, D_reg), (algo, M, N, K)
@@ -188,6 +202,9 @@ def test_kernel_properties():
     assert mfl.kernel_info("lds128w1")["threads"] == 64
     assert mfl.kernel_info("splitk")["lds_bytes"] == 3 * (128 + 64) * 128 * 2   # three stages
     assert mfl.kernel_info("splitk")["threads"] == 256
+    assert mfl.kernel_info("lds256w4_16")["lds_bytes"] == 2 * (256 + 256) * 64 * 2
+    assert mfl.kernel_info("lds256_16")["threads"] == 512
+    assert mfl.kernel_info("lds128_16")["lds_bytes"] == 2 * (128 + 128) * 64 * 2
     say("[gpu] kernel info", {a: mfl.kernel_info(a) for a in ALGOS})
 
 
@@ -195,9 +212,10 @@ def test_kernel_properties():
 NAMED = [
     ("tiny_32x16x16", ["direct", "lds128", "lds256"], False),
     ("direct_256", ["direct"], True),
-    ("lds_4096", ["lds128", "lds256", "lds256w4", "lds256+reg", "lds128w1"], True),
-    ("accum_mmajor_8192x8192x2048", ["auto", "lds128", "lds256+reg"], True),
-    ("ragged_8191x6143x4097", ["auto", "lds128", "lds256w4", "lds128w1", "splitk"], True),
+    ("lds_4096", ["lds128", "lds256", "lds256w4", "lds256+reg", "lds128w1"] + X16, True),
+    ("accum_mmajor_8192x8192x2048", ["auto", "lds128", "lds256+reg", "lds256_16"], True),
+    ("ragged_8191x6143x4097", ["auto", "lds128", "lds256w4", "lds128w1", "splitk",
+                               "lds256w4_16"], True),
     ("shard_512x4096x4096", ["auto", "splitk", "lds128"], True),
 ]
 
@@ -215,6 +233,8 @@ def test_named_workload(name, algo, integer):
     w = W.WORKLOADS[name]
     if integer:
         w = w.twin()
+    if refused(w, algo):
+        return
     x = W.make_inputs(w)
     D, checks = run_gemm(w, x, algo)
     _assert_checks(checks)

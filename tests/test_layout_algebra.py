@@ -16,10 +16,15 @@ from helpers import keyed
 P = L.parse
 F = L.format_layout
 
-# BM, BN, BK, waves along M, N and K
-KERNEL_TILES = {"lds128": (128, 128, 32, 2, 2, 1), "lds256": (256, 256, 64, 2, 4, 1),
-                "lds256w4": (256, 256, 64, 2, 2, 1), "lds128w1": (128, 128, 32, 1, 1, 1),
-                "splitk": (128, 64, 128, 1, 1, 4)}
+A32, A16 = "f32_32x32x16_f16", "f32_16x16x32_f16"
+# BM, BN, BK, waves along M, N, K, and the matrix instruction
+KERNEL_TILES = {"lds128": (128, 128, 32, 2, 2, 1, A32), "lds256": (256, 256, 64, 2, 4, 1, A32),
+                "lds256w4": (256, 256, 64, 2, 2, 1, A32), "lds128w1": (128, 128, 32, 1, 1, 1, A32),
+                "splitk": (128, 64, 128, 1, 1, 4, A32),
+                "lds256w4_16": (256, 256, 64, 2, 2, 1, A16),
+                "lds256_16": (256, 256, 64, 2, 4, 1, A16),
+                "lds128_16": (128, 128, 64, 2, 2, 1, A16)}
+ATOM = {A32: (32, 16, 16), A16: (16, 32, 4)}      # atom M = N, atom K, values per lane
 
 
 def _tab(text):
@@ -309,27 +314,33 @@ def test_error_codes():
 @pytest.mark.parametrize("algo", sorted(KERNEL_TILES))
 def test_kernel_accumulators_are_partition_c(algo):
     """The kernels' accumulator coordinates are partition_C of the block tile
-    for the 32x32x16 atom with tile permutations: M (32, WM, RM):(1, 32RM, 32)
-    (wave-contiguous repeats), N (32, WN, RN):(RN, 32RN, 1) (the same, with a
-    lane's repeats on adjacent columns for vector stores).  A
-    lane's RN accumulators of a row are adjacent columns.  partition_C selects (lane, wm,
-    wn) only, so every K-group of a split-K tile holds the same view."""
-    BM, BN, BK, WM, WN, WK = KERNEL_TILES[algo]
-    RM, RN = BM // WM // 32, BN // WN // 32
-    tile = (F(((32, WM, RM), (1, 32 * RM, 32))), F(((32, WN, RN), (RN, 32 * RN, 1))))
+    for their atom (AM x AM, 32x32x16 or 16x16x32) with tile permutations:
+    M (AM, WM, RM):(1, AM RM, AM) (wave-contiguous repeats), N (AM, WN, V,
+    RN/V):(V, AM RN, 1, AM V) (the same, with a lane's repeats on runs of V =
+    min(RN, 4) adjacent columns for vector stores).  partition_C selects
+    (lane, wm, wn) only, so every K-group of a split-K tile holds the same
+    view."""
+    BM, BN, BK, WM, WN, WK, op = KERNEL_TILES[algo]
+    AM, _, NV = ATOM[op]
+    RM, RN = BM // WM // AM, BN // WN // AM
+    V = min(RN, 4)
+    if RN // V > 1:
+        tn = F(((AM, WN, V, RN // V), (V, AM * RN, 1, AM * V)))
+    else:
+        tn = F(((AM, WN, RN), (RN, AM * RN, 1)))
+    tile = (F(((AM, WM, RM), (1, AM * RM, AM))), tn)
     c = F(((BM, BN), (1, BM)))
-    thr, val = mfl.layout_partition_c(c, _mfma_tv("f32_32x32x16_f16", "C"), (32, 32),
-                                      (WM, WN), tile=tile)
-    T, V = np.array(_tab(thr)), np.array(_tab(val))
-    fc = mfl.fragment_coords(algo, "C")                 # slot = (i RN + j) 16 + v
+    thr, val = mfl.layout_partition_c(c, _mfma_tv(op, "C"), (AM, AM), (WM, WN), tile=tile)
+    T, Vt = np.array(_tab(thr)), np.array(_tab(val))
+    fc = mfl.fragment_coords(algo, "C")                 # slot = (i RN + j) NV + v
     want = fc[..., 0] + BM * fc[..., 1]
-    i, j, v = np.meshgrid(np.arange(RM), np.arange(RN), np.arange(16), indexing="ij")
-    order = (v + 16 * (i + RM * j)).reshape(-1)        # value layout index of each slot
+    i, j, v = np.meshgrid(np.arange(RM), np.arange(RN), np.arange(NV), indexing="ij")
+    order = (v + NV * (i + RM * j)).reshape(-1)        # value layout index of each slot
     thr = np.arange(want.shape[0]) % (64 * WM * WN)      # the thread's (lane, wm, wn)
     assert want.shape[0] == 64 * WM * WN * WK
-    assert np.array_equal(T[thr][:, None] + V[None, order], want)
+    assert np.array_equal(T[thr][:, None] + Vt[None, order], want)
     # the oracle's chain gives the same
-    _check_partition(c, _mfma_tv("f32_32x32x16_f16", "C"), (32, 32), 64, (WM, WN), tile)
+    _check_partition(c, _mfma_tv(op, "C"), (AM, AM), 64, (WM, WN), tile)
 
 
 @pytest.mark.parametrize("op", ["f32_32x32x16_f16", "f32_16x16x32_f16"])

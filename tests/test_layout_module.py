@@ -156,23 +156,31 @@ def test_mfma_tv_layouts_equal_oracle_closed_forms(op):
 
 
 # --------------------------------------------- kernel fragment addressing
-# BM, BN, BK, waves along M, N and K (K-groups split each stage's sub-steps)
-KERNEL_TILES = {"direct": (128, 128, 32, 2, 2, 1), "lds128": (128, 128, 32, 2, 2, 1),
-                "lds256": (256, 256, 64, 2, 4, 1), "lds256w4": (256, 256, 64, 2, 2, 1),
-                "lds128w1": (128, 128, 32, 1, 1, 1), "splitk": (128, 64, 128, 1, 1, 4)}
-LDS_KERNELS = ["lds128", "lds256", "lds256w4", "lds128w1", "splitk"]
+# BM, BN, BK, waves along M, N and K (K-groups split each stage's sub-steps),
+# and the matrix instruction
+A32, A16 = "f32_32x32x16_f16", "f32_16x16x32_f16"
+KERNEL_TILES = {"direct": (128, 128, 32, 2, 2, 1, A32), "lds128": (128, 128, 32, 2, 2, 1, A32),
+                "lds256": (256, 256, 64, 2, 4, 1, A32), "lds256w4": (256, 256, 64, 2, 2, 1, A32),
+                "lds128w1": (128, 128, 32, 1, 1, 1, A32), "splitk": (128, 64, 128, 1, 1, 4, A32),
+                "lds256w4_16": (256, 256, 64, 2, 2, 1, A16),
+                "lds256_16": (256, 256, 64, 2, 4, 1, A16),
+                "lds128_16": (128, 128, 64, 2, 2, 1, A16)}
+LDS_KERNELS = ["lds128", "lds256", "lds256w4", "lds128w1", "splitk", "lds256w4_16", "lds256_16",
+               "lds128_16"]
+ATOM = {A32: (32, 16, 16), A16: (16, 32, 4)}      # atom M = N, atom K, values per lane
 
 
 @pytest.mark.parametrize("algo", sorted(KERNEL_TILES))
 def test_fragment_coords_follow_the_atom_layout(algo):
-    BM, BN, BK, WM, WN, WK = KERNEL_TILES[algo]
-    op = "f32_32x32x16_f16"
+    BM, BN, BK, WM, WN, WK, op = KERNEL_TILES[algo]
+    AM, AK, NV = ATOM[op]
     fa = mfl.fragment_coords(algo, "A")
     fb = mfl.fragment_coords(algo, "B")
     fc = mfl.fragment_coords(algo, "C")
     T = 64 * WM * WN * WK
     assert fa.shape[0] == fb.shape[0] == fc.shape[0] == T
-    RM, RN, KW = BM // WM // 32, BN // WN // 32, BK // 16 // WK
+    RM, RN, KW = BM // WM // AM, BN // WN // AM, BK // AK // WK
+    V = min(RN, 4)
     for t in range(T):
         w, lane = divmod(t, 64)
         wm, wn, wk = w % WM, (w // WM) % WN, w // (WM * WN)
@@ -181,60 +189,65 @@ def test_fragment_coords_follow_the_atom_layout(algo):
             for i in range(RM):
                 for v in range(8):
                     r, k = L.mfma_ab_coord(op, lane, v)
-                    assert tuple(fa[t, s]) == (wm * (BM // WM) + 32 * i + r,
-                                               16 * (wk * KW + kk) + k)
+                    assert tuple(fa[t, s]) == (wm * (BM // WM) + AM * i + r,
+                                               AK * (wk * KW + kk) + k)
                     s += 1
         s = 0
         for kk in range(KW):
             for j in range(RN):
                 for v in range(8):
                     r, k = L.mfma_ab_coord(op, lane, v)
-                    assert tuple(fb[t, s]) == (wn * (BN // WN) + 32 * j + r,
-                                               16 * (wk * KW + kk) + k)
+                    assert tuple(fb[t, s]) == (wn * (BN // WN) + AM * j + r,
+                                               AK * (wk * KW + kk) + k)
                     s += 1
         s = 0
         for i in range(RM):
             for j in range(RN):
-                for v in range(16):
-                    # the N permutation: repeat j of atom column n is column RN*n + j
+                for v in range(NV):
+                    # the N permutation: repeat j of atom column n is column
+                    # AM V (j // V) + V n + j % V (V = RN when RN <= 4)
                     m, n = L.mfma_c_coord(op, lane, v)
-                    assert tuple(fc[t, s]) == (wm * (BM // WM) + 32 * i + m,
-                                               wn * (BN // WN) + RN * n + j)
+                    assert tuple(fc[t, s]) == (wm * (BM // WM) + AM * i + m,
+                                               wn * (BN // WN) + AM * V * (j // V) + V * n
+                                               + j % V)
                     s += 1
 
 
-def _perm_n(n, WTN, RN):
+def _perm_n(n, WTN, RN, AN):
     """Logical column (wave, repeat, atom column) -> physical column."""
+    V = min(RN, 4)
     w, r = divmod(n, WTN)
-    return w * WTN + RN * (r % 32) + r // 32
+    j, c = divmod(r, AN)
+    return w * WTN + AN * V * (j // V) + V * c + j % V
 
 
 @pytest.mark.parametrize("algo", sorted(KERNEL_TILES))
 def test_output_columns_are_the_permuted_b_rows(algo):
     """Each lane's accumulator column for repeat j is the B row it multiplies
-    (lane % 32 of the fragment for repeat j), through the N permutation that
-    the B fetch applies: LDS row r holds global row perm(r).  A transposed or
-    unpermuted pairing fails this for every lane but the first."""
-    BM, BN, BK, WM, WN, WK = KERNEL_TILES[algo]
-    RM, RN, KW = BM // WM // 32, BN // WN // 32, BK // 16 // WK
+    (the lane's row of the fragment for repeat j), through the N permutation
+    that the B fetch applies: LDS row r holds global row perm(r).  A
+    transposed or unpermuted pairing fails this for every lane but the
+    first."""
+    BM, BN, BK, WM, WN, WK, op = KERNEL_TILES[algo]
+    AM, AK, NV = ATOM[op]
+    RM, RN, KW = BM // WM // AM, BN // WN // AM, BK // AK // WK
     fb = mfl.fragment_coords(algo, "B")            # (T, KW*RN*8, 2): LDS rows
-    fc = mfl.fragment_coords(algo, "C")            # (T, RM*RN*16, 2): physical
+    fc = mfl.fragment_coords(algo, "C")            # (T, RM*RN*NV, 2): physical
     for t in range(fb.shape[0]):
-        lane = t % 64
         for j in range(RN):
             brow = fb[t, (0 * RN + j) * 8, 0]      # kk = 0, repeat j, value 0
             for i in range(RM):
-                for v in range(16):
-                    col = fc[t, (i * RN + j) * 16 + v, 1]
-                    assert col == _perm_n(brow, BN // WN, RN), (algo, t, j)
-    assert sorted({_perm_n(n, BN // WN, RN) for n in range(BN)}) == list(range(BN))
+                for v in range(NV):
+                    col = fc[t, (i * RN + j) * NV + v, 1]
+                    assert col == _perm_n(brow, BN // WN, RN, AM), (algo, t, j)
+    assert sorted({_perm_n(n, BN // WN, RN, AM) for n in range(BN)}) == list(range(BN))
 
 
 @pytest.mark.parametrize("algo", sorted(KERNEL_TILES))
 def test_fragment_multiplicities(algo):
     """A held WAVES_N times, B WAVES_M times, C once per K-group (the pages'
     2/2/1, and C twice for two K-direction warp groups)."""
-    BM, BN, BK, WM, WN, WK = KERNEL_TILES[algo]
+    BM, BN, BK, WM, WN, WK, _ = KERNEL_TILES[algo]
     for operand, rows, mult in (("A", BM, WN), ("B", BN, WM)):
         f = mfl.fragment_coords(algo, operand).reshape(-1, 2)
         idx = f[:, 0] * BK + f[:, 1]
