@@ -46,6 +46,29 @@ int mfl_probe_lds_tr16(const int32_t* lane_offsets, const uint16_t* lds_in, uint
  * -5 on a launch error. */
 int mfl_probe_xcc(int32_t nblocks, int32_t* out, void* stream);
 
+/* Register dump of an LDS kernel (test-only): the kernel of configuration
+ * `algo` (mfl_algo value, 2..9 except 1) with fetch policies fetch_a /
+ * fetch_b (0 direct-to-LDS, 1 registers, 2 M-contiguous A transposed in
+ * registers, 3 M-contiguous A direct-to-LDS) runs one K-step (K must equal
+ * the configuration's BK) over M x N of whole tiles, A (M,K) K-contiguous
+ * (or (K,M) M-contiguous for policies 2 and 3, lda >= M) and B (N,K) in
+ * device memory with 16-byte aligned bases and lda, ldb multiples of 8.  In
+ * place of the epilogue every thread of workgroup b writes, at out[(b *
+ * threads + t) * words ..], its operand fragment registers (for each register
+ * buffer, the RM A then the RN B fragments, 8 halves = 4 words each) and
+ * then its RM x RN x NV fp32 accumulators: what the compiled fetch, LDS
+ * layout, fragment reads and matrix instructions put in each register (the
+ * per-thread coordinate dump of "cute(7) simple_gemm" §4, here for every
+ * lane).  With out == NULL only *words_per_thread and *threads are set.
+ * Returns 0, -4 for sizes, alignments or an out buffer outside these rules,
+ * -6 when no dump instance exists for the combination, -5 on a launch
+ * error.  Instances: every configuration with policies (0, 0); LDS_256 with
+ * (1, 1), (2, 0), (3, 0); LDS_256_W4_16 with (1, 1), (3, 0). */
+int mfl_probe_fragments(int32_t algo, int32_t fetch_a, int32_t fetch_b, int32_t M, int32_t N,
+                        int32_t K, const uint16_t* A, int32_t lda, const uint16_t* B,
+                        int32_t ldb, uint32_t* out, int64_t out_words, int32_t* words_per_thread,
+                        int32_t* threads, void* stream);
+
 /* Measurement-only entry points: the rates the GEMM kernels are priced
  * against (a contraction is bound by the matrix cores; the pages' GEMMs, e.g.
  * "cute(7) simple_gemm" §10, only say the shared-memory version is faster).

@@ -127,6 +127,9 @@ def _load() -> ctypes.CDLL:
     lib.mfl_probe_lds_tr16.restype = ctypes.c_int
     lib.mfl_probe_xcc.argtypes = [i32, vp, vp]
     lib.mfl_probe_xcc.restype = ctypes.c_int
+    lib.mfl_probe_fragments.argtypes = [i32, i32, i32, i32, i32, i32, vp, i32, vp, i32, vp, i64,
+                                        P(i32), P(i32), vp]
+    lib.mfl_probe_fragments.restype = ctypes.c_int
     lib.mfl_bench_mfma.argtypes = [i32, vp, i32, i32, i32, vp, vp, vp]
     lib.mfl_bench_mfma.restype = ctypes.c_int
     lib.mfl_bench_lds_read.argtypes = [i32, i32, i32, vp, vp, vp]
@@ -517,3 +520,23 @@ def wall_clock_khz() -> int:
     out = ctypes.c_int32(0)
     _check(_lib.mfl_wall_clock_khz(ctypes.byref(out)))
     return int(out.value)
+
+
+def probe_fragments(algo: str, fetch_a: int, fetch_b: int, A: torch.Tensor, lda: int,
+                    B: torch.Tensor, ldb: int, M: int, N: int, K: int) -> np.ndarray:
+    """Register dump of one K-step of an LDS kernel (mfl_probe_fragments):
+    A and B are device fp16 tensors laid out as the fetch policies expect.
+    Returns uint32 words, shape (tiles, threads, words per thread)."""
+    words, threads = ctypes.c_int32(0), ctypes.c_int32(0)
+    code = algo_code(algo)
+    _check(_lib.mfl_probe_fragments(code, fetch_a, fetch_b, M, N, K, None, lda, None, ldb, None,
+                                    0, ctypes.byref(words), ctypes.byref(threads), None))
+    info = kernel_info(algo)
+    tiles = (M // info["bm"]) * (N // info["bn"])
+    out = torch.zeros(tiles * threads.value * words.value, dtype=torch.int32, device=A.device)
+    stream = torch.cuda.current_stream(A.device).cuda_stream
+    _check(_lib.mfl_probe_fragments(code, fetch_a, fetch_b, M, N, K, A.data_ptr(), lda,
+                                    B.data_ptr(), ldb, out.data_ptr(), out.numel(),
+                                    ctypes.byref(words), ctypes.byref(threads), stream))
+    torch.cuda.synchronize()
+    return out.cpu().numpy().view(np.uint32).reshape(tiles, threads.value, words.value)

@@ -23,7 +23,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["gemm_inst_256.hip", "gemm_inst_256w4.hip", "gemm_inst_128.hip",
            "gemm_inst_128w1.hip", "gemm_inst_splitk.hip", "gemm_inst_256w4x16.hip",
-           "gemm_inst_256x16.hip", "gemm_inst_128x16.hip", "chain_inst.hip", "gemm_dispatch.hip", "probe_kernels.hip", "microbench.hip", "capi.cpp"]
+           "gemm_inst_256x16.hip", "gemm_inst_128x16.hip", "chain_inst.hip", "gemm_dispatch.hip", "probe_kernels.hip", "microbench.hip", "probe_dump.hip", "capi.cpp"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-mcode-object-version=5",
@@ -33,14 +33,13 @@ FLAGS = [
 ]
 
 
-# Sources whose kernels issue v_mfma_f32_16x16x32_f16 with the accumulator
-# tied by hand (inline assembly): the compiler cannot see the hazards of those
-# instructions.  The generated code of every GEMM instance source is checked
-# (check_mfma_fences), these more strictly.
-TIED_MFMA_SOURCES = {"gemm_inst_256w4x16.hip", "gemm_inst_256x16.hip", "gemm_inst_128x16.hip"}
-CHECKED_SOURCES = TIED_MFMA_SOURCES | {"gemm_inst_256.hip", "gemm_inst_256w4.hip",
-                                       "gemm_inst_128.hip", "gemm_inst_128w1.hip",
-                                       "gemm_inst_splitk.hip"}
+# The generated code of every GEMM instance source is checked
+# (check_mfma_fences); kernels that issue v_mfma_f32_16x16x32_f16 with the
+# accumulator tied by hand (inline assembly), whose hazards the compiler
+# cannot see, more strictly.
+CHECKED_SOURCES = {"gemm_inst_256w4x16.hip", "gemm_inst_256x16.hip", "gemm_inst_128x16.hip",
+                   "gemm_inst_256.hip", "gemm_inst_256w4.hip", "gemm_inst_128.hip",
+                   "gemm_inst_128w1.hip", "gemm_inst_splitk.hip", "probe_dump.hip"}
 TIED_MFMA = "v_mfma_f32_16x16x32_f16"
 
 
@@ -101,13 +100,14 @@ def _blocks(lines):
     return blocks, succ
 
 
-def check_mfma_fences(asm_text: str, where: str, tied: bool = True) -> int:
+def check_mfma_fences(asm_text: str, where: str, tied=None) -> int:
     """Walk each kernel's control-flow graph with the fact "a matrix
     instruction may have run since the last drain" (the drain: three s_nop 7
     in a row, 24 wait states), and reject an accumulator access (v_accvgpr_*)
     while the fact holds:
-      * with `tied` (kernels issuing the hand-tied v_mfma_f32_16x16x32_f16,
-        whose hazards the compiler cannot see): any such access;
+      * for kernels issuing the hand-tied v_mfma_f32_16x16x32_f16 (whose
+        hazards the compiler cannot see; `tied` None: decided per kernel by
+        the presence of that instruction): any such access;
       * otherwise (builtin instructions, whose hazards the compiler tracks
         inside a block and along single paths): an access in a block with
         two or more predecessors before any instruction of its own, the
@@ -115,9 +115,10 @@ def check_mfma_fences(asm_text: str, where: str, tied: bool = True) -> int:
     Also requires wait states (an s_nop) between the last accumulator write
     and the first instruction on the straight-line prologue.  Returns the
     number of kernels checked; raises RuntimeError naming each violation."""
-    mfma = TIED_MFMA if tied else "v_mfma_"
     bad, checked = [], 0
     for name, lines in _kernels(asm_text).items():
+        k_tied = any(t.startswith(TIED_MFMA) for t in lines) if tied is None else tied
+        mfma = TIED_MFMA if k_tied else "v_mfma_"
         idx = [i for i, t in enumerate(lines) if t.startswith(mfma)]
         if not idx:
             continue
@@ -143,7 +144,7 @@ def check_mfma_fences(asm_text: str, where: str, tied: bool = True) -> int:
                     live = live and nops < 3
                     continue
                 nops = 0
-                if live and ACC_ACCESS.match(t) and (tied or (not ran and npred[i] >= 2)):
+                if live and ACC_ACCESS.match(t) and (k_tied or (not ran and npred[i] >= 2)):
                     if report:
                         bad.append(f"{name}: accumulator access while a matrix instruction "
                                    f"may be in flight: {t}")
@@ -179,8 +180,7 @@ def _compile(src: str) -> str:
         asm = os.path.join(OBJDIR, f"{stem}-hip-amdgcn-amd-amdhsa-gfx950.s")
         with open(asm) as f:
             text = f.read()
-        tied = src in TIED_MFMA_SOURCES
-        if check_mfma_fences(text, src, tied=tied) == 0:
+        if check_mfma_fences(text, src) == 0:
             raise RuntimeError(f"{src}: no kernel issues a matrix instruction")
     return obj
 

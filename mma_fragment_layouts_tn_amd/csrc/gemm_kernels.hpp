@@ -791,6 +791,19 @@ struct BoolC {
   static constexpr bool value = B;
 };
 
+// C kind of the test-only register dump instances (never a valid C dtype):
+// instead of the epilogue, every thread writes its operand fragment
+// registers and accumulators to p.D (as 32-bit words, see dump_words).
+constexpr int kDumpC = 3;
+
+// words per thread of a dump: NBUF x (RM + RN) fragments of 8 halves (4 words
+// each), then RM x RN x NV accumulators
+template <class Cfg>
+constexpr int dump_words() {
+  constexpr int nbuf = Cfg::kFragDist == 1 ? 2 : Cfg::KSUB_W;
+  return nbuf * (Cfg::RM + Cfg::RN) * 4 + Cfg::RM * Cfg::RN * Cfg::kNV;
+}
+
 // Wait until at most VM vector-memory operations of this wave are in flight
 // and all its LDS operations are done (s_waitcnt vmcnt(VM) lgkmcnt(0); the
 // export counter is not waited on).  Vector-memory loads complete in issue
@@ -1081,6 +1094,31 @@ __global__ void __launch_bounds__(Cfg::kThreads, 1) gemm_tiled(const GemmParams 
     }
   }
   mma_end<Cfg>(acc);
+  if constexpr (CK == kDumpC) {
+    // the registers as the compiled fetch, LDS layout, fragment reads and
+    // matrix instructions left them: fragments [buf][A 0..RM-1, B 0..RN-1],
+    // then accumulators [i][j][v]
+    unsigned* out = (unsigned*)p.D + ((int64_t)blockIdx.x * Cfg::kThreads + tid) * dump_words<Cfg>();
+    int o = 0;
+#pragma unroll
+    for (int b = 0; b < NBUF; ++b) {
+#pragma unroll
+      for (int r = 0; r < RM + RN; ++r) {
+        const half8 h = r < RM ? fa[b][r] : fb[b][r - RM];
+        unsigned u[4];
+        __builtin_memcpy(u, &h, 16);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[o++] = u[e];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < RM; ++i)
+#pragma unroll
+      for (int j = 0; j < RN; ++j)
+#pragma unroll
+        for (int v = 0; v < Cfg::kNV; ++v) out[o++] = __float_as_uint(acc[i][j][v]);
+    return;
+  }
   // Interior tiles with vector-aligned rows: vectors straight from the
   // registers.  Other tiles: split-K owners address each vector; the other
   // kernels stage through LDS into row runs of 4 (one code path less in the

@@ -66,5 +66,12 @@ def test_builtin_kernels_checked_at_merge_blocks_only():
     assert B.check_mfma_fences(drained, "builtin", tied=False) == 1
 
 
-def test_kernels_without_the_instruction_are_not_counted():
-    assert B.check_mfma_fences(_kernel(T32), "other") == 0
+def test_kernel_kind_is_decided_by_its_instructions():
+    """A kernel with only builtin instructions gets the builtin rules (an
+    access inside the instruction's block is the compiler's to fence); with
+    the tied rules forced it has no tied instruction and is not counted."""
+    k = _kernel("s_nop 4", T32, "v_accvgpr_read_b32 v2, a3", T32)
+    assert B.check_mfma_fences(k, "auto") == 1
+    assert B.check_mfma_fences(k, "tied", tied=True) == 0
+    with pytest.raises(RuntimeError, match="in flight"):
+        B.check_mfma_fences(_kernel("s_nop 4", T16, "v_accvgpr_read_b32 v2, a3", T16), "auto")
