@@ -11,6 +11,8 @@
 
 #include <stdint.h>
 
+#include "mfl_gemm.h"
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -68,6 +70,21 @@ int mfl_probe_fragments(int32_t algo, int32_t fetch_a, int32_t fetch_b, int32_t 
                         int32_t K, const uint16_t* A, int32_t lda, const uint16_t* B,
                         int32_t ldb, uint32_t* out, int64_t out_words, int32_t* words_per_thread,
                         int32_t* threads, void* stream);
+
+/* gemm_tn (mfl_gemm.h: same arguments, checks and kernel choice) on a
+ * test-only instance of the chosen LDS kernel that first fills its whole LDS
+ * array with fp16 NaN: a fragment or epilogue read of any LDS location the
+ * kernel did not write shows up in D.  Instances exist for C absent with fp32
+ * D, fp16 C with fp16 D and fp32 C with fp32 D, on: LDS_128 with A/B fetch
+ * direct-to-LDS or registers; LDS_256 with M-contiguous A direct-to-LDS and B
+ * direct, or A transposed in registers and B in registers; LDS_128_W1 with A
+ * direct and B in registers; LDS_SPLITK direct; LDS_256_W4_16 registers;
+ * LDS_256_16 direct; LDS_128_16 M-contiguous A direct-to-LDS and B direct.
+ * Returns gemm_tn's codes; MFL_E_ALGO_CASE (-6) where no instance exists for
+ * the plan (force the kernel and fetch with the algo field). */
+int mfl_probe_gemm_poisoned(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                            const void* B, int64_t ldb, const void* C, int64_t ldc, void* D,
+                            int64_t ldd, gemm_dtypes_t dtypes, void* stream);
 
 /* Measurement-only entry points: the rates the GEMM kernels are priced
  * against (a contraction is bound by the matrix cores; the pages' GEMMs, e.g.

@@ -127,6 +127,9 @@ def _load() -> ctypes.CDLL:
     lib.mfl_probe_lds_tr16.restype = ctypes.c_int
     lib.mfl_probe_xcc.argtypes = [i32, vp, vp]
     lib.mfl_probe_xcc.restype = ctypes.c_int
+    lib.mfl_probe_gemm_poisoned.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp, i64,
+                                            GemmDtypes, vp]
+    lib.mfl_probe_gemm_poisoned.restype = ctypes.c_int
     lib.mfl_probe_fragments.argtypes = [i32, i32, i32, i32, i32, i32, vp, i32, vp, i32, vp, i64,
                                         P(i32), P(i32), vp]
     lib.mfl_probe_fragments.restype = ctypes.c_int
@@ -161,6 +164,13 @@ def gemm_tn_raw(M: int, N: int, K: int, A: int, lda: int, B: int, ldb: int, C: O
                 ldc: int, D: int, ldd: int, dt: GemmDtypes, stream: int) -> int:
     """Direct call of the C ABI with integer pointers; returns the code."""
     return _lib.gemm_tn(M, N, K, A, lda, B, ldb, C, ldc, D, ldd, dt, stream)
+
+
+def gemm_tn_poisoned_raw(M: int, N: int, K: int, A: int, lda: int, B: int, ldb: int,
+                         C: Optional[int], ldc: int, D: int, ldd: int, dt: GemmDtypes,
+                         stream: int) -> int:
+    """gemm_tn on the LDS-poisoned test instances (mfl_probe_gemm_poisoned)."""
+    return _lib.mfl_probe_gemm_poisoned(M, N, K, A, lda, B, ldb, C, ldc, D, ldd, dt, stream)
 
 
 def validate(M, N, K, A, lda, B, ldb, C, ldc, D, ldd, dt: GemmDtypes) -> Tuple[int, int]:

@@ -11,15 +11,24 @@
 #include "../../include/mfl_gemm.h"
 #include "../../include/mfl_chain.h"
 #include "../../include/mfl_layout.h"
+#include "../../include/mfl_probe.h"
 #include "chain.hpp"
 #include "gemm_launch.hpp"
 #include "gemm_tile.hpp"
 #include "layout.hpp"
 #include "mfma_atoms.hpp"
 
+namespace mfl {
+const void* poisoned_symbol(int algo, int fa, int fb, int ck, int dk);
+}
+
 namespace {
 
 using mfl::GemmParams;
+
+int gemm_launch(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                int64_t ldb, const void* C, int64_t ldc, void* D, int64_t ldd,
+                gemm_dtypes_t dtypes, void* stream, bool poisoned);
 
 bool dtype_ok_cd(int32_t c, int32_t d) {
   return (c == MFL_NONE || c == MFL_F16 || c == MFL_F32) && (d == MFL_F16 || d == MFL_F32);
@@ -460,6 +469,20 @@ int gemm_tn_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, co
 int gemm_tn(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
             int64_t ldb, const void* C, int64_t ldc, void* D, int64_t ldd,
             gemm_dtypes_t dtypes, void* stream) {
+  return gemm_launch(M, N, K, A, lda, B, ldb, C, ldc, D, ldd, dtypes, stream, false);
+}
+
+int mfl_probe_gemm_poisoned(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                            const void* B, int64_t ldb, const void* C, int64_t ldc, void* D,
+                            int64_t ldd, gemm_dtypes_t dtypes, void* stream) {
+  return gemm_launch(M, N, K, A, lda, B, ldb, C, ldc, D, ldd, dtypes, stream, true);
+}
+}  // extern "C"
+
+namespace {
+int gemm_launch(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                int64_t ldb, const void* C, int64_t ldc, void* D, int64_t ldd,
+                gemm_dtypes_t dtypes, void* stream, bool poisoned) {
   Plan plan{};
   const int rc = check(M, N, K, A, lda, B, ldb, C, ldc, D, ldd, dtypes, &plan);
   if (rc != MFL_OK) return rc;
@@ -482,10 +505,22 @@ int gemm_tn(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const v
   p.B = B;
   p.C = C;
   p.D = D;
+  if (poisoned) {
+    const void* fn = mfl::poisoned_symbol(plan.algo, plan.fetch_a, plan.fetch_b, dtypes.c,
+                                          dtypes.d);
+    if (!fn) return MFL_E_ALGO_CASE;
+    void* args[] = {(void*)&p};
+    const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)(p.tiles_m * p.tiles_n)),
+                                         dim3(ki.threads), args, 0, (hipStream_t)stream);
+    return e == hipSuccess ? MFL_OK : MFL_E_LAUNCH;
+  }
   const int lr = mfl::launch_gemm(plan.algo, plan.fetch_a, plan.fetch_b, dtypes.c, dtypes.d, p,
                                   (hipStream_t)stream);
   return lr == 0 ? MFL_OK : (lr == -1 ? MFL_E_UNSUPPORTED : MFL_E_LAUNCH);
 }
+}  // namespace
+
+extern "C" {
 
 const char* gemm_strerror(int code) {
   switch (code) {

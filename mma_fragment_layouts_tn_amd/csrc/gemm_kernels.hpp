@@ -817,7 +817,10 @@ __device__ __forceinline__ void wait_vm_lds() {
 // ---------------------------------------------------------------------------
 // LDS-staged pipelined kernel
 // ---------------------------------------------------------------------------
-template <class Cfg, int FA, int FB, int CK, int DK>
+// POISON (test-only instances): the whole LDS array is first filled with
+// fp16 NaN, so a fragment or epilogue read of any location the kernel did
+// not write shows up in D.
+template <class Cfg, int FA, int FB, int CK, int DK, bool POISON = false>
 __global__ void __launch_bounds__(Cfg::kThreads, 1) gemm_tiled(const GemmParams p) {
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK;
   // KSUB: this wave's K sub-steps of each stage (all of them unless the
@@ -837,6 +840,11 @@ __global__ void __launch_bounds__(Cfg::kThreads, 1) gemm_tiled(const GemmParams 
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const TileIndex ti = tile_of_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m);
   const int m0 = ti.tm * BM, n0 = ti.tn * BN;
+  if constexpr (POISON) {
+    for (int i = tid; i < NST * kStage / 2; i += Cfg::kThreads)
+      ((unsigned*)smem)[i] = 0x7E007E00u;   // two fp16 NaNs
+    __syncthreads();
+  }
 
   using FetchA = typename FetchSel<Cfg, BM, FA, false>::type;
   using FetchB = typename FetchSel<Cfg, BN, FB, true>::type;   // rows in N-permuted order

@@ -56,6 +56,52 @@ const void* dump_symbol(int algo, int fa, int fb, int* words, int* threads) {
       algo, fa, fb, words, threads);
 }
 
+// LDS-poisoned instances (test-only): a few configurations and fetch paths,
+// C absent / fp16 / fp32 with the matching D
+namespace {
+template <class Cfg, int FA, int FB>
+const void* poisoned_of(int ck) {
+  switch (ck) {
+    case 0: return (const void*)gemm_tiled<Cfg, FA, FB, 0, 2, true>;
+    case 1: return (const void*)gemm_tiled<Cfg, FA, FB, 1, 1, true>;
+    case 2: return (const void*)gemm_tiled<Cfg, FA, FB, 2, 2, true>;
+    default: return nullptr;
+  }
+}
+
+template <int ALGO, class Cfg, int FA, int FB>
+struct PoisonEntry {
+  static bool take(int algo, int fa, int fb, int ck, const void** fn) {
+    if (algo != ALGO || fa != FA || fb != FB) return false;
+    *fn = poisoned_of<Cfg, FA, FB>(ck);
+    return true;
+  }
+};
+
+template <class... E>
+const void* poison_lookup(int algo, int fa, int fb, int ck) {
+  const void* fn = nullptr;
+  (void)(E::take(algo, fa, fb, ck, &fn) || ...);
+  return fn;
+}
+}  // namespace
+
+// nullptr where no poisoned instance exists (d_kind must be 2 for ck 0 and 2,
+// 1 for ck 1)
+const void* poisoned_symbol(int algo, int fa, int fb, int ck, int dk) {
+  if ((ck == 1) != (dk == 1)) return nullptr;
+  return poison_lookup<PoisonEntry<kAlgoLds128, CfgLds128, kFetchDma, kFetchDma>,
+                       PoisonEntry<kAlgoLds128, CfgLds128, kFetchReg, kFetchReg>,
+                       PoisonEntry<kAlgoLds256, CfgLds256, kFetchDmaT, kFetchDma>,
+                       PoisonEntry<kAlgoLds256, CfgLds256, kFetchRegT, kFetchReg>,
+                       PoisonEntry<kAlgoLds128W1, CfgLds128W1, kFetchDma, kFetchReg>,
+                       PoisonEntry<kAlgoLdsSplitK, CfgLdsSplitK, kFetchDma, kFetchDma>,
+                       PoisonEntry<kAlgoLds256W4x16, CfgLds256W4x16, kFetchReg, kFetchReg>,
+                       PoisonEntry<kAlgoLds256x16, CfgLds256x16, kFetchDma, kFetchDma>,
+                       PoisonEntry<kAlgoLds128x16, CfgLds128x16, kFetchDmaT, kFetchDma>>(
+      algo, fa, fb, ck);
+}
+
 }  // namespace mfl
 
 extern "C" int mfl_probe_fragments(int32_t algo, int32_t fetch_a, int32_t fetch_b, int32_t M,

@@ -81,9 +81,11 @@ def refused(w: W.Workload, algo: str) -> bool:
     return False
 
 
-def run_gemm(w: W.Workload, x: W.Inputs, algo: str, in_place: bool = False):
-    """Upload, call gemm_tn through the C ABI, download.  Returns
-    (D as float64 (M,N) array, raw output bits, checks dict)."""
+def run_gemm(w: W.Workload, x: W.Inputs, algo: str, in_place: bool = False,
+             poisoned: bool = False):
+    """Upload, call gemm_tn through the C ABI (with `poisoned`, its
+    LDS-poisoned test instances), download.  Returns (D as float64 (M,N)
+    array, checks dict)."""
     say(f"[gpu] {w.name} algo={algo} M={w.M} N={w.N} K={w.K} a={w.a_order} "
         f"c={w.c} d={w.d} int={x.integer}")
     A = Guarded(x.A)
@@ -100,7 +102,8 @@ def run_gemm(w: W.Workload, x: W.Inputs, algo: str, in_place: bool = False):
     a_order = mfl.A_KMAJOR if w.a_order == "k" else mfl.A_MMAJOR
     dt = mfl.dtypes(ckind, dkind, a_order, mfl.algo_code(algo))
     stream = torch.cuda.current_stream().cuda_stream
-    rc = mfl.gemm_tn_raw(w.M, w.N, w.K, A.ptr, w.lda_, B.ptr, w.ldb_,
+    entry = mfl.gemm_tn_poisoned_raw if poisoned else mfl.gemm_tn_raw
+    rc = entry(w.M, w.N, w.K, A.ptr, w.lda_, B.ptr, w.ldb_,
                          None if C is None else C.ptr, w.ldc_ if C is not None else 0,
                          Dt.data_ptr(), ldd, dt, stream)
     assert rc == 0, (rc, mfl.strerror(rc))
