@@ -23,9 +23,11 @@
  *     的寄存器", 第二步).
  * Output text is written into a caller buffer `out` of `cap` bytes (NUL
  * terminated).  Every function returns 0 or a negative code:
- *   -10 too many leaves/modes (16 leaves, 8 modes), -11 not composable
- *   (divisibility fails), -12 malformed text, -13 index out of range or
- *   buffer too small, -14 negative stride where not supported.
+ *   -10 too many leaves/modes (16 leaves, 8 modes), or a size, offset or
+ *   intermediate value beyond int64 (inputs: integers up to 2^40 in
+ *   magnitude, size and reach of every offset within int64), -11 not
+ *   composable (divisibility fails), -12 malformed text, -13 index out of
+ *   range or buffer too small, -14 negative stride where not supported.
  * Pure host code: no GPU is touched.
  */
 #ifndef MFL_LAYOUT_H

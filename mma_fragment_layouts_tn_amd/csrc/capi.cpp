@@ -233,6 +233,16 @@ int parse_layout(const char* text, mfl::Layout& L) {
       L.push_leaf(sh[k], st[k]);
     }
   }
+  // the size and every offset of the domain must fit int64 (then plain
+  // evaluation inside the domain cannot overflow)
+  int ovf = mfl::kLayoutOk;
+  mfl::size(L, &ovf);
+  int64_t reach = 0;
+  for (int i = 0; i < L.nleaves; ++i)
+    reach = mfl::ck_add(reach, mfl::ck_mul(L.shape[i] - 1, L.stride[i] < 0 ? -L.stride[i]
+                                                                          : L.stride[i], ovf),
+                        ovf);
+  if (ovf != mfl::kLayoutOk) return ovf;
   return L.status;
 }
 
@@ -420,14 +430,20 @@ int chain_check(int64_t batch, int64_t M, int64_t N1, int64_t N2, int64_t K, con
   if (lda < K || ldb < K || ldw < (N1 > one ? N1 : one) || ldd < (N2 > one ? N2 : one))
     return MFL_E_LEADING_DIM;
   if (sa < 0 || sb < 0 || sw < 0 || sd < 0) return MFL_E_LEADING_DIM;
+  // bounds that keep every offset below (row * ld, batch * stride, M * ldd)
+  // far inside int64: 2^48 elements is beyond any device's memory
+  if (M > INT_MAX / 2 || N1 > INT_MAX / 2 || N2 > INT_MAX / 2 || batch > INT_MAX ||
+      lda > INT_MAX || ldb > INT_MAX || ldw > INT_MAX || ldd > INT_MAX)
+    return MFL_E_TOO_LARGE;
+  const int64_t span = int64_t(1) << 48;
+  for (const int64_t st : {sa, sb, sw, sd})
+    if (st > 0 && batch > span / st) return MFL_E_TOO_LARGE;
   if (batch > 1 && M > 0 && N2 > 0 && sd < M * ldd) return MFL_E_ALIAS;
   const bool work = batch > 0 && M > 0 && N2 > 0;
   if (work && !D) return MFL_E_NULL_POINTER;
   if (work && N1 > 0 && (!A || !B || !W)) return MFL_E_NULL_POINTER;
   if (((uintptr_t)A & 1) || ((uintptr_t)B & 1) || ((uintptr_t)W & 1)) return MFL_E_MISALIGNED;
   if (D && ((uintptr_t)D % (uintptr_t)elem_size(dk))) return MFL_E_MISALIGNED;
-  if (M > INT_MAX / 2 || N1 > INT_MAX / 2 || N2 > INT_MAX / 2 || batch > INT_MAX)
-    return MFL_E_TOO_LARGE;
   const int64_t bn = mfl::chain::tile_n(N2);
   const int64_t tiles = batch * ((M + mfl::chain::BM - 1) / mfl::chain::BM) * ((N2 + bn - 1) / bn);
   if (tiles > INT_MAX) return MFL_E_TOO_LARGE;

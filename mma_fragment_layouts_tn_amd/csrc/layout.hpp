@@ -95,6 +95,33 @@ struct Layout {
   }
 };
 
+// ------------------------------------------------------ checked arithmetic
+// Text input can describe layouts whose sizes or offsets leave int64.  The
+// algebra's products and sums below go through these: an overflow (or the
+// value INT64_MIN, which has no negation) sets `st` to kLayoutTooLarge and
+// yields INT64_MAX, never 0, so later divisions stay defined.  The per-lane
+// evaluation that kernels run (eval, eval2) stays plain; it only ever sees
+// the small layouts of the instructions and tiles.
+constexpr int64_t kInt64Max = int64_t(~uint64_t(0) >> 1);
+
+MFL_HD constexpr int64_t ck_mul(int64_t a, int64_t b, int& st) {
+  int64_t r = 0;
+  if (__builtin_mul_overflow(a, b, &r) || r == -kInt64Max - 1) {
+    st = kLayoutTooLarge;
+    return kInt64Max;
+  }
+  return r;
+}
+
+MFL_HD constexpr int64_t ck_add(int64_t a, int64_t b, int& st) {
+  int64_t r = 0;
+  if (__builtin_add_overflow(a, b, &r) || r == -kInt64Max - 1) {
+    st = kLayoutTooLarge;
+    return kInt64Max;
+  }
+  return r;
+}
+
 // ---------------------------------------------------------------- builders
 MFL_HD constexpr Layout make_flat(int n, const int64_t* s, const int64_t* d) {
   Layout L;
@@ -114,15 +141,20 @@ MFL_HD constexpr Layout make_modes(int n, const int64_t* s, const int64_t* d) {
 }
 
 // ------------------------------------------------------------- evaluation
-MFL_HD constexpr int64_t size(const Layout& L) {
+// size and cosize saturate at INT64_MAX and report that in *st, if given
+MFL_HD constexpr int64_t size(const Layout& L, int* st = nullptr) {
+  int s = kLayoutOk;
   int64_t n = 1;
-  for (int i = 0; i < L.nleaves; ++i) n *= L.shape[i];
+  for (int i = 0; i < L.nleaves; ++i) n = ck_mul(n, L.shape[i], s);
+  if (st && s != kLayoutOk) *st = s;
   return n;
 }
 
-MFL_HD constexpr int64_t size_mode(const Layout& L, int m) {
+MFL_HD constexpr int64_t size_mode(const Layout& L, int m, int* st = nullptr) {
+  int s = kLayoutOk;
   int64_t n = 1;
-  for (int i = L.mode_begin(m); i < L.mode_end[m]; ++i) n *= L.shape[i];
+  for (int i = L.mode_begin(m); i < L.mode_end[m]; ++i) n = ck_mul(n, L.shape[i], s);
+  if (st && s != kLayoutOk) *st = s;
   return n;
 }
 
@@ -141,13 +173,23 @@ MFL_HD constexpr int64_t eval(const Layout& L, int64_t idx) {
   return eval_leaves(L, 0, L.nleaves, idx);
 }
 
-// as eval, but the last leaf takes whatever index remains (indices past
-// size(L) continue along the last leaf), the reading composition uses
-MFL_HD constexpr int64_t eval_unbounded(const Layout& L, int64_t idx) {
+// eval with checked arithmetic, for layouts built from arbitrary input
+MFL_HD constexpr int64_t eval_ck(const Layout& L, int64_t idx, int& st) {
   int64_t off = 0;
   for (int i = 0; i < L.nleaves; ++i) {
-    if (i == L.nleaves - 1) return off + idx * L.stride[i];
-    off += (idx % L.shape[i]) * L.stride[i];
+    off = ck_add(off, ck_mul(idx % L.shape[i], L.stride[i], st), st);
+    idx /= L.shape[i];
+  }
+  return off;
+}
+
+// as eval_ck, but the last leaf takes whatever index remains (indices past
+// size(L) continue along the last leaf), the reading composition uses
+MFL_HD constexpr int64_t eval_unbounded(const Layout& L, int64_t idx, int& st) {
+  int64_t off = 0;
+  for (int i = 0; i < L.nleaves; ++i) {
+    if (i == L.nleaves - 1) return ck_add(off, ck_mul(idx, L.stride[i], st), st);
+    off = ck_add(off, ck_mul(idx % L.shape[i], L.stride[i], st), st);
     idx /= L.shape[i];
   }
   return off;
@@ -162,10 +204,13 @@ MFL_HD constexpr int64_t eval2(const Layout& L, int64_t c0, int64_t c1) {
   return eval_mode(L, 0, c0) + eval_mode(L, 1, c1);
 }
 
-MFL_HD constexpr int64_t cosize(const Layout& L) {
+MFL_HD constexpr int64_t cosize(const Layout& L, int* st = nullptr) {
+  int s = kLayoutOk;
   int64_t hi = 0;
-  for (int i = 0; i < L.nleaves; ++i) hi += (L.shape[i] - 1) * L.stride[i];
-  return hi + 1;
+  for (int i = 0; i < L.nleaves; ++i) hi = ck_add(hi, ck_mul(L.shape[i] - 1, L.stride[i], s), s);
+  hi = ck_add(hi, 1, s);
+  if (st && s != kLayoutOk) *st = s;
+  return hi;
 }
 
 // ------------------------------------------------------------- coalesce
@@ -174,18 +219,20 @@ MFL_HD constexpr int64_t cosize(const Layout& L) {
 MFL_HD constexpr Layout coalesce(const Layout& L) {
   Layout out;
   out.open_mode();
+  int ovf = kLayoutOk;
   for (int i = 0; i < L.nleaves; ++i) {
     const int64_t s = L.shape[i], d = L.stride[i];
     if (s == 1) continue;
     const int n = out.nleaves;
-    if (n > 0 && out.stride[n - 1] * out.shape[n - 1] == d) {
-      out.shape[n - 1] *= s;
+    int st = kLayoutOk;
+    if (n > 0 && ck_mul(out.stride[n - 1], out.shape[n - 1], st) == d && st == kLayoutOk) {
+      out.shape[n - 1] = ck_mul(out.shape[n - 1], s, ovf);
       continue;
     }
     out.push_leaf(s, d);
   }
   if (out.nleaves == 0) out.push_leaf(1, 0);
-  out.status = L.status;
+  out.status = L.status != kLayoutOk ? L.status : ovf != kLayoutOk ? ovf : out.status;
   return out;
 }
 
@@ -199,6 +246,10 @@ MFL_HD constexpr void compose_leaf(const Layout& A, int64_t s, int64_t d, Layout
   }
   if (d == 0) {
     out.push_leaf(s, 0);
+    return;
+  }
+  if (d < 0) {   // the division of A by d below is defined for d > 0 only
+    out.status = kLayoutNegativeStride;
     return;
   }
   const int n = A.nleaves;
@@ -218,7 +269,7 @@ MFL_HD constexpr void compose_leaf(const Layout& A, int64_t s, int64_t d, Layout
   }
   bool last = (i == n - 1);
   int64_t cur_shape = last ? 0 : A.shape[i] / rest;
-  int64_t cur_stride = A.stride[i] * rest;
+  int64_t cur_stride = ck_mul(A.stride[i], rest, out.status);
   int64_t need = s;
   while (need > 1) {
     if (last) {
@@ -268,10 +319,12 @@ MFL_HD constexpr Layout compose(const Layout& A, const Layout& B) {
 // true when compose(A, B) equals A(B(c)) at every c (brute force; for
 // checks of arbitrary inputs)
 MFL_HD constexpr bool compose_is_exact(const Layout& A, const Layout& B, const Layout& AB) {
-  const int64_t n = size(B);
-  if (size(AB) != n) return false;
+  int st = kLayoutOk;
+  const int64_t n = size(B, &st);
+  if (size(AB, &st) != n || st != kLayoutOk) return false;
   for (int64_t i = 0; i < n; ++i)
-    if (eval(AB, i) != eval_unbounded(A, eval(B, i))) return false;
+    if (eval_ck(AB, i, st) != eval_unbounded(A, eval_ck(B, i, st), st) || st != kLayoutOk)
+      return false;
   return true;
 }
 
@@ -297,9 +350,10 @@ MFL_HD constexpr Layout right_inverse(const Layout& L) {
   const Layout c = coalesce(L);
   int64_t dom[kMaxLeaves] = {};  // domain stride of each leaf
   int64_t p = 1;
+  int ovf = kLayoutOk;
   for (int i = 0; i < c.nleaves; ++i) {
     dom[i] = p;
-    p *= c.shape[i];
+    p = ck_mul(p, c.shape[i], ovf);
     if (c.stride[i] < 0) {
       Layout bad;
       bad.status = kLayoutNegativeStride;
@@ -320,10 +374,10 @@ MFL_HD constexpr Layout right_inverse(const Layout& L) {
     if (pick < 0) break;
     used[pick] = true;
     out.push_leaf(c.shape[pick], dom[pick]);
-    cur *= c.shape[pick];
+    cur = ck_mul(cur, c.shape[pick], ovf);
   }
   if (out.nleaves == 0) out.push_leaf(1, 0);
-  out.status = c.status;
+  out.status = c.status != kLayoutOk ? c.status : ovf != kLayoutOk ? ovf : out.status;
   return out;
 }
 
@@ -356,9 +410,9 @@ MFL_HD constexpr Layout complement(const Layout& L, int64_t cotarget) {
       return out;
     }
     if (st[i] / cur > 1) out.push_leaf(st[i] / cur, cur);
-    cur = sh[i] * st[i];
+    cur = ck_mul(sh[i], st[i], out.status);
   }
-  const int64_t rest = (cotarget + cur - 1) / cur;
+  const int64_t rest = cotarget / cur + (cotarget % cur > 0 ? 1 : 0);   // ceil, no overflow
   if (rest > 1) out.push_leaf(rest, cur);
   Layout c = coalesce(out);
   if (L.status != kLayoutOk) c.status = L.status;
@@ -384,7 +438,9 @@ MFL_HD constexpr void append_leaves(Layout& dst, const Layout& src) {
 // A divided by the single layout B over A's whole domain: mode 0 the tile
 // (B's leaves composed into A), mode 1 the rest (B's complement)
 MFL_HD constexpr Layout logical_divide(const Layout& A, const Layout& B, bool verify = false) {
-  const Layout R = complement(B, size(A));
+  int ovf = kLayoutOk;
+  Layout R = complement(B, size(A, &ovf));
+  if (ovf != kLayoutOk) R.status = ovf;
   Layout BR;
   BR.open_mode();
   append_leaves(BR, B);
@@ -455,7 +511,8 @@ MFL_HD constexpr Layout zipped_divide(const Layout& A, const Layout* tilers, con
 
 // ------------------------------------------------------------- product
 MFL_HD constexpr Layout logical_product(const Layout& A, const Layout& B, bool verify = false) {
-  const Layout C = complement(A, size(A) * cosize(B));
+  int ovf = kLayoutOk;
+  const Layout C = complement(A, ck_mul(size(A, &ovf), cosize(B, &ovf), ovf));
   const Layout CB = compose_v(C, B, verify);
   Layout out;
   out.open_mode();
@@ -463,6 +520,7 @@ MFL_HD constexpr Layout logical_product(const Layout& A, const Layout& B, bool v
   out.open_mode();
   append_leaves(out, CB);
   if (A.status != kLayoutOk) out.status = A.status;
+  if (ovf != kLayoutOk) out.status = ovf;
   return out;
 }
 
@@ -471,7 +529,8 @@ MFL_HD constexpr Layout logical_product(const Layout& A, const Layout& B, bool v
 // atoms over M, N, K this is the tiled MMA's thread layout (TiledMMA page,
 // "第二个参数怎样把一个 warp 扩展成四个")
 MFL_HD constexpr Layout tiled_product(const Layout& A, const Layout& B, bool verify = false) {
-  const Layout C = complement(A, size(A) * cosize(B));
+  int ovf = kLayoutOk;
+  const Layout C = complement(A, ck_mul(size(A, &ovf), cosize(B, &ovf), ovf));
   const Layout CB = compose_v(C, B, verify);
   Layout out;
   out.open_mode();
@@ -482,6 +541,8 @@ MFL_HD constexpr Layout tiled_product(const Layout& A, const Layout& B, bool ver
   }
   if (A.status != kLayoutOk) out.status = A.status;
   if (C.status != kLayoutOk) out.status = C.status;
+  if (CB.status != kLayoutOk) out.status = CB.status;
+  if (ovf != kLayoutOk) out.status = ovf;
   return out;
 }
 
@@ -523,14 +584,17 @@ MFL_HD constexpr Layout upcast(const Layout& L, int64_t n) {
 MFL_HD constexpr Layout compact(const Layout& shape_only) {
   Layout out;
   int64_t d = 1;
+  int ovf = kLayoutOk;
   for (int m = 0; m < shape_only.nmodes; ++m) {
     out.open_mode();
     for (int i = shape_only.mode_begin(m); i < shape_only.mode_end[m]; ++i) {
       out.push_leaf(shape_only.shape[i], d);
-      d *= shape_only.shape[i];
+      d = ck_mul(d, shape_only.shape[i], ovf);
     }
   }
-  out.status = shape_only.status;
+  out.status = shape_only.status != kLayoutOk ? shape_only.status
+               : ovf != kLayoutOk             ? ovf
+                                              : out.status;
   return out;
 }
 
@@ -574,7 +638,8 @@ MFL_HD constexpr CPartition partition_c(const Layout& C, const Layout* tile, con
                                         int64_t atom_m, int64_t atom_n, int64_t warps_m,
                                         int64_t warps_n, bool verify = false) {
   CPartition r;
-  Layout t2[2] = {unit_leaf(atom_m * warps_m), unit_leaf(atom_n * warps_n)};
+  int ovf = kLayoutOk;
+  Layout t2[2] = {unit_leaf(ck_mul(atom_m, warps_m, ovf)), unit_leaf(ck_mul(atom_n, warps_n, ovf))};
   if (tile) {
     t2[0] = tile[0];
     t2[1] = tile[1];
@@ -601,11 +666,14 @@ MFL_HD constexpr CPartition partition_c(const Layout& C, const Layout* tile, con
   for (const Layout* l : chk)
     if (l->status != kLayoutOk) st = l->status;
   // the tile must divide C, the atom the tile and the warps the atom blocks
-  if (C.nmodes != 2 || size_mode(C, 0) % size(t2[0]) != 0 ||
-      size_mode(C, 1) % size(t2[1]) != 0 || size(t2[0]) % atom_m != 0 ||
-      size(t2[1]) % atom_n != 0 || size(arest[0]) % warps_m != 0 ||
-      size(arest[1]) % warps_n != 0 || size(atom_tv) != atom_m * atom_n)
+  // (the counts are positive: a zero count divides nothing)
+  if (C.nmodes != 2 || atom_m < 1 || atom_n < 1 || warps_m < 1 || warps_n < 1 ||
+      size_mode(C, 0, &ovf) % size(t2[0], &ovf) != 0 ||
+      size_mode(C, 1, &ovf) % size(t2[1], &ovf) != 0 || size(t2[0], &ovf) % atom_m != 0 ||
+      size(t2[1], &ovf) % atom_n != 0 || size(arest[0], &ovf) % warps_m != 0 ||
+      size(arest[1], &ovf) % warps_n != 0 || size(atom_tv, &ovf) != ck_mul(atom_m, atom_n, ovf))
     st = kLayoutBadIndex;
+  if (ovf != kLayoutOk) st = ovf;
   r.thr.status = r.val.status = st;
   return r;
 }
@@ -628,14 +696,15 @@ MFL_HD constexpr CPartition partition_c(const Layout& C, const Layout* tile, con
 MFL_HD constexpr Layout retile(const Layout& frag, const Layout& tv, const Layout& tile_shape,
                                int64_t nthr, int64_t atom_nval, bool verify = false) {
   Layout out;
-  const int64_t V = size_mode(frag, 0);
+  int ovf = kLayoutOk;
+  const int64_t V = size_mode(frag, 0, &ovf);
   const Layout ri = right_inverse(tv);
-  if (size(ri) != size(tile_shape)) {   // tv must cover the tile exactly
-    out.status = kLayoutBadIndex;
+  if (nthr < 1 || atom_nval < 1 || size(ri, &ovf) != size(tile_shape, &ovf)) {
+    out.status = kLayoutBadIndex;   // tv must cover the tile exactly
     return out;
   }
   const Layout inv = with_shape(ri, tile_shape, verify);
-  const Layout mn = upcast(inv, nthr * V);
+  const Layout mn = upcast(inv, ck_mul(nthr, V, ovf));
   const Layout G = right_inverse(mn);
   const Layout prod = logical_product(unit_leaf(V), G, verify);
   const Layout fv = logical_divide(prod, unit_leaf(atom_nval), verify);
@@ -648,7 +717,7 @@ MFL_HD constexpr Layout retile(const Layout& frag, const Layout& tv, const Layou
   tilers[0] = unit_leaf(V);
   all[0] = true;
   for (int m = 1; m < frag.nmodes; ++m) {
-    tilers[m] = unit_leaf(size_mode(mn, m - 1));
+    tilers[m] = unit_leaf(size_mode(mn, m - 1, &ovf));
     all[m] = true;
   }
   Layout tile[kMaxModes], rest[kMaxModes];
@@ -666,8 +735,9 @@ MFL_HD constexpr Layout retile(const Layout& frag, const Layout& tv, const Layou
     if (l->status != kLayoutOk) out.status = l->status;
   for (int m = 0; m < frag.nmodes; ++m)
     if (tile[m].status != kLayoutOk) out.status = tile[m].status;
-  if (size(rest[0]) != 1 || size(prod) % atom_nval != 0)
+  if (size(rest[0], &ovf) != 1 || size(prod, &ovf) % atom_nval != 0)
     out.status = kLayoutBadIndex;
+  if (ovf != kLayoutOk) out.status = ovf;
   return out;
 }
 

@@ -167,6 +167,9 @@ def test_chain_validation():
     assert _cv(W=None) == mfl.ERR["NULL_POINTER"]
     assert _cv(A=P + 1) == mfl.ERR["MISALIGNED"]
     assert _cv(D=P + 2, d=mfl.F32) == mfl.ERR["MISALIGNED"]
+    for kw in (dict(M=1 << 40), dict(N2=1 << 31), dict(ldd=1 << 40), dict(batch=1 << 31),
+               dict(batch=1 << 20, sa=1 << 30), dict(batch=2, sw=(1 << 62) + 1)):
+        assert _cv(**kw) == mfl.ERR["TOO_LARGE"], kw
 
 
 def _cplan(**kw):

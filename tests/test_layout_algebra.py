@@ -395,3 +395,30 @@ def test_k_gather_with_the_32x32x8_atom():
     t = P(tiled)
     pos = {L.evaluate(t, (lane, c)) for lane in range(64) for c in range(8)}
     assert pos == set(range(512))
+
+
+def _code(fn, *args):
+    try:
+        fn(*args)
+    except mfl.LayoutError as e:
+        return int(str(e).rsplit("code", 1)[1])
+    return 0
+
+
+def test_out_of_range_inputs_are_refused():
+    """Inputs the algebra cannot represent come back as error codes, never as
+    wrapped int64 values or a division by zero: a negative stride on the
+    right of a composition (-14), sizes and offsets beyond int64 at parsing
+    (-10), and intermediate values beyond int64 inside an operation (-10)."""
+    big = 1 << 40
+    assert _code(mfl.layout_compose, "(4,8):(1,4)", "4:-1") == -14
+    assert _code(mfl.layout_compose, "(4,8):(1,4)", "(2,2):(1,-4)") == -14
+    assert _code(mfl.layout_size, f"({big},{big}):(1,0)") == -10
+    assert _code(mfl.layout_eval, f"({big},{1 << 24}):({big},1)", 0) == -10
+    assert _code(mfl.layout_logical_product, f"({1 << 20},{1 << 20}):(1,{1 << 20})",
+                 f"{1 << 20}:{big}") == -10
+    assert _code(mfl.layout_tiled_product, f"({1 << 20},{1 << 20}):(1,{1 << 20})",
+                 f"({1 << 20},2):({big},1)") == -10
+    # the same operations on representable inputs still succeed
+    assert mfl.layout_compose("(4,8):(1,4)", "4:2") == "4:2"
+    assert mfl.layout_size(f"({1 << 20},{1 << 20}):(1,0)") == 1 << 40
