@@ -987,15 +987,22 @@ __global__ void __launch_bounds__(Cfg::kThreads, 1) gemm_tiled(const GemmParams 
       issue(1, 1);
       if constexpr (NST == 3 && kAnyReg) stash(1);
     }
+    // Only tile 0 must have landed before the first barrier: the later tiles
+    // are waited for by the step that reads them, before its own barrier.
     if constexpr (NST == 3) {
       if (nfull > 2) {
         issue(2, 2);
-        wait_vm_lds<2 * kVmem>();   // tile 0 has landed; tiles 1 and 2 may be in flight
+        wait_vm_lds<2 * kVmem>();   // tiles 1 and 2 may be in flight
+      } else if (nfull > 1) {
+        wait_vm_lds<kVmem>();
       } else {
         wait_vm_lds<0>();
       }
     } else {
-      wait_vm_lds<0>();
+      if (nfull > 1)
+        wait_vm_lds<kVmem>();       // tile 1 may be in flight
+      else
+        wait_vm_lds<0>();
     }
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
