@@ -84,38 +84,41 @@ int mfl_layout_upcast(const char* layout, int64_t n, char* out, int64_t cap);
 int mfl_layout_with_shape(const char* layout, const char* shape, char* out, int64_t cap);
 int mfl_layout_tiled_product(const char* a, const char* b, char* out, int64_t cap);
 
-/* partition_C of a tiled MMA, derived with the operations above in the four
- * steps of the TiledMMA page, section "partition_C 怎样把分工应用到一个 Tensor":
- * the output tensor `c` (two modes, M then N: its storage layout) is divided
- * by the tile, then by the atom (atom_m, atom_n); the atom block (index
- * m + atom_m*n) is composed with the atom's C TV layout `atom_tv` (lane +
- * nlanes*value -> m + atom_m*n); the remaining blocks are divided by the
- * warp counts (warps_m, warps_n).  `tile` is "" (compact atom*warps per
- * direction) or "Lm;Ln", the tiled MMA's M and N permutations (section "用
- * Layout 改变 M 方向的坐标顺序"; "_" for an unpermuted direction).
+/* partition_C of a tiled MMA (TiledMMA page, section "partition_C 怎样把分工
+ * 应用到一个 Tensor"), from the element each thread holds.  The atom
+ * (atom_m x atom_n, C TV layout `atom_tv`: lane + nlanes*value -> m +
+ * atom_m*n) is repeated over warps_m x warps_n warps; the output tensor `c`
+ * (two modes, M then N: its storage layout) is covered by tiles whose rows
+ * (columns) are permuted by the tile entries; `tile` is "" (compact
+ * atom*warps per direction) or "Lm;Ln" (section "用 Layout 改变 M 方向的坐标
+ * 顺序"; "_" for an unpermuted direction; each entry must permute its tile).
+ * Along M the atom-row blocks are numbered down a tile, then across tiles,
+ * and warp row wm holds blocks wm, wm + warps_m, ...; likewise along N.
  * Outputs, each `cap` bytes: thr_out, one mode, thread lane + nlanes*(wm +
  * warps_m*wn) -> storage offset of that thread's first value; val_out,
- * (value, rest M, rest N) -> offset relative to it.  The view of thread t
- * is the layout val_out starting at offset thr_out(t).  -13 when c is not
+ * (value, rest M, rest N) -> offset relative to it.  Each mode is factored
+ * from that element map and the whole map is checked.  -13 when c is not
  * rank 2, the tile does not divide c, the atom the tile, or the warp counts
- * the atom blocks. */
+ * the atom blocks; -11 when a tile entry is not a permutation or the map is
+ * not a layout. */
 int mfl_layout_partition_c(const char* c, const char* tile, const char* atom_tv, int64_t atom_m,
                            int64_t atom_n, int64_t warps_m, int64_t warps_n, char* thr_out,
                            char* val_out, int64_t cap);
 
-/* retile_D's regrouping of a register fragment (retile page, sections "带着 8
- * 和 2，读一遍 retile 的源码" and "两个 K fragment 怎样连成一组"): `frag` is
+/* retile_D's regrouping of a register fragment (retile page, sections "先确
+ * 定要从哪些 fragment 位置取值" to "两个 K fragment 怎样连成一组"): `frag` is
  * one thread's fragment layout (mode 0 the V values of one MMA, then one mode
  * per repeat direction, values = register slots), `tv` the copy's tiled TV
  * layout over the reference tile of shape `tile_shape` (thread + nthr*value
- * -> position, first coordinate fastest; it must cover the tile exactly) and
- * atom_nval the values one copy instruction writes per thread.  Computes
- *   mn = upcast<nthr*V>(right_inverse(tv).with_shape(tile_shape)),
- *   fv = logical_divide(logical_product(V:1, right_inverse(mn)), atom_nval:1),
- *   the fragment divided by (V, product_each(mn)...),
- * and returns (tile o fv, rest modes 1..): mode 0 = (values of one copy,
- * copy groups) -> register slot, then the repeats the copy leaves.  -13 when
- * frag's rank is not rank(tile_shape)+1 or the value mode is not taken whole. */
+ * -> position, first coordinate fastest; it must cover the tile once) and
+ * atom_nval the values one copy instruction writes per thread.  The copy
+ * orders a thread's values as the MMA orders its fragment: values c of block
+ * c / V are the V values of one MMA; a block's fragment repeat is where the
+ * block lies in the tile (the blocks met walking each tile axis, in order of
+ * first appearance).  Returns mode 0 = (values of one copy, copy groups) ->
+ * register slot, then the repeats the copy leaves.  -13 when frag's rank is
+ * not rank(tile_shape)+1, tv does not cover the tile once, or the counts do
+ * not divide; -11 when the blocks do not form a grid. */
 int mfl_layout_retile(const char* frag, const char* tv, const char* tile_shape, int64_t nthr,
                       int64_t atom_nval, char* out, int64_t cap);
 

@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <string>
+#include <vector>
 
 #include "../../include/mfl_gemm.h"
 #include "../../include/mfl_chain.h"
@@ -536,6 +537,150 @@ int gemm_launch(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, con
 }
 }  // namespace
 
+namespace {
+
+// retile_D's regrouping (retile page, "读懂 CuTe 的 retile_D", sections
+// "先确定要从哪些 fragment 位置取值" to "两个 K fragment 怎样连成一组"), from
+// where each value lies in the copy's reference tile.
+//
+// The copy's TV layout maps thread t's copy value c to a position of the
+// reference tile (positions numbered first coordinate fastest) and must cover
+// the tile once.  The tiled copy orders a thread's values as the MMA orders
+// its fragment: copy values c of one block b = c / V (V = the fragment's
+// value count, mode 0) are the V values of one MMA, value c % V.  Which
+// fragment repeat that block is follows from where the block lies: walking
+// each tile axis from the origin, the block numbers met, in order of first
+// appearance, are the repeat coordinates along that axis (block numbers are
+// additive over the axes).  So copy value c of a thread is the fragment
+// element (c % V, g_1 + e_1 r_1, ..., g_n + e_n r_n), with (g_d) the block's
+// axis coordinates, e_d the blocks along axis d, and (r_d) the repeats the
+// copy leaves (fragment mode d / e_d).  The result has mode 0 = (value of one
+// copy instruction, instruction) -> register slot, then one mode per r_d;
+// each part is factored from the table and the whole table is compared.
+mfl::Layout retile_by_position(const mfl::Layout& frag, const mfl::Layout& tv,
+                               const mfl::Layout& shape, int64_t nthr, int64_t nval) {
+  mfl::Layout bad;
+  bad.status = mfl::kLayoutBadIndex;
+  const int nd = shape.nmodes;
+  if (frag.nmodes != nd + 1 || nd < 1 || nd > mfl::kMaxModes - 1) return bad;
+  const int64_t P = mfl::size(shape);
+  if (P <= 0 || P > (int64_t(1) << 20) || mfl::size(tv) != P || P % nthr != 0) return bad;
+  const int64_t V = mfl::size_mode(frag, 0);
+  const int64_t per_thr = P / nthr;
+  if (V < 1 || per_thr % V != 0 || per_thr % nval != 0) return bad;
+  const int64_t K = per_thr / V;   // blocks (MMAs) per thread
+  // position -> TV index, and its block number
+  std::vector<int64_t> blk(P, -1);
+  for (int64_t q = 0; q < P; ++q) {
+    const int64_t p = mfl::eval(tv, q);
+    if (p < 0 || p >= P || blk[p] >= 0) return bad;   // not a cover of the tile
+    blk[p] = (q / nthr) / V;
+  }
+  // block numbers met along each axis, in order of first appearance
+  int64_t ext[mfl::kMaxModes] = {}, stride[mfl::kMaxModes] = {};
+  std::vector<std::vector<int64_t>> seen(nd);
+  int64_t st = 1, nblocks = 1;
+  for (int d = 0; d < nd; ++d) {
+    ext[d] = mfl::size_mode(shape, d);
+    stride[d] = st;
+    st *= ext[d];
+    for (int64_t x = 0; x < ext[d]; ++x) {
+      const int64_t b = blk[x * stride[d]];
+      bool have = false;
+      for (int64_t y : seen[d]) have = have || y == b;
+      if (!have) seen[d].push_back(b);
+    }
+    nblocks *= (int64_t)seen[d].size();
+  }
+  if (nblocks != K) return bad;
+  // additivity: the block of a position is the sum of its axis blocks
+  for (int64_t p = 0; p < P; ++p) {
+    int64_t sum = 0, rem = p;
+    for (int d = 0; d < nd; ++d) {
+      sum += blk[(rem % ext[d]) * stride[d]];
+      rem /= ext[d];
+    }
+    if (sum != blk[p]) {
+      mfl::Layout nc;
+      nc.status = mfl::kLayoutNotComposable;
+      return nc;
+    }
+  }
+  // axis coordinates of every block
+  std::vector<std::vector<int64_t>> gcoord(K, std::vector<int64_t>(nd, -1));
+  std::vector<int64_t> g(nd, 0);
+  for (int64_t cell = 0; cell < K; ++cell) {
+    int64_t rem = cell, b = 0;
+    for (int d = 0; d < nd; ++d) {
+      g[d] = rem % (int64_t)seen[d].size();
+      rem /= (int64_t)seen[d].size();
+      b += seen[d][g[d]];
+    }
+    if (b < 0 || b >= K || gcoord[b][0] >= 0) return bad;
+    gcoord[b] = g;
+  }
+  // repeats the copy leaves along each fragment mode
+  int64_t reps[mfl::kMaxModes] = {};
+  for (int d = 0; d < nd; ++d) {
+    const int64_t fm = mfl::size_mode(frag, d + 1), e = (int64_t)seen[d].size();
+    if (fm % e != 0) return bad;
+    reps[d] = fm / e;
+  }
+  // register slot of copy value c with leftover repeats given as one index
+  auto slot = [&](int64_t c, const int64_t* r) {
+    const int64_t b = c / V;
+    int64_t off = mfl::eval_mode(frag, 0, c % V);
+    for (int d = 0; d < nd; ++d)
+      off += mfl::eval_mode(frag, d + 1, gcoord[b][d] + (int64_t)seen[d].size() * r[d]);
+    return off;
+  };
+  const int64_t zero[mfl::kMaxModes] = {};
+  const int64_t base = slot(0, zero);
+  mfl::Layout out;
+  // mode 0: values of one instruction, then instructions (kept as two parts)
+  mfl::append_factored(out, nval, [&](int64_t j) { return slot(j, zero) - base; });
+  mfl::Layout groups;
+  mfl::append_factored(groups, per_thr / nval,
+                       [&](int64_t gi) { return slot(nval * gi, zero) - base; });
+  for (int i = 0; i < groups.nleaves; ++i) out.push_leaf(groups.shape[i], groups.stride[i]);
+  for (int d = 0; d < nd; ++d) {
+    mfl::append_factored(out, reps[d], [&](int64_t rd) {
+      int64_t r[mfl::kMaxModes] = {};
+      r[d] = rd;
+      return slot(0, r) - base;
+    });
+  }
+  if (out.status != mfl::kLayoutOk || groups.status != mfl::kLayoutOk) return bad;
+  if (base != 0) {
+    mfl::Layout nc;
+    nc.status = mfl::kLayoutNotComposable;
+    return nc;
+  }
+  // the whole table: every copy value of every leftover repeat
+  int64_t nrest = 1;
+  for (int d = 0; d < nd; ++d) nrest *= reps[d];
+  for (int64_t ri = 0; ri < nrest; ++ri) {
+    int64_t r[mfl::kMaxModes] = {}, rem = ri, idx = 0;
+    for (int d = 0; d < nd; ++d) {
+      r[d] = rem % reps[d];
+      rem /= reps[d];
+    }
+    for (int64_t c = 0; c < per_thr; ++c) {
+      int64_t got = mfl::eval_mode(out, 0, c);
+      for (int d = 0; d < nd; ++d) got += mfl::eval_mode(out, d + 1, r[d]);
+      (void)idx;
+      if (got != slot(c, r)) {
+        mfl::Layout nc;
+        nc.status = mfl::kLayoutNotComposable;
+        return nc;
+      }
+    }
+  }
+  return out;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* gemm_strerror(int code) {
@@ -720,7 +865,7 @@ int mfl_layout_retile(const char* frag, const char* tv, const char* tile_shape, 
   rc = parse_shape(tile_shape, S);
   if (rc) return rc;
   if (nthr < 1 || atom_nval < 1) return mfl::kLayoutBadIndex;
-  return emit(mfl::retile(F, TV, S, nthr, atom_nval, true), out, cap);
+  return emit(retile_by_position(F, TV, S, nthr, atom_nval), out, cap);
 }
 
 int mfl_layout_right_inverse(const char* layout, char* out, int64_t cap) {

@@ -34,8 +34,8 @@
 //   with_shape(L, S)    L o make_layout(S): the same function on a domain
 //                       reshaped to S
 //   tiled_product       logical_product with B's modes kept apart
-//   partition_c         the four steps of a tiled MMA's C partition
-//   retile              retile_D's regrouping of a register fragment
+//   partition_c         a tiled MMA's C partition, from the element each
+//                       (thread, value) holds, factored into layouts
 // Results that would nest three levels deep keep their leaves flattened
 // inside a top-level mode; as functions they are unchanged.
 // All functions are constexpr so kernels can fold them at compile time.
@@ -617,18 +617,60 @@ MFL_HD constexpr Layout flat_join(const Layout* parts, int n) {
   return out;
 }
 
+// ------------------------------------------------------------- factoring
+// One mode of a layout for a function f on [0, n) with f(0) = 0: the index
+// is split into prime digits, smallest prime first, and each digit becomes a
+// leaf whose stride is f at that digit's unit; a digit that continues the
+// previous leaf's progression (stride = that leaf's shape x stride) widens
+// it instead.  The mode equals f exactly when f is linear over these digits,
+// which holds for every layout whose leaves have power-of-two shapes; other
+// inputs are checked by the caller against the whole table.
+template <class F>
+MFL_HD constexpr void append_factored(Layout& out, int64_t n, const F& f) {
+  out.open_mode();
+  const int first = out.nleaves;
+  int64_t rest = n, unit = 1;
+  while (rest > 1) {
+    int64_t p = 2;
+    while (rest % p != 0) ++p;
+    const int64_t d = f(unit);
+    const int k = out.nleaves;
+    int st = kLayoutOk;
+    if (k > first && ck_mul(out.shape[k - 1], out.stride[k - 1], st) == d && st == kLayoutOk)
+      out.shape[k - 1] = ck_mul(out.shape[k - 1], p, out.status);
+    else
+      out.push_leaf(p, d);
+    unit = ck_mul(unit, p, out.status);
+    rest /= p;
+  }
+  if (out.nleaves == first) out.push_leaf(1, 0);
+}
+
 // ------------------------------------------------------------ partition_C
 // The C partition of a tiled MMA (TiledMMA page, "partition_C 怎样把分工应
-// 用到一个 Tensor"): the output tensor C (mode 0 = M, mode 1 = N) is
-//   1. divided mode by mode by the tile (tile_m, tile_n): the tiled MMA's
-//      permutations, or compact (atom_m * warps_m):1 where none is given;
-//   2. divided again by the atom (atom_m:1, atom_n:1), tile parts together;
-//   3. the atom block (index m + atom_m * n) composed with the atom's C TV
-//      layout: (lane, value) -> offset;
-//   4. the remaining blocks divided by the warps (warps_m:1, warps_n:1).
-// Result `thr`: one mode, thread lane + nlanes * (wm + warps_m * wn) -> offset
-// of the thread's first value; `val`: (value, rest M, rest N) -> offset from
-// it.  The view of thread t is offset thr(t) with layout val.
+// 用到一个 Tensor"), computed from the element each (thread, value, repeat)
+// holds and then written as layouts.
+//
+// The tiled MMA repeats an atom_m x atom_n atom over warps_m x warps_n warps
+// (warp w = wm + warps_m wn; thread t = lane + nlanes w).  C (mode 0 = M,
+// mode 1 = N, its storage layout) is cut into tiles of tile_m x tile_n
+// (the sizes of the tile entries, or atom x warps); inside a tile, logical
+// row i sits at physical row tile_m(i) (the entry permutes the tile's rows,
+// section "用 Layout 改变 M 方向的坐标顺序"; compact when absent).  Along M
+// the atom-row blocks are numbered down each tile and then across tiles
+// (block b: tile b / (tile_m/atom_m), logical rows atom_m (b % (tile_m/
+// atom_m)) + 0 .. atom_m-1), and warp row wm takes blocks wm, wm + warps_m,
+// wm + 2 warps_m, ...: its rm-th repeat is block wm + warps_m rm.  Likewise
+// along N.  Value v of lane l is the atom element q = atom_tv(l + nlanes v),
+// at (q % atom_m, q / atom_m) inside its block.  So thread t's value v of
+// repeat (rm, rn) is C at
+//   m = tile_m(q % atom_m + atom_m (bm % (tile_m/atom_m))) + tile_m_size (bm / (tile_m/atom_m)),
+//   bm = wm + warps_m rm, and n the same way.
+// The results: `thr`, one mode, thread -> offset of its first value (value
+// 0 of repeat (0, 0)); `val`, (value, rest M, rest N) -> offset from it.
+// Each mode is factored from that function (append_factored); with `verify`
+// every (thread, value) is compared, and the tile entries must permute
+// their tiles' rows.
 struct CPartition {
   Layout thr;
   Layout val;
@@ -638,107 +680,79 @@ MFL_HD constexpr CPartition partition_c(const Layout& C, const Layout* tile, con
                                         int64_t atom_m, int64_t atom_n, int64_t warps_m,
                                         int64_t warps_n, bool verify = false) {
   CPartition r;
+  auto fail = [&](int st) {
+    r.thr = Layout{};
+    r.val = Layout{};
+    r.thr.status = r.val.status = st;
+    return r;
+  };
+  if (C.status != kLayoutOk) return fail(C.status);
+  if (atom_tv.status != kLayoutOk) return fail(atom_tv.status);
+  if (tile && (tile[0].status != kLayoutOk || tile[1].status != kLayoutOk))
+    return fail(tile[0].status != kLayoutOk ? tile[0].status : tile[1].status);
+  if (C.nmodes != 2 || atom_tv.nmodes != 2 || atom_m < 1 || atom_n < 1 || warps_m < 1 ||
+      warps_n < 1)
+    return fail(kLayoutBadIndex);
   int ovf = kLayoutOk;
-  Layout t2[2] = {unit_leaf(ck_mul(atom_m, warps_m, ovf)), unit_leaf(ck_mul(atom_n, warps_n, ovf))};
-  if (tile) {
-    t2[0] = tile[0];
-    t2[1] = tile[1];
+  const int64_t ext[2] = {size_mode(C, 0, &ovf), size_mode(C, 1, &ovf)};
+  const int64_t atom[2] = {atom_m, atom_n}, warps[2] = {warps_m, warps_n};
+  const int64_t nlanes = size_mode(atom_tv, 0, &ovf), nvals = size_mode(atom_tv, 1, &ovf);
+  int64_t tsz[2] = {0, 0}, per_tile[2] = {0, 0}, reps[2] = {0, 0};
+  for (int d = 0; d < 2; ++d) {
+    tsz[d] = tile ? size(tile[d], &ovf) : ck_mul(atom[d], warps[d], ovf);
+    // the tile must divide C, the atom the tile and the warps the atom blocks
+    if (ovf != kLayoutOk) return fail(ovf);
+    if (tsz[d] < 1 || ext[d] % tsz[d] != 0 || tsz[d] % atom[d] != 0) return fail(kLayoutBadIndex);
+    per_tile[d] = tsz[d] / atom[d];
+    const int64_t blocks = ck_mul(per_tile[d], ext[d] / tsz[d], ovf);
+    if (blocks % warps[d] != 0) return fail(kLayoutBadIndex);
+    reps[d] = blocks / warps[d];
   }
-  const bool all[2] = {true, true};
-  const Layout t_tensor = logical_divide_modes(C, t2, all, 2, verify);
-  const Layout a2[2] = {unit_leaf(atom_m), unit_leaf(atom_n)};
-  Layout atile[2], arest[2];
-  divide_modes(t_tensor, a2, all, 2, atile, arest, verify);
-  const Layout block = flat_join(atile, 2);
-  const Layout tv = compose_v(block, atom_tv, verify);
-  const Layout w2[2] = {unit_leaf(warps_m), unit_leaf(warps_n)};
-  Layout q0 = logical_divide(arest[0], w2[0], verify), q1 = logical_divide(arest[1], w2[1], verify);
-  const Layout thr_parts[3] = {mode_of(tv, 0), mode_of(q0, 0), mode_of(q1, 0)};
-  r.thr = flat_join(thr_parts, 3);
-  r.val.open_mode();
-  append_leaves(r.val, mode_of(tv, 1));
-  r.val.open_mode();
-  append_leaves(r.val, mode_of(q0, 1));
-  r.val.open_mode();
-  append_leaves(r.val, mode_of(q1, 1));
-  int st = kLayoutOk;
-  const Layout* chk[] = {&C, &t_tensor, &atile[0], &atile[1], &arest[0], &arest[1], &tv, &q0, &q1};
-  for (const Layout* l : chk)
-    if (l->status != kLayoutOk) st = l->status;
-  // the tile must divide C, the atom the tile and the warps the atom blocks
-  // (the counts are positive: a zero count divides nothing)
-  if (C.nmodes != 2 || atom_m < 1 || atom_n < 1 || warps_m < 1 || warps_n < 1 ||
-      size_mode(C, 0, &ovf) % size(t2[0], &ovf) != 0 ||
-      size_mode(C, 1, &ovf) % size(t2[1], &ovf) != 0 || size(t2[0], &ovf) % atom_m != 0 ||
-      size(t2[1], &ovf) % atom_n != 0 || size(arest[0], &ovf) % warps_m != 0 ||
-      size(arest[1], &ovf) % warps_n != 0 || size(atom_tv, &ovf) != ck_mul(atom_m, atom_n, ovf))
-    st = kLayoutBadIndex;
-  if (ovf != kLayoutOk) st = ovf;
-  r.thr.status = r.val.status = st;
-  return r;
-}
+  if (ck_mul(atom_m, atom_n, ovf) != size(atom_tv, &ovf)) return fail(kLayoutBadIndex);
+  const int64_t nthr = ck_mul(nlanes, ck_mul(warps_m, warps_n, ovf), ovf);
+  const int64_t nval = ck_mul(nvals, ck_mul(reps[0], reps[1], ovf), ovf);
+  if (ovf != kLayoutOk) return fail(ovf);
 
-// ----------------------------------------------------------------- retile
-// retile_D (retile page, "带着 8 和 2，读一遍 retile 的源码" and "两个 K
-// fragment 怎样连成一组"): the register fragment `frag` of one thread (mode 0
-// the V values of one MMA, then one mode per repeat direction) regrouped for a
-// copy atom that writes `atom_nval` values per thread, given the copy's tiled
-// TV layout `tv` (thread + nthr * value -> position in the reference tile,
-// first coordinate fastest) and the tile's shape:
-//   frg_layout_mn = upcast<nthr*V>(right_inverse(tv).with_shape(tile_shape))
-//   frg_layout_v  = divide(logical_product(V:1, right_inverse(frg_layout_mn)),
-//                          atom_nval:1)
-//   t_tensor      = zipped_divide(frag, (V, product_each(frg_layout_mn)...))
-//   result        = (t_tensor's tile o frg_layout_v, rest modes 1..)
-// The value mode's own rest has size 1 and is dropped.  Mode 0 of the result
-// is (copy values, copy groups) flattened: a copy group takes values
-// across fragments wherever frg_layout_mn keeps more than one position.
-MFL_HD constexpr Layout retile(const Layout& frag, const Layout& tv, const Layout& tile_shape,
-                               int64_t nthr, int64_t atom_nval, bool verify = false) {
-  Layout out;
-  int ovf = kLayoutOk;
-  const int64_t V = size_mode(frag, 0, &ovf);
-  const Layout ri = right_inverse(tv);
-  if (nthr < 1 || atom_nval < 1 || size(ri, &ovf) != size(tile_shape, &ovf)) {
-    out.status = kLayoutBadIndex;   // tv must cover the tile exactly
-    return out;
+  // the C offset of thread t's value u = v + nvals (rm + reps_m rn)
+  auto coord = [&](int d, int64_t a, int64_t w, int64_t rep) {   // a: atom coordinate
+    const int64_t b = w + warps[d] * rep;
+    const int64_t i = a + atom[d] * (b % per_tile[d]);
+    return (tile ? eval(tile[d], i) : i) + tsz[d] * (b / per_tile[d]);
+  };
+  auto offset = [&](int64_t t, int64_t u) {
+    const int64_t lane = t % nlanes, w = t / nlanes;
+    const int64_t v = u % nvals, ru = u / nvals;
+    const int64_t q = eval(atom_tv, lane + nlanes * v);
+    const int64_t m = coord(0, q % atom_m, w % warps_m, ru % reps[0]);
+    const int64_t n = coord(1, q / atom_m, w / warps_m, ru / reps[0]);
+    return eval_mode(C, 0, m) + eval_mode(C, 1, n);
+  };
+  if (offset(0, 0) != 0) return fail(kLayoutNotComposable);   // not a layout
+  append_factored(r.thr, nthr, [&](int64_t t) { return offset(t, 0); });
+  append_factored(r.val, nvals, [&](int64_t v) { return offset(0, v); });
+  append_factored(r.val, reps[0], [&](int64_t rm) { return offset(0, nvals * rm); });
+  append_factored(r.val, reps[1], [&](int64_t rn) { return offset(0, nvals * reps[0] * rn); });
+  if (r.thr.status != kLayoutOk || r.val.status != kLayoutOk)
+    return fail(r.thr.status != kLayoutOk ? r.thr.status : r.val.status);
+  if (verify) {
+    if (ck_mul(nthr, nval, ovf) > kVerifyMax || ovf != kLayoutOk) return fail(kLayoutTooLarge);
+    if (tile) {   // each entry permutes its tile's rows
+      for (int d = 0; d < 2; ++d) {
+        if (tsz[d] > 4096) return fail(kLayoutTooLarge);
+        bool seen[4096] = {};
+        for (int64_t i = 0; i < tsz[d]; ++i) {
+          const int64_t x = eval(tile[d], i);
+          if (x < 0 || x >= tsz[d] || seen[x]) return fail(kLayoutNotComposable);
+          seen[x] = true;
+        }
+      }
+    }
+    // the C coordinates stay inside C, and the layouts equal the rule
+    for (int64_t t = 0; t < nthr; ++t)
+      for (int64_t u = 0; u < nval; ++u)
+        if (eval(r.thr, t) + eval(r.val, u) != offset(t, u)) return fail(kLayoutNotComposable);
   }
-  const Layout inv = with_shape(ri, tile_shape, verify);
-  const Layout mn = upcast(inv, ck_mul(nthr, V, ovf));
-  const Layout G = right_inverse(mn);
-  const Layout prod = logical_product(unit_leaf(V), G, verify);
-  const Layout fv = logical_divide(prod, unit_leaf(atom_nval), verify);
-  if (frag.nmodes != mn.nmodes + 1 || frag.nmodes > kMaxModes) {
-    out.status = kLayoutBadIndex;
-    return out;
-  }
-  Layout tilers[kMaxModes];
-  bool all[kMaxModes] = {};
-  tilers[0] = unit_leaf(V);
-  all[0] = true;
-  for (int m = 1; m < frag.nmodes; ++m) {
-    tilers[m] = unit_leaf(size_mode(mn, m - 1, &ovf));
-    all[m] = true;
-  }
-  Layout tile[kMaxModes], rest[kMaxModes];
-  divide_modes(frag, tilers, all, frag.nmodes, tile, rest, verify);
-  const Layout t0 = flat_join(tile, frag.nmodes);
-  const Layout vt = compose_v(t0, fv, verify);
-  out.open_mode();
-  append_leaves(out, vt);
-  for (int m = 1; m < frag.nmodes; ++m) {
-    out.open_mode();
-    append_leaves(out, rest[m]);
-  }
-  const Layout* chk[] = {&tv, &inv, &mn, &G, &prod, &fv, &t0, &vt};
-  for (const Layout* l : chk)
-    if (l->status != kLayoutOk) out.status = l->status;
-  for (int m = 0; m < frag.nmodes; ++m)
-    if (tile[m].status != kLayoutOk) out.status = tile[m].status;
-  if (size(rest[0], &ovf) != 1 || size(prod, &ovf) % atom_nval != 0)
-    out.status = kLayoutBadIndex;
-  if (ovf != kLayoutOk) out.status = ovf;
-  return out;
+  return r;
 }
 
 }  // namespace mfl

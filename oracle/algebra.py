@@ -3,14 +3,13 @@
 Test infrastructure only (see ``oracle/__init__.py``).  Pages cited by the
 titles listed in ``oracle/layout.py``.
 
-The pages build their partitions from a few layout operations: the
-``logical_divide`` / ``zipped_divide`` steps of partition_C ([TiledMMA]
-"partition_C 怎样把分工应用到一个 Tensor"), and ``upcast``, ``with_shape``,
-``logical_product`` and the divides inside retile ([retile] "带着 8 和 2，读一
-遍 retile 的源码" and "两个 K fragment 怎样连成一组").  The pages name the
-operations and print their results; they do not define them.  Here each one
-is written as a function of integer indices (a table), from the property
-that pins it, never by manipulating shape:stride text:
+The pages build their partitions from a few layout operations: divides
+([TiledMMA] "partition_C 怎样把分工应用到一个 Tensor"), and ``upcast``,
+``with_shape``, ``logical_product`` and the divides inside retile ([retile]
+"带着 8 和 2，读一遍 retile 的源码" and "两个 K fragment 怎样连成一组").  The
+pages name the operations and print their results; they do not define them.
+Here each one is written as a function of integer indices (a table), from
+the property that pins it, never by manipulating shape:stride text:
 
   complement(B, M)     the increasing offsets r_0 < r_1 < ... where r_j is the
                        smallest offset in [0, M) not yet reached by B + r_k
@@ -27,6 +26,10 @@ that pins it, never by manipulating shape:stride text:
 A result is returned as (mode sizes, table): the sizes of its top-level
 modes and the offset of every flattened index (first mode fastest).  Tests
 compare them with the pages' printed layouts evaluated by ``layout.table``.
+
+partition_C is computed from the element each (thread, value, repeat)
+holds, in plain loops; retile, which the pages define only by its
+algorithm, by that algorithm's steps on tables.
 """
 from __future__ import annotations
 
@@ -174,9 +177,10 @@ def _shape_div(a: int, b: int) -> int:
 
 
 def upcast(layout, n: int):
-    """Leaf (s, d): s becomes s / (n / d) and d becomes d / n, each rounded
-    up to 1 when the unit is larger ([retile] "upcast<32*8> 按 256 个元素为一
-    个单位压缩布局"); stride-0 leaves are unchanged."""
+    """The layout read in units of n elements, leaf by leaf ([retile] "带着 8
+    和 2，读一遍 retile 的源码"): leaf (s, d) keeps s / (n / d) coordinates at
+    stride d / n, and a leaf whose whole extent lies inside one unit shrinks
+    to one coordinate; stride-0 leaves are unchanged."""
     shape, stride = layout
 
     def leaf(s, d):
@@ -266,66 +270,71 @@ def right_inverse_shaped(tv, shape: Tuple[int, ...]):
     return factor_table(inv, shape)
 
 
-def _divided(mode_fn, n: int, tiler) -> List[int]:
-    """One mode (a function of its index, domain n) divided by ``tiler``:
-    index i + |T| j -> mode(T(i) + R(j)), R = complement(T, n)."""
-    tt = table(tiler)
-    rest = complement_offsets(tt, n)
-    return [mode_fn(tt[i] + rest[j]) for j in range(len(rest)) for i in range(len(tt))]
+def _warp_block(w: int, nwarps: int, reps: int, rep: int) -> int:
+    """Atom block held by warp w in its rep-th repeat along one direction: the
+    warps take turns, block w + nwarps * rep."""
+    return w + nwarps * rep
+
+
+def _atom_mn(q: int, am: int):
+    """Element q of the atom's C block (first coordinate fastest) -> (m, n)."""
+    return q % am, q // am
+
+
+def _c_row(perm: Sequence[int], am: int, a: int, b: int) -> int:
+    """Row of C for atom coordinate a of atom block b, blocks numbered down a
+    tile first and then across tiles; inside a tile the logical row i is the
+    physical row perm[i]."""
+    per_tile = len(perm) // am
+    return perm[a + am * (b % per_tile)] + len(perm) * (b // per_tile)
 
 
 def partition_c(c_layout, atom_tv, atom_mn, nlanes: int, warps_mn, tile=None):
-    """partition_C ([TiledMMA] "partition_C 怎样把分工应用到一个 Tensor") of
-    the rank-2 tensor ``c_layout`` (M, N), on functions of indices:
+    """partition_C of a tiled MMA ([TiledMMA] "partition_C 怎样把分工应用到一个
+    Tensor"), as the element every thread holds, by brute force over threads,
+    values and repeats.
 
-      1. each mode divided by the tile entry: ``tile`` = (layout M, layout N),
-         the tiled MMA's permutations ("用 Layout 改变 M 方向的坐标顺序"),
-         default compact (AtomM*WM):1, (AtomN*WN):1;
-      2. each mode divided again by the atom extent (AtomM:1, AtomN:1):
-         index = a + Atom*b, the atom parts (aM, aN) zipped into one mode
-         q = aM + AtomM*aN and the block indices (bM, bN) into the other;
-      3. q replaced by the atom's C TV layout: (lane, value) -> q;
-      4. each block index divided by the warp count: b = w + W*r.
+    The atom (AtomM x AtomN, C layout ``atom_tv``: lane + nlanes*value -> q, q
+    = m + AtomM*n) is repeated over WM x WN warps; C (modes M, N of the storage
+    layout ``c_layout``) is covered by tiles whose rows are permuted by the
+    tile entries ("用 Layout 改变 M 方向的坐标顺序"; default compact
+    AtomM*WM:1, AtomN*WN:1).  Along M the atom-sized row blocks are numbered
+    down a tile and then across tiles, and warp row wm holds blocks wm, wm +
+    WM, wm + 2 WM, ... (the interleaving of "把剩余块分给 M、N 方向的线程组");
+    likewise along N.  Lane l's value v is atom element q = atom_tv(l, v).
 
-    Returns ({thread: [offset of (value, rM, rN), value fastest]}, step 1
-    result, step 2 result), thread = lane + nlanes*(wM + WM*wN)."""
+    Returns {thread: [C offset of (value, rM, rN), value fastest]}, thread =
+    lane + nlanes*(wM + WM*wN).  The tile entries must permute their rows."""
     am, an = atom_mn
     wm_n, wn_n = warps_mn
-    shape, stride = c_layout
-    nM, nN = size(shape[0]), size(shape[1])
-    cm = lambda k: _at_unbounded((shape[0], stride[0]), k)
-    cn = lambda k: _at_unbounded((shape[1], stride[1]), k)
+    shape, _ = c_layout
+    n_m, n_n = size(shape[0]), size(shape[1])
     tiles = tile or ((am * wm_n, 1), (an * wn_n, 1))
-    # step 1
-    fM = _divided(cm, nM, tiles[0])
-    fN = _divided(cn, nN, tiles[1])
-    step1 = (len(fM), len(fN)), [fM[i] + fN[j] for j in range(len(fN)) for i in range(len(fM))]
-    # step 2
-    gM = _divided(lambda k: fM[k], len(fM), (am, 1))
-    gN = _divided(lambda k: fN[k], len(fN), (an, 1))
-    bM, bN = len(gM) // am, len(gN) // an
-    assert bM * am == len(gM) and bN * an == len(gN), "the atom must divide the tile"
-
-    def c_tensor(q, b):
-        return gM[q % am + am * (b % bM)] + gN[q // am + an * (b // bM)]
-
-    step2 = (am * an, bM * bN), [c_tensor(q, b) for b in range(bM * bN) for q in range(am * an)]
-    # steps 3 and 4
+    perm_m, perm_n = table(tiles[0]), table(tiles[1])
+    assert sorted(perm_m) == list(range(len(perm_m))), "the M entry must permute the tile's rows"
+    assert sorted(perm_n) == list(range(len(perm_n))), "the N entry must permute the tile's columns"
+    assert n_m % len(perm_m) == 0 and n_n % len(perm_n) == 0, "the tile must divide C"
+    assert len(perm_m) % am == 0 and len(perm_n) % an == 0, "the atom must divide the tile"
+    blocks_m = len(perm_m) // am * (n_m // len(perm_m))
+    blocks_n = len(perm_n) // an * (n_n // len(perm_n))
+    assert blocks_m % wm_n == 0 and blocks_n % wn_n == 0, "the warps must divide the blocks"
+    r_m, r_n = blocks_m // wm_n, blocks_n // wn_n
     tv = table(atom_tv)
     nvals = len(tv) // nlanes
-    rM, rN = bM // wm_n, bN // wn_n
-    assert rM * wm_n == bM and rN * wn_n == bN, "the warps must divide the blocks"
     out = {}
     for wn in range(wn_n):
         for wm in range(wm_n):
             for lane in range(nlanes):
                 vals = []
-                for jn in range(rN):
-                    for im in range(rM):
-                        b = (wm + wm_n * im) + bM * (wn + wn_n * jn)
-                        vals.extend(c_tensor(tv[lane + nlanes * v], b) for v in range(nvals))
+                for jn in range(r_n):
+                    for im in range(r_m):
+                        for v in range(nvals):
+                            ma, na = _atom_mn(tv[lane + nlanes * v], am)
+                            m = _c_row(perm_m, am, ma, _warp_block(wm, wm_n, r_m, im))
+                            n = _c_row(perm_n, an, na, _warp_block(wn, wn_n, r_n, jn))
+                            vals.append(evaluate(c_layout, (m, n)))
                 out[lane + nlanes * (wm + wm_n * wn)] = vals
-    return out, step1, step2
+    return out
 
 
 def tiled_product(a, b) -> Result:
@@ -337,21 +346,25 @@ def tiled_product(a, b) -> Result:
 
 
 def retile(frag, tiled_tv, tile_shape: Tuple[int, ...], nthr: int, atom_nval: int):
-    """retile_D's chain ([retile] "带着 8 和 2，读一遍 retile 的源码" and "两个 K
-    fragment 怎样连成一组") for a register fragment ``frag`` (tCrX: mode 0 the
-    V values of one MMA, then one mode per repeat direction), the tiled TV
-    layout of the copy's reference tile ``tiled_tv`` over ``tile_shape``:
+    """retile_D ([retile] "带着 8 和 2，读一遍 retile 的源码" and "两个 K
+    fragment 怎样连成一组"): the pages define it only by its algorithm, so this
+    follows the algorithm's steps in the pages' order, each on a function
+    table.  ``frag`` is one thread's register fragment (mode 0 the V values
+    of one MMA, then a mode per repeat direction); ``tiled_tv`` the copy's TV
+    layout over the reference tile of ``tile_shape``.
 
-      frg_layout_mn = upcast<nthr*V>(right_inverse(TV).with_shape(tile))
-      G             = right_inverse(frg_layout_mn)
-      frg_layout_v  = divide(logical_product(V:1, G), atom_nval:1)
-      t_tensor      = zipped_divide(frag, (V, product_each(frg_layout_mn)...))
-      result        = t_tensor with mode 0 composed with frg_layout_v, the
-                      rest coordinate of the value mode fixed to 0
+    First the tile positions are numbered by the copy index that reaches
+    them (the right inverse, reshaped to the tile) and read in units of
+    nthr*V, which gives each position the MMA block it belongs to; the right
+    inverse of that gives each block number its coarse position.  Pairing
+    the V values of a block with that position (a logical product) and
+    cutting the result into groups of ``atom_nval`` gives the copy's value
+    order; the fragment, split into the V values and the blocks the copy
+    covers along each repeat mode, is then read in that order.
 
-    Returns a dict of the intermediate results and ``slots``: {(copy index
-    c, rest index r): register slot}, c over the copy atom's values (and its
-    groups), r over the remaining repeats (first fastest)."""
+    Returns the intermediate results and ``slots``: {(copy index c, rest
+    index r): register slot}, c over the copy atom's values and groups, r over
+    the repeats the copy leaves (first fastest)."""
     from .layout import right_inverse_table
     V = size(frag[0][0])
     shaped = right_inverse_shaped(tiled_tv, tile_shape)

@@ -198,8 +198,9 @@ def right_inverse_table(values: Sequence[int]) -> List[int]:
 
 
 def tv_table(layout, nthr: int) -> List[int]:
-    """Flatten a TV layout as tv = t + nthr*v ([retile] 'TV 编号按
-    thread+32*value 展平')."""
+    """A TV layout as a table over one index, thread fastest: entry t +
+    nthr*v is thread t's value v ([retile] "先确定要从哪些 fragment 位置取
+    值")."""
     shape, _ = layout
     nval = size(shape) // nthr
     return [evaluate(layout, (t, v)) for v in range(nval) for t in range(nthr)]

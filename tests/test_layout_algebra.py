@@ -242,7 +242,7 @@ def test_with_shape_of_inverse_matches_oracle(tv, shape):
 def _partition_oracle(c, tv_text, atom, nl, warps, tile):
     tl = None if tile is None else tuple(P(t) if t else (atom[i] * warps[i], 1)
                                          for i, t in enumerate(tile))
-    out, _, _ = G.partition_c(P(c), P(tv_text), atom, nl, warps, tile=tl)
+    out = G.partition_c(P(c), P(tv_text), atom, nl, warps, tile=tl)
     return out
 
 

@@ -165,13 +165,18 @@ def test_tiled_product_matches_page():
 
 
 def test_partition_c_page_steps():
+    """The printed intermediate tensors pin the divides the page applies (by
+    the tile, then by the atom); the partition itself is pinned by thread 0's
+    printed view and the printed start coordinates."""
     c = P(_golden("pc_c")[0][0])
-    out, s1, s2 = G.partition_c(c, P(L.SM80_C_TV), (16, 8), 32, (2, 2))
+    out = G.partition_c(c, P(L.SM80_C_TV), (16, 8), 32, (2, 2))
     want_sizes = [_tup(x) for x in _golden("pc_t_tensor_sizes")[0]]
-    assert s1[0] == tuple(a * b for a, b in want_sizes)
     assert _tup(_golden("pc_t_tile")[0][0]) == (16 * 2, 8 * 2)
+    s1 = G.logical_divide_modes(c, [(32, 1), (16, 1)])
+    assert s1[0] == tuple(a * b for a, b in want_sizes)
     # the printed c_tensor is the tiling fixture's only such line
     (only,) = [s for s in lines("tiledmma_tiling.txt") if s.startswith("c_tensor")]
+    s2 = G.zipped_divide(c, [(16, 1), (8, 1)])
     assert s2[1] == L.table(P(only.split()[1]))
     # lane 0 value 2 -> block (8,0) -> offset 128
     toks = _golden("pc_tv")[0]
@@ -192,13 +197,13 @@ def test_partition_c_page_steps():
 def test_partition_c_larger_input_view():
     view = next(iter(keyed("tiledmma_tiling.txt", "partition_C_view")))
     c = P("(64,32):(32,1)")
-    out, _, _ = G.partition_c(c, P(L.SM80_C_TV), (16, 8), 32, (2, 2))
+    out = G.partition_c(c, P(L.SM80_C_TV), (16, 8), 32, (2, 2))
     assert out[0] == L.table(P(view[1]))
 
 
 def test_partition_c_with_perm_m_matches_printed_coords():
     c = P("(32,16):(16,1)")
-    out, _, _ = G.partition_c(c, P(L.SM80_C_TV), (16, 8), 32, (2, 2),
+    out = G.partition_c(c, P(L.SM80_C_TV), (16, 8), 32, (2, 2),
                               tile=(P("(8,4):(4,1)"), (16, 1)))
     from helpers import table as gtable
     rows = gtable("tiledmma_tiling.txt", "C perm_m")
@@ -219,7 +224,7 @@ def test_partition_c_equals_closed_form_model(name):
         tile = ((64, 1), (32, 1))
     if name == "perm_m":
         tile = (P("(8,4):(4,1)"), (16, 1))
-    out, _, _ = G.partition_c(c, P(L.SM80_C_TV), (16, 8), 32, (cfg.WM, cfg.WN), tile=tile)
+    out = G.partition_c(c, P(L.SM80_C_TV), (16, 8), 32, (cfg.WM, cfg.WN), tile=tile)
     for t in range(cfg.nthreads):
         lane, wm, wn, wk = cfg.flat_coord(t)
         got = out[lane + 32 * (wm + cfg.WM * wn)]
@@ -400,6 +405,21 @@ def _mut_factor_swapped(tab, shape):
     return (lay[0][::-1], lay[1][::-1])
 
 
+def _mut_warp_block_consecutive(w, nwarps, reps, rep):
+    """Mistake: each warp takes a run of consecutive blocks."""
+    return w * reps + rep
+
+
+def _mut_atom_mn_swapped(q, am):
+    """Mistake: the atom element read n fastest."""
+    return q // am, q % am
+
+
+def _mut_c_row_unpermuted(perm, am, a, b):
+    """Mistake: the tile entry's row permutation ignored."""
+    return a + am * b
+
+
 _ORIG = {"zipped_divide": G.zipped_divide, "factor_table": G.factor_table}
 
 
@@ -409,6 +429,9 @@ _ORIG = {"zipped_divide": G.zipped_divide, "factor_table": G.factor_table}
     ("upcast", _mut_upcast_floor),
     ("product_tables", _mut_product_no_complement),
     ("factor_table", _mut_factor_swapped),
+    ("_warp_block", _mut_warp_block_consecutive),
+    ("_atom_mn", _mut_atom_mn_swapped),
+    ("_c_row", _mut_c_row_unpermuted),
 ])
 def test_planted_mistakes_are_caught(monkeypatch, name, fn):
     monkeypatch.setattr(G, name, fn)
