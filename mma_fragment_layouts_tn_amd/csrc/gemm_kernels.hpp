@@ -285,6 +285,16 @@ MFL_HD constexpr bool c_columns_per_lane() {
 static_assert(c_columns_per_lane<kMfma32x32x16>() && c_columns_per_lane<kMfma16x16x32>(),
               "accumulator column must not depend on the value");
 
+// Wait until at most VM vector-memory operations of this wave are in flight
+// and all its LDS operations are done (s_waitcnt vmcnt(VM) lgkmcnt(0); the
+// export counter is not waited on).  Vector-memory loads complete in issue
+// order, so this leaves exactly the VM most recent ones outstanding.
+template <int VM>
+__device__ __forceinline__ void wait_vm_lds() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt has 6 bits");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | (((VM >> 4) & 3) << 14) | (7 << 4));
+}
+
 // whole tile inside D, vector-aligned rows, and every row of the tile within
 // reach of one buffer descriptor
 template <class Cfg, int CK, int DK>
@@ -358,6 +368,85 @@ __device__ __forceinline__ void epilogue_regs(const GemmParams& p, int w, int la
           }
         }
       }
+    }
+  }
+}
+
+// The register epilogue with fp32 C taken through LDS.  Loading C with
+// per-lane vector loads leaves a few KB in flight per wave and waits for each
+// batch, so the C read runs far below the memory's rate.  Here the operand
+// stages hold a wave row band of C (CR = WTM rows) at a time: the WAVES_N
+// waves of that band fetch its rows straight into LDS (one 1 KB run per
+// instruction, all runs of the band in flight together, and no store of
+// theirs queued ahead, so their wait covers loads alone), then add each
+// accumulator to the C value at its position and store D as the register
+// epilogue does.
+template <class Cfg>
+struct CViaLds {
+  static constexpr int kBytes = Cfg::kStages * (Cfg::BM + Cfg::BN) * Cfg::BK * 2;
+  static constexpr int CR = Cfg::WTM;          // rows per pass: one wave row band
+  static constexpr int RPI = 256 / Cfg::BN;    // rows per 1 KB run
+  static constexpr int kRuns = CR / RPI;       // runs per pass
+  // (the 16x16x32 kernels tie their accumulators by hand and have no
+  // registers to spare for this path)
+  static constexpr bool ok = Cfg::WAVES_K == 1 && Cfg::kOp == kMfma32x32x16 &&
+                             (Cfg::BN == 128 || Cfg::BN == 256) && CR * Cfg::BN * 4 <= kBytes &&
+                             kRuns % Cfg::WAVES_N == 0;
+};
+
+template <class Cfg, int DK>
+__device__ __forceinline__ void epilogue_c_lds(const GemmParams& p, _Float16* smem, int w,
+                                               int lane, int m0, int n0,
+                                               const AccT<Cfg> (&acc)[Cfg::RM][Cfg::RN]) {
+  using X = CViaLds<Cfg>;
+  static_assert(X::ok, "configuration without a C pass through LDS");
+  constexpr int RM = Cfg::RM, V = Cfg::kVec, NG = Cfg::RN / V, NV = Cfg::kNV;
+  constexpr int AM = Cfg::kAtomM, AN = Cfg::kAtomN, BN = Cfg::BN, ES = DK == 1 ? 2 : 4;
+  const float* C = (const float*)p.C;
+  float* cs = (float*)smem;
+  const int wm = wave_m<Cfg>(w), wn = wave_n<Cfg>(w);
+  const RowK cl = atom_c_coord_of<Cfg::kOp>(lane, 0);
+  const RowK w0 = frag_c_coord<Cfg>(w, 0, 0, 0, 0);     // the wave's tile origin
+  const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(
+      (char*)p.D + ((int64_t)(m0 + w0.row) * p.ldd + (n0 + w0.k)) * ES, (short)0, 0x7fffffff,
+      0x00020000);
+  const int voff = (cl.row * p.ldd + V * cl.k) * ES;
+  for (int band = 0; band < Cfg::WAVES_M; ++band) {
+    __syncthreads();   // the stages, or the previous band's C, are no longer read
+    if (wm == band) {
+#pragma unroll
+      for (int k = 0; k < X::kRuns / Cfg::WAVES_N; ++k) {
+        const int run = wn + Cfg::WAVES_N * k;
+        const int row = run * X::RPI + lane / (BN / 4), col = 4 * (lane % (BN / 4));
+        const float* src = C + (int64_t)(m0 + band * X::CR + row) * p.ldc + n0 + col;
+        __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr_t)((char*)cs + run * 1024),
+                                         16, 0, 0);
+      }
+      wait_vm_lds<0>();
+    }
+    __syncthreads();
+    if (wm == band) {
+#pragma unroll
+      for (int i = 0; i < RM; ++i)
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+          const int row = i * AM + atom_c_coord_of<Cfg::kOp>(lane, v).row;
+#pragma unroll
+          for (int g = 0; g < NG; ++g) {
+            typedef float fv __attribute__((ext_vector_type(V)));
+            const int col = frag_c_coord<Cfg>(w, lane, i, g * V, v).k;   // start of the run
+            const fv c = *(const fv*)&cs[row * BN + col];
+            float x[V];
+#pragma unroll
+            for (int jl = 0; jl < V; ++jl) {
+              x[jl] = acc[i][g * V + jl][v];
+              x[jl] += c[jl];
+            }
+            buffer_store_d<DK, V>(
+                x, rd, voff,
+                (i * AM + atom_c_coord_of<Cfg::kOp>(0, v).row) * p.ldd * ES + g * AN * V * ES);
+          }
+        }
     }
   }
 }
@@ -804,16 +893,6 @@ constexpr int dump_words() {
   return nbuf * (Cfg::RM + Cfg::RN) * 4 + Cfg::RM * Cfg::RN * Cfg::kNV;
 }
 
-// Wait until at most VM vector-memory operations of this wave are in flight
-// and all its LDS operations are done (s_waitcnt vmcnt(VM) lgkmcnt(0); the
-// export counter is not waited on).  Vector-memory loads complete in issue
-// order, so this leaves exactly the VM most recent ones outstanding.
-template <int VM>
-__device__ __forceinline__ void wait_vm_lds() {
-  static_assert(VM >= 0 && VM < 64, "vmcnt has 6 bits");
-  __builtin_amdgcn_s_waitcnt((VM & 15) | (((VM >> 4) & 3) << 14) | (7 << 4));
-}
-
 // ---------------------------------------------------------------------------
 // LDS-staged pipelined kernel
 // ---------------------------------------------------------------------------
@@ -1146,9 +1225,12 @@ __global__ void __launch_bounds__(Cfg::kThreads, 1) gemm_tiled(const GemmParams 
     else
       epilogue_any<Cfg, CK, DK>(p, w, lane, m0, n0, acc, own);
   } else {
-    if (register_epilogue_ok<Cfg, CK, DK>(p, m0, n0))
-      epilogue_regs<Cfg, CK, DK>(p, w, lane, m0, n0, acc);
-    else
+    if (register_epilogue_ok<Cfg, CK, DK>(p, m0, n0)) {
+      if constexpr (CK == 2 && CViaLds<Cfg>::ok)
+        epilogue_c_lds<Cfg, DK>(p, smem, w, lane, m0, n0, acc);
+      else
+        epilogue_regs<Cfg, CK, DK>(p, w, lane, m0, n0, acc);
+    } else
       epilogue_lds<Cfg, CK, DK>(p, (float*)smem, w, lane, m0, n0, acc);
   }
 }
