@@ -209,9 +209,10 @@ def cpu_baseline_chain(w, x, target_s: float):
 
 
 def measure_and_report(step, stream, args, flops, metric, config, traffic, source_hash,
-                       cpu_leg):
+                       cpu_leg, extra=None):
     """Time the step (time_steps), read the clocks, print the one JSON line.
-    `cpu_leg()` times the oracle unless --no-cpu-baseline."""
+    `cpu_leg()` times the oracle unless --no-cpu-baseline; `extra()`, if
+    given, returns more keys for the line (measured after the timed steps)."""
     import numpy as np
     import torch
     ms_per_step, kern_ms, per, cold = time_steps(step, stream, args)
@@ -259,6 +260,8 @@ def measure_and_report(step, stream, args, flops, metric, config, traffic, sourc
                         "how": f"rocm-smi during {args.clock_seconds:g} s of back-to-back steps"}
     if args.copy_mib:
         out["config"]["copy_mib_per_step"] = args.copy_mib
+    if extra is not None:
+        out.update(extra())
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_leg()
@@ -431,10 +434,69 @@ def main_chain(args) -> int:
               "intermediate": "S rounded once to f16",
               "kernel": f"gemm_chain 256x{tile_n} tile, N1 chunks of {32 if w.K >= 256 else 64}, "
                         f"{staging} staging"}
+    def phases():
+        """Cycles per iteration of the N1 loop by phase, from the timed
+        instance of the kernel (mfl_probe_chain_phases): lane 0 of every wave
+        of workgroups 0..7 reads the shader clock at the start of each
+        iteration, before the conversion of the next chunk's S, before the
+        barrier and after it."""
+        stamps = torch.zeros(int(np.prod(mfl.CHAIN_STAMP_SHAPE)), dtype=torch.int32, device=dev)
+
+        def run():
+            r = mfl.probe_chain_phases_raw(*args_c, stamps.data_ptr(), sptr)
+            if r != 0:
+                raise RuntimeError(mfl.strerror(r))
+        for _ in range(args.warmup):
+            run()
+        torch.cuda.synchronize()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for _ in range(args.steps):
+            run()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        timed_ms = ev0.elapsed_time(ev1) / args.steps
+        t = stamps.view(*mfl.CHAIN_STAMP_SHAPE).cpu().numpy().astype(np.int64) & 0xFFFFFFFF
+        nwg = min(mfl.CHAIN_STAMP_SHAPE[0],
+                  w.batch * (-(-w.M // 256)) * (-(-w.N2 // 128)))
+        t = t[:nwg]
+        nch = (w.N1 + 63) // 64
+        cs = np.arange(2, min(nch - 1, 64) - 2)      # steady iterations with a barrier
+        d = lambda a, b: (b - a) % (1 << 32)
+        s0, s1, s2, s3 = (t[:, :, 4 * cs + k] for k in range(4))
+        nxt = t[:, :, 4 * (cs + 1)]
+        names = {"K chunks 0..2H-2 of the second product with the next chunk's first product "
+                 "and the fetch of slot c+2": d(s0, s1),
+                 "wait for this wave's fetch of slot c+1": d(s1, s2),
+                 "workgroup barrier": d(s2, s3),
+                 "last K chunk with the first reads of slot c+1": d(s3, nxt)}
+        total = d(s0, nxt)
+        whole = d(t[:, :, 256], t[:, :, 258])
+        prologue = d(t[:, :, 256], t[:, :, 0])
+        loop = d(t[:, :, 0], t[:, :, 257])
+        epilogue = d(t[:, :, 257], t[:, :, 258])
+        return {"phases": {
+            "how": "shader-clock stamps (s_memtime) of the timed kernel instance, lane 0 of "
+                   f"each wave of workgroups 0..{nwg - 1}, iterations {cs[0]}..{cs[-1]}",
+            "timed_kernel_ms": round(timed_ms, 5),
+            "cycles_per_iteration": round(float(total.mean()), 1),
+            "iterations": nch,
+            "wave_cycles": {"start to end": round(float(whole.mean()), 1),
+                            "prologue (A fragments, first slots, first product of chunk 0)":
+                                round(float(prologue.mean()), 1),
+                            "N1 loop": round(float(loop.mean()), 1),
+                            "epilogue (D stores issued)": round(float(epilogue.mean()), 1)},
+            "mfma_cycles_per_iteration": 64 * 32,
+            "phase_cycles_mean": {k: round(float(v.mean()), 1) for k, v in names.items()},
+            "phase_cycles_by_wave": {k: [round(float(x), 1) for x in v.mean(axis=(0, 2))]
+                                     for k, v in names.items()}}}
+
     return measure_and_report(step, stream, args, float(w.flops), METRIC_CHAIN, config,
                               load_traffic(w.name, "chain", CHAIN_SOURCES),
                               kernel_source_hash(CHAIN_SOURCES),
-                              lambda: cpu_baseline_chain(w, x, args.cpu_seconds))
+                              lambda: cpu_baseline_chain(w, x, args.cpu_seconds),
+                              phases if args.phases else None)
 
 
 def main() -> int:
@@ -463,6 +525,9 @@ def main() -> int:
                     help="operand data of the MFMA issue-rate workloads")
     ap.add_argument("--threads", type=int, default=512,
                     help="threads per workgroup of the LDS read-rate workload")
+    ap.add_argument("--phases", action="store_true",
+                    help="back-to-back GEMM: also report cycles per loop phase from the timed "
+                         "kernel instance")
     ap.add_argument("--iters", type=int, default=0,
                     help="loop iterations of the microbenchmark kernels (0 = default)")
     args = ap.parse_args()

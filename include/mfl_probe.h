@@ -121,6 +121,28 @@ int mfl_bench_lds_read(int32_t threads, int32_t iters, int32_t nwg, uint32_t* si
  * pointer, -5 when the runtime does not report it. */
 int mfl_wall_clock_khz(int32_t* khz);
 
+/* Phase timing of the back-to-back GEMM of mfl_chain.h (the Tensor Core
+ * page "CuTe Layout 到 Tensor Core", §17: the accumulator of one MMA read as
+ * the next MMA's operand).  Same arguments, checks, result in D and error
+ * codes as gemm_tn_chain, for the configuration K = 128, N2 > 64, fp16 D,
+ * direct-to-LDS staging (else -4); the kernel is a separate instance in which
+ * lane 0 of every wave also records the low 32 bits of the shader-clock
+ * counter (s_memtime) at fixed points.  stamps: device memory of 8 x 4 x 260
+ * uint32, written for workgroups 0..7 (fewer if the grid is smaller), wave w
+ * of workgroup g at [(4 g + w) * 260 + q]: for iteration c < 64 of the N1
+ * loop, q = 4c at its start, 4c + 1 before the wave waits for its fetch of
+ * the next slot, 4c + 2 before the workgroup barrier, 4c + 3 after it
+ * (the last iteration records only 4c); q = 256 kernel start, 257 after the
+ * loop, 258 after the epilogue.  Stamps of one wave come from one counter.
+ * The kernel keeps the readings in registers until its end (no LDS traffic,
+ * no added waits): they cost a few scalar and vector instructions per
+ * iteration.  NULL stamps: -3. */
+int mfl_probe_chain_phases(int64_t batch, int64_t M, int64_t N1, int64_t N2, int64_t K,
+                           const void* A, int64_t lda, int64_t stride_a, const void* B,
+                           int64_t ldb, int64_t stride_b, const void* W, int64_t ldw,
+                           int64_t stride_w, void* D, int64_t ldd, int64_t stride_d,
+                           int32_t d_dtype, uint32_t* stamps, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -133,6 +133,8 @@ def _load() -> ctypes.CDLL:
     lib.mfl_probe_fragments.argtypes = [i32, i32, i32, i32, i32, i32, vp, i32, vp, i32, vp, i64,
                                         P(i32), P(i32), vp]
     lib.mfl_probe_fragments.restype = ctypes.c_int
+    lib.mfl_probe_chain_phases.argtypes = [i64] * 5 + [vp, i64, i64] * 4 + [i32, vp, vp]
+    lib.mfl_probe_chain_phases.restype = ctypes.c_int
     lib.mfl_bench_mfma.argtypes = [i32, vp, i32, i32, i32, vp, vp, vp]
     lib.mfl_bench_mfma.restype = ctypes.c_int
     lib.mfl_bench_lds_read.argtypes = [i32, i32, i32, vp, vp, vp]
@@ -254,6 +256,18 @@ def gemm_chain_raw(batch, M, N1, N2, K, A, lda, sa, B, ldb, sb, W, ldw, sw, D, l
     """Direct call of gemm_tn_chain with integer pointers; returns the code."""
     return _lib.gemm_tn_chain(batch, M, N1, N2, K, A, lda, sa, B, ldb, sb, W, ldw, sw, D, ldd,
                               sd, d_dtype, stream)
+
+
+# phase stamps of the timed chain instance: workgroups x waves x slots
+CHAIN_STAMP_SHAPE = (8, 4, 260)
+
+
+def probe_chain_phases_raw(batch, M, N1, N2, K, A, lda, sa, B, ldb, sb, W, ldw, sw, D, ldd, sd,
+                           d_dtype: int, stamps: int, stream: int) -> int:
+    """mfl_probe_chain_phases with integer pointers; `stamps` points to
+    8 * 4 * 260 uint32 of device memory (CHAIN_STAMP_SHAPE)."""
+    return _lib.mfl_probe_chain_phases(batch, M, N1, N2, K, A, lda, sa, B, ldb, sb, W, ldw, sw,
+                                       D, ldd, sd, d_dtype, stamps, stream)
 
 
 def gemm_chain_validate(batch, M, N1, N2, K, A, lda, sa, B, ldb, sb, W, ldw, sw, D, ldd, sd,

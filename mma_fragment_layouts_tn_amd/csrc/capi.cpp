@@ -459,6 +459,54 @@ bool chain_dma(int64_t K, int64_t N1, const void* B, int64_t ldb, int64_t sb, co
          sb % 8 == 0 && sw % 8 == 0;
 }
 
+// launch of the back-to-back GEMM; `timed` takes the phase-stamp instance
+// (K = 128, fp16 D, direct-to-LDS staging, 128-column N2 tiles only)
+int chain_launch(bool timed, int64_t batch, int64_t M, int64_t N1, int64_t N2, int64_t K,
+                 const void* A, int64_t lda, int64_t stride_a, const void* B, int64_t ldb,
+                 int64_t stride_b, const void* W, int64_t ldw, int64_t stride_w, void* D,
+                 int64_t ldd, int64_t stride_d, int32_t d_dtype, uint32_t* stamps, void* stream) {
+  const int rc = chain_check(batch, M, N1, N2, K, A, lda, stride_a, B, ldb, stride_b, W, ldw,
+                             stride_w, D, ldd, stride_d, d_dtype);
+  if (rc != MFL_OK) return rc;
+  if (batch == 0 || M == 0 || N2 == 0) return MFL_OK;
+  const int bn = mfl::chain::tile_n(N2);
+  const bool dma = chain_dma(K, N1, B, ldb, stride_b, W, ldw, stride_w);
+  const void* fn = timed ? (K == 128 && d_dtype == MFL_F16 && dma && bn == 128
+                                ? mfl::chain_timed_symbol()
+                                : nullptr)
+                         : mfl::chain_symbol((int)K, d_dtype, dma, bn);
+  if (!fn) return MFL_E_UNSUPPORTED;
+  mfl::ChainParams p{};
+  p.batch = (int)batch;
+  p.M = (int)M;
+  p.N1 = (int)N1;
+  p.N2 = (int)N2;
+  p.lda = lda;
+  p.ldb = ldb;
+  p.ldw = ldw;
+  p.ldd = ldd;
+  p.sa = stride_a;
+  p.sb = stride_b;
+  p.sw = stride_w;
+  p.sd = stride_d;
+  p.tiles_m = (int)(batch * ((M + mfl::chain::BM - 1) / mfl::chain::BM));
+  p.tiles_n = (int)((N2 + bn - 1) / bn);
+  p.group_m = 8;
+  p.d_vec = ((uintptr_t)D % (uintptr_t)(4 * elem_size(d_dtype)) == 0) && (ldd % 4 == 0) &&
+            (stride_d % 4 == 0);
+  p.A = A;
+  p.B = B;
+  p.W = W;
+  p.D = D;
+  p.stamps = stamps;
+  void* args[] = {(void*)&p};
+  const int64_t nb = (int64_t)p.tiles_m * p.tiles_n;
+  const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)nb), dim3(mfl::chain::THREADS), args, 0,
+                                       (hipStream_t)stream);
+  return e == hipSuccess ? MFL_OK : MFL_E_LAUNCH;
+}
+
+
 extern "C" {
 
 int gemm_tn_validate(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
@@ -967,41 +1015,18 @@ int gemm_tn_chain(int64_t batch, int64_t M, int64_t N1, int64_t N2, int64_t K, c
                   int64_t lda, int64_t stride_a, const void* B, int64_t ldb, int64_t stride_b,
                   const void* W, int64_t ldw, int64_t stride_w, void* D, int64_t ldd,
                   int64_t stride_d, int32_t d_dtype, void* stream) {
-  const int rc = chain_check(batch, M, N1, N2, K, A, lda, stride_a, B, ldb, stride_b, W, ldw,
-                             stride_w, D, ldd, stride_d, d_dtype);
-  if (rc != MFL_OK) return rc;
-  if (batch == 0 || M == 0 || N2 == 0) return MFL_OK;
-  const int bn = mfl::chain::tile_n(N2);
-  const void* fn =
-      mfl::chain_symbol((int)K, d_dtype, chain_dma(K, N1, B, ldb, stride_b, W, ldw, stride_w), bn);
-  if (!fn) return MFL_E_UNSUPPORTED;
-  mfl::ChainParams p{};
-  p.batch = (int)batch;
-  p.M = (int)M;
-  p.N1 = (int)N1;
-  p.N2 = (int)N2;
-  p.lda = lda;
-  p.ldb = ldb;
-  p.ldw = ldw;
-  p.ldd = ldd;
-  p.sa = stride_a;
-  p.sb = stride_b;
-  p.sw = stride_w;
-  p.sd = stride_d;
-  p.tiles_m = (int)(batch * ((M + mfl::chain::BM - 1) / mfl::chain::BM));
-  p.tiles_n = (int)((N2 + bn - 1) / bn);
-  p.group_m = 8;
-  p.d_vec = ((uintptr_t)D % (uintptr_t)(4 * elem_size(d_dtype)) == 0) && (ldd % 4 == 0) &&
-            (stride_d % 4 == 0);
-  p.A = A;
-  p.B = B;
-  p.W = W;
-  p.D = D;
-  void* args[] = {(void*)&p};
-  const int64_t nb = (int64_t)p.tiles_m * p.tiles_n;
-  const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)nb), dim3(mfl::chain::THREADS), args, 0,
-                                       (hipStream_t)stream);
-  return e == hipSuccess ? MFL_OK : MFL_E_LAUNCH;
+  return chain_launch(false, batch, M, N1, N2, K, A, lda, stride_a, B, ldb, stride_b, W, ldw,
+                      stride_w, D, ldd, stride_d, d_dtype, nullptr, stream);
+}
+
+int mfl_probe_chain_phases(int64_t batch, int64_t M, int64_t N1, int64_t N2, int64_t K,
+                           const void* A, int64_t lda, int64_t stride_a, const void* B,
+                           int64_t ldb, int64_t stride_b, const void* W, int64_t ldw,
+                           int64_t stride_w, void* D, int64_t ldd, int64_t stride_d,
+                           int32_t d_dtype, uint32_t* stamps, void* stream) {
+  if (!stamps) return MFL_E_NULL_POINTER;
+  return chain_launch(true, batch, M, N1, N2, K, A, lda, stride_a, B, ldb, stride_b, W, ldw,
+                      stride_w, D, ldd, stride_d, d_dtype, stamps, stream);
 }
 
 }  // extern "C"

@@ -37,6 +37,7 @@ struct ChainParams {
   const void* B;
   const void* W;
   void* D;
+  unsigned* stamps;                 // phase clock stamps (timed probe instance only)
 };
 
 // ---------------------------------------------------------------- the pi map
@@ -193,7 +194,15 @@ __device__ __forceinline__ void wait_vm() {
 }
 }  // namespace chain
 
-template <int KD, int DK, bool DMA, int BN>
+// Phase stamps of the timed probe instance: per wave, kStampIters x 4
+// shader-clock readings (iteration c: 4c + 0 at its start, + 1 before the
+// wait for the next slot's fetch, + 2 before the barrier, + 3 after it), then
+// 3 more (kernel start, after the loop, after the epilogue).
+namespace chain {
+constexpr int kStampIters = 64, kStampsPerWave = 4 * kStampIters + 4, kStampBlocks = 8;
+}
+
+template <int KD, int DK, bool DMA, int BN, bool TIMED = false>
 __global__ void __launch_bounds__(chain::THREADS, 1) gemm_chain(const ChainParams p) {
   using namespace chain;
   static_assert(KD == 32 || KD == 64 || KD == 128 || KD == 256, "K is 32, 64, 128 or 256");
@@ -218,6 +227,28 @@ __global__ void __launch_bounds__(chain::THREADS, 1) gemm_chain(const ChainParam
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // timed instance: the shader clock at fixed points.  A reading stays in a
+  // scalar register until a point where the wave waits for its LDS reads
+  // anyway (the barrier, the end of the iteration), and goes to lane c of
+  // tv[k] for iteration c: the readings add no LDS traffic and no waits.
+  auto now = [&]() -> unsigned {
+    unsigned t = 0;
+    if constexpr (TIMED) {
+      __builtin_amdgcn_sched_barrier(0);
+      t = (unsigned)__builtin_amdgcn_s_memtime();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return t;
+  };
+  unsigned tv[4] = {0, 0, 0, 0};
+  auto keep = [&](int k, int c, unsigned t) {
+    if constexpr (TIMED) {
+      __builtin_amdgcn_sched_barrier(0);
+      tv[k] = lane == c ? t : tv[k];
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  const unsigned t_start = now();
   const TileIndex ti = tile_of_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m);
   const int mt_per_b = (p.M + BM - 1) / BM;
   const int b = ti.tm / mt_per_b;
@@ -288,38 +319,39 @@ __global__ void __launch_bounds__(chain::THREADS, 1) gemm_chain(const ChainParam
     }
   }
   auto stage_of = [](int slot) { return (slot + NST) % NST; };
-  // issue the loads of slot s (DMA: straight into its stage)
-  auto issue = [&](int s) {
+  // DMA instruction j of slot s: B rows for j < NB, W rows after
+  auto issue_one = [&](int s, int j) {
     _Float16* st = smem + stage_of(s) * STAGE;
     const int cb = s + 1, cw = s;
-    if (cb < nch) {
-      if constexpr (DMA) {
-        const _Float16* base = B + (int64_t)(CW * cb) * p.ldb;
+    if (j < NB) {
+      if (cb < nch) {
+        const void* g = B + (int64_t)(CW * cb) * p.ldb + boff[j];
+        const lds_t l = (lds_t)(st + (w * NB + j) * 32 * SZB);
+        if constexpr (SZB == 16)
+          __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+        else
+          __builtin_amdgcn_global_load_lds(g, l, 4, 0, 0);
+      }
+    } else if (cw >= 0 && cw < nch) {
+      __builtin_amdgcn_global_load_lds((const void*)(Wm + CW * cw + woff[j - NB]),
+                                       (lds_t)(st + BSTAGE + (w * NW + j - NB) * 512), 16, 0, 0);
+    }
+  };
+  // issue the loads of slot s (DMA: straight into its stage)
+  auto issue = [&](int s) {
+    if constexpr (DMA) {
 #pragma unroll
-        for (int i = 0; i < NB; ++i) {
-          const void* g = base + boff[i];
-          const lds_t l = (lds_t)(st + (w * NB + i) * 32 * SZB);
-          if constexpr (SZB == 16)
-            __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
-          else
-            __builtin_amdgcn_global_load_lds(g, l, 4, 0, 0);
-        }
-      } else {
+      for (int j = 0; j < NB + NW; ++j) issue_one(s, j);
+    } else {
+      const int cb = s + 1, cw = s;
+      if (cb < nch) {
 #pragma unroll
         for (int t = 0; t < BPT; ++t) {
           const int n1 = min(CW * cb + brow[t], p.N1 - 1);   // zeroed when written
           rb[t] = load16(B + (int64_t)n1 * p.ldb + boff[t]);
         }
       }
-    }
-    if (cw >= 0 && cw < nch) {
-      if constexpr (DMA) {
-        const _Float16* base = Wm + CW * cw;
-#pragma unroll
-        for (int i = 0; i < NW; ++i)
-          __builtin_amdgcn_global_load_lds((const void*)(base + woff[i]),
-                                           (lds_t)(st + BSTAGE + (w * NW + i) * 512), 16, 0, 0);
-      } else {
+      if (cw >= 0 && cw < nch) {
 #pragma unroll
         for (int t = 0; t < WPT; ++t)
           if (CW * cw + wn1[t] + 8 <= p.N1) rw[t] = load16(Wm + CW * cw + woff[t]);
@@ -382,6 +414,13 @@ __global__ void __launch_bounds__(chain::THREADS, 1) gemm_chain(const ChainParam
 #pragma unroll
         for (int v = 0; v < 8; ++v) out[i][kc][v] = (_Float16)st[i][kc / 2][8 * (kc % 2) + v];   // RNE
   };
+  // one piece of it, out[i][kc]; the empty asm keeps the piece where it is
+  // made (beside the MFMAs it runs under) instead of sinking it to its use
+  auto convert_one = [&](const floatx16 (&st)[RM][H], Frag& out, int i, int kc) {
+#pragma unroll
+    for (int v = 0; v < 8; ++v) out[i][kc][v] = (_Float16)st[i][kc / 2][8 * (kc % 2) + v];
+    asm volatile("" : "+v"(out[i][kc]));
+  };
   auto zero_st = [&](floatx16 (&st)[RM][H]) {
 #pragma unroll
     for (int i = 0; i < RM; ++i)
@@ -412,25 +451,41 @@ __global__ void __launch_bounds__(chain::THREADS, 1) gemm_chain(const ChainParam
 
   // Iteration c on slot c: the second product of chunk c over its 2H K
   // chunks (P in registers) with the FS steps of the first product of chunk
-  // c+1 spread over all but the last K chunk.  P of chunk c+1 is converted
-  // before the barrier that closes the slot; after it the last K chunk runs
-  // on fragments already in registers while the first fragments of slot c+1
-  // are read and slot c+2 is fetched into the stage slot c-1 used (every wave
-  // is past it).  So the matrix core has work on both sides of the barrier.
-  constexpr int FS = KSUB * H, NPRE = (2 * H - 1) * RM * RN;
-  Frag pf, pn;
-  half8 wf0[RN], bf0, bf1;   // carried: W of the next chunk, K chunk 0; its B, steps 0 and 1
+  // c+1 spread over all but the last K chunk.  The barrier that closes the
+  // slot comes before the last K chunk, which runs on fragments already in
+  // registers while the first fragments of slot c+1 are read.  Slot c+2 goes
+  // to the stage of slot c-1, which every wave left at the previous barrier:
+  // direct-to-LDS, one DMA instruction at a time spread over the K chunks
+  // before the barrier (it has until the next iteration's barrier to land);
+  // through registers, loaded after the barrier and written to LDS in the
+  // next iteration.  P of chunk c+1 is converted piece by piece beside the
+  // MFMAs: block h of S in K chunk 2H-2 (all but the last block, whose
+  // first-product steps are done by then) or 2H-1 (the last block).
+  constexpr int FS = KSUB * H, NPRE = (2 * H - 1) * RM * RN, NI = NB + NW;
+  auto convert_at = [&](const floatx16 (&st)[RM][H], Frag& out, int kc, int g) {
+#pragma unroll
+    for (int h = 0; h < H; ++h)
+      if ((h == H - 1 ? 2 * H - 1 : 2 * H - 2) == kc)
+#pragma unroll
+        for (int q = 0; q < 2 * RM; ++q)
+          if (q * RM * RN / (2 * RM) == g) convert_one(st, out, q / 2, 2 * h + q % 2);
+  };
   // Fragments are read ahead of their use, after the MFMAs of the slot they
   // follow: W of K chunk kc+1 after the first MFMA of K chunk kc, B of step
-  // s1+2 after the MFMAs of step s1.  A wait for one is then a wait for reads
+  // s1+RA after the MFMAs of step s1.  A wait for one is then a wait for reads
   // issued several MFMAs earlier, not for the read just issued.
+  constexpr int RA = FS < 2 ? FS : 2;
+  Frag pf, pn;
+  half8 wf0[RN], bc[RA];   // carried: W of the next chunk, K chunk 0; its B, steps 0..RA-1
   auto iteration = [&](int c, auto more) {
     constexpr bool MORE = decltype(more)::value;
+    const unsigned t0 = now();
+    unsigned t1 = 0, t2 = 0, t3 = 0;
     const _Float16* sb = smem + stage_of(c) * STAGE;
     const _Float16* sw = sb + BSTAGE;
     floatx16 st[RM][H];
     zero_st(st);
-    half8 wf[RN], wn[RN], bq[2];
+    half8 wf[RN], wn[RN], bq[RA];
 #pragma unroll
     for (int j = 0; j < RN; ++j) wf[j] = wf0[j];
 #pragma unroll
@@ -441,10 +496,18 @@ __global__ void __launch_bounds__(chain::THREADS, 1) gemm_chain(const ChainParam
       }
       if (kc == 2 * H - 1) {
         if constexpr (MORE) {
-          convert(st, pn);
+          t1 = now();
           stash(c + 1);          // registers: slot c+1, loaded one iteration ago
-          wait_vm<0>();          // direct-to-LDS: slot c+1 has landed
+          if constexpr (DMA)
+            wait_before(c + 2);  // slot c+1 has landed; slot c+2 may be in flight
+          else
+            wait_vm<0>();
+          t2 = now();
           barrier();             // ... in every wave; slot c-1 is free
+          t3 = now();
+          keep(0, c, t0);
+          keep(1, c, t1);
+          keep(2, c, t2);
         }
       }
 #pragma unroll
@@ -454,21 +517,31 @@ __global__ void __launch_bounds__(chain::THREADS, 1) gemm_chain(const ChainParam
 #pragma unroll
             for (int s1 = 0; s1 < FS; ++s1)
               if (s1 * NPRE / FS == kc * RM * RN + g) {
-                first_step(st, s1 == 0 ? bf0 : s1 == 1 ? bf1 : bq[s1 % 2], s1);
-                if (s1 + 2 < FS) bq[s1 % 2] = read_b(sb, s1 + 2);
+                first_step(st, s1 < RA ? bc[s1] : bq[s1 % RA], s1);
+                if (s1 + RA < FS) bq[s1 % RA] = read_b(sb, s1 + RA);
               }
-          } else if (g == 0) {
-            // after the barrier: the next slot's first fragments, the fetch
-            // of slot c+2 (B of chunk c+2 may not exist: its value is then
-            // stale and unused, the last iteration has no first product)
-            const _Float16* nb = smem + stage_of(c + 1) * STAGE;
-            read_w(nb + BSTAGE, 0, wf0);
-            bf0 = read_b(nb, 0);
-            bf1 = read_b(nb, 1);
-            issue(c + 2);
           }
         }
         second(pf, kc, g, wf);
+        if constexpr (MORE) {
+          if (kc == 2 * H - 1) {
+            if (g == 0) {
+              // after the barrier: the next slot's first fragments (B of
+              // chunk c+2 may not exist: its value is then stale and unused,
+              // the last iteration has no first product)
+              const _Float16* nb = smem + stage_of(c + 1) * STAGE;
+              read_w(nb + BSTAGE, 0, wf0);
+#pragma unroll
+              for (int r = 0; r < RA; ++r) bc[r] = read_b(nb, r);
+              if constexpr (!DMA) issue(c + 2);
+            }
+          } else if constexpr (DMA) {
+#pragma unroll
+            for (int j = 0; j < NI; ++j)
+              if (j * NPRE / NI == kc * RM * RN + g) issue_one(c + 2, j);
+          }
+          convert_at(st, pn, kc, g);
+        }
         if (g == 0 && kc + 1 < 2 * H) read_w(sw, kc + 1, wn);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -478,6 +551,9 @@ __global__ void __launch_bounds__(chain::THREADS, 1) gemm_chain(const ChainParam
       for (int i = 0; i < RM; ++i)
 #pragma unroll
         for (int kc = 0; kc < 2 * H; ++kc) pf[i][kc] = pn[i][kc];
+      keep(3, c, t3);
+    } else {
+      keep(0, c, t0);
     }
   };
 
@@ -497,15 +573,18 @@ __global__ void __launch_bounds__(chain::THREADS, 1) gemm_chain(const ChainParam
       const _Float16* sb = smem + stage_of(-1) * STAGE;
 #pragma unroll
       for (int s1 = 0; s1 < FS; ++s1) first_step(st, read_b(sb, s1), s1);
+      // direct-to-LDS: iteration 0 fetches slot 2 into this stage
+      if constexpr (DMA) barrier();
       convert(st, pf);
       const _Float16* s0 = smem + stage_of(0) * STAGE;
       read_w(s0 + BSTAGE, 0, wf0);
-      bf0 = read_b(s0, 0);           // B of chunk 1, used only if it exists
-      bf1 = read_b(s0, 1);
+#pragma unroll
+      for (int r = 0; r < RA; ++r) bc[r] = read_b(s0, r);   // B of chunk 1, if it exists
     }
     for (int c = 0; c + 1 < nch; ++c) iteration(c, BoolC<true>{});
     iteration(nch - 1, BoolC<false>{});
   }
+  const unsigned t_loop = now();
 
   // epilogue: acc[i][j][v] of lane l is D(m0 + 64 w + 32 i + atom_c(l, v).row,
   // n0 + 4 (l % 32) + j): one 4-element vector per (i, v)
@@ -546,10 +625,26 @@ __global__ void __launch_bounds__(chain::THREADS, 1) gemm_chain(const ChainParam
         }
       }
     }
+  if constexpr (TIMED) {
+    const unsigned t_end = now();
+    if (blockIdx.x < kStampBlocks) {
+      unsigned* out = p.stamps + (blockIdx.x * WAVES + w) * kStampsPerWave;
+      if (lane < kStampIters)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) out[4 * lane + k] = tv[k];
+      if (lane == 0) {
+        out[4 * kStampIters] = t_start;
+        out[4 * kStampIters + 1] = t_loop;
+        out[4 * kStampIters + 2] = t_end;
+      }
+    }
+  }
 }
 
 // host: kernel symbol for K, the D type (1 fp16, 2 fp32), the staging
 // (direct-to-LDS or through registers) and the N2 tile width; nullptr if none
 const void* chain_symbol(int kd, int dk, bool dma, int bn);
+// the timed probe instance (K = 128, fp16 D, direct-to-LDS, 128-column tiles)
+const void* chain_timed_symbol();
 
 }  // namespace mfl

@@ -29,4 +29,5 @@ const void* chain_symbol(int kd, int dk, bool dma, int bn) {
     default: return nullptr;
   }
 }
+const void* chain_timed_symbol() { return (const void*)gemm_chain<128, 1, true, 128, true>; }
 }  // namespace mfl

@@ -209,6 +209,24 @@ def test_chain_n2_tile_rule():
     assert [tile(n) for n in (1, 63, 64, 65, 128, 129, 1000)] == [64, 64, 64, 128, 128, 128, 128]
 
 
+def test_chain_phase_probe_arguments():
+    """The timed instance exists only for K = 128, fp16 D, direct-to-LDS
+    staging and 128-column N2 tiles; anything else, or no stamp buffer, is
+    refused before a launch."""
+    def probe(stamps=P, **kw):
+        a = dict(batch=2, M=100, N1=256, N2=128, K=128, A=P, lda=128, sa=100 * 128, B=P,
+                 ldb=128, sb=256 * 128, W=P, ldw=256, sw=128 * 256, D=P, ldd=128, sd=100 * 128,
+                 d=mfl.F16)
+        a.update(kw)
+        return mfl.probe_chain_phases_raw(*a.values(), stamps, 0)
+    assert probe(stamps=0) == mfl.ERR["NULL_POINTER"]
+    assert probe(K=64, lda=64, ldb=64) == mfl.ERR["UNSUPPORTED"]
+    assert probe(d=mfl.F32) == mfl.ERR["UNSUPPORTED"]
+    assert probe(N1=250) == mfl.ERR["UNSUPPORTED"]                 # register staging
+    assert probe(N2=64, ldd=64, sd=100 * 64, sw=64 * 256) == mfl.ERR["UNSUPPORTED"]
+    assert probe(M=-1) == mfl.ERR["NEGATIVE_DIM"]
+    assert mfl.CHAIN_STAMP_SHAPE == (8, 4, 4 * 64 + 4)
+
 def test_chain_perm_is_derived_from_the_atoms():
     """The map behind the kernel's B row order: position p = 16 kc + 8 h + v
     of the second product's K is accumulator row 8 (2 kc + v / 4) + 4 h +

@@ -165,12 +165,13 @@ def test_float_within_derived_bound(shape, d, dist):
         f"max |D| {np.abs(ref).max():.3g}")
 
 
+@pytest.mark.parametrize("name", sorted(W.CHAIN_WORKLOADS))
 @pytest.mark.parametrize("integer", [False, True])
-def test_named_workload(integer):
-    """The attention-shaped workload at full size, in the launch the bench
+def test_named_workload(integer, name):
+    """The attention-shaped workloads at full size, in the launch the bench
     times: every element of every batch against the oracle, batch by batch
     (integer inputs bit-exact, random ones within the derived bound)."""
-    w = W.CHAIN_WORKLOADS["chain_b32_2048x2048_k128_n128"]
+    w = W.CHAIN_WORKLOADS[name]
     if integer:
         w = w.twin()
     x = W.make_chain_inputs(w)
@@ -222,6 +223,41 @@ def test_float_stagings_bit_identical(K):
     ref, S, P = oracle_chain(x, with_s=True)
     assert (np.abs(D_dma - ref) <= _float_bound(x, S, P, "f32", ref)).all()
 
+
+def test_phase_probe_matches_and_stamps_are_ordered():
+    """The timed instance behind the phase breakdown computes what the
+    product computes: D bit-identical to gemm_tn_chain on the same inputs,
+    and each wave's shader-clock stamps rise through every iteration's four
+    phases, the loop and the epilogue."""
+    w = W.ChainWorkload("phases", 4, 512, 1024, 128, 128, d="f16", dist="unif", seed=31)
+    x = W.make_chain_inputs(w)
+    D_ref, checks = run_chain(x, "f16")
+    assert all(checks.values()), checks
+    dev = torch.device("cuda", 0)
+    A, B, Wt = (torch.from_numpy(np.ascontiguousarray(t)).to(dev) for t in (x.A, x.B, x.W))
+    D = torch.full((w.batch, w.M, w.N2), float("nan"), dtype=torch.float16, device=dev)
+    stamps = torch.zeros(int(np.prod(mfl.CHAIN_STAMP_SHAPE)), dtype=torch.int32, device=dev)
+    say(f"[gpu] chain phase probe batch={w.batch} M={w.M} N1={w.N1} N2={w.N2} K={w.K}")
+    rc = mfl.probe_chain_phases_raw(w.batch, w.M, w.N1, w.N2, w.K,
+                                    A.data_ptr(), w.K, w.M * w.K, B.data_ptr(), w.K, w.N1 * w.K,
+                                    Wt.data_ptr(), w.N1, w.N2 * w.N1, D.data_ptr(), w.N2,
+                                    w.M * w.N2, mfl.F16, stamps.data_ptr(),
+                                    torch.cuda.current_stream().cuda_stream)
+    assert rc == 0, mfl.strerror(rc)
+    torch.cuda.synchronize()
+    assert np.array_equal(D.cpu().numpy().astype(np.float64), D_ref)
+    t = stamps.view(*mfl.CHAIN_STAMP_SHAPE).cpu().numpy().astype(np.int64) & 0xFFFFFFFF
+    nch = w.N1 // 64
+    for blk in range(mfl.CHAIN_STAMP_SHAPE[0]):
+        for wave in range(mfl.CHAIN_STAMP_SHAPE[1]):
+            s = t[blk, wave]
+            seq = [s[256]]
+            for c in range(nch - 1):
+                seq += list(s[4 * c:4 * c + 4])
+            seq += [s[4 * (nch - 1)], s[257], s[258]]
+            steps = np.diff(np.array(seq)) % (1 << 32)
+            assert (steps < (1 << 24)).all(), (blk, wave, steps.max())   # no step backwards
+            assert steps.sum() > 0, (blk, wave)
 
 def test_every_kernel_variant_ran():
     """Collected after the cases above: each K ran through both stagings

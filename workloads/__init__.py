@@ -279,4 +279,8 @@ CHAIN_WORKLOADS = {
         twin_seed=107,
         note="attention-shaped: 32 batch x heads, sequence 2048 for queries and keys, "
              "head dimension 128 for both products, fp16 out"),
+    "chain_b8_2048x2048_k128_n128": ChainWorkload(
+        "chain_b8_2048x2048_k128_n128", 8, 2048, 2048, 128, 128, d="f16", seed=8,
+        twin_seed=108,
+        note="the same shape with 8 batches: 64 workgroups, a quarter of the compute units"),
 }
