@@ -285,7 +285,8 @@ def main_micro(args) -> int:
         operand registers filled from random (or zero) fp16 data, 2^20 FLOP
         (32x32x16) or 2^21 FLOP (16x16x32) per wave per iteration, nothing
         else in the loop;
-      lds_read_b128: every wave issues conflict-free 16-byte LDS reads."""
+      lds_read_b128: every wave issues conflict-free 16-byte LDS reads,
+        --depth of them in flight."""
     import numpy as np
     import torch
 
@@ -319,13 +320,13 @@ def main_micro(args) -> int:
                 raise RuntimeError(mfl.strerror(r))
     else:
         threads = args.threads
-        iters = args.iters or 65536
+        iters = args.iters or 32768
         sink = torch.empty(nwg, dtype=torch.int32, device=dev)
-        nbytes = float(nwg * (threads // 64) * iters * 8 * 1024)
+        nbytes = float(nwg * (threads // 64) * iters * 16 * 1024)
 
         def step():
-            r = mfl.bench_lds_read_raw(threads, iters, nwg, sink.data_ptr(), clocks.data_ptr(),
-                                       sptr)
+            r = mfl.bench_lds_read_raw(threads, iters, nwg, args.depth, sink.data_ptr(),
+                                       clocks.data_ptr(), sptr)
             if r != 0:
                 raise RuntimeError(mfl.strerror(r))
 
@@ -355,6 +356,8 @@ def main_micro(args) -> int:
           f"max {mhz.max():.0f}", file=sys.stderr, flush=True)
     config = {"workload": args.workload, "instruction": instr, "workgroups": nwg,
               "threads": threads, "iterations": iters}
+    if kind == "lds":
+        config["reads_in_flight_per_wave"] = args.depth
     clock = {"sclk_mhz_in_kernel_median": round(sclk, 1), "sclk_mhz_min": round(float(mhz.min()), 1),
              "sclk_mhz_max": round(float(mhz.max()), 1),
              "how": "s_memtime cycles / s_memrealtime ticks around the loop, per workgroup, "
@@ -525,6 +528,8 @@ def main() -> int:
                     help="operand data of the MFMA issue-rate workloads")
     ap.add_argument("--threads", type=int, default=512,
                     help="threads per workgroup of the LDS read-rate workload")
+    ap.add_argument("--depth", type=int, default=8, choices=[1, 4, 8, 16],
+                    help="LDS reads in flight per wave in the LDS read-rate workload")
     ap.add_argument("--phases", action="store_true",
                     help="back-to-back GEMM: also report cycles per loop phase from the timed "
                          "kernel instance")

@@ -107,14 +107,16 @@ int mfl_probe_gemm_poisoned(int64_t M, int64_t N, int64_t K, const void* A, int6
  *
  * mfl_bench_lds_read: nwg workgroups of `threads` threads (a multiple of 64,
  * at most 1024), each with 96 KB of LDS (one workgroup per compute unit);
- * every wave issues iters x 8 ds_read_b128, each covering 1 KB contiguously
- * (64 lanes x 16 bytes, every bank once per 16-lane pass): 8 KB per wave per
- * iteration.  sink: device, nwg uint32.  Returns 0, -4 for a bad size or NULL
+ * every wave issues iters x 16 ds_read_b128, each covering 1 KB contiguously
+ * (64 lanes x 16 bytes, every bank once per 16-lane pass): 16 KB per wave per
+ * iteration, in groups of `depth` reads (1, 4, 8 or 16) that are all issued
+ * before the first is consumed, so `depth` reads are in flight per wave.
+ * sink: device, nwg uint32.  Returns 0, -4 for a bad size, depth or NULL
  * pointer, -5 on a launch error. */
 int mfl_bench_mfma(int32_t op, const uint16_t* operands, int32_t n_operands, int32_t iters,
                    int32_t nwg, float* sink, uint64_t* clocks, void* stream);
-int mfl_bench_lds_read(int32_t threads, int32_t iters, int32_t nwg, uint32_t* sink,
-                       uint64_t* clocks, void* stream);
+int mfl_bench_lds_read(int32_t threads, int32_t iters, int32_t nwg, int32_t depth,
+                       uint32_t* sink, uint64_t* clocks, void* stream);
 
 /* The rate of the real-time counter the two entry points above record, in
  * kHz, for the current device (*khz, host memory).  Returns 0, -4 for a NULL

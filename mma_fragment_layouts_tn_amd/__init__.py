@@ -137,7 +137,7 @@ def _load() -> ctypes.CDLL:
     lib.mfl_probe_chain_phases.restype = ctypes.c_int
     lib.mfl_bench_mfma.argtypes = [i32, vp, i32, i32, i32, vp, vp, vp]
     lib.mfl_bench_mfma.restype = ctypes.c_int
-    lib.mfl_bench_lds_read.argtypes = [i32, i32, i32, vp, vp, vp]
+    lib.mfl_bench_lds_read.argtypes = [i32, i32, i32, i32, vp, vp, vp]
     lib.mfl_bench_lds_read.restype = ctypes.c_int
     lib.mfl_wall_clock_khz.argtypes = [P(i32)]
     lib.mfl_wall_clock_khz.restype = ctypes.c_int
@@ -533,10 +533,10 @@ def bench_mfma_raw(op: int, operands: int, n_operands: int, iters: int, nwg: int
     return _lib.mfl_bench_mfma(op, operands, n_operands, iters, nwg, sink, clocks, stream)
 
 
-def bench_lds_read_raw(threads: int, iters: int, nwg: int, sink: int, clocks: int,
+def bench_lds_read_raw(threads: int, iters: int, nwg: int, depth: int, sink: int, clocks: int,
                        stream: int) -> int:
     """Enqueue the LDS read-rate kernel (mfl_bench_lds_read); raw pointers."""
-    return _lib.mfl_bench_lds_read(threads, iters, nwg, sink, clocks, stream)
+    return _lib.mfl_bench_lds_read(threads, iters, nwg, depth, sink, clocks, stream)
 
 
 def wall_clock_khz() -> int:

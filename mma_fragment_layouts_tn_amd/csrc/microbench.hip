@@ -114,13 +114,17 @@ __global__ void __launch_bounds__(256, 1) mfma_rate(const uint16_t* ops, int nop
 // LDS read rate.  The workgroup's LDS (kLdsBytes, more than half the CU's
 // 160 KB so one workgroup runs per CU) is filled once; then each wave reads
 // 1 KB runs (lane l at byte 16 l of the run, so every 16-lane pass of a
-// ds_read_b128 covers the 64 banks once), 8 reads per iteration, the run
-// index taken modulo a runtime mask so the compiler cannot reuse a load.
-// An empty asm statement consumes each loaded value.
-constexpr int kLdsBytes = 96 * 1024;
+// ds_read_b128 covers the 64 banks once), 16 reads per iteration in groups of
+// DEPTH: a group's reads go to distinct registers and are all issued before
+// the first is consumed, so DEPTH reads are in flight per wave.  The run
+// index is taken modulo a runtime mask so the compiler cannot reuse a load;
+// an empty asm statement consumes each loaded value.
+constexpr int kLdsBytes = 96 * 1024, kLdsReadsPerIter = 16;
 
+template <int DEPTH>
 __global__ void __launch_bounds__(1024, 1) lds_read_rate(int iters, int run_mask,
                                                           uint32_t* sink, uint64_t* clocks) {
+  static_assert(kLdsReadsPerIter % DEPTH == 0, "groups divide an iteration");
   __shared__ __attribute__((aligned(1024))) uint32_t lds[kLdsBytes / 4];
   for (int i = threadIdx.x; i < kLdsBytes / 4; i += blockDim.x) lds[i] = i * 2654435761u;
   __syncthreads();
@@ -129,10 +133,16 @@ __global__ void __launch_bounds__(1024, 1) lds_read_rate(int iters, int run_mask
   stamp(clocks, 0);
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int run = ((it * 8 + u + w * 3) & run_mask);
-      const u32x4 v = *(const u32x4*)(base + run * 1024);
-      asm volatile("" ::"v"(v));
+    for (int g = 0; g < kLdsReadsPerIter / DEPTH; ++g) {
+      u32x4 v[DEPTH];
+#pragma unroll
+      for (int u = 0; u < DEPTH; ++u) {
+        const int run = ((it * kLdsReadsPerIter + g * DEPTH + u + w * 3) & run_mask);
+        v[u] = *(const u32x4*)(base + run * 1024);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < DEPTH; ++u) asm volatile("" ::"v"(v[u]));
     }
   }
   __syncthreads();
@@ -158,14 +168,20 @@ extern "C" int mfl_bench_mfma(int32_t op, const uint16_t* operands, int32_t n_op
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
-extern "C" int mfl_bench_lds_read(int32_t threads, int32_t iters, int32_t nwg, uint32_t* sink,
-                                  uint64_t* clocks, void* stream) {
+extern "C" int mfl_bench_lds_read(int32_t threads, int32_t iters, int32_t nwg, int32_t depth,
+                                  uint32_t* sink, uint64_t* clocks, void* stream) {
   if (threads <= 0 || threads > 1024 || threads % 64 != 0 || iters <= 0 || nwg <= 0 ||
       nwg > 65536 || !sink || !clocks)
     return -4;
   // runs of 1 KB inside the 96 KB array: the mask keeps run indices below 64
-  hipLaunchKernelGGL(lds_read_rate, dim3(nwg), dim3(threads), 0, (hipStream_t)stream, iters, 63,
-                     sink, clocks);
+  hipStream_t s = (hipStream_t)stream;
+  switch (depth) {
+    case 1: hipLaunchKernelGGL(lds_read_rate<1>, dim3(nwg), dim3(threads), 0, s, iters, 63, sink, clocks); break;
+    case 4: hipLaunchKernelGGL(lds_read_rate<4>, dim3(nwg), dim3(threads), 0, s, iters, 63, sink, clocks); break;
+    case 8: hipLaunchKernelGGL(lds_read_rate<8>, dim3(nwg), dim3(threads), 0, s, iters, 63, sink, clocks); break;
+    case 16: hipLaunchKernelGGL(lds_read_rate<16>, dim3(nwg), dim3(threads), 0, s, iters, 63, sink, clocks); break;
+    default: return -4;
+  }
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
