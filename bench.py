@@ -273,6 +273,7 @@ MICRO_WORKLOADS = {
     "mfma_rate_32x32x16": ("mfma", 0, "v_mfma_f32_32x32x16_f16"),
     "mfma_rate_16x16x32": ("mfma", 1, "v_mfma_f32_16x16x32_f16"),
     "lds_read_b128": ("lds", None, "ds_read_b128"),
+    "lds_dma_b128": ("dma", None, "global_load_lds_dwordx4"),
 }
 
 
@@ -286,7 +287,9 @@ def main_micro(args) -> int:
         (32x32x16) or 2^21 FLOP (16x16x32) per wave per iteration, nothing
         else in the loop;
       lds_read_b128: every wave issues conflict-free 16-byte LDS reads,
-        --depth of them in flight."""
+        --depth of them in flight;
+      lds_dma_b128: every wave fetches L2-resident data straight into LDS,
+        --depth instructions in flight."""
     import numpy as np
     import torch
 
@@ -318,15 +321,29 @@ def main_micro(args) -> int:
                                    clocks.data_ptr(), sptr)
             if r != 0:
                 raise RuntimeError(mfl.strerror(r))
-    else:
+    elif kind == "lds":
         threads = args.threads
+        depth = args.depth or 8
         iters = args.iters or 32768
         sink = torch.empty(nwg, dtype=torch.int32, device=dev)
         nbytes = float(nwg * (threads // 64) * iters * 16 * 1024)
 
         def step():
-            r = mfl.bench_lds_read_raw(threads, iters, nwg, args.depth, sink.data_ptr(),
+            r = mfl.bench_lds_read_raw(threads, iters, nwg, depth, sink.data_ptr(),
                                        clocks.data_ptr(), sptr)
+            if r != 0:
+                raise RuntimeError(mfl.strerror(r))
+    else:
+        threads = args.threads
+        depth = args.depth or 12
+        iters = args.iters or 98304 // depth
+        sink = torch.empty(nwg, dtype=torch.int32, device=dev)
+        buf = torch.zeros(nwg * 65536, dtype=torch.uint8, device=dev)
+        nbytes = float(nwg * (threads // 64) * iters * depth * 1024)
+
+        def step():
+            r = mfl.bench_dma_rate_raw(threads, iters, nwg, depth, buf.data_ptr(),
+                                       sink.data_ptr(), clocks.data_ptr(), sptr)
             if r != 0:
                 raise RuntimeError(mfl.strerror(r))
 
@@ -356,8 +373,8 @@ def main_micro(args) -> int:
           f"max {mhz.max():.0f}", file=sys.stderr, flush=True)
     config = {"workload": args.workload, "instruction": instr, "workgroups": nwg,
               "threads": threads, "iterations": iters}
-    if kind == "lds":
-        config["reads_in_flight_per_wave"] = args.depth
+    if kind != "mfma":
+        config["in_flight_per_wave"] = depth
     clock = {"sclk_mhz_in_kernel_median": round(sclk, 1), "sclk_mhz_min": round(float(mhz.min()), 1),
              "sclk_mhz_max": round(float(mhz.max()), 1),
              "how": "s_memtime cycles / s_memrealtime ticks around the loop, per workgroup, "
@@ -378,8 +395,9 @@ def main_micro(args) -> int:
         value = nbytes / (kern_ms * 1e-3) / 1e12
         per_clk = nbytes / (loop_ms * 1e-3) / (sclk * 1e6) / nwg
         clock["bytes_per_clk_per_cu"] = round(per_clk, 1)
-        out = {"metric": "LDS read rate (ds_read_b128, conflict-free), TB/s over 256 CUs and "
-                         "bytes per clock per CU",
+        what = ("LDS read rate (ds_read_b128, conflict-free)" if kind == "lds" else
+                "direct-to-LDS fetch rate (global_load_lds_dwordx4, L2-resident data)")
+        out = {"metric": f"{what}, TB/s over 256 CUs and bytes per clock per CU",
                "value": round(value, 2), "unit": "TB/s", "roofline": None, "dtype": "u32"}
     out.update({"n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
                 "ms_per_step": round(wall * 1e3 / args.steps, 5), "higher_is_better": True,
@@ -528,8 +546,10 @@ def main() -> int:
                     help="operand data of the MFMA issue-rate workloads")
     ap.add_argument("--threads", type=int, default=512,
                     help="threads per workgroup of the LDS read-rate workload")
-    ap.add_argument("--depth", type=int, default=8, choices=[1, 4, 8, 16],
-                    help="LDS reads in flight per wave in the LDS read-rate workload")
+    ap.add_argument("--depth", type=int, default=0, choices=[0, 1, 4, 8, 12, 16, 24],
+                    help="instructions in flight per wave in the LDS read-rate (1, 4, 8, 16; "
+                         "default 8) and direct-to-LDS fetch-rate (4, 12, 24; default 12) "
+                         "workloads")
     ap.add_argument("--phases", action="store_true",
                     help="back-to-back GEMM: also report cycles per loop phase from the timed "
                          "kernel instance")

@@ -118,7 +118,20 @@ int mfl_bench_mfma(int32_t op, const uint16_t* operands, int32_t n_operands, int
 int mfl_bench_lds_read(int32_t threads, int32_t iters, int32_t nwg, int32_t depth,
                        uint32_t* sink, uint64_t* clocks, void* stream);
 
-/* The rate of the real-time counter the two entry points above record, in
+/* Direct-to-LDS fetch rate: nwg workgroups of `threads` threads (a multiple
+ * of 64, at most 1024), each with 96 KB of LDS (one workgroup per compute
+ * unit); workgroup g re-reads bytes [g * 65536, (g + 1) * 65536) of buf
+ * (device, nwg * 65536 bytes, contents ignored; the region stays in L2) in
+ * 1 KB runs with global_load_lds_dwordx4, every wave issuing iters x `depth`
+ * instructions (depth 4, 12 or 24) and waiting for each batch of `depth`
+ * before the next: iters x depth KB per wave.  sink (device, nwg uint32) and
+ * clocks (device, 4 * nwg uint64: cycle and real-time counters before and
+ * after the loop, per workgroup) as in mfl_bench_lds_read.  Returns 0, -4
+ * for a bad size, depth or NULL pointer, -5 on a launch error. */
+int mfl_bench_dma_rate(int32_t threads, int32_t iters, int32_t nwg, int32_t depth,
+                       const uint8_t* buf, uint32_t* sink, uint64_t* clocks, void* stream);
+
+/* The rate of the real-time counter the three entry points above record, in
  * kHz, for the current device (*khz, host memory).  Returns 0, -4 for a NULL
  * pointer, -5 when the runtime does not report it. */
 int mfl_wall_clock_khz(int32_t* khz);

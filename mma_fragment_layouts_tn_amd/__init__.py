@@ -138,6 +138,8 @@ def _load() -> ctypes.CDLL:
     lib.mfl_bench_mfma.argtypes = [i32, vp, i32, i32, i32, vp, vp, vp]
     lib.mfl_bench_mfma.restype = ctypes.c_int
     lib.mfl_bench_lds_read.argtypes = [i32, i32, i32, i32, vp, vp, vp]
+    lib.mfl_bench_dma_rate.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp]
+    lib.mfl_bench_dma_rate.restype = ctypes.c_int
     lib.mfl_bench_lds_read.restype = ctypes.c_int
     lib.mfl_wall_clock_khz.argtypes = [P(i32)]
     lib.mfl_wall_clock_khz.restype = ctypes.c_int
@@ -531,6 +533,12 @@ def bench_mfma_raw(op: int, operands: int, n_operands: int, iters: int, nwg: int
                    clocks: int, stream: int) -> int:
     """Enqueue the MFMA issue-rate kernel (mfl_bench_mfma); raw pointers."""
     return _lib.mfl_bench_mfma(op, operands, n_operands, iters, nwg, sink, clocks, stream)
+
+
+def bench_dma_rate_raw(threads: int, iters: int, nwg: int, depth: int, buf: int, sink: int,
+                       clocks: int, stream: int) -> int:
+    """Enqueue the direct-to-LDS fetch-rate kernel (mfl_bench_dma_rate); raw pointers."""
+    return _lib.mfl_bench_dma_rate(threads, iters, nwg, depth, buf, sink, clocks, stream)
 
 
 def bench_lds_read_raw(threads: int, iters: int, nwg: int, depth: int, sink: int, clocks: int,

@@ -7,6 +7,8 @@
 //    at the clock the chip holds under that load.
 //  * LDS read rate: every wave of a full-chip launch issues 16-byte LDS reads
 //    that touch each bank once per pass, with no other work.
+//  * Direct-to-LDS fetch rate: every wave issues global_load_lds_dwordx4 from
+//    a region of global memory that stays in L2, with no other work.
 //
 // Both record, per workgroup, the shader-clock cycle counter (s_memtime) and
 // the constant 100 MHz real-time counter (s_memrealtime) before and after the
@@ -150,6 +152,37 @@ __global__ void __launch_bounds__(1024, 1) lds_read_rate(int iters, int run_mask
   if (threadIdx.x == 0) sink[blockIdx.x] = lds[blockIdx.x % (kLdsBytes / 4)];
 }
 
+// Direct-to-LDS fetch rate.  Workgroup g re-reads its own 64 KB region of
+// `buf` (L2-resident after the first pass) in 1 KB runs, lane l taking bytes
+// 16 l .. 16 l + 15 of a run, straight into 1 KB slots of a 96 KB LDS array
+// (one workgroup per CU); each wave issues DEPTH instructions, then waits
+// for all of them.
+constexpr int kDmaRegion = 64 * 1024;
+
+template <int DEPTH>
+__global__ void __launch_bounds__(1024, 1) dma_rate(const uint8_t* buf, int iters, uint32_t* sink,
+                                                     uint64_t* clocks) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const uint8_t* base = buf + (size_t)blockIdx.x * kDmaRegion + lane * 16;
+  __syncthreads();
+  stamp(clocks, 0);
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int u = 0; u < DEPTH; ++u) {
+      const int run = (it * DEPTH + u + w * 7) & (kDmaRegion / 1024 - 1);
+      const int slot = (w * DEPTH + u) % (kLdsBytes / 1024);
+      __builtin_amdgcn_global_load_lds((const void*)(base + run * 1024),
+                                       (__attribute__((address_space(3))) void*)(lds + slot * 1024),
+                                       16, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));   // vmcnt(0)
+  }
+  __syncthreads();
+  stamp(clocks, 1);
+  if (threadIdx.x == 0) sink[blockIdx.x] = lds[blockIdx.x % kLdsBytes];
+}
+
 }  // namespace
 
 extern "C" int mfl_bench_mfma(int32_t op, const uint16_t* operands, int32_t n_operands,
@@ -180,6 +213,22 @@ extern "C" int mfl_bench_lds_read(int32_t threads, int32_t iters, int32_t nwg, i
     case 4: hipLaunchKernelGGL(lds_read_rate<4>, dim3(nwg), dim3(threads), 0, s, iters, 63, sink, clocks); break;
     case 8: hipLaunchKernelGGL(lds_read_rate<8>, dim3(nwg), dim3(threads), 0, s, iters, 63, sink, clocks); break;
     case 16: hipLaunchKernelGGL(lds_read_rate<16>, dim3(nwg), dim3(threads), 0, s, iters, 63, sink, clocks); break;
+    default: return -4;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+extern "C" int mfl_bench_dma_rate(int32_t threads, int32_t iters, int32_t nwg, int32_t depth,
+                                  const uint8_t* buf, uint32_t* sink, uint64_t* clocks,
+                                  void* stream) {
+  if (threads <= 0 || threads > 1024 || threads % 64 != 0 || iters <= 0 || nwg <= 0 ||
+      nwg > 65536 || !buf || !sink || !clocks)
+    return -4;
+  hipStream_t s = (hipStream_t)stream;
+  switch (depth) {
+    case 4: hipLaunchKernelGGL(dma_rate<4>, dim3(nwg), dim3(threads), 0, s, buf, iters, sink, clocks); break;
+    case 12: hipLaunchKernelGGL(dma_rate<12>, dim3(nwg), dim3(threads), 0, s, buf, iters, sink, clocks); break;
+    case 24: hipLaunchKernelGGL(dma_rate<24>, dim3(nwg), dim3(threads), 0, s, buf, iters, sink, clocks); break;
     default: return -4;
   }
   return hipGetLastError() == hipSuccess ? 0 : -5;

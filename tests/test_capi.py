@@ -209,6 +209,15 @@ def test_chain_n2_tile_rule():
     assert [tile(n) for n in (1, 63, 64, 65, 128, 129, 1000)] == [64, 64, 64, 128, 128, 128, 128]
 
 
+def test_microbenchmark_arguments():
+    """The rate kernels refuse bad sizes, depths and NULL pointers before any
+    launch."""
+    assert mfl.lib.mfl_bench_dma_rate(256, 10, 256, 5, P, P, P, None) == -4      # depth
+    assert mfl.lib.mfl_bench_dma_rate(100, 10, 256, 12, P, P, P, None) == -4     # threads
+    assert mfl.lib.mfl_bench_dma_rate(256, 10, 256, 12, 0, P, P, None) == -4     # buf
+    assert mfl.lib.mfl_bench_lds_read(256, 10, 256, 3, P, P, None) == -4         # depth
+    assert mfl.lib.mfl_bench_lds_read(256, 0, 256, 8, P, P, None) == -4          # iters
+
 def test_chain_phase_probe_arguments():
     """The timed instance exists only for K = 128, fp16 D, direct-to-LDS
     staging and 128-column N2 tiles; anything else, or no stamp buffer, is
