@@ -488,7 +488,7 @@ def main_chain(args) -> int:
         s0, s1, s2, s3 = (t[:, :, 4 * cs + k] for k in range(4))
         nxt = t[:, :, 4 * (cs + 1)]
         names = {"K chunks 0..2H-2 of the second product with the next chunk's first product "
-                 "and the fetch of slot c+2": d(s0, s1),
+                 "and the fetch of slot c+3": d(s0, s1),
                  "wait for this wave's fetch of slot c+1": d(s1, s2),
                  "workgroup barrier": d(s2, s3),
                  "last K chunk with the first reads of slot c+1": d(s3, nxt)}

@@ -106,18 +106,18 @@ static_assert(chain_runs_of_4(), "pi must keep runs of 4 N1 columns");
 // Software pipeline: iteration c issues the second product of chunk c (its
 // P in registers) interleaved with the first product of chunk c+1, so the
 // matrix core never waits for a first product before the second can start.
-// Slot c of the LDS ring (stage c mod 3) holds B of chunk c+1 and W of chunk
+// Slot c of the LDS ring (stage c mod 4) holds B of chunk c+1 and W of chunk
 // c, the operands of iteration c; slot -1 holds B of chunk 0 for the
 // prologue.  One barrier per iteration, before the second product's last K
-// chunk: after it every wave is done with slot c-1 and can read slot c+1,
-// and the last K chunk runs on registers while the next slot's first
-// fragments are read and slot c+2 is fetched into slot c-1's stage.  Fetch:
-// direct global-to-LDS loads when B and W are 16-byte aligned and N1 fills
-// whole chunks (slot c+2 lands before the barrier of iteration c+1);
-// otherwise through registers with zero fill, loaded after the barrier of
-// iteration c and written to LDS before that of iteration c+1.
+// chunk: after it every wave is done with slot c and can read slot c+1, and
+// the last K chunk runs on registers while the next slot's first fragments
+// are read.  Fetch: direct global-to-LDS loads when B and W are 16-byte
+// aligned and N1 fills whole chunks, slot c+3 issued during iteration c into
+// the stage slot c-1 left (it lands before the barrier of iteration c+2);
+// otherwise through registers with zero fill, slot c+2 loaded after the
+// barrier of iteration c and written to LDS before that of iteration c+1.
 namespace chain {
-constexpr int BM = 256, RM = 2, WAVES = 4, THREADS = 256, NST = 3;
+constexpr int BM = 256, RM = 2, WAVES = 4, THREADS = 256, NST = 4;
 // N2 columns per workgroup: 128 (RN = 4 atom columns per wave), 64 when N2
 // fits in it (RN = 2: no MFMAs on columns past N2)
 MFL_HD constexpr int tile_n(int64_t n2) { return n2 <= 64 ? 64 : 128; }
@@ -385,12 +385,14 @@ __global__ void __launch_bounds__(chain::THREADS, 1) gemm_chain(const ChainParam
       }
     }
   };
-  // DMA: wait until every slot before s has landed (slot s may be in flight)
-  auto wait_before = [&](int s) {
+  // DMA: wait until every slot before s has landed (slots s and s+1 may be
+  // in flight; a slot brings NB + NW instructions, only NW for the last
+  // chunk's W, none past it)
+  auto wait_before_two = [&](int s) {
     if constexpr (DMA) {
-      const bool hb = s + 1 < nch, hw = s < nch;
-      if (hb && hw) wait_vm<NB + NW>();
-      else if (hw) wait_vm<NW>();
+      if (s + 2 < nch) wait_vm<2 * (NB + NW)>();
+      else if (s + 1 < nch) wait_vm<NB + 2 * NW>();
+      else if (s < nch) wait_vm<NW>();
       else wait_vm<0>();
     }
   };
@@ -453,11 +455,11 @@ __global__ void __launch_bounds__(chain::THREADS, 1) gemm_chain(const ChainParam
   // chunks (P in registers) with the FS steps of the first product of chunk
   // c+1 spread over all but the last K chunk.  The barrier that closes the
   // slot comes before the last K chunk, which runs on fragments already in
-  // registers while the first fragments of slot c+1 are read.  Slot c+2 goes
-  // to the stage of slot c-1, which every wave left at the previous barrier:
-  // direct-to-LDS, one DMA instruction at a time spread over the K chunks
-  // before the barrier (it has until the next iteration's barrier to land);
-  // through registers, loaded after the barrier and written to LDS in the
+  // registers while the first fragments of slot c+1 are read.  Direct-to-LDS,
+  // slot c+3 goes to the stage of slot c-1, which every wave left at the
+  // previous barrier, one DMA instruction at a time spread over the K chunks
+  // before the barrier; it has two iterations to land.  Through registers,
+  // slot c+2 is loaded after the barrier and written to its stage in the
   // next iteration.  P of chunk c+1 is converted piece by piece beside the
   // MFMAs: block h of S in K chunk 2H-2 (all but the last block, whose
   // first-product steps are done by then) or 2H-1 (the last block).
@@ -499,7 +501,7 @@ __global__ void __launch_bounds__(chain::THREADS, 1) gemm_chain(const ChainParam
           t1 = now();
           stash(c + 1);          // registers: slot c+1, loaded one iteration ago
           if constexpr (DMA)
-            wait_before(c + 2);  // slot c+1 has landed; slot c+2 may be in flight
+            wait_before_two(c + 2);   // slot c+1 has landed; c+2 and c+3 may be in flight
           else
             wait_vm<0>();
           t2 = now();
@@ -538,7 +540,7 @@ __global__ void __launch_bounds__(chain::THREADS, 1) gemm_chain(const ChainParam
           } else if constexpr (DMA) {
 #pragma unroll
             for (int j = 0; j < NI; ++j)
-              if (j * NPRE / NI == kc * RM * RN + g) issue_one(c + 2, j);
+              if (j * NPRE / NI == kc * RM * RN + g) issue_one(c + 3, j);
           }
           convert_at(st, pn, kc, g);
         }
@@ -565,7 +567,10 @@ __global__ void __launch_bounds__(chain::THREADS, 1) gemm_chain(const ChainParam
     issue(0);
     stash(0);
     issue(1);                        // registers: written in iteration 0
-    wait_before(1);
+    if constexpr (DMA) {
+      issue(2);
+      wait_before_two(1);
+    }
     barrier();
     {
       floatx16 st[RM][H];
@@ -573,7 +578,7 @@ __global__ void __launch_bounds__(chain::THREADS, 1) gemm_chain(const ChainParam
       const _Float16* sb = smem + stage_of(-1) * STAGE;
 #pragma unroll
       for (int s1 = 0; s1 < FS; ++s1) first_step(st, read_b(sb, s1), s1);
-      // direct-to-LDS: iteration 0 fetches slot 2 into this stage
+      // direct-to-LDS: iteration 0 fetches slot 3 into this stage
       if constexpr (DMA) barrier();
       convert(st, pf);
       const _Float16* s0 = smem + stage_of(0) * STAGE;
