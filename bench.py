@@ -531,7 +531,7 @@ def main() -> int:
     ap.add_argument("--workload", default="lds_4096")
     ap.add_argument("--algo", default="auto",
                     help="auto, direct, lds128, lds256, lds256w4, lds128w1, splitk, lds256w4_16, "
-                         "lds256_16, lds128_16; '+reg' "
+                         "lds256_16, lds128_16, splitk_16; '+reg' "
                          "forces register fetch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--clock-seconds", type=float, default=2.0,

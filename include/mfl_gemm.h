@@ -77,9 +77,11 @@ typedef enum { MFL_A_KMAJOR = 0, MFL_A_MMAJOR = 1 } mfl_a_order;
  * The *_16 kernels run the same block tiles on v_mfma_f32_16x16x32_f16
  * (the others on v_mfma_f32_32x32x16_f16): LDS_256_W4_16 with 4 waves of
  * 128x128, LDS_256_16 with 8 waves of 128x64, LDS_128_16 128x128x64 tiles
- * with 4 waves of 64x64.  They do not transpose an M-contiguous A in
- * registers, and LDS_256_16 fetches only straight into LDS; LDS_256_W4 does
- * not combine an M-contiguous A straight into LDS with B through registers.
+ * with 4 waves of 64x64, LDS_SPLITK_16 the 128x64x128 split-K tile as 2
+ * K-groups of 4 waves of 32x64.  They do not transpose an M-contiguous A in
+ * registers, and LDS_256_16 and LDS_SPLITK_16 fetch only straight into LDS;
+ * LDS_256_W4 does not combine an M-contiguous A straight into LDS with B
+ * through registers.
  * A forced kernel that does not offer the fetch path a call needs returns
  * MFL_E_ALGO_CASE. */
 typedef enum {
@@ -93,7 +95,8 @@ typedef enum {
   MFL_ALGO_LDS_256_W4_16 = 7,
   MFL_ALGO_LDS_256_16 = 8,
   MFL_ALGO_LDS_128_16 = 9,
-  MFL_ALGO_COUNT = 10,
+  MFL_ALGO_LDS_SPLITK_16 = 10,
+  MFL_ALGO_COUNT = 11,
   MFL_ALGO_MASK = 0xff,
   MFL_ALGO_REG_FETCH = 0x100
 } mfl_algo;

@@ -49,7 +49,7 @@ int mfl_probe_lds_tr16(const int32_t* lane_offsets, const uint16_t* lds_in, uint
 int mfl_probe_xcc(int32_t nblocks, int32_t* out, void* stream);
 
 /* Register dump of an LDS kernel (test-only): the kernel of configuration
- * `algo` (mfl_algo value, 2..9 except 1) with fetch policies fetch_a /
+ * `algo` (mfl_algo value, 2..10) with fetch policies fetch_a /
  * fetch_b (0 direct-to-LDS, 1 registers, 2 M-contiguous A transposed in
  * registers, 3 M-contiguous A direct-to-LDS) runs one K-step (K must equal
  * the configuration's BK) over M x N of whole tiles, A (M,K) K-contiguous
@@ -79,7 +79,8 @@ int mfl_probe_fragments(int32_t algo, int32_t fetch_a, int32_t fetch_b, int32_t 
  * direct-to-LDS or registers; LDS_256 with M-contiguous A direct-to-LDS and B
  * direct, or A transposed in registers and B in registers; LDS_128_W1 with A
  * direct and B in registers; LDS_SPLITK direct; LDS_256_W4_16 registers;
- * LDS_256_16 direct; LDS_128_16 M-contiguous A direct-to-LDS and B direct.
+ * LDS_256_16 direct; LDS_128_16 M-contiguous A direct-to-LDS and B direct;
+ * LDS_SPLITK_16 direct.
  * Returns gemm_tn's codes; MFL_E_ALGO_CASE (-6) where no instance exists for
  * the plan (force the kernel and fetch with the algo field). */
 int mfl_probe_gemm_poisoned(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,

@@ -26,7 +26,7 @@ LIB_PATH = os.path.join(_PKG, "libmfl_gemm.so")
 NONE, F16, F32 = 0, 1, 2
 A_KMAJOR, A_MMAJOR = 0, 1
 ALGOS = {"auto": 0, "direct": 1, "lds128": 2, "lds256": 3, "lds256w4": 4, "lds128w1": 5,
-         "splitk": 6, "lds256w4_16": 7, "lds256_16": 8, "lds128_16": 9}
+         "splitk": 6, "lds256w4_16": 7, "lds256_16": 8, "lds128_16": 9, "splitk_16": 10}
 REG_FETCH = 0x100          # or-ed into the algo: fetch through registers
 FETCH_NAMES = {0: "dma", 1: "reg", 2: "regT", 3: "dmaT"}
 ALGO_NAMES = {v: k for k, v in ALGOS.items()}

@@ -23,7 +23,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["gemm_inst_256.hip", "gemm_inst_256w4.hip", "gemm_inst_128.hip",
            "gemm_inst_128w1.hip", "gemm_inst_splitk.hip", "gemm_inst_256w4x16.hip",
-           "gemm_inst_256x16.hip", "gemm_inst_128x16.hip", "chain_inst.hip", "gemm_dispatch.hip", "probe_kernels.hip", "microbench.hip", "probe_dump.hip", "capi.cpp"]
+           "gemm_inst_256x16.hip", "gemm_inst_128x16.hip", "gemm_inst_splitk16.hip", "chain_inst.hip", "gemm_dispatch.hip", "probe_kernels.hip", "microbench.hip", "probe_dump.hip", "capi.cpp"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-mcode-object-version=5",
@@ -38,6 +38,7 @@ FLAGS = [
 # accumulator tied by hand (inline assembly), whose hazards the compiler
 # cannot see, more strictly.
 CHECKED_SOURCES = {"gemm_inst_256w4x16.hip", "gemm_inst_256x16.hip", "gemm_inst_128x16.hip",
+                   "gemm_inst_splitk16.hip",
                    "gemm_inst_256.hip", "gemm_inst_256w4.hip", "gemm_inst_128.hip",
                    "gemm_inst_128w1.hip", "gemm_inst_splitk.hip", "probe_dump.hip"}
 TIED_MFMA = "v_mfma_f32_16x16x32_f16"

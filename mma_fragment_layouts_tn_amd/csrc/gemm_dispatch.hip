@@ -13,6 +13,7 @@ const void* tiled_symbol_splitk(int fa, int fb, int ck, int dk);
 const void* tiled_symbol_256w4x16(int fa, int fb, int ck, int dk);
 const void* tiled_symbol_256x16(int fa, int fb, int ck, int dk);
 const void* tiled_symbol_128x16(int fa, int fb, int ck, int dk);
+const void* tiled_symbol_splitk16(int fa, int fb, int ck, int dk);
 const void* direct_symbol(int ck, int dk);
 
 namespace {
@@ -33,6 +34,7 @@ KernelInfo kernel_info(int algo) {
     case kAlgoLds256W4x16: return info_of<CfgLds256W4x16>(algo);
     case kAlgoLds256x16: return info_of<CfgLds256x16>(algo);
     case kAlgoLds128x16: return info_of<CfgLds128x16>(algo);
+    case kAlgoLdsSplitK16: return info_of<CfgLdsSplitK16>(algo);
     default: return KernelInfo{-1, 0, 0, 0, 0};
   }
 }
@@ -49,6 +51,7 @@ const void* kernel_symbol(int algo, int fetch_a, int fetch_b, int c_kind, int d_
     case kAlgoLds256W4x16: return tiled_symbol_256w4x16(fetch_a, fetch_b, c_kind, d_kind);
     case kAlgoLds256x16: return tiled_symbol_256x16(fetch_a, fetch_b, c_kind, d_kind);
     case kAlgoLds128x16: return tiled_symbol_128x16(fetch_a, fetch_b, c_kind, d_kind);
+    case kAlgoLdsSplitK16: return tiled_symbol_splitk16(fetch_a, fetch_b, c_kind, d_kind);
     default: return nullptr;
   }
 }

@@ -35,7 +35,8 @@ enum Algo : int {
   kAlgoLds256W4x16 = 7,   // 4 waves of 128x128, 16x16x32 instructions
   kAlgoLds256x16 = 8,     // 8 waves of 128x64, 16x16x32 instructions
   kAlgoLds128x16 = 9,     // 128x128x64, 4 waves of 64x64, 16x16x32 instructions
-  kAlgoCount = 10
+  kAlgoLdsSplitK16 = 10,  // 128x64x128, 2 K-groups of 4 waves of 32x64, 16x16x32
+  kAlgoCount = 11
 };
 
 // how an operand tile travels from global memory to LDS
@@ -73,12 +74,17 @@ using CfgLdsSplitK = TileCfg<128, 64, 128, 1, 1, 1, 4, 3>;
 using CfgLds256W4x16 = TileCfg<256, 256, 64, 2, 2, 1, 1, 2, kMfma16x16x32>;
 using CfgLds256x16 = TileCfg<256, 256, 64, 2, 4, 1, 1, 2, kMfma16x16x32>;
 using CfgLds128x16 = TileCfg<128, 128, 64, 2, 2, 1, 1, 2, kMfma16x16x32>;
+// The split-K tile on it with two waves per SIMD: 2 K-groups of 4 waves of
+// 32x64, so while one wave of a SIMD is held by a direct-to-LDS instruction
+// that finds the CU's fetch path busy, the other issues MFMAs.
+using CfgLdsSplitK16 = TileCfg<128, 64, 128, 4, 1, 1, 2, 3, kMfma16x16x32>;
 
 static_assert(frag_c_is_partition_c<CfgLds128>() && frag_c_is_partition_c<CfgLds256>() &&
                   frag_c_is_partition_c<CfgLds256W4>() && frag_c_is_partition_c<CfgLds128W1>() &&
                   frag_c_is_partition_c<CfgLdsSplitK>() &&
                   frag_c_is_partition_c<CfgLds256W4x16>() &&
-                  frag_c_is_partition_c<CfgLds256x16>() && frag_c_is_partition_c<CfgLds128x16>(),
+                  frag_c_is_partition_c<CfgLds256x16>() && frag_c_is_partition_c<CfgLds128x16>() &&
+                  frag_c_is_partition_c<CfgLdsSplitK16>(),
               "accumulator coordinates must be the tiled MMA's partition_C");
 
 struct KernelInfo {

@@ -48,6 +48,7 @@ const void* dump_symbol(int algo, int fa, int fb, int* words, int* threads) {
                      DumpEntry<kAlgoLds256W4x16, CfgLds256W4x16, kFetchDma, kFetchDma>,
                      DumpEntry<kAlgoLds256x16, CfgLds256x16, kFetchDma, kFetchDma>,
                      DumpEntry<kAlgoLds128x16, CfgLds128x16, kFetchDma, kFetchDma>,
+                     DumpEntry<kAlgoLdsSplitK16, CfgLdsSplitK16, kFetchDma, kFetchDma>,
                      DumpEntry<kAlgoLds256, CfgLds256, kFetchReg, kFetchReg>,
                      DumpEntry<kAlgoLds256, CfgLds256, kFetchRegT, kFetchDma>,
                      DumpEntry<kAlgoLds256, CfgLds256, kFetchDmaT, kFetchDma>,
@@ -98,7 +99,8 @@ const void* poisoned_symbol(int algo, int fa, int fb, int ck, int dk) {
                        PoisonEntry<kAlgoLdsSplitK, CfgLdsSplitK, kFetchDma, kFetchDma>,
                        PoisonEntry<kAlgoLds256W4x16, CfgLds256W4x16, kFetchReg, kFetchReg>,
                        PoisonEntry<kAlgoLds256x16, CfgLds256x16, kFetchDma, kFetchDma>,
-                       PoisonEntry<kAlgoLds128x16, CfgLds128x16, kFetchDmaT, kFetchDma>>(
+                       PoisonEntry<kAlgoLds128x16, CfgLds128x16, kFetchDmaT, kFetchDma>,
+                       PoisonEntry<kAlgoLdsSplitK16, CfgLdsSplitK16, kFetchDma, kFetchDma>>(
       algo, fa, fb, ck);
 }
 

@@ -59,7 +59,7 @@ def out_buffer(M, ldd, d, dev="cuda"):
 # configurations that offer only some fetch paths (the 16x16x32 ones, and
 # the four-wave 256x256 one without M-contiguous A straight to LDS with B
 # through registers)
-PARTIAL_FETCH_ALGOS = {"lds256w4_16", "lds256_16", "lds128_16", "lds256w4"}
+PARTIAL_FETCH_ALGOS = {"lds256w4_16", "lds256_16", "lds128_16", "splitk_16", "lds256w4"}
 
 
 def refused(w: W.Workload, algo: str) -> bool:

@@ -60,7 +60,7 @@ def test_valid_cases():
     (dict(A=0), -3), (dict(B=0), -3), (dict(D=0), -3),
     (dict(c=mfl.F32, ldc=64), -3), (dict(C=P + 4096, ldc=64), -3),
     (dict(d=mfl.NONE), -4), (dict(c=7, C=P, ldc=64), -4), (dict(a_order=2), -4),
-    (dict(algo=10), -4),
+    (dict(algo=11), -4),
     (dict(a_order=mfl.A_MMAJOR, algo=1), -6),
     # the 16x16x32 configurations have no register-transposing fetch for an
     # M-contiguous A: rows off 16-byte alignment need a 32x32x16 one
@@ -117,9 +117,13 @@ def test_auto_choice():
     assert _v(M=4096, N=4096, K=4096, lda=4100)[1] == mfl.ALGOS["lds256"]
     assert _v(M=256, N=256, K=256)[1] == mfl.ALGOS["lds128"]
     assert _v(M=32, N=16, K=16, algo=1)[1] == mfl.ALGOS["direct"]
-    # fewer 128x128 tiles than CUs and a long K: split K inside the workgroup
-    assert _v(M=512, N=4096, K=4096)[1] == mfl.ALGOS["splitk"]
-    assert _v(M=256, N=4096, K=8192)[1] == mfl.ALGOS["splitk"]
+    # fewer 128x128 tiles than CUs and a long K: split K inside the workgroup,
+    # on the 16x16x32 tile when both operands go straight into LDS and C is
+    # absent, else on the 32x32x16 one
+    assert _v(M=512, N=4096, K=4096)[1] == mfl.ALGOS["splitk_16"]
+    assert _v(M=256, N=4096, K=8192)[1] == mfl.ALGOS["splitk_16"]
+    assert _v(M=512, N=4096, K=4096, lda=4100)[1] == mfl.ALGOS["splitk"]
+    assert _v(M=512, N=4096, K=4096, c=mfl.F32, C=P, ldc=4096)[1] == mfl.ALGOS["splitk"]
     assert _v(M=512, N=4096, K=512)[1] == mfl.ALGOS["lds128"]       # K too short
     assert _v(M=1024, N=4096, K=4096)[1] == mfl.ALGOS["lds128"]     # 256 tiles fill the CUs
 

@@ -34,7 +34,8 @@ A32, A16 = "f32_32x32x16_f16", "f32_16x16x32_f16"
 CFG = {"lds128": (128, 128, 32, 2, 2, 1, 1, A32), "lds256": (256, 256, 64, 2, 4, 1, 1, A32),
        "lds256w4": (256, 256, 64, 2, 2, 1, 2, A32), "lds128w1": (128, 128, 32, 1, 1, 1, 1, A32),
        "splitk": (128, 64, 128, 1, 1, 4, 1, A32), "lds256w4_16": (256, 256, 64, 2, 2, 1, 1, A16),
-       "lds256_16": (256, 256, 64, 2, 4, 1, 1, A16), "lds128_16": (128, 128, 64, 2, 2, 1, 1, A16)}
+       "lds256_16": (256, 256, 64, 2, 4, 1, 1, A16), "lds128_16": (128, 128, 64, 2, 2, 1, 1, A16),
+       "splitk_16": (128, 64, 128, 4, 1, 2, 1, A16)}
 ATOM = {A32: (32, 16, 16), A16: (16, 32, 4)}      # atom M = N, atom K, accumulator values
 CASES = [(a, DMA, DMA) for a in CFG] + [("lds256", REG, REG), ("lds256", REGT, DMA),
                                         ("lds256", DMAT, DMA), ("lds256w4_16", REG, REG),

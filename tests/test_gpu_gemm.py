@@ -21,7 +21,7 @@ from gpu_helpers import (freivalds_exact, oracle_full, oracle_full_cached, refus
 pytestmark = pytest.mark.gpu
 
 # the 16x16x32 configurations (same block tiles on the other f16 instruction)
-X16 = ["lds256w4_16", "lds256_16", "lds128_16"]
+X16 = ["lds256w4_16", "lds256_16", "lds128_16", "splitk_16"]
 ALGOS = ["direct", "lds128", "lds256", "lds256w4", "lds128w1", "splitk"] + X16
 LDS_ALGOS = ["lds128", "lds256", "lds256w4", "lds128w1", "splitk"] + X16
 
@@ -205,6 +205,8 @@ def test_kernel_properties():
     assert mfl.kernel_info("lds256w4_16")["lds_bytes"] == 2 * (256 + 256) * 64 * 2
     assert mfl.kernel_info("lds256_16")["threads"] == 512
     assert mfl.kernel_info("lds128_16")["lds_bytes"] == 2 * (128 + 128) * 64 * 2
+    assert mfl.kernel_info("splitk_16")["lds_bytes"] == 3 * (128 + 64) * 128 * 2
+    assert mfl.kernel_info("splitk_16")["threads"] == 512
     say("[gpu] kernel info", {a: mfl.kernel_info(a) for a in ALGOS})
 
 

@@ -25,7 +25,7 @@ POISONED = [("lds128", False, True, True), ("lds128", False, False, False),
             ("lds256", True, True, True), ("lds256", True, False, False),
             ("lds128w1", False, True, False), ("splitk", False, True, True),
             ("lds256w4_16", False, False, False), ("lds256_16", False, True, True),
-            ("lds128_16", True, True, True)]
+            ("lds128_16", True, True, True), ("splitk_16", False, True, True)]
 SHAPES = [(130, 70, 65), (257, 300, 129), (64, 64, 64), (33, 200, 300), (512, 256, 1000)]
 
 
@@ -55,10 +55,11 @@ def test_poisoned_lds_never_reaches_d(algo, mm, al_a, al_b):
 
 
 @pytest.mark.parametrize("algo", ["lds128", "lds256", "lds256w4", "lds128w1", "splitk",
-                                  "lds256w4_16", "lds256_16", "lds128_16", "direct"])
+                                  "lds256w4_16", "lds256_16", "lds128_16", "splitk_16",
+                                  "direct"])
 def test_one_k_tile_equals_many(algo):
     bk = {"lds256": 64, "lds256w4": 64, "splitk": 128, "lds256w4_16": 64, "lds256_16": 64,
-          "lds128_16": 64}.get(algo, 32)
+          "lds128_16": 64, "splitk_16": 128}.get(algo, 32)
     M, N = 300, 260
     w1 = W.custom(M, N, bk, c="f32", d="f32", dist="unif", seed=77, lda=bk, ldb=bk)
     x1 = W.make_inputs(w1)

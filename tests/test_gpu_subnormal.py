@@ -21,7 +21,7 @@ from oracle import gemm as G
 pytestmark = pytest.mark.gpu
 
 ALGOS = ["direct", "lds128", "lds256", "lds256w4", "lds128w1", "splitk", "lds256w4_16",
-         "lds256_16", "lds128_16"]
+         "lds256_16", "lds128_16", "splitk_16"]
 TINY = 2.0 ** -24   # the smallest fp16 subnormal
 
 

@@ -15,7 +15,7 @@ from gpu_helpers import oracle_full, refused, run_gemm, say, verdict
 pytestmark = pytest.mark.gpu
 
 ALGOS = ["direct", "lds128", "lds256", "lds256w4", "lds128w1", "splitk", "lds256w4_16",
-         "lds256_16", "lds128_16"]
+         "lds256_16", "lds128_16", "splitk_16"]
 SIZES = list(range(1, 41)) + [63, 64, 65, 127, 128, 129]
 _rng = np.random.default_rng(20261202)
 SHAPES = [(1, 1, 1), (129, 129, 129), (40, 1, 129), (1, 129, 40), (128, 64, 65), (65, 127, 63)]

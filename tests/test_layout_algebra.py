@@ -23,7 +23,8 @@ KERNEL_TILES = {"lds128": (128, 128, 32, 2, 2, 1, A32), "lds256": (256, 256, 64,
                 "splitk": (128, 64, 128, 1, 1, 4, A32),
                 "lds256w4_16": (256, 256, 64, 2, 2, 1, A16),
                 "lds256_16": (256, 256, 64, 2, 4, 1, A16),
-                "lds128_16": (128, 128, 64, 2, 2, 1, A16)}
+                "lds128_16": (128, 128, 64, 2, 2, 1, A16),
+                "splitk_16": (128, 64, 128, 4, 1, 2, A16)}
 ATOM = {A32: (32, 16, 16), A16: (16, 32, 4)}      # atom M = N, atom K, values per lane
 
 
