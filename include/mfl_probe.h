@@ -143,9 +143,9 @@ int mfl_wall_clock_khz(int32_t* khz);
  * codes as gemm_tn_chain, for the configuration K = 128, N2 > 64, fp16 D,
  * direct-to-LDS staging (else -4); the kernel is a separate instance in which
  * lane 0 of every wave also records the low 32 bits of the shader-clock
- * counter (s_memtime) at fixed points.  stamps: device memory of 8 x 4 x 260
+ * counter (s_memtime) at fixed points.  stamps: device memory of 8 x 8 x 260
  * uint32, written for workgroups 0..7 (fewer if the grid is smaller), wave w
- * of workgroup g at [(4 g + w) * 260 + q]: for iteration c < 64 of the N1
+ * (0..7) of workgroup g at [(8 g + w) * 260 + q]: for iteration c < 64 of the N1
  * loop, q = 4c at its start, 4c + 1 before the wave waits for its fetch of
  * the next slot, 4c + 2 before the workgroup barrier, 4c + 3 after it
  * (the last iteration records only 4c); q = 256 kernel start, 257 after the

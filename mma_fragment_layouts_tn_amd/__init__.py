@@ -261,13 +261,13 @@ def gemm_chain_raw(batch, M, N1, N2, K, A, lda, sa, B, ldb, sb, W, ldw, sw, D, l
 
 
 # phase stamps of the timed chain instance: workgroups x waves x slots
-CHAIN_STAMP_SHAPE = (8, 4, 260)
+CHAIN_STAMP_SHAPE = (8, 8, 260)
 
 
 def probe_chain_phases_raw(batch, M, N1, N2, K, A, lda, sa, B, ldb, sb, W, ldw, sw, D, ldd, sd,
                            d_dtype: int, stamps: int, stream: int) -> int:
     """mfl_probe_chain_phases with integer pointers; `stamps` points to
-    8 * 4 * 260 uint32 of device memory (CHAIN_STAMP_SHAPE)."""
+    8 * 8 * 260 uint32 of device memory (CHAIN_STAMP_SHAPE)."""
     return _lib.mfl_probe_chain_phases(batch, M, N1, N2, K, A, lda, sa, B, ldb, sb, W, ldw, sw,
                                        D, ldd, sd, d_dtype, stamps, stream)
 

@@ -51,8 +51,8 @@ bool dma_ok(const void* X, int64_t ld) { return ((uintptr_t)X % 16 == 0) && (ld 
 
 // Large outputs take the 256x256 tile.  Below that the 128x128 tile, unless
 // its grid leaves CUs idle (fewer tiles than the 256 CUs) while K is long:
-// then the split-K tile (128x64, four K-groups per workgroup) runs twice as
-// many workgroups, each with four waves.
+// then the split-K tile (128x64, its K split between groups of waves inside
+// the workgroup) runs twice as many workgroups.
 int pick_algo(int64_t M, int64_t N, int64_t K) {
   const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
   if (t256 >= 192) return mfl::kAlgoLds256;
@@ -507,7 +507,7 @@ int chain_launch(bool timed, int64_t batch, int64_t M, int64_t N1, int64_t N2, i
   p.stamps = stamps;
   void* args[] = {(void*)&p};
   const int64_t nb = (int64_t)p.tiles_m * p.tiles_n;
-  const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)nb), dim3(mfl::chain::THREADS), args, 0,
+  const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)nb), dim3(mfl::chain::threads((int)K)), args, 0,
                                        (hipStream_t)stream);
   return e == hipSuccess ? MFL_OK : MFL_E_LAUNCH;
 }

@@ -92,10 +92,15 @@ static_assert(chain_k_perm().ok, "the accumulator must read as the next operand"
 static_assert(chain_runs_of_4(), "pi must keep runs of 4 N1 columns");
 
 // ------------------------------------------------------------------ kernel
-// Workgroup: 4 waves, 256 rows of M (64 per wave, RM = 2 atom rows) x BN
-// columns of N2 (RN = BN / 32 atom columns, N-permuted: repeat j of atom
-// column c is column RN c + j, so D leaves in RN-element vectors).  N1 is consumed in
-// chunks of CW = 32 H columns, H blocks of 32.
+// Workgroup: 256 rows of M x BN columns of N2 (RN = BN / 32 atom columns,
+// N-permuted: repeat j of atom column c is column RN c + j, so D leaves in
+// RN-element vectors).  At K = 64 and 128, 8 waves of 32 rows (RM = 1 atom
+// row), two per SIMD, so one wave's own issue work (fetch instructions,
+// fragment reads, the S -> P conversion, waits) runs under the other's
+// MFMAs; otherwise 4 waves of 64 rows (RM = 2), where the fetch does not
+// divide over 8 waves (K = 32: a B chunk is 4 KiB) or the registers do not
+// allow two waves (K = 256).  N1 is consumed in chunks of CW = 32 H columns,
+// H blocks of 32.
 //
 // Where pi goes: LDS row 32 h + r of a B chunk holds N1 row 32 h + pi^-1(r)
 // of it, so the first product's accumulator value at atom row r of block h
@@ -117,7 +122,10 @@ static_assert(chain_runs_of_4(), "pi must keep runs of 4 N1 columns");
 // otherwise through registers with zero fill, slot c+2 loaded after the
 // barrier of iteration c and written to LDS before that of iteration c+1.
 namespace chain {
-constexpr int BM = 256, RM = 2, WAVES = 4, THREADS = 256, NST = 4;
+constexpr int BM = 256, NST = 4;
+// waves per workgroup (two per SIMD at K = 64 and 128) and threads
+MFL_HD constexpr int waves(int kd) { return kd == 64 || kd == 128 ? 8 : 4; }
+MFL_HD constexpr int threads(int kd) { return 64 * waves(kd); }
 // N2 columns per workgroup: 128 (RN = 4 atom columns per wave), 64 when N2
 // fits in it (RN = 2: no MFMAs on columns past N2)
 MFL_HD constexpr int tile_n(int64_t n2) { return n2 <= 64 ? 64 : 128; }
@@ -197,14 +205,18 @@ __device__ __forceinline__ void wait_vm() {
 // Phase stamps of the timed probe instance: per wave, kStampIters x 4
 // shader-clock readings (iteration c: 4c + 0 at its start, + 1 before the
 // wait for the next slot's fetch, + 2 before the barrier, + 3 after it), then
-// 3 more (kernel start, after the loop, after the epilogue).
+// 3 more (kernel start, after the loop, after the epilogue); kStampWaves per
+// workgroup.
 namespace chain {
-constexpr int kStampIters = 64, kStampsPerWave = 4 * kStampIters + 4, kStampBlocks = 8;
+constexpr int kStampIters = 64, kStampsPerWave = 4 * kStampIters + 4, kStampBlocks = 8,
+              kStampWaves = 8;
 }
 
 template <int KD, int DK, bool DMA, int BN, bool TIMED = false>
-__global__ void __launch_bounds__(chain::THREADS, 1) gemm_chain(const ChainParams p) {
+__global__ void __launch_bounds__(chain::threads(KD), 1) gemm_chain(const ChainParams p) {
   using namespace chain;
+  constexpr int WAVES = waves(KD), THREADS = threads(KD), RM = BM / WAVES / 32;
+  static_assert(!TIMED || WAVES <= kStampWaves, "stamp slots for every wave");
   static_assert(KD == 32 || KD == 64 || KD == 128 || KD == 256, "K is 32, 64, 128 or 256");
   static_assert(BN == 64 || BN == 128, "N2 tiles of 64 or 128 columns");
   constexpr int RN = BN / 32;
@@ -259,12 +271,12 @@ __global__ void __launch_bounds__(chain::THREADS, 1) gemm_chain(const ChainParam
   const int nch = (p.N1 + CW - 1) / CW;
 
   // this wave's A rows as the second operand of the first product:
-  // fragment (i, kk) of lane l: row m0 + 64 w + 32 i + l % 32, k = 16 kk + 8 (l / 32)
+  // fragment (i, kk) of lane l: row m0 + 32 RM w + 32 i + l % 32, k = 16 kk + 8 (l / 32)
   const RowK al = atom_ab_coord(lane);
   half8 af[RM][KSUB];
 #pragma unroll
   for (int i = 0; i < RM; ++i) {
-    const int m = min(m0 + 64 * w + 32 * i + al.row, p.M - 1);
+    const int m = min(m0 + 32 * RM * w + 32 * i + al.row, p.M - 1);
 #pragma unroll
     for (int kk = 0; kk < KSUB; ++kk) {
       const uint4 u = load16(A + (int64_t)m * p.lda + 16 * kk + al.k);
@@ -591,14 +603,14 @@ __global__ void __launch_bounds__(chain::THREADS, 1) gemm_chain(const ChainParam
   }
   const unsigned t_loop = now();
 
-  // epilogue: acc[i][j][v] of lane l is D(m0 + 64 w + 32 i + atom_c(l, v).row,
+  // epilogue: acc[i][j][v] of lane l is D(m0 + 32 RM w + 32 i + atom_c(l, v).row,
   // n0 + 4 (l % 32) + j): one 4-element vector per (i, v)
   const RowK cl = atom_c_coord(lane, 0);
 #pragma unroll
   for (int i = 0; i < RM; ++i)
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int m = m0 + 64 * w + 32 * i + atom_c_coord(lane, v).row;
+      const int m = m0 + 32 * RM * w + 32 * i + atom_c_coord(lane, v).row;
       const int n = n0 + RN * cl.k;
       if (m >= p.M) continue;
       float x[RN];
@@ -633,7 +645,7 @@ __global__ void __launch_bounds__(chain::THREADS, 1) gemm_chain(const ChainParam
   if constexpr (TIMED) {
     const unsigned t_end = now();
     if (blockIdx.x < kStampBlocks) {
-      unsigned* out = p.stamps + (blockIdx.x * WAVES + w) * kStampsPerWave;
+      unsigned* out = p.stamps + (blockIdx.x * kStampWaves + w) * kStampsPerWave;
       if (lane < kStampIters)
 #pragma unroll
         for (int k = 0; k < 4; ++k) out[4 * lane + k] = tv[k];

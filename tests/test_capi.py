@@ -238,7 +238,7 @@ def test_chain_phase_probe_arguments():
     assert probe(N1=250) == mfl.ERR["UNSUPPORTED"]                 # register staging
     assert probe(N2=64, ldd=64, sd=100 * 64, sw=64 * 256) == mfl.ERR["UNSUPPORTED"]
     assert probe(M=-1) == mfl.ERR["NEGATIVE_DIM"]
-    assert mfl.CHAIN_STAMP_SHAPE == (8, 4, 4 * 64 + 4)
+    assert mfl.CHAIN_STAMP_SHAPE == (8, 8, 4 * 64 + 4)
 
 def test_chain_perm_is_derived_from_the_atoms():
     """The map behind the kernel's B row order: position p = 16 kc + 8 h + v
