@@ -269,6 +269,47 @@ def measure_and_report(step, stream, args, flops, metric, config, traffic, sourc
     return 0
 
 
+def ramp_report(step, stream, n: int, what: str) -> int:
+    """The first n launches of this process, each timed by its own event pair
+    and followed by a short full-chip MFMA kernel that reads the shader clock
+    (cycle counter against the real-time counter, per workgroup): how launch
+    time and clock move from the start of the load.  Prints one JSON line of
+    per-bucket means instead of the metric line."""
+    import numpy as np
+    import torch
+
+    import mma_fragment_layouts_tn_amd as mfl
+    dev = stream.device
+    nwg, n_ops = 256, 1 << 20
+    rng = np.random.default_rng(11)
+    ops = torch.from_numpy(rng.uniform(-1.0, 1.0, n_ops).astype(np.float16)).to(dev)
+    sink = torch.empty(nwg * 256, dtype=torch.float32, device=dev)
+    clk = torch.zeros((n, 4 * nwg), dtype=torch.int64, device=dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n)]
+    torch.cuda.synchronize()
+    for i in range(n):
+        ev[2 * i].record(stream)
+        step()
+        ev[2 * i + 1].record(stream)
+        r = mfl.bench_mfma_raw(1, ops.data_ptr(), n_ops, 4, nwg, sink.data_ptr(),
+                               clk[i].data_ptr(), stream.cuda_stream)
+        if r != 0:
+            raise RuntimeError(mfl.strerror(r))
+    torch.cuda.synchronize()
+    t = np.array([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(n)])
+    c = clk.view(n, nwg, 4).cpu().numpy().astype(np.float64)
+    mhz = np.median((c[:, :, 2] - c[:, :, 0]) / (c[:, :, 3] - c[:, :, 1]), axis=1) * \
+        mfl.wall_clock_khz() / 1e3
+    edges = [e for e in (0, 1, 2, 5, 10, 25, 50, 100, 150, 200, 300, 500, 1000, 2000) if e < n] + [n]
+    rows = [{"launches": f"{a}-{b - 1}", "ms": round(float(t[a:b].mean()), 4),
+             "sclk_mhz": round(float(mhz[a:b].mean()))} for a, b in zip(edges, edges[1:])]
+    print(json.dumps({"ramp": what, "launches": n, "buckets": rows,
+                      "how": "event pair per launch; shader clock from a 4-iteration "
+                             "v_mfma_f32_16x16x32_f16 kernel on 256 workgroups after each "
+                             "launch"}), flush=True)
+    return 0
+
+
 MICRO_WORKLOADS = {
     "mfma_rate_32x32x16": ("mfma", 0, "v_mfma_f32_32x32x16_f16"),
     "mfma_rate_16x16x32": ("mfma", 1, "v_mfma_f32_16x16x32_f16"),
@@ -350,6 +391,8 @@ def main_micro(args) -> int:
     print(f"[bench] {args.workload} ({instr}, data {args.data if kind == 'mfma' else '-'}) "
           f"{nwg} workgroups x {threads} threads, {iters} iterations; warmup={args.warmup} "
           f"steps={args.steps}", file=sys.stderr, flush=True)
+    if args.ramp:
+        return ramp_report(step, stream, args.ramp, args.workload)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -523,9 +566,9 @@ def main_chain(args) -> int:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    # From idle the chip needs ~1000 back-to-back launches (~0.1 s at 4096^3)
-    # before the clock settles under the power limit; the defaults warm up
-    # well past that and time steady state.
+    # A few milliseconds into the load the power controller pulls the shader
+    # clock down (launches 10-50 at 4096^3) before it settles (--ramp shows
+    # it); the defaults warm up well past that and time steady state.
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--workload", default="lds_4096")
@@ -553,6 +596,9 @@ def main() -> int:
     ap.add_argument("--phases", action="store_true",
                     help="back-to-back GEMM: also report cycles per loop phase from the timed "
                          "kernel instance")
+    ap.add_argument("--ramp", type=int, default=0,
+                    help="print launch time and shader clock of the first N launches of this "
+                         "process (GEMM and MFMA-rate workloads) instead of the metric line")
     ap.add_argument("--iters", type=int, default=0,
                     help="loop iterations of the microbenchmark kernels (0 = default)")
     args = ap.parse_args()
@@ -621,6 +667,8 @@ def main() -> int:
                            mfl.FETCH_NAMES[fetch_b])
     metric = METRIC if (w.M, w.N, w.K) == (4096, 4096, 4096) else (
         f"TFLOP/s for fp16 TN GEMM at {w.M}x{w.N}x{w.K} (fp32 acc) and % of dense FP16 MFMA peak")
+    if args.ramp:
+        return ramp_report(step, stream, args.ramp, f"{w.name} algo={algo_name}")
     return measure_and_report(step, stream, args, float(w.flops), metric, config, traffic,
                               kernel_source_hash(), lambda: cpu_baseline(w, x, args.cpu_seconds))
 

@@ -28,4 +28,4 @@ def test_more_than_one_gpu_is_refused(args, env):
 def test_help_lists_the_workload_flag():
     r = _run(["--help"])
     assert r.returncode == 0
-    assert "--workload" in r.stdout and "--gpus" in r.stdout
+    assert "--workload" in r.stdout and "--gpus" in r.stdout and "--ramp" in r.stdout
