@@ -148,10 +148,16 @@ __device__ __forceinline__ float c_value(const GemmParams& p, int m, int n) {
   return 0.0f;
 }
 
-// Stores of D are non-temporal (the `nt` cache policy): D is written once
-// and never read back by the kernel, and leaving it out of the L2s shortens
-// the write-back at the end of the kernel (about 1 % at 4096^3).
-constexpr int kNtStore = 2;   // cache-policy operand of the buffer-store builtins: nt
+// The `nt` cache policy (non-temporal) on data the kernel touches once:
+// the stores of D, which leaves D out of the L2s and shortens the write-back
+// at the end of the kernel (about 1 % at 4096^3), and the C rows fetched
+// straight into LDS (whole 1 KB runs per instruction), which leaves the L2s
+// to the operand tiles that other workgroups read again (8192^2 x 2048 with
+// an fp32 C: 4-5 % faster).  Per-lane C vectors keep the default policy:
+// there a cache line is shared by neighbouring instructions, and with nt the
+// aligned fp16 C case ran 3.5 % slower, the ragged one 9 %.  A and B keep it
+// too: with nt on their fetch the 4096^3 kernel takes 121 us against 101.
+constexpr int kNt = 2;   // cache-policy operand of the buffer and direct-to-LDS builtins: nt
 
 template <int DK>
 __device__ __forceinline__ void d_store(const GemmParams& p, int m, int n, float x) {
@@ -192,7 +198,7 @@ __device__ __forceinline__ float half_hi(unsigned u) {
   return (float)__builtin_bit_cast(_Float16, (unsigned short)(u >> 16));
 }
 
-// RN values -> one D vector through a buffer descriptor (kNtStore: D is
+// RN values -> one D vector through a buffer descriptor (kNt: D is
 // written once and not read back by this kernel)
 template <int DK, int RN>
 __device__ __forceinline__ void buffer_store_d(const float (&x)[RN], __amdgpu_buffer_rsrc_t r,
@@ -201,15 +207,15 @@ __device__ __forceinline__ void buffer_store_d(const float (&x)[RN], __amdgpu_bu
   if constexpr (DK == 2 && RN == 4) {
     const u32x4 d = {__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]),
                      __float_as_uint(x[3])};
-    __builtin_amdgcn_raw_buffer_store_b128(d, r, voff, soff, kNtStore);
+    __builtin_amdgcn_raw_buffer_store_b128(d, r, voff, soff, kNt);
   } else if constexpr (DK == 2) {
     const u32x2 d = {__float_as_uint(x[0]), __float_as_uint(x[1])};
-    __builtin_amdgcn_raw_buffer_store_b64(d, r, voff, soff, kNtStore);
+    __builtin_amdgcn_raw_buffer_store_b64(d, r, voff, soff, kNt);
   } else if constexpr (RN == 4) {
     const u32x2 d = {pack_half2(x[0], x[1]), pack_half2(x[2], x[3])};
-    __builtin_amdgcn_raw_buffer_store_b64(d, r, voff, soff, kNtStore);
+    __builtin_amdgcn_raw_buffer_store_b64(d, r, voff, soff, kNt);
   } else {
-    __builtin_amdgcn_raw_buffer_store_b32(pack_half2(x[0], x[1]), r, voff, soff, kNtStore);
+    __builtin_amdgcn_raw_buffer_store_b32(pack_half2(x[0], x[1]), r, voff, soff, kNt);
   }
 }
 
@@ -420,7 +426,7 @@ __device__ __forceinline__ void epilogue_c_lds(const GemmParams& p, _Float16* sm
         const int row = run * X::RPI + lane / (BN / 4), col = 4 * (lane % (BN / 4));
         const float* src = C + (int64_t)(m0 + band * X::CR + row) * p.ldc + n0 + col;
         __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr_t)((char*)cs + run * 1024),
-                                         16, 0, 0);
+                                         16, 0, kNt);
       }
       wait_vm_lds<0>();
     }
